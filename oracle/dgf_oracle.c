@@ -1,0 +1,414 @@
+/*
+ * CPU oracle for the deterministic gated FFN.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the benchmark's
+ * CPU-baseline leg load this library; the product path never links, calls or
+ * falls back to it.  It shares no code, header, table or helper with the HIP
+ * library.  It is deliberately plain and slow: one output element is computed
+ * by one thread, leaf by leaf, node by node, in the order the method defines.
+ *
+ * Method (RL-Kernel PR #325 "feat(ffn): add deterministic distributed Triton FFN
+ * for ROCm", section "Design"): the bias-free gated Qwen3 FFN
+ *     y = W_down . (silu(W_gate . x) * (W_up . x)),   weights in [out, in] layout
+ * (section "Operator test matrix"), with every K-reduction evaluated by one
+ * canonical tree: FP32 leaves rounded to BF16, and midpoint-split internal
+ * nodes that add two BF16 children in FP32 and round to BF16; BF16 stage
+ * boundaries are kept in forward and backward.  In backward the gate and up
+ * contributions to dHidden stay separate until a final ordered addition, gate
+ * first (section "Communication overlap assessment").
+ *
+ * Readings taken where the pages are silent (each is also listed in the design doc):
+ *  - leaf width 64 contiguous K elements; the last leaf holds the K tail;
+ *  - midpoint split mid = lo + floor((hi-lo)/2), so 3 leaves = L0 + (L1 + L2);
+ *  - all roundings are round-to-nearest-even, denormals kept (no flush);
+ *  - the order of FP32 accumulation inside a leaf is the matrix-core block rule
+ *    of oracle_block_step() below: the leaf consumes its K elements in
+ *    ascending blocks of 8, each block adding its 8 exact products to the FP32
+ *    running value with one rounding (parity of this choice is unpinned by the
+ *    pages; it is pinned by hand-worked cases in the tests);
+ *  - silu(g) = g * sigma(g), sigma(g) = 1 / (1 + e), e = exp(-g) correctly
+ *    rounded to FP32, each FP32 operation rounded separately (no contraction);
+ *    the activation is rounded to BF16 once: a = bf16(fl32(silu(g) * u)).
+ *
+ * Build: gcc -O2 -std=c11 -fopenmp -ffp-contract=off -fPIC -shared (no fast-math).
+ */
+#include <stdint.h>
+#include <stddef.h>
+#include <string.h>
+#include <math.h>
+
+typedef uint16_t bf16_t;
+
+/* ---------------------------------------------------------------- BF16 <-> FP32 */
+
+static float bf16_to_f32(bf16_t h)
+{
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+/* Round-to-nearest-even FP32 -> BF16: add 0x7FFF plus the lowest kept bit, then
+ * drop the low 16 bits (a carry into the exponent is the correct rounding up). */
+static bf16_t f32_to_bf16(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu))
+        return (bf16_t)((u >> 16) | 0x0040u); /* quiet NaN */
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (bf16_t)(u >> 16);
+}
+
+/* One node of the tree: two BF16 children added in FP32, rounded to BF16. */
+static bf16_t node_add(bf16_t l, bf16_t r)
+{
+    float s = bf16_to_f32(l) + bf16_to_f32(r);
+    return f32_to_bf16(s);
+}
+
+/* ------------------------------------------------------------ exact integer tools */
+
+typedef __int128 i128;
+
+static int bitlen_u128(unsigned __int128 v)
+{
+    int n = 0;
+    while (v) { v >>= 1; ++n; }
+    return n;
+}
+
+/* floor(v / 2^s) for s >= 0 (toward minus infinity). */
+static i128 floor_shift(i128 v, int s)
+{
+    if (s <= 0) return v;
+    if (s >= 126) return v < 0 ? -1 : 0;
+    i128 d = (i128)1 << s;
+    i128 q = v / d;              /* truncates toward zero */
+    if (v < 0 && q * d != v) q -= 1;
+    return q;
+}
+
+/* trunc(v / 2^s) for s >= 0 (toward zero). */
+static int64_t trunc_shift(int64_t v, int s)
+{
+    if (s <= 0) return v;
+    if (s >= 63) return 0;
+    int64_t m = v < 0 ? -v : v;
+    m >>= s;
+    return v < 0 ? -m : m;
+}
+
+/* Round the exact value v * 2^e (v a signed integer, |v| < 2^100) to the
+ * nearest FP32, ties to even, with gradual underflow and overflow to infinity. */
+static float round_to_f32(i128 v, int e)
+{
+    if (v == 0) return 0.0f;
+    int neg = v < 0;
+    unsigned __int128 m = neg ? (unsigned __int128)(-v) : (unsigned __int128)v;
+    int lead = bitlen_u128(m) - 1 + e;           /* exponent of the leading bit */
+    int q = lead - 23;                           /* exponent of the FP32 ulp */
+    if (q < -149) q = -149;
+    int s = q - e;                               /* bits to drop */
+    if (s > 0) {
+        if (s > 101) {
+            m = 0;                               /* m < 2^100 < half an ulp */
+        } else {
+            unsigned __int128 hi = m >> s;
+            unsigned __int128 rem = m - (hi << s);
+            unsigned __int128 half = (unsigned __int128)1 << (s - 1);
+            if (rem > half || (rem == half && (hi & 1))) hi += 1;
+            m = hi;
+        }
+        e = q;
+    }
+    /* m * 2^e is now exactly representable unless it overflowed */
+    double d = ldexp((double)m, e);               /* m < 2^25: exact in double */
+    if (d >= 3.4028235677973366e38) return neg ? -INFINITY : INFINITY;
+    float f = (float)d;                          /* exact */
+    return neg ? -f : f;
+}
+
+/* ------------------------------------------------------------ the FP32 leaf */
+
+/* Split a finite BF16 into signed integer significand and exponent so that
+ * value = sig * 2^(ex - 7); zero returns 0.  Denormals use ex = -126. */
+static int bf16_split(bf16_t h, int32_t *sig, int *ex)
+{
+    int be = (h >> 7) & 0xFF;
+    int32_t m = h & 0x7F;
+    if (be == 0 && m == 0) return 0;
+    if (be == 0) *ex = -126;
+    else { *ex = be - 127; m |= 0x80; }
+    *sig = (h & 0x8000) ? -m : m;
+    return 1;
+}
+
+/* Split a finite FP32 so that value = sig * 2^(ex - 23); zero returns 0. */
+static int f32_split(float f, int64_t *sig, int *ex)
+{
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    int be = (u >> 23) & 0xFF;
+    int64_t m = u & 0x7FFFFF;
+    if (be == 0 && m == 0) return 0;
+    if (be == 0) *ex = -126;
+    else { *ex = be - 127; m |= 0x800000; }
+    *sig = (u & 0x80000000u) ? -m : m;
+    return 1;
+}
+
+/*
+ * One block step of the FP32 leaf: acc + (a[0]*b[0] + ... + a[n-1]*b[n-1]),
+ * n <= 8, evaluated with the matrix-core alignment rule:
+ *   1. every product a_k*b_k is exact; its nominal exponent is ea+eb;
+ *   2. the block's grid is 2^(E-24), E the largest nominal exponent among the
+ *      nonzero products (a block of zero products leaves acc unchanged);
+ *   3. each product is cut to the grid toward zero, the accumulator is cut to
+ *      the grid toward minus infinity;
+ *   4. the exact sum T of the cut terms is cut toward minus infinity to 8 bits
+ *      below its own FP32 ulp (never finer than 2^-157);
+ *   5. that value is rounded to FP32, nearest even.
+ */
+float oracle_block_step(float acc, const bf16_t *a, ptrdiff_t sa,
+                        const bf16_t *b, ptrdiff_t sb, int n)
+{
+    int32_t psig[8];
+    int pexp[8], nz[8];
+    int emax = -100000, any = 0;
+    for (int k = 0; k < n; ++k) {
+        int32_t sa_, sb_;
+        int ea, eb;
+        nz[k] = bf16_split(a[k * sa], &sa_, &ea) & bf16_split(b[k * sb], &sb_, &eb);
+        if (!nz[k]) continue;
+        psig[k] = sa_ * sb_;                    /* |psig| < 2^16 */
+        pexp[k] = ea + eb;                      /* product = psig * 2^(pexp-14) */
+        if (pexp[k] > emax) emax = pexp[k];
+        any = 1;
+    }
+    if (!any) return acc;
+    const int grid = emax - 24;                 /* grid exponent */
+
+    int64_t sp = 0;                             /* products, in grid units */
+    for (int k = 0; k < n; ++k) {
+        if (!nz[k]) continue;
+        int sh = (pexp[k] - 14) - grid;         /* = 10 - (emax - pexp) */
+        if (sh >= 0) sp += (int64_t)psig[k] << sh;
+        else sp += trunc_shift(psig[k], -sh);
+    }
+
+    int64_t csig;
+    int cex;
+    i128 t;
+    if (f32_split(acc, &csig, &cex)) {
+        int sh = (cex - 23) - grid;
+        if (sh > 64) {
+            /* The accumulator dominates: |sp| < 2^29 while the cut in step 4 is
+             * at least 2^(sh-9) grid units, so steps 4-5 return acc itself. */
+            return acc;
+        }
+        i128 ct = sh >= 0 ? ((i128)csig << sh) : floor_shift((i128)csig, -sh);
+        t = ct + (i128)sp;
+    } else {
+        t = (i128)sp;
+    }
+    if (t == 0) return 0.0f;
+
+    /* step 4: cut toward minus infinity to 8 bits below the FP32 ulp of T */
+    unsigned __int128 mag = t < 0 ? (unsigned __int128)(-t) : (unsigned __int128)t;
+    int lead = bitlen_u128(mag) - 1 + grid;
+    int cut = lead - 31;
+    if (cut < -157) cut = -157;
+    int e = grid;
+    if (cut > e) {
+        t = floor_shift(t, cut - e);
+        e = cut;
+    }
+    return round_to_f32(t, e);
+}
+
+/* The FP32 leaf over n <= 64 consecutive K elements: ascending blocks of 8
+ * starting from an accumulator of +0. */
+static float leaf_f32(const bf16_t *a, ptrdiff_t sa, const bf16_t *b, ptrdiff_t sb, int64_t n)
+{
+    float acc = 0.0f;
+    for (int64_t k = 0; k < n; k += 8) {
+        int w = (int)(n - k < 8 ? n - k : 8);
+        acc = oracle_block_step(acc, a + k * sa, sa, b + k * sb, sb, w);
+    }
+    return acc;
+}
+
+float oracle_leaf_f32(const bf16_t *a, ptrdiff_t sa, const bf16_t *b, ptrdiff_t sb, int64_t n)
+{
+    return leaf_f32(a, sa, b, sb, n);
+}
+
+/* ------------------------------------------------------------ the tree */
+
+enum { LEAF = 64 };
+
+/* T(lo, hi) over leaves [lo, hi): a single leaf is the BF16-rounded FP32 leaf;
+ * otherwise split at mid = lo + floor((hi - lo) / 2) and add the two BF16
+ * children in FP32, rounding to BF16. */
+static bf16_t tree(const bf16_t *a, ptrdiff_t sa, const bf16_t *b, ptrdiff_t sb,
+                   int64_t K, int64_t lo, int64_t hi)
+{
+    if (hi - lo == 1) {
+        int64_t k0 = lo * LEAF;
+        int64_t n = K - k0 < LEAF ? K - k0 : LEAF;
+        return f32_to_bf16(leaf_f32(a + k0 * sa, sa, b + k0 * sb, sb, n));
+    }
+    int64_t mid = lo + (hi - lo) / 2;
+    bf16_t l = tree(a, sa, b, sb, K, lo, mid);
+    bf16_t r = tree(a, sa, b, sb, K, mid, hi);
+    return node_add(l, r);
+}
+
+/* One output element: the canonical tree over K of a[k*sa] * b[k*sb].
+ * K = 0 gives +0. */
+bf16_t oracle_dot_tree(const bf16_t *a, ptrdiff_t sa, const bf16_t *b, ptrdiff_t sb, int64_t K)
+{
+    if (K <= 0) return 0;
+    int64_t L = (K + LEAF - 1) / LEAF;
+    return tree(a, sa, b, sb, K, 0, L);
+}
+
+/* The tree over the leaves [leaf_lo, leaf_hi) of a length-K reduction: the
+ * partial a contiguous K shard contributes (a subtree when the shard is one). */
+bf16_t oracle_dot_subtree(const bf16_t *a, ptrdiff_t sa, const bf16_t *b, ptrdiff_t sb,
+                          int64_t K, int64_t leaf_lo, int64_t leaf_hi)
+{
+    return tree(a, sa, b, sb, K, leaf_lo, leaf_hi);
+}
+
+/* C[m*ldc + n] = T_K( sum_k A[m*sam + k*sak] * B[k*sbk + n*sbn] ). */
+void oracle_gemm_tree(const bf16_t *A, int64_t sam, int64_t sak,
+                      const bf16_t *B, int64_t sbk, int64_t sbn,
+                      bf16_t *C, int64_t ldc, int64_t M, int64_t N, int64_t K)
+{
+#pragma omp parallel for collapse(2) schedule(dynamic, 64)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n)
+            C[m * ldc + n] = oracle_dot_tree(A + m * sam, sak, B + n * sbn, sbk, K);
+}
+
+/* The fixed balanced combine over S in {1,2,4,8} parts, in rank order:
+ * ((p0+p1)+(p2+p3))+((p4+p5)+(p6+p7)), every node BF16-rounded; this is the
+ * midpoint tree over the parts (PR #357 "Design"; PR #356 "Design"). */
+static bf16_t combine_range(const bf16_t *const *parts, int64_t i, int lo, int hi)
+{
+    if (hi - lo == 1) return parts[lo][i];
+    int mid = lo + (hi - lo) / 2;
+    return node_add(combine_range(parts, i, lo, mid), combine_range(parts, i, mid, hi));
+}
+
+int oracle_tree_combine(const bf16_t *const *parts, int S, bf16_t *out, int64_t n)
+{
+    if (!(S == 1 || S == 2 || S == 4 || S == 8)) return 2;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) out[i] = combine_range(parts, i, 0, S);
+    return 0;
+}
+
+/* ------------------------------------------------------------ activation */
+
+/* e = exp(-g) rounded once to FP32 (computed in double, then rounded). */
+static float exp_neg_f32(float g)
+{
+    return (float)exp(-(double)g);
+}
+
+float oracle_sigma(float g)
+{
+    float e = exp_neg_f32(g);
+    float den = 1.0f + e;
+    return 1.0f / den;
+}
+
+float oracle_silu(float g)
+{
+    float sg = oracle_sigma(g);
+    return g * sg;
+}
+
+/* silu'(g) = sigma * (1 + g * (1 - sigma)), FP32 step by step. */
+float oracle_dsilu(float g)
+{
+    float sg = oracle_sigma(g);
+    float one_m = 1.0f - sg;
+    float t = g * one_m;
+    float onep = 1.0f + t;
+    return sg * onep;
+}
+
+/* a = bf16(silu(g) * u), one BF16 rounding. */
+void oracle_act_fwd(const bf16_t *g, const bf16_t *u, bf16_t *a, int64_t n)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) {
+        float s = oracle_silu(bf16_to_f32(g[i]));
+        a[i] = f32_to_bf16(s * bf16_to_f32(u[i]));
+    }
+}
+
+/* dU = bf16(dA * silu(g)), dG = bf16((dA * u) * silu'(g)); a is recomputed. */
+void oracle_act_bwd(const bf16_t *da, const bf16_t *g, const bf16_t *u,
+                    bf16_t *dg, bf16_t *du, bf16_t *a, int64_t n)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) {
+        float gv = bf16_to_f32(g[i]), uv = bf16_to_f32(u[i]), dav = bf16_to_f32(da[i]);
+        float s = oracle_silu(gv);
+        float ds = oracle_dsilu(gv);
+        du[i] = f32_to_bf16(dav * s);
+        float dau = dav * uv;
+        dg[i] = f32_to_bf16(dau * ds);
+        if (a) a[i] = f32_to_bf16(s * uv);
+    }
+}
+
+/* ------------------------------------------------------------ the FFN */
+
+/* Forward: g = T_H(x W_gate^T), u = T_H(x W_up^T), a = bf16(silu(g) u),
+ * y = T_I(a W_down^T).  Row-major, contiguous: x [M,H], W_gate/W_up [I,H],
+ * W_down [H,I]; g, u, a [M,I]; y [M,H]. */
+void oracle_ffn_fwd(const bf16_t *x, const bf16_t *wg, const bf16_t *wu, const bf16_t *wd,
+                    bf16_t *g, bf16_t *u, bf16_t *a, bf16_t *y,
+                    int64_t M, int64_t H, int64_t I)
+{
+    oracle_gemm_tree(x, H, 1, wg, 1, H, g, I, M, I, H);
+    oracle_gemm_tree(x, H, 1, wu, 1, H, u, I, M, I, H);
+    oracle_act_fwd(g, u, a, M * I);
+    oracle_gemm_tree(a, I, 1, wd, 1, I, y, H, M, H, I);
+}
+
+/* Backward from dY [M,H] and the saved g, u:
+ *   dA = T_H(dY W_down)                 (K = H, over the rows of W_down)
+ *   dU = bf16(dA silu(g)), dG = bf16(dA u silu'(g)), a recomputed
+ *   G  = T_I(dG W_gate), U = T_I(dU W_up),  dX = bf16(G + U)  (gate first)
+ *   dW_gate = T_M(dG^T x), dW_up = T_M(dU^T x), dW_down = T_M(dY^T a). */
+void oracle_ffn_bwd(const bf16_t *dy, const bf16_t *x, const bf16_t *g, const bf16_t *u,
+                    const bf16_t *wg, const bf16_t *wu, const bf16_t *wd,
+                    bf16_t *da, bf16_t *dg, bf16_t *du, bf16_t *a,
+                    bf16_t *gl, bf16_t *ul, bf16_t *dx,
+                    bf16_t *dwg, bf16_t *dwu, bf16_t *dwd,
+                    int64_t M, int64_t H, int64_t I)
+{
+    oracle_gemm_tree(dy, H, 1, wd, I, 1, da, I, M, I, H);
+    oracle_act_bwd(da, g, u, dg, du, a, M * I);
+    oracle_gemm_tree(dg, I, 1, wg, H, 1, gl, H, M, H, I);
+    oracle_gemm_tree(du, I, 1, wu, H, 1, ul, H, M, H, I);
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < M * H; ++i) {
+        bf16_t acc = gl[i];              /* gate contribution first */
+        acc = node_add(acc, ul[i]);      /* then the up contribution */
+        dx[i] = acc;
+    }
+    oracle_gemm_tree(dg, 1, I, x, H, 1, dwg, H, I, H, M);
+    oracle_gemm_tree(du, 1, I, x, H, 1, dwu, H, I, H, M);
+    oracle_gemm_tree(dy, 1, H, a, I, 1, dwd, I, H, I, M);
+}
+
+int oracle_leaf_size(void) { return LEAF; }
