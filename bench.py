@@ -1,0 +1,230 @@
+"""Benchmark of the deterministic gated FFN on one MI355X.
+
+A step is one pass of the whole hot path over one batch: the training forward
+(gate/up tree GEMM with the fused activation, down tree GEMM) and the backward
+(dA with dsilu, the two dX lanes and their ordered add, the dW tree GEMMs) at
+M=32 tokens, H=4096, I=12288 (the Qwen3-8B FFN shape), BF16, synthetic seeded
+inputs already resident in HBM.  Weights rotate over three resident copies so
+every step reads them from HBM rather than from the 256 MB last-level cache.
+
+Prints one JSON line.  `value` is the step's algorithmic HBM throughput
+(bytes that must cross HBM once per step / step time).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+METRIC = "FFN fwd & fwd+bwd µs + HBM GB/s, H=4096 I=12288 BF16 M=1/8/32"
+H, I = 4096, 12288
+BF = 2
+
+
+def step_bytes(M: int) -> int:
+    """Algorithmic HBM bytes of a training fwd+bwd step: weights read twice, dW
+    written, g/u saved and reloaded, x read twice, y and dX written, dY read."""
+    w = 3 * H * I * BF
+    return 2 * w + w + 2 * 2 * M * I * BF + 5 * M * H * BF
+
+
+def fwd_bytes(M: int) -> int:
+    return 3 * H * I * BF + 2 * M * H * BF
+
+
+def kernel_bytes(name: str, M: int) -> int | None:
+    """Algorithmic bytes of one launch (inputs read once, outputs written once)."""
+    W = H * I * BF
+    act_mi, act_mh = M * I * BF, M * H * BF
+    table = {
+        "gate/up tree GEMM": 2 * W + act_mh + act_mi + 2 * act_mi,   # W_gate, W_up, x -> a, g, u
+        "down tree GEMM": W + act_mi + act_mh,                        # W_down, a -> y
+        "transpose x": 2 * act_mh,
+        "transpose dY": 2 * act_mh,
+        "dA tree GEMM": W + act_mh + 2 * act_mi + 5 * act_mi,         # W_down, dY, g, u -> dG, dU, dG^T, dU^T, a^T
+        "dX gate-lane tree GEMM": W + act_mi + act_mh,
+        "dX up-lane tree GEMM": W + act_mi + act_mh,
+        "dX ordered add": 3 * act_mh,
+        "dW_gate/dW_up tree GEMM": 2 * W + 2 * act_mi + act_mh,       # dG^T, dU^T, x^T -> dW_gate, dW_up
+        "dW_down tree GEMM": W + act_mh + act_mi,                     # dY^T, a^T -> dW_down
+    }
+    return table.get(name)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--copies", type=int, default=3, help="resident weight copies rotated per step")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--quick", action="store_true", help="skip the forward-only and CPU legs (profiling runs)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE={world}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from deterministic_gated_ffn_amd import binding as dgf
+    from deterministic_gated_ffn_amd import inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    dgf.load()
+    print(f"[bench] device {torch.cuda.get_device_name(0)}; building inputs", file=sys.stderr, flush=True)
+
+    M = 32
+    wg_c, wu_c, wd_c = inputs.ffn_weights()
+    W = [(wg_c.cuda(), wu_c.cuda(), wd_c.cuda())]
+    for _ in range(args.copies - 1):
+        W.append(tuple(t.clone() for t in W[0]))
+    x_c, dy_c = inputs.activations(M)
+    x, dy = x_c.cuda(), dy_c.cuda()
+    torch.cuda.synchronize()
+
+    def step(k):
+        wg, wu, wd = W[k % len(W)]
+        y, g, u = dgf.ffn_fwd(x, wg, wu, wd, training=True)
+        return dgf.ffn_bwd(dy, x, g, u, wg, wu, wd)
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    print("[bench] warmup done", file=sys.stderr, flush=True)
+
+    timer = dgf.KernelTimer(max_kernels=16 * args.steps + 16)
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record()
+    timer.start()
+    for k in range(args.steps):
+        step(k)
+    timer.stop()
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    value = step_bytes(M) / (ms_step * 1e-3) / 1e9
+    print(f"[bench] fwd+bwd M=32: {ms_step * 1e3:.1f} us/step, {value:.0f} GB/s", file=sys.stderr, flush=True)
+
+    # per-kernel durations over the timed region
+    per = {}
+    for name, ms in timer.durations_ms():
+        per.setdefault(name, []).append(ms)
+    kernels = {n: {"launches": len(v), "avg_us": 1e3 * sum(v) / len(v)} for n, v in per.items()}
+    dom = max(per, key=lambda n: sum(per[n]))
+    dom_us = kernels[dom]["avg_us"]
+    dom_bytes = kernel_bytes(dom, M)
+    achieved = dom_bytes / (dom_us * 1e-6) / 1e9 if dom_bytes else None
+    for n, v in kernels.items():
+        b = kernel_bytes(n, M)
+        v["GBps"] = round(b / (v["avg_us"] * 1e-6) / 1e9, 1) if b else None
+        v["avg_us"] = round(v["avg_us"], 2)
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "deterministic gated FFN training step (forward + backward), Qwen3-8B shape, "
+                               "M=32 tokens, H=4096, I=12288, BF16, weights [out,in] N(0,0.02), x and dY N(0,1)",
+                   "M": M, "H": H, "I": I, "weight_copies_rotated": len(W),
+                   "step_algorithmic_bytes": step_bytes(M)},
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1) if achieved else None,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4) if achieved else None,
+                     "bytes_per_launch": dom_bytes, "avg_launch_us": round(dom_us, 2), "traffic": None},
+        "kernels": kernels,
+        "wall_s_timed_region": round(wall, 3),
+    }
+
+    if not args.quick:
+        fwd = {}
+        for Mf in (1, 8, 32):
+            xf = x[:Mf]
+            for k in range(args.warmup):
+                wg, wu, wd = W[k % len(W)]
+                dgf.ffn_fwd(xf, wg, wu, wd)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for k in range(args.steps):
+                wg, wu, wd = W[k % len(W)]
+                dgf.ffn_fwd(xf, wg, wu, wd)
+            e1.record()
+            torch.cuda.synchronize()
+            us = 1e3 * e0.elapsed_time(e1) / args.steps
+            gbps = fwd_bytes(Mf) / (us * 1e-6) / 1e9
+            fwd[str(Mf)] = {"us": round(us, 2), "GBps": round(gbps, 1), "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
+                            "algorithmic_bytes": fwd_bytes(Mf)}
+            print(f"[bench] forward M={Mf}: {us:.1f} us, {gbps:.0f} GB/s", file=sys.stderr, flush=True)
+        result["forward"] = fwd
+        result["fwd_bwd_us"] = round(ms_step * 1e3, 2)
+
+    if not args.no_cpu_baseline and not args.quick:
+        result["cpu_baseline"] = cpu_baseline(M)
+
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(M: int) -> dict:
+    """The CPU oracle on a bounded sample of the same step: the full M=32
+    forward, the full dA and dX, and 1/64 of the dW rows (scaled by 64)."""
+    import numpy as np
+
+    import oracle
+    from deterministic_gated_ffn_amd import inputs
+
+    os.environ.setdefault("OMP_NUM_THREADS", str(len(os.sched_getaffinity(0))))
+    cores = int(os.environ["OMP_NUM_THREADS"])
+    oracle.lib()
+    wg, wu, wd = (inputs.bits(t) for t in inputs.ffn_weights())
+    x, dy = (inputs.bits(t) for t in inputs.activations(M))
+    t0 = time.perf_counter()
+    o = oracle.ffn_fwd(x, wg, wu, wd)
+    t_fwd = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    da = oracle.gemm_tree(dy, wd, "NN")
+    dg, du, a = oracle.act_bwd(da, o["g"], o["u"])
+    G = oracle.gemm_tree(dg, wg, "NN")
+    U = oracle.gemm_tree(du, wu, "NN")
+    oracle.tree_combine([G, U])
+    t_dx = time.perf_counter() - t0
+    frac = 64
+    t0 = time.perf_counter()
+    oracle.gemm_tree(np.ascontiguousarray(dg[:, :I // frac]), x, "TN")
+    oracle.gemm_tree(np.ascontiguousarray(du[:, :I // frac]), x, "TN")
+    oracle.gemm_tree(np.ascontiguousarray(dy[:, :H // frac]), a, "TN")
+    t_dw = (time.perf_counter() - t0) * frac
+    total = t_fwd + t_dx + t_dw
+    return {"value": round(step_bytes(M) / total / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"C oracle (OpenMP, {os.environ.get('OMP_NUM_THREADS')} threads) on the M=32 training step: "
+                      f"full forward ({t_fwd:.1f} s), full dA/dsilu/dX ({t_dx:.1f} s), dW on 1/{frac} of the rows "
+                      f"scaled x{frac} ({t_dw:.1f} s)",
+            "seconds_per_step": round(total, 2), "cpu": platform.processor() or platform.machine(),
+            "os_cpu_count": os.cpu_count()}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,464 @@
+// C ABI of libdgf: argument validation, workspace layout and the launch
+// sequence of the forward and backward passes (declarations in include/dgf.h).
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "dgf.h"
+#include "dgf_kernels.hpp"
+
+using namespace dgf;
+
+namespace {
+
+thread_local std::string g_err;
+
+dgf_status fail(dgf_status st, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+dgf_status ok() {
+  g_err.clear();
+  return DGF_OK;
+}
+
+dgf_status hip_check(hipError_t e, const char *what) {
+  if (e != hipSuccess) return fail(DGF_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return DGF_OK;
+}
+
+// Kernel timing hook: caller-created events recorded around each launch.
+struct Prof {
+  hipEvent_t *ev = nullptr;
+  int pairs = 0;
+  int used = 0;
+  const char *names[256] = {};
+};
+thread_local Prof g_prof;
+
+template <class F>
+hipError_t timed(hipStream_t s, const char *name, F &&launch) {
+  const int k = g_prof.used;
+  const bool rec = g_prof.ev && k < g_prof.pairs;
+  if (rec) {
+    hipError_t e = hipEventRecord(g_prof.ev[2 * k], s);
+    if (e != hipSuccess) return e;
+  }
+  hipError_t e = launch();
+  if (rec && e == hipSuccess) e = hipEventRecord(g_prof.ev[2 * k + 1], s);
+  if (g_prof.ev) {
+    if (k < 256) g_prof.names[k] = name;
+    g_prof.used = k + 1;
+  }
+  return e;
+}
+
+#define DGF_TRY(expr)                  \
+  do {                                 \
+    dgf_status st_ = (expr);           \
+    if (st_ != DGF_OK) return st_;     \
+  } while (0)
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
+
+// A row-major BF16 matrix operand: non-null, 16-byte aligned, ld >= cols, ld % 8 == 0.
+dgf_status check_mat(const char *name, const void *p, int64_t ld, int64_t rows, int64_t cols) {
+  if (rows == 0 || cols == 0) return DGF_OK;
+  if (!p) return fail(DGF_EINVAL, "%s is NULL", name);
+  if (!aligned16(p)) return fail(DGF_EINVAL, "%s is not 16-byte aligned", name);
+  if (ld < cols) return fail(DGF_EINVAL, "%s: leading dimension %lld < row width %lld", name, (long long)ld, (long long)cols);
+  if (ld % 8 != 0) return fail(DGF_EINVAL, "%s: leading dimension %lld is not a multiple of 8", name, (long long)ld);
+  return DGF_OK;
+}
+
+dgf_status check_dims(int64_t M, int64_t N, int64_t K) {
+  if (M < 0 || N < 0 || K < 0) return fail(DGF_EINVAL, "negative dimension (M=%lld N=%lld K=%lld)", (long long)M, (long long)N, (long long)K);
+  if (M > ((int64_t)1 << 21) || N > ((int64_t)1 << 30) || K > ((int64_t)1 << 24))
+    return fail(DGF_EUNSUPPORTED, "dimensions beyond this build's limits (M<=2^21, N<=2^30, K<=2^24)");
+  return DGF_OK;
+}
+
+int64_t round8(int64_t v) { return (v + 7) & ~(int64_t)7; }
+size_t round256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+int leaves(int64_t K) { return (int)((K + 63) / 64); }
+
+// Waves per workgroup: the largest power of two <= min(8, L).
+int pick_waves(int L) {
+  int w = 1;
+  while (w * 2 <= 8 && w * 2 <= L) w *= 2;
+  return w;
+}
+
+// Depth of the midpoint tree over n leaves: ceil(log2 n).
+int tree_depth(int n) {
+  int d = 0;
+  while ((1 << d) < n) ++d;
+  return d;
+}
+
+GemmParams blank() {
+  GemmParams p;
+  memset(&p, 0, sizeof p);
+  return p;
+}
+
+dgf_status run_gemm(int layout, int nb, int epi, GemmParams p, hipStream_t s, const char *what) {
+  if (p.M == 0 || p.N == 0) return DGF_OK;
+  if ((p.M + 31) / 32 > 65535 || (p.N + 15) / 16 > 0x7fffffff)
+    return fail(DGF_EUNSUPPORTED, "%s: %lld x %lld output exceeds the launch grid", what, (long long)p.M, (long long)p.N);
+  p.L = leaves(p.K);
+  const int waves = pick_waves(p.L);
+  // LDS tree stack: one slot per level of the deepest wave subtree
+  const int per_wave = (p.L + waves - 1) / waves;
+  p.stack_slots = tree_depth(per_wave) > 1 ? tree_depth(per_wave) : 1;
+  const int mt = p.M <= 16 ? 1 : 2;
+  const size_t lds_bytes = (size_t)waves * p.stack_slots * (nb * mt * 2) * 64 * 4 +
+                           (layout == DGF_LAYOUT_NN ? (size_t)waves * nb * 16 * 72 * 2 : 0);
+  if (lds_bytes > 64 * 1024)
+    return fail(DGF_EUNSUPPORTED, "%s: K=%lld needs %zu bytes of LDS for the tree stack", what, (long long)p.K, lds_bytes);
+  return hip_check(timed(s, what, [&] { return launch_gemm(layout, nb, epi, p, waves, s); }), what);
+}
+
+// Zero-fill an [M, N] output (K = 0 products).
+__global__ void k_zero2d(uint16_t *C, int64_t ldc, int64_t M, int64_t N) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < M * N; i += (int64_t)gridDim.x * blockDim.x)
+    C[(i / N) * ldc + (i % N)] = 0;
+}
+
+dgf_status zero_mat(uint16_t *C, int64_t ldc, int64_t M, int64_t N, hipStream_t s) {
+  if (M == 0 || N == 0) return DGF_OK;
+  int64_t blocks = (M * N + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  return hip_check(timed(s, "zero fill", [&] {
+                     hipLaunchKernelGGL(k_zero2d, dim3((unsigned)blocks), dim3(256), 0, s, C, ldc, M, N);
+                     return hipGetLastError();
+                   }),
+                   "zero fill");
+}
+
+struct Carve {
+  char *base;
+  size_t used;
+  uint16_t *take(size_t elems) {
+    uint16_t *p = (uint16_t *)(base + used);
+    used += round256(elems * 2);
+    return p;
+  }
+};
+
+size_t bwd_ws_bytes(int64_t M, int64_t H, int64_t I) {
+  const int64_t Mp = round8(M);
+  return round256((size_t)M * round8(I) * 2) * 2  // dG, dU row-major [M, I] (ld = I rounded to 8)
+         + round256((size_t)I * Mp * 2) * 3       // dG^T, dU^T, a^T [I, Mp]
+         + round256((size_t)H * Mp * 2) * 2       // x^T, dY^T [H, Mp]
+         + round256((size_t)M * round8(H) * 2) * 2;  // the dX lanes G, U [M, H]
+}
+
+size_t fwd_ws_bytes(int64_t M, int64_t H, int64_t I) {
+  (void)H;
+  return round256((size_t)M * round8(I) * 2);  // a [M, I]
+}
+
+size_t gemm_ws_bytes(int layout, int64_t M, int64_t N, int64_t K) {
+  if (layout != DGF_TN) return 0;
+  const int64_t Kp = round8(K);
+  return round256((size_t)M * Kp * 2) + round256((size_t)N * Kp * 2);
+}
+
+}  // namespace
+
+extern "C" {
+
+int dgf_abi_version(void) { return 1; }
+
+int dgf_leaf_size(void) { return 64; }
+
+const char *dgf_last_error(void) { return g_err.c_str(); }
+
+dgf_status dgf_profile_begin(void *const *events, int n_pairs) {
+  if (n_pairs < 0 || (n_pairs > 0 && !events)) return fail(DGF_EINVAL, "profile_begin: bad event array");
+  for (int i = 0; i < 2 * n_pairs; ++i)
+    if (!events[i]) return fail(DGF_EINVAL, "profile_begin: event %d is NULL", i);
+  g_prof = Prof{};
+  g_prof.ev = n_pairs > 0 ? (hipEvent_t *)events : nullptr;
+  g_prof.pairs = n_pairs;
+  return ok();
+}
+
+int dgf_profile_end(void) {
+  const int n = g_prof.used;
+  g_prof.ev = nullptr;
+  g_prof.pairs = 0;
+  return n;
+}
+
+const char *dgf_profile_name(int k) {
+  if (k < 0 || k >= 256 || k >= g_prof.used || !g_prof.names[k]) return "";
+  return g_prof.names[k];
+}
+
+size_t dgf_ffn_fwd_workspace(int64_t M, int64_t H, int64_t I) {
+  if (M <= 0 || H <= 0 || I <= 0) return 0;
+  return fwd_ws_bytes(M, H, I);
+}
+
+dgf_status dgf_ffn_fwd(const void *x, int64_t ldx, const void *w_gate, int64_t ld_wg, const void *w_up, int64_t ld_wu,
+                       const void *w_down, int64_t ld_wd, void *y, int64_t ldy, void *g_save, void *u_save,
+                       int64_t ld_gu, int64_t M, int64_t H, int64_t I, void *ws, size_t ws_bytes, void *stream) {
+  DGF_TRY(check_dims(M, I, H));
+  DGF_TRY(check_dims(M, H, I));
+  if (H == 0 || I == 0) return fail(DGF_EINVAL, "H and I must be positive (H=%lld I=%lld)", (long long)H, (long long)I);
+  if (M == 0) return ok();
+  DGF_TRY(check_mat("x", x, ldx, M, H));
+  DGF_TRY(check_mat("w_gate", w_gate, ld_wg, I, H));
+  DGF_TRY(check_mat("w_up", w_up, ld_wu, I, H));
+  DGF_TRY(check_mat("w_down", w_down, ld_wd, H, I));
+  DGF_TRY(check_mat("y", y, ldy, M, H));
+  if ((g_save == nullptr) != (u_save == nullptr)) return fail(DGF_EINVAL, "g_save and u_save must both be given or both be NULL");
+  if (g_save) {
+    DGF_TRY(check_mat("g_save", g_save, ld_gu, M, I));
+    DGF_TRY(check_mat("u_save", u_save, ld_gu, M, I));
+  }
+  const size_t need = fwd_ws_bytes(M, H, I);
+  if (!ws || ws_bytes < need || !aligned16(ws))
+    return fail(DGF_EWORKSPACE, "forward workspace: need %zu bytes (16-byte aligned), got %zu", need, ws ? ws_bytes : 0);
+  hipStream_t s = (hipStream_t)stream;
+  Carve cv{(char *)ws, 0};
+  uint16_t *a = cv.take((size_t)M * round8(I));
+  const int64_t lda_ = round8(I);
+
+  GemmParams p = blank();
+  p.A[0] = p.A[1] = (const uint16_t *)x;
+  p.lda[0] = p.lda[1] = ldx;
+  p.shared_a = 1;
+  p.B[0] = (const uint16_t *)w_gate;
+  p.ldb[0] = ld_wg;
+  p.B[1] = (const uint16_t *)w_up;
+  p.ldb[1] = ld_wu;
+  p.C[0] = (uint16_t *)g_save;
+  p.C[1] = (uint16_t *)u_save;
+  p.ldc[0] = p.ldc[1] = ld_gu;
+  p.act_out = a;
+  p.ld_act = lda_;
+  p.M = M; p.N = I; p.K = H;
+  DGF_TRY(run_gemm(DGF_LAYOUT_NT, 2, EPI_ACT, p, s, "gate/up tree GEMM"));
+
+  GemmParams q = blank();
+  q.A[0] = a;
+  q.lda[0] = lda_;
+  q.B[0] = (const uint16_t *)w_down;
+  q.ldb[0] = ld_wd;
+  q.C[0] = (uint16_t *)y;
+  q.ldc[0] = ldy;
+  q.M = M; q.N = H; q.K = I;
+  DGF_TRY(run_gemm(DGF_LAYOUT_NT, 1, EPI_STORE, q, s, "down tree GEMM"));
+  return ok();
+}
+
+size_t dgf_ffn_bwd_workspace(int64_t M, int64_t H, int64_t I) {
+  if (M <= 0 || H <= 0 || I <= 0) return 0;
+  return bwd_ws_bytes(M, H, I);
+}
+
+dgf_status dgf_ffn_bwd(const void *dy, int64_t lddy, const void *x, int64_t ldx, const void *g, const void *u,
+                       int64_t ld_gu, const void *w_gate, int64_t ld_wg, const void *w_up, int64_t ld_wu,
+                       const void *w_down, int64_t ld_wd, void *dx, void *dx_gate_lane, void *dx_up_lane,
+                       int64_t lddx, void *dw_gate, int64_t ld_dwg, void *dw_up, int64_t ld_dwu, void *dw_down,
+                       int64_t ld_dwd, int64_t M, int64_t H, int64_t I, void *ws, size_t ws_bytes, void *stream) {
+  DGF_TRY(check_dims(M, I, H));
+  DGF_TRY(check_dims(M, H, I));
+  if (H == 0 || I == 0) return fail(DGF_EINVAL, "H and I must be positive (H=%lld I=%lld)", (long long)H, (long long)I);
+  if (M == 0) return ok();
+  DGF_TRY(check_mat("dy", dy, lddy, M, H));
+  DGF_TRY(check_mat("x", x, ldx, M, H));
+  DGF_TRY(check_mat("g", g, ld_gu, M, I));
+  DGF_TRY(check_mat("u", u, ld_gu, M, I));
+  DGF_TRY(check_mat("w_gate", w_gate, ld_wg, I, H));
+  DGF_TRY(check_mat("w_up", w_up, ld_wu, I, H));
+  DGF_TRY(check_mat("w_down", w_down, ld_wd, H, I));
+  if (!dx && !dx_gate_lane && !dx_up_lane) return fail(DGF_EINVAL, "no dX output given (dx and both lanes are NULL)");
+  if (dx) DGF_TRY(check_mat("dx", dx, lddx, M, H));
+  if (dx_gate_lane) DGF_TRY(check_mat("dx_gate_lane", dx_gate_lane, lddx, M, H));
+  if (dx_up_lane) DGF_TRY(check_mat("dx_up_lane", dx_up_lane, lddx, M, H));
+  DGF_TRY(check_mat("dw_gate", dw_gate, ld_dwg, I, H));
+  DGF_TRY(check_mat("dw_up", dw_up, ld_dwu, I, H));
+  DGF_TRY(check_mat("dw_down", dw_down, ld_dwd, H, I));
+  const size_t need = bwd_ws_bytes(M, H, I);
+  if (!ws || ws_bytes < need || !aligned16(ws))
+    return fail(DGF_EWORKSPACE, "backward workspace: need %zu bytes (16-byte aligned), got %zu", need, ws ? ws_bytes : 0);
+
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t Mp = round8(M);
+  Carve cv{(char *)ws, 0};
+  const int64_t ld_d = round8(I);
+  uint16_t *dG = cv.take((size_t)M * ld_d), *dU = cv.take((size_t)M * ld_d);
+  uint16_t *dGT = cv.take((size_t)I * Mp), *dUT = cv.take((size_t)I * Mp), *aT = cv.take((size_t)I * Mp);
+  uint16_t *xT = cv.take((size_t)H * Mp), *dYT = cv.take((size_t)H * Mp);
+  const int64_t ld_lane = round8(H);
+  uint16_t *Gw = cv.take((size_t)M * ld_lane), *Uw = cv.take((size_t)M * ld_lane);
+
+  DGF_TRY(hip_check(timed(s, "transpose x", [&] { return launch_transpose((const uint16_t *)x, ldx, M, H, xT, Mp, s); }),
+                    "transpose x"));
+  DGF_TRY(hip_check(timed(s, "transpose dY", [&] { return launch_transpose((const uint16_t *)dy, lddy, M, H, dYT, Mp, s); }),
+                    "transpose dY"));
+
+  // dA = T_H(dY W_down) with the dsilu epilogue
+  GemmParams p = blank();
+  p.A[0] = (const uint16_t *)dy;
+  p.lda[0] = lddy;
+  p.B[0] = (const uint16_t *)w_down;
+  p.ldb[0] = ld_wd;
+  p.M = M; p.N = I; p.K = H;
+  p.sg = (const uint16_t *)g;
+  p.su = (const uint16_t *)u;
+  p.ld_gu = ld_gu;
+  p.dG = dG; p.dU = dU; p.a_rm = nullptr; p.ld_d = ld_d;
+  p.dGT = dGT; p.dUT = dUT; p.aT = aT; p.ld_t = Mp;
+  DGF_TRY(run_gemm(DGF_LAYOUT_NN, 1, EPI_DSILU, p, s, "dA tree GEMM"));
+
+  // dX lanes G = T_I(dG W_gate), U = T_I(dU W_up), each its own tree GEMM
+  // (written to the caller's lane buffers when given, else to the workspace)
+  uint16_t *G = dx_gate_lane ? (uint16_t *)dx_gate_lane : Gw;
+  uint16_t *U = dx_up_lane ? (uint16_t *)dx_up_lane : Uw;
+  const int64_t ldG = dx_gate_lane ? lddx : ld_lane, ldU = dx_up_lane ? lddx : ld_lane;
+  for (int lane_i = 0; lane_i < 2; ++lane_i) {
+    GemmParams q = blank();
+    q.A[0] = lane_i == 0 ? dG : dU;
+    q.lda[0] = ld_d;
+    q.B[0] = (const uint16_t *)(lane_i == 0 ? w_gate : w_up);
+    q.ldb[0] = lane_i == 0 ? ld_wg : ld_wu;
+    q.C[0] = lane_i == 0 ? G : U;
+    q.ldc[0] = lane_i == 0 ? ldG : ldU;
+    q.M = M; q.N = H; q.K = I;
+    DGF_TRY(run_gemm(DGF_LAYOUT_NN, 1, EPI_STORE, q, s, lane_i == 0 ? "dX gate-lane tree GEMM" : "dX up-lane tree GEMM"));
+  }
+  // dX = bf16(G + U): the ordered add, gate lane first
+  if (dx)
+    DGF_TRY(hip_check(timed(s, "dX ordered add", [&] { return launch_add_lanes(G, ldG, U, ldU, (uint16_t *)dx, lddx, M, H, s); }),
+                      "dX ordered add"));
+
+  // dW_gate = T_M(dG^T x), dW_up = T_M(dU^T x): NT over the transposed operands
+  GemmParams w = blank();
+  w.A[0] = dGT; w.A[1] = dUT;
+  w.lda[0] = w.lda[1] = Mp;
+  w.B[0] = w.B[1] = xT;
+  w.ldb[0] = w.ldb[1] = Mp;
+  w.C[0] = (uint16_t *)dw_gate; w.ldc[0] = ld_dwg;
+  w.C[1] = (uint16_t *)dw_up; w.ldc[1] = ld_dwu;
+  w.M = I; w.N = H; w.K = M;
+  DGF_TRY(run_gemm(DGF_LAYOUT_NT, 2, EPI_STORE, w, s, "dW_gate/dW_up tree GEMM"));
+
+  // dW_down = T_M(dY^T a)
+  GemmParams v = blank();
+  v.A[0] = dYT; v.lda[0] = Mp;
+  v.B[0] = aT; v.ldb[0] = Mp;
+  v.C[0] = (uint16_t *)dw_down; v.ldc[0] = ld_dwd;
+  v.M = H; v.N = I; v.K = M;
+  DGF_TRY(run_gemm(DGF_LAYOUT_NT, 1, EPI_STORE, v, s, "dW_down tree GEMM"));
+  return ok();
+}
+
+dgf_status dgf_tree_combine(const void *const *parts, int S, void *out, int64_t n, void *stream) {
+  if (n < 0) return fail(DGF_EINVAL, "negative length %lld", (long long)n);
+  if (!(S == 1 || S == 2 || S == 4 || S == 8)) return fail(DGF_EUNSUPPORTED, "S=%d: only 1, 2, 4 or 8 parts", S);
+  if (n == 0) return ok();
+  if (!parts) return fail(DGF_EINVAL, "parts is NULL");
+  if (!out) return fail(DGF_EINVAL, "out is NULL");
+  for (int i = 0; i < S; ++i)
+    if (!parts[i]) return fail(DGF_EINVAL, "parts[%d] is NULL", i);
+  if (((uintptr_t)out & 1) != 0) return fail(DGF_EINVAL, "out is not 2-byte aligned");
+  for (int i = 0; i < S; ++i)
+    if (((uintptr_t)parts[i] & 1) != 0) return fail(DGF_EINVAL, "parts[%d] is not 2-byte aligned", i);
+  hipStream_t s = (hipStream_t)stream;
+  DGF_TRY(hip_check(timed(s, "tree_combine", [&] { return launch_combine((const uint16_t *const *)parts, S, (uint16_t *)out, n, s); }),
+                    "tree_combine"));
+  return ok();
+}
+
+size_t dgf_gemm_tree_workspace(int layout, int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || K <= 0) return 0;
+  return gemm_ws_bytes(layout, M, N, K);
+}
+
+dgf_status dgf_gemm_tree(int layout, const void *A, int64_t lda, const void *B, int64_t ldb, void *C, int64_t ldc,
+                         int64_t M, int64_t N, int64_t K, void *ws, size_t ws_bytes, void *stream) {
+  if (layout != DGF_NT && layout != DGF_NN && layout != DGF_TN) return fail(DGF_EINVAL, "unknown layout %d", layout);
+  DGF_TRY(check_dims(M, N, K));
+  if (M == 0 || N == 0) return ok();
+  DGF_TRY(check_mat("C", C, ldc, M, N));
+  hipStream_t s = (hipStream_t)stream;
+  if (K == 0) return zero_mat((uint16_t *)C, ldc, M, N, s) == DGF_OK ? ok() : DGF_EHIP;
+  if (layout == DGF_NT) {
+    DGF_TRY(check_mat("A", A, lda, M, K));
+    DGF_TRY(check_mat("B", B, ldb, N, K));
+  } else if (layout == DGF_NN) {
+    DGF_TRY(check_mat("A", A, lda, M, K));
+    DGF_TRY(check_mat("B", B, ldb, K, N));
+  } else {
+    DGF_TRY(check_mat("A", A, lda, K, M));
+    DGF_TRY(check_mat("B", B, ldb, K, N));
+  }
+  const size_t need = gemm_ws_bytes(layout, M, N, K);
+  if (need && (!ws || ws_bytes < need || !aligned16(ws)))
+    return fail(DGF_EWORKSPACE, "gemm_tree workspace: need %zu bytes (16-byte aligned), got %zu", need, ws ? ws_bytes : 0);
+
+  GemmParams p = blank();
+  p.M = M; p.N = N; p.K = K;
+  p.C[0] = (uint16_t *)C;
+  p.ldc[0] = ldc;
+  if (layout == DGF_TN) {
+    const int64_t Kp = round8(K);
+    Carve cv{(char *)ws, 0};
+    uint16_t *AT = cv.take((size_t)M * Kp), *BT = cv.take((size_t)N * Kp);
+    DGF_TRY(hip_check(timed(s, "transpose A", [&] { return launch_transpose((const uint16_t *)A, lda, K, M, AT, Kp, s); }),
+                      "transpose A"));
+    DGF_TRY(hip_check(timed(s, "transpose B", [&] { return launch_transpose((const uint16_t *)B, ldb, K, N, BT, Kp, s); }),
+                      "transpose B"));
+    p.A[0] = AT; p.lda[0] = Kp;
+    p.B[0] = BT; p.ldb[0] = Kp;
+    DGF_TRY(run_gemm(DGF_LAYOUT_NT, 1, EPI_STORE, p, s, "TN tree GEMM"));
+  } else {
+    p.A[0] = (const uint16_t *)A; p.lda[0] = lda;
+    p.B[0] = (const uint16_t *)B; p.ldb[0] = ldb;
+    DGF_TRY(run_gemm(layout == DGF_NT ? DGF_LAYOUT_NT : DGF_LAYOUT_NN, 1, EPI_STORE, p, s, "tree GEMM"));
+  }
+  return ok();
+}
+
+dgf_status dgf_act_fwd(const void *g, const void *u, void *a, int64_t n, void *stream) {
+  if (n < 0) return fail(DGF_EINVAL, "negative length");
+  if (n == 0) return ok();
+  if (!g || !u || !a) return fail(DGF_EINVAL, "NULL pointer");
+  if (((uintptr_t)g | (uintptr_t)u | (uintptr_t)a) & 1) return fail(DGF_EINVAL, "pointers must be 2-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  DGF_TRY(hip_check(timed(s, "act_fwd", [&] { return launch_act_fwd((const uint16_t *)g, (const uint16_t *)u, (uint16_t *)a, n, s); }),
+                    "act_fwd"));
+  return ok();
+}
+
+dgf_status dgf_act_bwd(const void *da, const void *g, const void *u, void *dg, void *du, void *a, int64_t n,
+                       void *stream) {
+  if (n < 0) return fail(DGF_EINVAL, "negative length");
+  if (n == 0) return ok();
+  if (!da || !g || !u || !dg || !du) return fail(DGF_EINVAL, "NULL pointer");
+  if (((uintptr_t)da | (uintptr_t)g | (uintptr_t)u | (uintptr_t)dg | (uintptr_t)du | (uintptr_t)a) & 1)
+    return fail(DGF_EINVAL, "pointers must be 2-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  DGF_TRY(hip_check(timed(s, "act_bwd", [&] {
+                      return launch_act_bwd((const uint16_t *)da, (const uint16_t *)g, (const uint16_t *)u, (uint16_t *)dg,
+                                            (uint16_t *)du, (uint16_t *)a, n, s);
+                    }),
+                    "act_bwd"));
+  return ok();
+}
+
+}  // extern "C"

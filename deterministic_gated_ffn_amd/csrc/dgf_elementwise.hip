@@ -1,0 +1,176 @@
+// Elementwise kernels: the activation and its derivative, the fixed balanced
+// combine of S partial results, and a BF16 transpose.
+#include "dgf_device.hpp"
+#include "dgf_kernels.hpp"
+
+namespace dgf {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+unsigned grid_for(int64_t work, int per_thread) {
+  int64_t blocks = (work + (int64_t)kThreads * per_thread - 1) / ((int64_t)kThreads * per_thread);
+  if (blocks > 65536) blocks = 65536;  // grid-stride loops cover the rest
+  if (blocks < 1) blocks = 1;
+  return (unsigned)blocks;
+}
+
+// a = bf16(silu(g) u), silu(g) = g * sigma(g)
+__global__ __launch_bounds__(kThreads) void k_act_fwd(const uint16_t *g, const uint16_t *u, uint16_t *a, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += (int64_t)gridDim.x * kThreads) {
+    const float gv = bf2f(g[i]);
+    const float s = gv * sigma_f(gv);
+    a[i] = f2bf(s * bf2f(u[i]));
+  }
+}
+
+// dU = bf16(dA silu(g)), dG = bf16((dA u) silu'(g)), silu' = sigma (1 + g (1 - sigma))
+__global__ __launch_bounds__(kThreads) void k_act_bwd(const uint16_t *da, const uint16_t *g, const uint16_t *u,
+                                                      uint16_t *dg, uint16_t *du, uint16_t *a, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += (int64_t)gridDim.x * kThreads) {
+    const float gv = bf2f(g[i]), uv = bf2f(u[i]), dav = bf2f(da[i]);
+    const float sg = sigma_f(gv);
+    const float s = gv * sg;
+    const float one_m = 1.0f - sg;
+    const float t = gv * one_m;
+    const float onep = 1.0f + t;
+    const float ds = sg * onep;
+    du[i] = f2bf(dav * s);
+    const float dau = dav * uv;
+    dg[i] = f2bf(dau * ds);
+    if (a) a[i] = f2bf(s * uv);
+  }
+}
+
+struct Parts {
+  const uint16_t *p[8];
+};
+
+// Balanced combine over S parts, 8 elements per thread with 16-byte accesses.
+template <int S>
+__global__ __launch_bounds__(kThreads) void k_combine_vec(Parts parts, uint16_t *out, int64_t nvec) {
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nvec; i += (int64_t)gridDim.x * kThreads) {
+    uint32_t r[S][4];
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const uint4 v = reinterpret_cast<const uint4 *>(parts.p[s])[i];
+      r[s][0] = v.x; r[s][1] = v.y; r[s][2] = v.z; r[s][3] = v.w;
+    }
+#pragma unroll
+    for (int width = S; width > 1; width >>= 1)
+#pragma unroll
+      for (int j = 0; j < width / 2; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) r[j][q] = node2(r[2 * j][q], r[2 * j + 1][q]);
+    reinterpret_cast<uint4 *>(out)[i] = make_uint4(r[0][0], r[0][1], r[0][2], r[0][3]);
+  }
+}
+
+// The same arithmetic one element at a time (unaligned or offset views, tails).
+template <int S>
+__global__ __launch_bounds__(kThreads) void k_combine_scalar(Parts parts, uint16_t *out, int64_t begin, int64_t n) {
+  for (int64_t i = begin + (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += (int64_t)gridDim.x * kThreads) {
+    float r[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) r[s] = bf2f(parts.p[s][i]);
+#pragma unroll
+    for (int width = S; width > 1; width >>= 1)
+#pragma unroll
+      for (int j = 0; j < width / 2; ++j) r[j] = bf2f(f2bf(r[2 * j] + r[2 * j + 1]));
+    out[i] = f2bf(r[0]);
+  }
+}
+
+// dx = bf16(G + U), the gate contribution first (an FP32 add of two BF16 lanes,
+// rounded to BF16); 8 elements per thread, rows of N (a multiple of 8 leading dims).
+__global__ __launch_bounds__(kThreads) void k_add_lanes(const uint16_t *G, int64_t ldg, const uint16_t *U, int64_t ldu,
+                                                        uint16_t *dx, int64_t lddx, int64_t M, int64_t N) {
+  const int64_t per_row = (N + 7) / 8;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < M * per_row; i += (int64_t)gridDim.x * kThreads) {
+    const int64_t m = i / per_row, c = (i % per_row) * 8;
+    const uint16_t *g = G + m * ldg + c, *u = U + m * ldu + c;
+    uint16_t *o = dx + m * lddx + c;
+    if (c + 8 <= N) {
+      const uint4 gv = *reinterpret_cast<const uint4 *>(g), uv = *reinterpret_cast<const uint4 *>(u);
+      *reinterpret_cast<uint4 *>(o) = make_uint4(node2(gv.x, uv.x), node2(gv.y, uv.y), node2(gv.z, uv.z), node2(gv.w, uv.w));
+    } else {
+      for (int64_t j = 0; c + j < N; ++j) o[j] = f2bf(bf2f(g[j]) + bf2f(u[j]));
+    }
+  }
+}
+
+// dst [C, R] = src [R, C]^T through a 64 x 64 LDS tile.
+__global__ __launch_bounds__(kThreads) void k_transpose(const uint16_t *src, int64_t lds_, int64_t R, int64_t C,
+                                                        uint16_t *dst, int64_t ldd) {
+  __shared__ uint16_t tile[64][65];
+  const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int i = ty; i < 64; i += kThreads / 64) {
+    const int64_t r = r0 + i, c = c0 + tx;
+    tile[i][tx] = (r < R && c < C) ? src[r * lds_ + c] : (uint16_t)0;
+  }
+  __syncthreads();
+  for (int i = ty; i < 64; i += kThreads / 64) {
+    const int64_t c = c0 + i, r = r0 + tx;
+    if (c < C && r < R) dst[c * ldd + r] = tile[tx][i];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_act_fwd(const uint16_t *g, const uint16_t *u, uint16_t *a, int64_t n, hipStream_t s) {
+  hipLaunchKernelGGL(k_act_fwd, dim3(grid_for(n, 1)), dim3(kThreads), 0, s, g, u, a, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_act_bwd(const uint16_t *da, const uint16_t *g, const uint16_t *u, uint16_t *dg, uint16_t *du,
+                          uint16_t *a, int64_t n, hipStream_t s) {
+  hipLaunchKernelGGL(k_act_bwd, dim3(grid_for(n, 1)), dim3(kThreads), 0, s, da, g, u, dg, du, a, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const uint16_t *const *parts, int S, uint16_t *out, int64_t n, hipStream_t s) {
+  Parts P{};
+  bool aligned = ((uintptr_t)out & 15) == 0;
+  for (int i = 0; i < S; ++i) {
+    P.p[i] = parts[i];
+    aligned = aligned && (((uintptr_t)parts[i] & 15) == 0);
+  }
+  const int64_t nvec = aligned ? n / 8 : 0;
+  if (nvec > 0) {
+    const dim3 g(grid_for(nvec, 1));
+    switch (S) {
+      case 1: hipLaunchKernelGGL(k_combine_vec<1>, g, dim3(kThreads), 0, s, P, out, nvec); break;
+      case 2: hipLaunchKernelGGL(k_combine_vec<2>, g, dim3(kThreads), 0, s, P, out, nvec); break;
+      case 4: hipLaunchKernelGGL(k_combine_vec<4>, g, dim3(kThreads), 0, s, P, out, nvec); break;
+      default: hipLaunchKernelGGL(k_combine_vec<8>, g, dim3(kThreads), 0, s, P, out, nvec); break;
+    }
+  }
+  const int64_t begin = nvec * 8;
+  if (begin < n) {
+    const dim3 g(grid_for(n - begin, 1));
+    switch (S) {
+      case 1: hipLaunchKernelGGL(k_combine_scalar<1>, g, dim3(kThreads), 0, s, P, out, begin, n); break;
+      case 2: hipLaunchKernelGGL(k_combine_scalar<2>, g, dim3(kThreads), 0, s, P, out, begin, n); break;
+      case 4: hipLaunchKernelGGL(k_combine_scalar<4>, g, dim3(kThreads), 0, s, P, out, begin, n); break;
+      default: hipLaunchKernelGGL(k_combine_scalar<8>, g, dim3(kThreads), 0, s, P, out, begin, n); break;
+    }
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_add_lanes(const uint16_t *G, int64_t ldg, const uint16_t *U, int64_t ldu, uint16_t *dx,
+                            int64_t lddx, int64_t M, int64_t N, hipStream_t s) {
+  hipLaunchKernelGGL(k_add_lanes, dim3(grid_for(M * ((N + 7) / 8), 1)), dim3(kThreads), 0, s, G, ldg, U, ldu, dx, lddx, M, N);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose(const uint16_t *src, int64_t lds_, int64_t R, int64_t C, uint16_t *dst, int64_t ldd,
+                            hipStream_t s) {
+  const dim3 g((unsigned)((C + 63) / 64), (unsigned)((R + 63) / 64));
+  hipLaunchKernelGGL(k_transpose, g, dim3(kThreads), 0, s, src, lds_, R, C, dst, ldd);
+  return hipGetLastError();
+}
+
+}  // namespace dgf

@@ -1,0 +1,49 @@
+// Host-visible kernel interfaces of libdgf (internal; the public ABI is include/dgf.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dgf {
+
+enum { DGF_LAYOUT_NT = 0, DGF_LAYOUT_NN = 1 };
+enum { EPI_STORE = 0, EPI_ACT = 1, EPI_DSILU = 2 };
+
+// Arguments of one tree-GEMM launch (two products when NB = 2).
+struct GemmParams {
+  const uint16_t *A[2];  // [M, K] K-contiguous activations
+  int64_t lda[2];
+  const uint16_t *B[2];  // NT: [N, K] K-contiguous; NN: [K, N] N-contiguous
+  int64_t ldb[2];
+  uint16_t *C[2];        // [M, N] outputs (EPI_STORE; optional g/u or lanes otherwise)
+  int64_t ldc[2];
+  int64_t M, N, K;
+  int L;                 // leaves = ceil(K / 64)
+  int stack_slots;       // LDS tree-stack slots per wave (>= 1, >= a wave subtree's depth)
+  int shared_a;          // NB = 2 with A[1] == A[0]
+  // EPI_ACT: a = bf16(silu(C0) * C1)
+  uint16_t *act_out;
+  int64_t ld_act;
+  // EPI_DSILU: saved g, u [M, N]; outputs dG, dU, a row-major and transposed
+  const uint16_t *sg, *su;
+  int64_t ld_gu;
+  uint16_t *dG, *dU, *a_rm;
+  int64_t ld_d;
+  uint16_t *dGT, *dUT, *aT;
+  int64_t ld_t;
+};
+
+hipError_t launch_gemm(int layout, int nb, int epi, GemmParams p, int waves, hipStream_t stream);
+
+hipError_t launch_act_fwd(const uint16_t *g, const uint16_t *u, uint16_t *a, int64_t n, hipStream_t s);
+hipError_t launch_act_bwd(const uint16_t *da, const uint16_t *g, const uint16_t *u, uint16_t *dg, uint16_t *du,
+                          uint16_t *a, int64_t n, hipStream_t s);
+hipError_t launch_combine(const uint16_t *const *parts, int S, uint16_t *out, int64_t n, hipStream_t s);
+// dx [M, N] = bf16(G + U) per element (the gate lane first), row-major with leading dims
+hipError_t launch_add_lanes(const uint16_t *G, int64_t ldg, const uint16_t *U, int64_t ldu, uint16_t *dx,
+                            int64_t lddx, int64_t M, int64_t N, hipStream_t s);
+// dst [C, R] (ldd) = transpose of src [R, C] (lds)
+hipError_t launch_transpose(const uint16_t *src, int64_t lds, int64_t R, int64_t C, uint16_t *dst, int64_t ldd,
+                            hipStream_t s);
+
+}  // namespace dgf

@@ -1,0 +1,115 @@
+"""The C-ABI library loads and exports every entry point include/dgf.h declares;
+argument validation answers before any HIP call (no GPU needed here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from deterministic_gated_ffn_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dgf.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(dgf_[a-z_0-9]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.lib_path()):
+        pytest.fail("libdgf.so is not built (python -m deterministic_gated_ffn_amd.build)")
+    return binding.load()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("dgf_ffn_fwd", "dgf_ffn_bwd", "dgf_tree_combine", "dgf_gemm_tree",
+                     "dgf_act_fwd", "dgf_act_bwd", "dgf_last_error"):
+        assert required in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert name in binding.SIGNATURES, f"binding lacks {name}"
+
+
+def test_constants(lib):
+    assert lib.dgf_abi_version() == 1
+    assert lib.dgf_leaf_size() == 64
+
+
+def test_workspace_queries(lib):
+    assert lib.dgf_ffn_fwd_workspace(0, 4096, 12288) == 0
+    assert lib.dgf_ffn_fwd_workspace(32, 4096, 12288) >= 32 * 12288 * 2
+    assert lib.dgf_ffn_bwd_workspace(32, 4096, 12288) >= 32 * 12288 * 2 * 5
+    assert lib.dgf_gemm_tree_workspace(binding.DGF_NT, 4, 4, 4) == 0
+    assert lib.dgf_gemm_tree_workspace(binding.DGF_TN, 4, 4, 4) > 0
+
+
+FAKE = 1 << 20  # a 16-byte aligned stand-in address; never dereferenced by these calls
+
+
+def test_fwd_validation(lib):
+    st = lib.dgf_ffn_fwd(None, 256, FAKE, 256, FAKE, 256, FAKE, 768, FAKE, 256, None, None, 0,
+                         4, 256, 768, FAKE, 1 << 20, None)
+    assert st == 1 and b"x is NULL" in lib.dgf_last_error()
+    st = lib.dgf_ffn_fwd(FAKE + 2, 256, FAKE, 256, FAKE, 256, FAKE, 768, FAKE, 256, None, None, 0,
+                         4, 256, 768, FAKE, 1 << 20, None)
+    assert st == 1 and b"aligned" in lib.dgf_last_error()
+    st = lib.dgf_ffn_fwd(FAKE, 100, FAKE, 256, FAKE, 256, FAKE, 768, FAKE, 256, None, None, 0,
+                         4, 256, 768, FAKE, 1 << 20, None)
+    assert st == 1 and b"leading dimension" in lib.dgf_last_error()
+    st = lib.dgf_ffn_fwd(FAKE, 260, FAKE, 256, FAKE, 256, FAKE, 768, FAKE, 256, None, None, 0,
+                         4, 256, 768, FAKE, 1 << 20, None)
+    assert st == 1 and b"multiple of 8" in lib.dgf_last_error()
+    st = lib.dgf_ffn_fwd(FAKE, 256, FAKE, 256, FAKE, 256, FAKE, 768, FAKE, 256, FAKE, None, 768,
+                         4, 256, 768, FAKE, 1 << 20, None)
+    assert st == 1 and b"g_save" in lib.dgf_last_error()
+    st = lib.dgf_ffn_fwd(FAKE, 256, FAKE, 256, FAKE, 256, FAKE, 768, FAKE, 256, None, None, 0,
+                         4, 256, 768, FAKE, 16, None)
+    assert st == 3 and b"workspace" in lib.dgf_last_error()
+    st = lib.dgf_ffn_fwd(FAKE, 256, FAKE, 256, FAKE, 256, FAKE, 768, FAKE, 256, None, None, 0,
+                         -1, 256, 768, FAKE, 1 << 20, None)
+    assert st == 1
+    # M = 0: nothing to do, no launch
+    assert lib.dgf_ffn_fwd(None, 0, None, 0, None, 0, None, 0, None, 0, None, None, 0,
+                           0, 256, 768, None, 0, None) == 0
+
+
+def test_bwd_validation(lib):
+    args = [FAKE, 256, FAKE, 256, FAKE, FAKE, 768, FAKE, 256, FAKE, 256, FAKE, 768,
+            None, None, None, 256, FAKE, 256, FAKE, 256, FAKE, 768, 4, 256, 768, FAKE, 1 << 24, None]
+    assert lib.dgf_ffn_bwd(*args) == 1 and b"no dX output" in lib.dgf_last_error()
+    args[13] = FAKE
+    args[17] = None
+    assert lib.dgf_ffn_bwd(*args) == 1 and b"dw_gate" in lib.dgf_last_error()
+    args[17] = FAKE
+    args[-2] = 100
+    assert lib.dgf_ffn_bwd(*args) == 3
+
+
+def test_combine_validation(lib):
+    arr = (ctypes.c_void_p * 3)(FAKE, FAKE, FAKE)
+    assert lib.dgf_tree_combine(arr, 3, FAKE, 10, None) == 2
+    assert b"S=3" in lib.dgf_last_error()
+    arr8 = (ctypes.c_void_p * 8)(*([FAKE] * 8))
+    assert lib.dgf_tree_combine(arr8, 8, FAKE, 0, None) == 0      # n = 0: no launch
+    assert lib.dgf_tree_combine(arr8, 8, None, 10, None) == 1
+    assert lib.dgf_tree_combine(arr8, 8, FAKE + 1, 10, None) == 1
+    assert lib.dgf_tree_combine(arr8, 8, FAKE, -1, None) == 1
+    arr2 = (ctypes.c_void_p * 2)(FAKE, None)
+    assert lib.dgf_tree_combine(arr2, 2, FAKE, 10, None) == 1
+
+
+def test_gemm_validation(lib):
+    assert lib.dgf_gemm_tree(7, FAKE, 8, FAKE, 8, FAKE, 8, 4, 4, 4, None, 0, None) == 1
+    assert lib.dgf_gemm_tree(binding.DGF_NT, FAKE, 8, FAKE, 8, FAKE, 8, 0, 4, 4, None, 0, None) == 0
+    assert lib.dgf_gemm_tree(binding.DGF_TN, FAKE, 8, FAKE, 8, FAKE, 8, 4, 4, 4, None, 0, None) == 3
+    assert lib.dgf_gemm_tree(binding.DGF_NN, FAKE, 4, FAKE, 8, FAKE, 8, 4, 4, 8, None, 0, None) == 1
+    assert lib.dgf_act_fwd(None, FAKE, FAKE, 10, None) == 1
+    assert lib.dgf_act_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == 0

@@ -1,0 +1,328 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle, element by
+element, bitwise (0 mismatches), plus run-to-run and shard invariance and the
+float64 relative-L2 bound.  The oracle's readings are in oracle/dgf_oracle.c."""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import fp64
+from deterministic_gated_ffn_amd import binding as dgf
+from deterministic_gated_ffn_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+F2B = oracle.f32_to_bf16_bits
+B2F = oracle.bf16_bits_to_f32
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible: the GPU tests need an MI355X")
+    dgf.load()
+    return torch.device("cuda:0")
+
+
+def dev(bits_or_t):
+    if isinstance(bits_or_t, np.ndarray):
+        return inputs.from_bits(bits_or_t).cuda()
+    return bits_or_t.cuda()
+
+
+def ordinal(b):
+    b = np.asarray(b, np.uint16).astype(np.int32)
+    return np.where(b & 0x8000, -(b & 0x7FFF), b & 0x7FFF)
+
+
+def assert_bitwise(got, expected_bits, name):
+    """0 mismatching BF16 bit patterns; on failure report the ulp distances."""
+    g = inputs.bits(got) if isinstance(got, torch.Tensor) else np.asarray(got, np.uint16)
+    e = np.asarray(expected_bits, np.uint16).reshape(g.shape)
+    bad = g != e
+    n = int(bad.sum())
+    if n:
+        d = np.abs(ordinal(g) - ordinal(e))[bad]
+        idx = np.argwhere(bad)[:5].tolist()
+        pytest.fail(f"{name}: {n}/{g.size} mismatches (exact fraction {1 - n / g.size:.6f}); "
+                    f"max ulp {d.max()}, >1 ulp: {(d > 1).sum()}; first at {idx}")
+
+
+def rnd(rng, shape, scale=1.0):
+    return F2B((rng.standard_normal(shape) * scale).astype(np.float32))
+
+
+def wide(rng, shape, lo=-20, hi=20):
+    """BF16 values with random exponents in [lo, hi] (stresses the block rule)."""
+    e = rng.integers(lo, hi + 1, size=shape) + 127
+    m = rng.integers(0, 128, size=shape)
+    s = rng.integers(0, 2, size=shape)
+    return ((s << 15) | (e << 7) | m).astype(np.uint16)
+
+
+def padded(bits, ld_extra=8):
+    """GPU view of a [R, C] matrix whose leading dimension exceeds its width."""
+    R, C = bits.shape
+    ld = ((C + 7) // 8) * 8 + ld_extra
+    full = np.zeros((R, ld), np.uint16)
+    full[:, :C] = bits
+    return dev(full)[:, :C]
+
+
+# ---------------------------------------------------------------- tree GEMMs
+SHAPES = [(1, 16, 64), (4, 48, 256), (5, 33, 100), (16, 20, 24), (17, 100, 1000), (32, 64, 4096),
+          (33, 40, 768), (64, 16, 192), (3, 7, 8), (40, 130, 520), (2, 1, 12288)]
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+@pytest.mark.parametrize("layout", ["NT", "NN", "TN"])
+def test_gemm_tree_matches_oracle(layout, M, N, K):
+    rng = np.random.default_rng(M * 1000 + N * 10 + K)
+    A = rnd(rng, (M, K)); Bnk = rnd(rng, (N, K), 0.02)
+    if layout == "NT":
+        a, b = A, Bnk
+    elif layout == "NN":
+        a, b = A, np.ascontiguousarray(Bnk.T)
+    else:
+        a, b = np.ascontiguousarray(A.T), np.ascontiguousarray(Bnk.T)
+    expect = oracle.gemm_tree(a, b, layout)
+    got = dgf.gemm_tree(layout, padded(a), padded(b))
+    torch.cuda.synchronize()
+    assert_bitwise(got, expect, f"{layout} {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("dist", ["wide", "wide60", "cancel", "tiny", "ties"])
+@pytest.mark.parametrize("K", [8, 32, 64, 128, 200])
+def test_leaf_block_rule_adversarial(dist, K):
+    # The FP32 leaf's accumulation rule on inputs that separate it from other
+    # summation orders (wide exponents, cancellation, near-ties, tiny products).
+    rng = np.random.default_rng(zlib.crc32(f"{dist}/{K}".encode()))
+    M, N = 32, 48
+    if dist == "wide":
+        A, B = wide(rng, (M, K)), wide(rng, (N, K))
+    elif dist == "wide60":
+        A, B = wide(rng, (M, K), -60, 60), wide(rng, (N, K), -60, 60)
+    elif dist == "cancel":
+        A = wide(rng, (M, K), -6, 6); B = F2B(np.ones((N, K), np.float32))
+        A[:, K // 2:] = A[:, :K - K // 2][:, :K // 2] ^ np.uint16(0x8000)
+        A[:, ::7] = wide(rng, (M, len(range(0, K, 7))), -40, -20)
+        B = np.where(rng.random((N, K)) < 0.2, wide(rng, (N, K), -2, 2), B).astype(np.uint16)
+    elif dist == "tiny":
+        A, B = wide(rng, (M, K), -70, -55), wide(rng, (N, K), -70, -55)
+    else:
+        A = F2B((np.where(rng.random((M, K)) < 0.3, 2.0 ** -rng.integers(22, 27, (M, K)), 0)
+                 * np.where(rng.random((M, K)) < 0.7, 1, -1)).astype(np.float32))
+        A[:, 0] = F2B(np.ones(M, np.float32))
+        B = F2B(np.ones((N, K), np.float32))
+    expect = oracle.gemm_tree(A, B, "NT")
+    got = dgf.gemm_tree("NT", dev(A), dev(B))
+    torch.cuda.synchronize()
+    assert_bitwise(got, expect, f"leaf {dist} K={K}")
+
+
+def test_gemm_k_zero_and_m_zero():
+    A = torch.zeros((4, 0), dtype=torch.bfloat16, device="cuda")
+    B = torch.zeros((8, 0), dtype=torch.bfloat16, device="cuda")
+    C = dgf.gemm_tree("NT", A, B)
+    torch.cuda.synchronize()
+    assert (C.float() == 0).all()
+    A0 = torch.zeros((0, 64), dtype=torch.bfloat16, device="cuda")
+    assert dgf.gemm_tree("NT", A0, torch.zeros((8, 64), dtype=torch.bfloat16, device="cuda")).shape == (0, 8)
+
+
+# ---------------------------------------------------------------- activation
+def test_activation_exhaustive_over_gate_values():
+    rng = np.random.default_rng(1)
+    g = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    gf = B2F(g)
+    g = g[np.isfinite(gf)]
+    u = rnd(rng, g.size); da = rnd(rng, g.size)
+    a_ref = oracle.act_fwd(g, u)
+    dg_ref, du_ref, a2_ref = oracle.act_bwd(da, g, u)
+    gd, ud, dad = dev(g), dev(u), dev(da)
+    a = dgf.act_fwd(gd, ud)
+    dg, du, a2 = dgf.act_bwd(dad, gd, ud)
+    torch.cuda.synchronize()
+    assert_bitwise(a, a_ref, "a")
+    assert_bitwise(dg, dg_ref, "dG")
+    assert_bitwise(du, du_ref, "dU")
+    assert_bitwise(a2, a2_ref, "a (backward)")
+
+
+# ---------------------------------------------------------------- combine
+@pytest.mark.parametrize("S", [1, 2, 4, 8])
+@pytest.mark.parametrize("n", [1, 7, 8, 1000, 4097])
+def test_tree_combine(S, n):
+    rng = np.random.default_rng(S * 7 + n)
+    parts = [rnd(rng, n) for _ in range(S)]
+    expect = oracle.tree_combine(parts)
+    got = dgf.tree_combine([dev(p) for p in parts])
+    torch.cuda.synchronize()
+    assert_bitwise(got, expect, f"combine S={S} n={n}")
+    # offset (unaligned) views take the element path with the same arithmetic
+    bufs = [torch.zeros(n + 1, dtype=torch.bfloat16, device="cuda") for _ in range(S)]
+    for b, p in zip(bufs, parts):
+        b[1:] = dev(p)
+    out = torch.zeros(n + 1, dtype=torch.bfloat16, device="cuda")
+    dgf.tree_combine_ptrs([b.data_ptr() + 2 for b in bufs], S, out.data_ptr() + 2, n)
+    torch.cuda.synchronize()
+    assert_bitwise(out[1:], expect, f"combine offset S={S} n={n}")
+    # in place into parts[0]
+    p0 = [dev(p) for p in parts]
+    dgf.tree_combine(p0, out=p0[0])
+    torch.cuda.synchronize()
+    assert_bitwise(p0[0], expect, f"combine in place S={S} n={n}")
+
+
+def test_tree_combine_hand_worked_and_errors():
+    one, a = 0x3F80, 0x3B80
+    vals = np.array([one, a, a, a, a, a, a, a], np.uint16)
+    parts = [dev(np.array([v], np.uint16)) for v in vals]
+    assert int(inputs.bits(dgf.tree_combine(parts))[0]) == 0x3F83
+    with pytest.raises(dgf.DgfError):
+        dgf.tree_combine(parts[:3])
+
+
+# ---------------------------------------------------------------- the FFN
+def _tiny():
+    c = inputs.tiny_case()
+    return c, {k: inputs.bits(v) for k, v in c.items()}
+
+
+def test_tiny_ffn_forward_backward_bitwise():
+    c, b = _tiny()
+    o = oracle.ffn_fwd(b["x"], b["w_gate"], b["w_up"], b["w_down"])
+    ob = oracle.ffn_bwd(b["dy"], b["x"], o["g"], o["u"], b["w_gate"], b["w_up"], b["w_down"])
+    d = {k: v.cuda() for k, v in c.items()}
+    y, g, u = dgf.ffn_fwd(d["x"], d["w_gate"], d["w_up"], d["w_down"], training=True)
+    y_inf = dgf.ffn_fwd(d["x"], d["w_gate"], d["w_up"], d["w_down"])
+    r = dgf.ffn_bwd(d["dy"], d["x"], g, u, d["w_gate"], d["w_up"], d["w_down"], lanes=True)
+    torch.cuda.synchronize()
+    assert_bitwise(g, o["g"], "g"); assert_bitwise(u, o["u"], "u"); assert_bitwise(y, o["y"], "y")
+    assert_bitwise(y_inf, o["y"], "y (inference)")
+    for k in ("dX", "G", "U", "dW_gate", "dW_up", "dW_down"):
+        assert_bitwise(r[k], ob[k], k)
+    f = fp64.ffn_fwd(b["x"], b["w_gate"], b["w_up"], b["w_down"])
+    fb = fp64.ffn_bwd(b["dy"], b["x"], b["w_gate"], b["w_up"], b["w_down"])
+    assert fp64.rel_l2(inputs.bits(y), f["y"]) <= 1e-2
+    for k in ("dX", "dW_gate", "dW_up", "dW_down"):
+        assert fp64.rel_l2(inputs.bits(r[k]), fb[k]) <= 1e-2, k
+
+
+@pytest.mark.parametrize("M,H,I", [(1, 64, 64), (3, 128, 320), (20, 256, 768), (37, 200, 136), (64, 128, 256)])
+def test_ffn_other_shapes_bitwise(M, H, I):
+    rng = np.random.default_rng(M + H + I)
+    x, dy = rnd(rng, (M, H)), rnd(rng, (M, H))
+    wg, wu, wd = rnd(rng, (I, H), 0.02), rnd(rng, (I, H), 0.02), rnd(rng, (H, I), 0.02)
+    o = oracle.ffn_fwd(x, wg, wu, wd)
+    ob = oracle.ffn_bwd(dy, x, o["g"], o["u"], wg, wu, wd)
+    y, g, u = dgf.ffn_fwd(padded(x), padded(wg), padded(wu), padded(wd), training=True)
+    r = dgf.ffn_bwd(padded(dy), padded(x), g, u, padded(wg), padded(wu), padded(wd), lanes=True)
+    torch.cuda.synchronize()
+    assert_bitwise(y, o["y"], "y")
+    for k in ("dX", "G", "U", "dW_gate", "dW_up", "dW_down"):
+        assert_bitwise(r[k], ob[k], k)
+
+
+# ---------------------------------------------------------------- Qwen3-8B shapes
+@pytest.fixture(scope="module")
+def qwen_weights():
+    wg, wu, wd = inputs.ffn_weights()
+    return (wg, wu, wd), (wg.cuda(), wu.cuda(), wd.cuda())
+
+
+def test_repeat_and_batch_invariance(qwen_weights):
+    _, (wg, wu, wd) = qwen_weights
+    x32, dy32 = (t.cuda() for t in inputs.activations(32))
+    ys = [inputs.bits(dgf.ffn_fwd(x32, wg, wu, wd)) for _ in range(3)]
+    assert all((y == ys[0]).all() for y in ys), "forward not bitwise repeatable"
+    y, g, u = dgf.ffn_fwd(x32, wg, wu, wd, training=True)
+    b1 = dgf.ffn_bwd(dy32, x32, g, u, wg, wu, wd)
+    b2 = dgf.ffn_bwd(dy32, x32, g, u, wg, wu, wd)
+    torch.cuda.synchronize()
+    assert (inputs.bits(y) == ys[0]).all(), "training forward differs from inference"
+    for k in b1:
+        assert (inputs.bits(b1[k]) == inputs.bits(b2[k])).all(), f"{k} not bitwise repeatable"
+    for M in (1, 8):
+        yM = inputs.bits(dgf.ffn_fwd(x32[:M], wg, wu, wd))
+        assert (yM == ys[0][:M]).all(), f"M={M} rows differ from the M=32 rows"
+
+
+def test_full_size_forward_backward_vs_oracle(qwen_weights):
+    (wg_c, wu_c, wd_c), (wg, wu, wd) = qwen_weights
+    x_c, dy_c = inputs.activations(32)
+    x, dy = x_c.cuda(), dy_c.cuda()
+    y, g, u = dgf.ffn_fwd(x, wg, wu, wd, training=True)
+    r = dgf.ffn_bwd(dy, x, g, u, wg, wu, wd, lanes=True)
+    torch.cuda.synchronize()
+    B = {k: inputs.bits(v) for k, v in (("x", x_c), ("dy", dy_c), ("wg", wg_c), ("wu", wu_c), ("wd", wd_c))}
+    o = oracle.ffn_fwd(B["x"], B["wg"], B["wu"], B["wd"])
+    for k, t in (("g", g), ("u", u), ("y", y)):
+        assert_bitwise(t, o[k], k)
+    # backward: all of dA-driven dX; dW on sampled rows (the oracle is slow at 50M outputs)
+    da = oracle.gemm_tree(B["dy"], B["wd"], "NN")
+    dg, du, a = oracle.act_bwd(da, o["g"], o["u"])
+    G = oracle.gemm_tree(dg, B["wg"], "NN"); U = oracle.gemm_tree(du, B["wu"], "NN")
+    assert_bitwise(r["G"], G, "G lane"); assert_bitwise(r["U"], U, "U lane")
+    assert_bitwise(r["dX"], oracle.tree_combine([G, U]).reshape(G.shape), "dX")
+    rows = np.random.default_rng(0).choice(12288, 48, replace=False)
+    rows_h = np.random.default_rng(1).choice(4096, 48, replace=False)
+    dwg_ref = oracle.gemm_tree(np.ascontiguousarray(dg[:, rows]), B["x"], "TN")
+    dwu_ref = oracle.gemm_tree(np.ascontiguousarray(du[:, rows]), B["x"], "TN")
+    dwd_ref = oracle.gemm_tree(np.ascontiguousarray(B["dy"][:, rows_h]), a, "TN")
+    assert_bitwise(r["dW_gate"][rows.tolist()], dwg_ref, "dW_gate rows")
+    assert_bitwise(r["dW_up"][rows.tolist()], dwu_ref, "dW_up rows")
+    assert_bitwise(r["dW_down"][rows_h.tolist()], dwd_ref, "dW_down rows")
+    # float64 brute force: relative L2 <= 1e-2
+    f = fp64.ffn_fwd(B["x"], B["wg"], B["wu"], B["wd"])
+    assert fp64.rel_l2(inputs.bits(y), f["y"]) <= 1e-2
+    fb = fp64.ffn_bwd(B["dy"], B["x"], B["wg"], B["wu"], B["wd"])
+    assert fp64.rel_l2(inputs.bits(r["dX"]), fb["dX"]) <= 1e-2
+    assert fp64.rel_l2(inputs.bits(r["dW_gate"])[rows], fb["dW_gate"][rows]) <= 1e-2
+
+
+@pytest.mark.parametrize("S", [2, 4, 8])
+def test_shard_invariance(qwen_weights, S):
+    # Contiguous K shards computed as separate partial GEMMs and combined with the
+    # balanced tree equal the unsharded result bit for bit (PR #325 "Design").
+    _, (wg, wu, wd) = qwen_weights
+    H, I = 4096, 12288
+    x, dy = (t.cuda() for t in inputs.activations(32))
+    y, g, u = dgf.ffn_fwd(x, wg, wu, wd, training=True)
+    full = dgf.ffn_bwd(dy, x, g, u, wg, wu, wd, lanes=True)
+    Is, Hs = I // S, H // S
+    # I-shards: the forward's down projection (K = I) and the backward's dX lanes (K = I)
+    ys, Gs, Us = [], [], []
+    for r in range(S):
+        sl = slice(r * Is, (r + 1) * Is)
+        yr, gr, ur = dgf.ffn_fwd(x, wg[sl], wu[sl], wd[:, sl], training=True)
+        br = dgf.ffn_bwd(dy, x, gr, ur, wg[sl], wu[sl], wd[:, sl], lanes=True)
+        ys.append(yr.contiguous()); Gs.append(br["G"].contiguous()); Us.append(br["U"].contiguous())
+        # dW under I-shards are slices of the unsharded dW (K = M is not sharded)
+        assert (inputs.bits(br["dW_gate"]) == inputs.bits(full["dW_gate"][sl])).all()
+        assert (inputs.bits(br["dW_down"]) == inputs.bits(full["dW_down"][:, sl])).all()
+    y_c = dgf.tree_combine(ys)
+    G_c, U_c = dgf.tree_combine(Gs), dgf.tree_combine(Us)
+    dx_c = dgf.tree_combine([G_c, U_c])  # gate lane first, then up
+    # H-shards: gate/up (K = H) and dA (K = H)
+    g_parts = [dgf.gemm_tree("NT", x[:, r * Hs:(r + 1) * Hs], wg[:, r * Hs:(r + 1) * Hs]).contiguous() for r in range(S)]
+    da_parts = [dgf.gemm_tree("NN", dy[:, r * Hs:(r + 1) * Hs], wd[r * Hs:(r + 1) * Hs]).contiguous() for r in range(S)]
+    g_c = dgf.tree_combine(g_parts)
+    da_c = dgf.tree_combine(da_parts)
+    da_full = dgf.gemm_tree("NN", dy, wd)
+    torch.cuda.synchronize()
+    for got, ref, name in ((y_c, y, "y"), (G_c, full["G"], "G"), (U_c, full["U"], "U"), (dx_c, full["dX"], "dX"),
+                           (g_c, g, "g"), (da_c, da_full, "dA")):
+        gb, rb = inputs.bits(got), inputs.bits(ref.contiguous())
+        assert int((gb != rb).sum()) == 0, f"S={S} {name}: {(gb != rb).sum()} mismatches vs unsharded"
+
+
+def test_bad_arguments_raise():
+    x = torch.zeros((4, 256), dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros((768, 256), dtype=torch.bfloat16, device="cuda")
+    wd = torch.zeros((256, 768), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(dgf.DgfError) as e:
+        dgf.ffn_fwd(x[:, 1:], w[:, 1:], w[:, 1:], wd[1:])  # misaligned views
+    assert e.value.status == 1
