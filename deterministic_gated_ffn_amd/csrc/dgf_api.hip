@@ -91,13 +91,6 @@ size_t round256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 int leaves(int64_t K) { return (int)((K + 63) / 64); }
 
-// Waves per workgroup: the largest power of two <= min(8, L).
-int pick_waves(int L) {
-  int w = 1;
-  while (w * 2 <= 8 && w * 2 <= L) w *= 2;
-  return w;
-}
-
 // Depth of the midpoint tree over n leaves: ceil(log2 n).
 int tree_depth(int n) {
   int d = 0;
@@ -111,21 +104,81 @@ GemmParams blank() {
   return p;
 }
 
-dgf_status run_gemm(int layout, int nb, int epi, GemmParams p, hipStream_t s, const char *what) {
+// Launch shape of one tree GEMM.  A workgroup holds at most 8 waves; the grid
+// aims at every workgroup being resident at once (no second round of
+// workgroups) with at least 6 waves per CU on 256 CUs.  `per_cu` is the waves
+// a CU holds for the kernel variant (register-bound).  Narrow outputs (few
+// 16-column tiles) split the K leaves over 2, 4 or 8 workgroups (each a
+// subtree), whose roots a combine kernel joins; only plain-store GEMMs do so.
+struct Plan {
+  int waves = 1, kdepth = 0, slots = 1;
+  size_t lds = 0;
+};
+
+constexpr int64_t kCUs = 256;
+
+Plan plan_gemm(int layout, int nb, int epi, int64_t M, int64_t N, int64_t K) {
+  Plan pl;
+  if (layout == DGF_LAYOUT_NT && epi == EPI_STORE && K <= 64) return pl;  // the one-leaf kernel
+  const int L = leaves(K);
+  const int mt = M <= 16 ? 1 : 2;
+  const int64_t tiles = ((N + 15) / 16) * ((M + 16 * mt - 1) / (16 * mt));
+  const int64_t per_cu = (nb == 2 && mt == 2) ? 8 : 12;
+  const int64_t capacity = per_cu * kCUs;
+  pl.waves = 1;
+  while (pl.waves * 2 <= 8 && pl.waves * 2 <= L && tiles * pl.waves * 2 <= capacity) pl.waves *= 2;
+  if (epi == EPI_STORE)
+    while (pl.kdepth < 3 && tiles * (pl.waves << pl.kdepth) < 6 * kCUs &&
+           tiles * (pl.waves << (pl.kdepth + 1)) <= capacity && (L >> (pl.kdepth + 1)) >= 4 * pl.waves)
+      ++pl.kdepth;
+  const int depth = pl.kdepth + tree_depth(pl.waves);
+  const int per_wave = (L + (1 << depth) - 1) >> depth;  // largest subtree at that depth
+  pl.slots = tree_depth(per_wave) > 1 ? tree_depth(per_wave) : 1;
+  pl.lds = (size_t)pl.waves * pl.slots * (nb * mt * 2) * 64 * 4 +
+           (layout == DGF_LAYOUT_NN ? (size_t)pl.waves * nb * 16 * 72 * 2 : 0);
+  return pl;
+}
+
+// Workspace bytes for the K-split partial roots of one GEMM (0 without a split).
+size_t partial_bytes(int layout, int nb, int epi, int64_t M, int64_t N, int64_t K) {
+  const Plan pl = plan_gemm(layout, nb, epi, M, N, K);
+  if (pl.kdepth == 0 || M == 0 || N == 0) return 0;
+  return round256((size_t)nb * ((size_t)1 << pl.kdepth) * M * round8(N) * 2);
+}
+
+// One tree GEMM: the MFMA kernel, then (K split) the combine of the partials.
+// `partials` must hold partial_bytes() of workspace.
+dgf_status run_gemm(int layout, int nb, int epi, GemmParams p, hipStream_t s, const char *what,
+                    uint16_t *partials = nullptr) {
   if (p.M == 0 || p.N == 0) return DGF_OK;
   if ((p.M + 31) / 32 > 65535 || (p.N + 15) / 16 > 0x7fffffff)
     return fail(DGF_EUNSUPPORTED, "%s: %lld x %lld output exceeds the launch grid", what, (long long)p.M, (long long)p.N);
   p.L = leaves(p.K);
-  const int waves = pick_waves(p.L);
-  // LDS tree stack: one slot per level of the deepest wave subtree
-  const int per_wave = (p.L + waves - 1) / waves;
-  p.stack_slots = tree_depth(per_wave) > 1 ? tree_depth(per_wave) : 1;
-  const int mt = p.M <= 16 ? 1 : 2;
-  const size_t lds_bytes = (size_t)waves * p.stack_slots * (nb * mt * 2) * 64 * 4 +
-                           (layout == DGF_LAYOUT_NN ? (size_t)waves * nb * 16 * 72 * 2 : 0);
-  if (lds_bytes > 64 * 1024)
-    return fail(DGF_EUNSUPPORTED, "%s: K=%lld needs %zu bytes of LDS for the tree stack", what, (long long)p.K, lds_bytes);
-  return hip_check(timed(s, what, [&] { return launch_gemm(layout, nb, epi, p, waves, s); }), what);
+  if (layout == DGF_LAYOUT_NT && epi == EPI_STORE && p.K <= 64 && (nb == 1 || p.B[1] == p.B[0]) &&
+      (p.M + 63) / 64 <= 65535)
+    return hip_check(timed(s, what, [&] { return launch_gemm_short(nb, p, s); }), what);
+  const Plan pl = plan_gemm(layout, nb, epi, p.M, p.N, p.K);
+  p.stack_slots = pl.slots;
+  p.ksplit_depth = pl.kdepth;
+  if (pl.lds > 64 * 1024)
+    return fail(DGF_EUNSUPPORTED, "%s: K=%lld needs %zu bytes of LDS for the tree stack", what, (long long)p.K, pl.lds);
+  if (pl.kdepth > 0) {
+    if (!partials) return fail(DGF_EWORKSPACE, "%s: no workspace for the K-split partials", what);
+    p.part = partials;
+    p.ldp = round8(p.N);
+    p.part_stride = p.M * p.ldp;
+  }
+  DGF_TRY(hip_check(timed(s, what, [&] { return launch_gemm(layout, nb, epi, p, pl.waves, s); }), what));
+  if (pl.kdepth > 0) {
+    const int S = 1 << pl.kdepth;
+    for (int b = 0; b < nb; ++b)
+      DGF_TRY(hip_check(timed(s, "K-split combine", [&] {
+                          return launch_combine_2d(p.part + (int64_t)b * S * p.part_stride, p.part_stride, p.ldp, S,
+                                                   p.C[b], p.ldc[b], p.M, p.N, s);
+                        }),
+                        "K-split combine"));
+  }
+  return DGF_OK;
 }
 
 // Zero-fill an [M, N] output (K = 0 products).
@@ -155,23 +208,33 @@ struct Carve {
   }
 };
 
+size_t bwd_partials(int64_t M, int64_t H, int64_t I) {
+  size_t a = partial_bytes(DGF_LAYOUT_NN, 1, EPI_STORE, M, H, I);             // dX lanes
+  size_t b = partial_bytes(DGF_LAYOUT_NT, 2, EPI_STORE, I, H, M);             // dW_gate, dW_up
+  size_t c = partial_bytes(DGF_LAYOUT_NT, 1, EPI_STORE, H, I, M);             // dW_down
+  return a > b ? (a > c ? a : c) : (b > c ? b : c);
+}
+
 size_t bwd_ws_bytes(int64_t M, int64_t H, int64_t I) {
   const int64_t Mp = round8(M);
-  return round256((size_t)M * round8(I) * 2) * 2  // dG, dU row-major [M, I] (ld = I rounded to 8)
-         + round256((size_t)I * Mp * 2) * 3       // dG^T, dU^T, a^T [I, Mp]
-         + round256((size_t)H * Mp * 2) * 2       // x^T, dY^T [H, Mp]
-         + round256((size_t)M * round8(H) * 2) * 2;  // the dX lanes G, U [M, H]
+  return round256((size_t)M * round8(I) * 2) * 2     // dG, dU row-major [M, I] (ld = I rounded to 8)
+         + round256((size_t)I * Mp * 2) * 3          // dG^T, dU^T, a^T [I, Mp]
+         + round256((size_t)H * Mp * 2) * 2          // x^T, dY^T [H, Mp]
+         + round256((size_t)M * round8(H) * 2) * 2   // the dX lanes G, U [M, H]
+         + bwd_partials(M, H, I);                    // K-split partial roots
 }
 
 size_t fwd_ws_bytes(int64_t M, int64_t H, int64_t I) {
-  (void)H;
-  return round256((size_t)M * round8(I) * 2);  // a [M, I]
+  return round256((size_t)M * round8(I) * 2)                     // a [M, I]
+         + partial_bytes(DGF_LAYOUT_NT, 1, EPI_STORE, M, H, I);  // down-projection partial roots
 }
 
 size_t gemm_ws_bytes(int layout, int64_t M, int64_t N, int64_t K) {
-  if (layout != DGF_TN) return 0;
+  const int lay = layout == DGF_NN ? DGF_LAYOUT_NN : DGF_LAYOUT_NT;
+  size_t b = partial_bytes(lay, 1, EPI_STORE, M, N, K);
+  if (layout != DGF_TN) return b;
   const int64_t Kp = round8(K);
-  return round256((size_t)M * Kp * 2) + round256((size_t)N * Kp * 2);
+  return round256((size_t)M * Kp * 2) + round256((size_t)N * Kp * 2) + b;
 }
 
 }  // namespace
@@ -235,6 +298,7 @@ dgf_status dgf_ffn_fwd(const void *x, int64_t ldx, const void *w_gate, int64_t l
   Carve cv{(char *)ws, 0};
   uint16_t *a = cv.take((size_t)M * round8(I));
   const int64_t lda_ = round8(I);
+  uint16_t *partials = (uint16_t *)((char *)ws + cv.used);
 
   GemmParams p = blank();
   p.A[0] = p.A[1] = (const uint16_t *)x;
@@ -260,7 +324,7 @@ dgf_status dgf_ffn_fwd(const void *x, int64_t ldx, const void *w_gate, int64_t l
   q.C[0] = (uint16_t *)y;
   q.ldc[0] = ldy;
   q.M = M; q.N = H; q.K = I;
-  DGF_TRY(run_gemm(DGF_LAYOUT_NT, 1, EPI_STORE, q, s, "down tree GEMM"));
+  DGF_TRY(run_gemm(DGF_LAYOUT_NT, 1, EPI_STORE, q, s, "down tree GEMM", partials));
   return ok();
 }
 
@@ -305,6 +369,7 @@ dgf_status dgf_ffn_bwd(const void *dy, int64_t lddy, const void *x, int64_t ldx,
   uint16_t *xT = cv.take((size_t)H * Mp), *dYT = cv.take((size_t)H * Mp);
   const int64_t ld_lane = round8(H);
   uint16_t *Gw = cv.take((size_t)M * ld_lane), *Uw = cv.take((size_t)M * ld_lane);
+  uint16_t *partials = (uint16_t *)((char *)ws + cv.used);
 
   DGF_TRY(hip_check(timed(s, "transpose x", [&] { return launch_transpose((const uint16_t *)x, ldx, M, H, xT, Mp, s); }),
                     "transpose x"));
@@ -339,7 +404,8 @@ dgf_status dgf_ffn_bwd(const void *dy, int64_t lddy, const void *x, int64_t ldx,
     q.C[0] = lane_i == 0 ? G : U;
     q.ldc[0] = lane_i == 0 ? ldG : ldU;
     q.M = M; q.N = H; q.K = I;
-    DGF_TRY(run_gemm(DGF_LAYOUT_NN, 1, EPI_STORE, q, s, lane_i == 0 ? "dX gate-lane tree GEMM" : "dX up-lane tree GEMM"));
+    DGF_TRY(run_gemm(DGF_LAYOUT_NN, 1, EPI_STORE, q, s, lane_i == 0 ? "dX gate-lane tree GEMM" : "dX up-lane tree GEMM",
+                     partials));
   }
   // dX = bf16(G + U): the ordered add, gate lane first
   if (dx)
@@ -355,7 +421,7 @@ dgf_status dgf_ffn_bwd(const void *dy, int64_t lddy, const void *x, int64_t ldx,
   w.C[0] = (uint16_t *)dw_gate; w.ldc[0] = ld_dwg;
   w.C[1] = (uint16_t *)dw_up; w.ldc[1] = ld_dwu;
   w.M = I; w.N = H; w.K = M;
-  DGF_TRY(run_gemm(DGF_LAYOUT_NT, 2, EPI_STORE, w, s, "dW_gate/dW_up tree GEMM"));
+  DGF_TRY(run_gemm(DGF_LAYOUT_NT, 2, EPI_STORE, w, s, "dW_gate/dW_up tree GEMM", partials));
 
   // dW_down = T_M(dY^T a)
   GemmParams v = blank();
@@ -363,7 +429,7 @@ dgf_status dgf_ffn_bwd(const void *dy, int64_t lddy, const void *x, int64_t ldx,
   v.B[0] = aT; v.ldb[0] = Mp;
   v.C[0] = (uint16_t *)dw_down; v.ldc[0] = ld_dwd;
   v.M = H; v.N = I; v.K = M;
-  DGF_TRY(run_gemm(DGF_LAYOUT_NT, 1, EPI_STORE, v, s, "dW_down tree GEMM"));
+  DGF_TRY(run_gemm(DGF_LAYOUT_NT, 1, EPI_STORE, v, s, "dW_down tree GEMM", partials));
   return ok();
 }
 
@@ -419,17 +485,18 @@ dgf_status dgf_gemm_tree(int layout, const void *A, int64_t lda, const void *B, 
     const int64_t Kp = round8(K);
     Carve cv{(char *)ws, 0};
     uint16_t *AT = cv.take((size_t)M * Kp), *BT = cv.take((size_t)N * Kp);
+    uint16_t *partials = (uint16_t *)((char *)ws + cv.used);
     DGF_TRY(hip_check(timed(s, "transpose A", [&] { return launch_transpose((const uint16_t *)A, lda, K, M, AT, Kp, s); }),
                       "transpose A"));
     DGF_TRY(hip_check(timed(s, "transpose B", [&] { return launch_transpose((const uint16_t *)B, ldb, K, N, BT, Kp, s); }),
                       "transpose B"));
     p.A[0] = AT; p.lda[0] = Kp;
     p.B[0] = BT; p.ldb[0] = Kp;
-    DGF_TRY(run_gemm(DGF_LAYOUT_NT, 1, EPI_STORE, p, s, "TN tree GEMM"));
+    DGF_TRY(run_gemm(DGF_LAYOUT_NT, 1, EPI_STORE, p, s, "TN tree GEMM", partials));
   } else {
     p.A[0] = (const uint16_t *)A; p.lda[0] = lda;
     p.B[0] = (const uint16_t *)B; p.ldb[0] = ldb;
-    DGF_TRY(run_gemm(layout == DGF_NT ? DGF_LAYOUT_NT : DGF_LAYOUT_NN, 1, EPI_STORE, p, s, "tree GEMM"));
+    DGF_TRY(run_gemm(layout == DGF_NT ? DGF_LAYOUT_NT : DGF_LAYOUT_NN, 1, EPI_STORE, p, s, "tree GEMM", (uint16_t *)ws));
   }
   return ok();
 }

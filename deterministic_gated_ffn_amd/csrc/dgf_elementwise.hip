@@ -82,6 +82,44 @@ __global__ __launch_bounds__(kThreads) void k_combine_scalar(Parts parts, uint16
   }
 }
 
+// out[m][n] = balanced combine over S partial roots (the top levels of the
+// tree above the workgroups' K pieces); 8 elements per thread.
+template <int S>
+__global__ __launch_bounds__(kThreads) void k_combine_2d(const uint16_t *part, int64_t part_stride, int64_t ldp,
+                                                         uint16_t *out, int64_t ldo, int64_t M, int64_t N) {
+  const int64_t per_row = (N + 7) / 8;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < M * per_row; i += (int64_t)gridDim.x * kThreads) {
+    const int64_t m = i / per_row, c = (i % per_row) * 8;
+    uint16_t *o = out + m * ldo + c;
+    if (c + 8 <= N) {
+      uint32_t r[S][4];
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        const uint4 v = *reinterpret_cast<const uint4 *>(part + s * part_stride + m * ldp + c);
+        r[s][0] = v.x; r[s][1] = v.y; r[s][2] = v.z; r[s][3] = v.w;
+      }
+#pragma unroll
+      for (int width = S; width > 1; width >>= 1)
+#pragma unroll
+        for (int j = 0; j < width / 2; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) r[j][q] = node2(r[2 * j][q], r[2 * j + 1][q]);
+      *reinterpret_cast<uint4 *>(o) = make_uint4(r[0][0], r[0][1], r[0][2], r[0][3]);
+    } else {
+      for (int64_t e = 0; c + e < N; ++e) {
+        float r[S];
+#pragma unroll
+        for (int s = 0; s < S; ++s) r[s] = bf2f(part[s * part_stride + m * ldp + c + e]);
+#pragma unroll
+        for (int width = S; width > 1; width >>= 1)
+#pragma unroll
+          for (int j = 0; j < width / 2; ++j) r[j] = bf2f(f2bf(r[2 * j] + r[2 * j + 1]));
+        o[e] = f2bf(r[0]);
+      }
+    }
+  }
+}
+
 // dx = bf16(G + U), the gate contribution first (an FP32 add of two BF16 lanes,
 // rounded to BF16); 8 elements per thread, rows of N (a multiple of 8 leading dims).
 __global__ __launch_bounds__(kThreads) void k_add_lanes(const uint16_t *G, int64_t ldg, const uint16_t *U, int64_t ldu,
@@ -156,6 +194,18 @@ hipError_t launch_combine(const uint16_t *const *parts, int S, uint16_t *out, in
       case 4: hipLaunchKernelGGL(k_combine_scalar<4>, g, dim3(kThreads), 0, s, P, out, begin, n); break;
       default: hipLaunchKernelGGL(k_combine_scalar<8>, g, dim3(kThreads), 0, s, P, out, begin, n); break;
     }
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_2d(const uint16_t *part, int64_t part_stride, int64_t ldp, int S, uint16_t *out, int64_t ldo,
+                             int64_t M, int64_t N, hipStream_t s) {
+  const dim3 g(grid_for(M * ((N + 7) / 8), 1));
+  switch (S) {
+    case 1: hipLaunchKernelGGL(k_combine_2d<1>, g, dim3(kThreads), 0, s, part, part_stride, ldp, out, ldo, M, N); break;
+    case 2: hipLaunchKernelGGL(k_combine_2d<2>, g, dim3(kThreads), 0, s, part, part_stride, ldp, out, ldo, M, N); break;
+    case 4: hipLaunchKernelGGL(k_combine_2d<4>, g, dim3(kThreads), 0, s, part, part_stride, ldp, out, ldo, M, N); break;
+    default: hipLaunchKernelGGL(k_combine_2d<8>, g, dim3(kThreads), 0, s, part, part_stride, ldp, out, ldo, M, N); break;
   }
   return hipGetLastError();
 }

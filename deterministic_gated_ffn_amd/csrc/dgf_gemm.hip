@@ -1,11 +1,14 @@
 // Deterministic tree GEMMs for gfx950.
 //
 // One workgroup owns a tile of 16 output columns n (weight rows in the NT form)
-// and 16*MT output rows m (tokens).  Its WAVES waves split the K leaves into
-// the WAVES subtrees at depth log2(WAVES) of the canonical midpoint tree; each
-// wave runs its subtree in post order, then wave 0 combines the WAVES roots
-// through LDS with the balanced top of the tree (RL-Kernel PR #325, section
-// "Design": contiguous K pieces are subtrees of the one canonical tree).
+// and 16*MT output rows m (tokens), for one of KSPLIT contiguous K pieces: the
+// subtree at depth log2(KSPLIT) of the canonical midpoint tree over the K
+// leaves.  Its WAVES waves split that piece further into the subtrees one
+// level log2(WAVES) deeper; each wave runs its subtree in post order, then
+// wave 0 combines the WAVES roots with the balanced top of the subtree.  With
+// KSPLIT > 1 the workgroup roots go to a partial buffer and a combine kernel
+// finishes the balanced top of the tree (RL-Kernel PR #325, section "Design":
+// contiguous K pieces are subtrees of the one canonical tree).
 //
 // MFMA roles: A operand = 16 weight rows x 32 K, B operand = 32 K x 16 tokens,
 // so lane l ends with D[4(l/16)+r][l%16]: four consecutive output columns of
@@ -56,16 +59,30 @@ __device__ __forceinline__ void store4(uint16_t *C, int64_t ldc, int64_t m, int6
   }
 }
 
+template <int W>
+constexpr int log2i() {
+  return W == 1 ? 0 : W == 2 ? 1 : W == 4 ? 2 : W == 8 ? 3 : 4;
+}
+
+// Streamed-once weight fragment: a non-temporal 16-byte load.
+__device__ __forceinline__ bf16x8 load_frag_nt(const uint16_t *row, int64_t k) {
+  return __builtin_nontemporal_load(reinterpret_cast<const bf16x8 *>(row + k));
+}
+
 // ------------------------------------------------------------------ NT
 
 // C_b[m][n] = T_K( A_b[m,:] . B_b[n,:] ), b < NB; A_b [M,K] and B_b [N,K] both
-// K-contiguous.
+// K-contiguous.  Weight and activation fragments are loaded D leaves ahead of
+// the MFMAs that use them, both at the same distance: loads complete in issue
+// order, so an activation load issued after a weight load would otherwise make
+// the wait for it also wait for that younger weight load.
 template <int NB, int MT, int WAVES, int EPI>
 __global__ __launch_bounds__(WAVES * 64) void k_gemm_nt(GemmParams p) {
-  // gate and up share the activation operand
-  constexpr bool SHARED_A = (EPI == EPI_ACT);
+  constexpr bool SHARED_A = (EPI == EPI_ACT);  // gate and up share the activation operand
+  constexpr int NA = SHARED_A ? 1 : NB;
   constexpr int NP = NB * MT * 2;
-  constexpr int DEPTH = WAVES == 1 ? 0 : WAVES == 2 ? 1 : WAVES == 4 ? 2 : 3;
+  constexpr int DW = log2i<WAVES>();
+  constexpr int P = 4, D = 3;  // ring of fragment buffers and prefetch distance (leaves)
   extern __shared__ __attribute__((aligned(16))) uint32_t dyn_lds[];
   const int stack_words = p.stack_slots * NP * 64;  // per wave
 
@@ -73,76 +90,57 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_nt(GemmParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t n0 = (int64_t)xcd_tile(blockIdx.x, gridDim.x) * 16;
   const int64_t m0 = (int64_t)blockIdx.y * (16 * MT);
+  const int ks = blockIdx.z;
   const int r16 = lane & 15, g4 = lane >> 4;
 
   int lo, hi;
-  subtree_range(p.L, DEPTH, wave, lo, hi);
+  subtree_range(p.L, p.ksplit_depth + DW, (ks << DW) | wave, lo, hi);
   const int nl = hi - lo;
+  const bool tail = (int64_t)hi * kLeaf > p.K;  // this wave owns the partial last leaf
+  const int nfull = tail ? nl - 1 : nl;
 
   // Rows past N and tokens past M read a valid row instead (clamped); their
   // MFMA outputs are never stored, and every output depends only on its own
   // weight row and token.
   const uint16_t *brow[NB];
-  const uint16_t *arow[NB][MT];
+  const uint16_t *arow[NA][MT];
   {
     const int64_t n = n0 + r16 < p.N ? n0 + r16 : p.N - 1;
 #pragma unroll
-    for (int b = 0; b < NB; ++b) brow[b] = p.B[b] + n * p.ldb[b];
+    for (int b = 0; b < NB; ++b) brow[b] = p.B[b] + n * p.ldb[b] + 8 * g4;
   }
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
     const int64_t m = m0 + 16 * t + r16 < p.M ? m0 + 16 * t + r16 : p.M - 1;
 #pragma unroll
-    for (int b = 0; b < NB; ++b) arow[b][t] = p.A[b] + m * p.lda[b];
+    for (int a = 0; a < NA; ++a) arow[a][t] = p.A[a] + m * p.lda[a] + 8 * g4;
   }
+
+  struct WF { bf16x8 v[NB][2]; };
+  struct XF { bf16x8 v[NA][MT][2]; };
+  auto load_w = [&](int leaf, WF &w) {
+    const int64_t k = (int64_t)leaf * kLeaf;
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int s = 0; s < 2; ++s) w.v[b][s] = load_frag_nt(brow[b], k + 32 * s);
+  };
+  auto load_x = [&](int leaf, XF &x) {
+    const int64_t k = (int64_t)leaf * kLeaf;
+#pragma unroll
+    for (int a = 0; a < NA; ++a)
+#pragma unroll
+      for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) x.v[a][t][s] = load_frag(arow[a][t], k + 32 * s);
+  };
 
   TreeStack<NP> st{dyn_lds + wave * stack_words + lane};
   uint32_t root[NP];
 #pragma unroll
   for (int q = 0; q < NP; ++q) root[q] = 0;
 
-  for (int j = 0; j < nl; ++j) {
-    const int64_t kb = (int64_t)(lo + j) * kLeaf;
-    f32x4 acc[NB][MT];
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-      for (int t = 0; t < MT; ++t) acc[b][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (kb + kLeaf <= p.K) {
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const int64_t k = kb + 32 * s + 8 * g4;
-        bf16x8 wf[NB], xf[NB][MT];
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-          wf[b] = load_frag(brow[b], k);
-#pragma unroll
-          for (int t = 0; t < MT; ++t) xf[b][t] = (b > 0 && SHARED_A) ? xf[0][t] : load_frag(arow[b][t], k);
-        }
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
-#pragma unroll
-          for (int t = 0; t < MT; ++t) acc[b][t] = mfma16(wf[b], xf[b][t], acc[b][t]);
-      }
-    } else {
-      // the partial last leaf: zeros past K; an all-zero block leaves the
-      // accumulator unchanged, so a half past K is skipped
-      for (int s = 0; s < 2; ++s) {
-        if (kb + 32 * s >= p.K) break;
-        const int64_t k = kb + 32 * s + 8 * g4;
-        bf16x8 wf[NB], xf[NB][MT];
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-          wf[b] = load_frag_tail(brow[b], k, p.K);
-#pragma unroll
-          for (int t = 0; t < MT; ++t) xf[b][t] = load_frag_tail(arow[b][t], k, p.K);
-        }
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
-#pragma unroll
-          for (int t = 0; t < MT; ++t) acc[b][t] = mfma16(wf[b], xf[b][t], acc[b][t]);
-      }
-    }
+  auto finish_leaf = [&](f32x4 (&acc)[NB][MT], int j) {
     uint32_t v[NP];
 #pragma unroll
     for (int b = 0; b < NB; ++b)
@@ -152,6 +150,82 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_nt(GemmParams p) {
         v[(b * MT + t) * 2 + 1] = pack_rne(acc[b][t][2], acc[b][t][3]);
       }
     tree_push<NP>(st, v, root, nl, j);
+  };
+
+  // Ring of P fragment buffers: leaf j lives in slot j % P.  The main loop
+  // issues its loads unconditionally (indices past the last full leaf are
+  // clamped to it) so that every wait counts a fixed number of younger loads;
+  // a conditional load would force the wait to drain the whole queue.
+  WF wb[P];
+  XF xb[P];
+  const int last = lo + nfull - 1;
+  if (nfull > 0) {
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+      load_w(min(lo + i, last), wb[i]);
+      load_x(min(lo + i, last), xb[i]);
+    }
+  }
+  const int ngroups = nfull / P;
+  for (int gi = 0; gi < ngroups; ++gi) {
+#pragma unroll
+    for (int q = 0; q < P; ++q) {
+      const int j = gi * P + q;
+      load_w(min(lo + j + D, last), wb[(q + D) % P]);
+      load_x(min(lo + j + D, last), xb[(q + D) % P]);
+      f32x4 acc[NB][MT];
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+          acc[b][t] = mfma16(wb[q].v[b][0], xb[q].v[SHARED_A ? 0 : b][t][0], f32x4{0.f, 0.f, 0.f, 0.f});
+          acc[b][t] = mfma16(wb[q].v[b][1], xb[q].v[SHARED_A ? 0 : b][t][1], acc[b][t]);
+        }
+      finish_leaf(acc, j);
+    }
+  }
+  // the remaining nfull % P (< P, so <= D) leaves are already in the ring
+#pragma unroll
+  for (int q = 0; q < P - 1; ++q) {
+    const int j = ngroups * P + q;
+    if (j < nfull) {
+      f32x4 acc[NB][MT];
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+          acc[b][t] = mfma16(wb[q].v[b][0], xb[q].v[SHARED_A ? 0 : b][t][0], f32x4{0.f, 0.f, 0.f, 0.f});
+          acc[b][t] = mfma16(wb[q].v[b][1], xb[q].v[SHARED_A ? 0 : b][t][1], acc[b][t]);
+        }
+      finish_leaf(acc, j);
+    }
+  }
+
+  if (tail) {
+    // the partial last leaf: zeros past K; an all-zero block leaves the
+    // accumulator unchanged, so a half past K is skipped
+    const int64_t kb = (int64_t)(hi - 1) * kLeaf;
+    f32x4 acc[NB][MT];
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int t = 0; t < MT; ++t) acc[b][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < 2; ++s) {
+      if (kb + 32 * s >= p.K) break;
+      const int64_t k = kb + 32 * s;
+      bf16x8 wf[NB], xf[NA][MT];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) wf[b] = load_frag_tail(brow[b], k, p.K - 8 * g4);
+#pragma unroll
+      for (int a = 0; a < NA; ++a)
+#pragma unroll
+        for (int t = 0; t < MT; ++t) xf[a][t] = load_frag_tail(arow[a][t], k, p.K - 8 * g4);
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int t = 0; t < MT; ++t) acc[b][t] = mfma16(wf[b], xf[SHARED_A ? 0 : b][t], acc[b][t]);
+    }
+    finish_leaf(acc, nl - 1);
   }
 
   if (!wg_combine<NP, WAVES>(root, dyn_lds, stack_words, wave, lane)) return;
@@ -162,8 +236,13 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_nt(GemmParams p) {
     const int64_t m = m0 + 16 * t + r16;
     if constexpr (EPI == EPI_STORE) {
 #pragma unroll
-      for (int b = 0; b < NB; ++b)
-        store4(p.C[b], p.ldc[b], m, n, p.M, p.N, root[(b * MT + t) * 2], root[(b * MT + t) * 2 + 1]);
+      for (int b = 0; b < NB; ++b) {
+        if (p.ksplit_depth > 0)
+          store4(p.part + ((int64_t)b * (1 << p.ksplit_depth) + ks) * p.part_stride, p.ldp, m, n, p.M, p.N,
+                 root[(b * MT + t) * 2], root[(b * MT + t) * 2 + 1]);
+        else
+          store4(p.C[b], p.ldc[b], m, n, p.M, p.N, root[(b * MT + t) * 2], root[(b * MT + t) * 2 + 1]);
+      }
     } else if constexpr (EPI == EPI_ACT) {
       // gate (b = 0) and up (b = 1) of the same (m, n): a = bf16(silu(g) u)
       uint32_t ap[2];
@@ -191,13 +270,14 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_nt(GemmParams p) {
 
 // C_b[m][n] = T_K( A_b[m,:] . B_b[:,n] ); A_b [M,K] K-contiguous, B_b [K,N]
 // N-contiguous.  Each wave transposes its 64 x 16 weight slab of every leaf
-// through its own LDS region so that the MFMA A operand is K-contiguous.
+// through its own LDS region so that the MFMA A operand is K-contiguous; the
+// next leaf's slab rows are loaded while the current leaf computes.
 constexpr int kTStride = 72;  // padded K stride of a transposed slab (elements)
 
 template <int NB, int MT, int WAVES, int EPI>
 __global__ __launch_bounds__(WAVES * 64) void k_gemm_nn(GemmParams p) {
   constexpr int NP = NB * MT * 2;
-  constexpr int DEPTH = WAVES == 1 ? 0 : WAVES == 2 ? 1 : WAVES == 4 ? 2 : 3;
+  constexpr int DW = log2i<WAVES>();
   __shared__ __attribute__((aligned(16))) uint16_t slab[WAVES][NB][16 * kTStride];
   extern __shared__ __attribute__((aligned(16))) uint32_t dyn_lds[];
   const int stack_words = p.stack_slots * NP * 64;  // per wave
@@ -206,10 +286,11 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_nn(GemmParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t n0 = (int64_t)xcd_tile(blockIdx.x, gridDim.x) * 16;
   const int64_t m0 = (int64_t)blockIdx.y * (16 * MT);
+  const int ks = blockIdx.z;
   const int r16 = lane & 15, g4 = lane >> 4;
 
   int lo, hi;
-  subtree_range(p.L, DEPTH, wave, lo, hi);
+  subtree_range(p.L, p.ksplit_depth + DW, (ks << DW) | wave, lo, hi);
   const int nl = hi - lo;
 
   const uint16_t *arow[NB][MT];
@@ -220,44 +301,76 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_nn(GemmParams p) {
     for (int b = 0; b < NB; ++b) arow[b][t] = p.A[b] + m * p.lda[b];
   }
   const bool full_n = n0 + 16 <= p.N;
+  const bool tail = (int64_t)hi * kLeaf > p.K;  // this wave owns the partial last leaf
+  const int nfull = tail ? nl - 1 : nl;
+
+  // lane l fetches weight row leaf*64 + l, columns n0..n0+15: two 16-byte
+  // pieces (full leaf, full column tile) or element by element with zeros
+  // outside the matrix
+  auto fetch_fast = [&](int leaf, uint32_t (&q)[NB][8]) {
+    const int64_t kr = (int64_t)leaf * kLeaf + lane;
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const uint16_t *src = p.B[b] + kr * p.ldb[b] + n0;
+      const u32x4 v0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src));
+      const u32x4 v1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src + 8));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { q[b][i] = v0[i]; q[b][4 + i] = v1[i]; }
+    }
+  };
+  auto fetch_slow = [&](int leaf, uint32_t (&q)[NB][8]) {
+    const int64_t kr = (int64_t)leaf * kLeaf + lane;
+    const bool kok = kr < p.K;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const uint16_t *src = p.B[b] + (kok ? kr : 0) * p.ldb[b] + n0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t lo16 = (kok && n0 + 2 * i < p.N) ? src[2 * i] : 0u;
+        const uint32_t hi16 = (kok && n0 + 2 * i + 1 < p.N) ? src[2 * i + 1] : 0u;
+        q[b][i] = lo16 | (hi16 << 16);
+      }
+    }
+  };
 
   TreeStack<NP> st{dyn_lds + wave * stack_words + lane};
   uint32_t root[NP];
 #pragma unroll
   for (int q = 0; q < NP; ++q) root[q] = 0;
 
-  for (int j = 0; j < nl; ++j) {
+  // activation fragments of one leaf (both K halves)
+  struct XF { bf16x8 v[NB][MT][2]; };
+  auto load_x = [&](int leaf, XF &x) {
+    const int64_t kb = (int64_t)leaf * kLeaf;
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) x.v[b][t][s] = load_frag(arow[b][t], kb + 32 * s + 8 * g4);
+  };
+  auto load_x_tail = [&](int leaf, XF &x) {
+    const int64_t kb = (int64_t)leaf * kLeaf;
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) x.v[b][t][s] = load_frag_tail(arow[b][t], kb + 32 * s + 8 * g4, p.K);
+  };
+
+  // stage the slab, transpose through LDS, two MFMA halves, then the tree
+  auto leaf_body = [&](int j, const uint32_t (&q)[NB][8], const XF &x, bool partial) {
     const int64_t kb = (int64_t)(lo + j) * kLeaf;
-    const bool full_leaf = kb + kLeaf <= p.K;
-    // lane l stages weight row kb + l, columns n0..n0+15, as slab[n][l]
-    const int64_t kr = kb + lane;
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      uint32_t q[8];
-      if (full_leaf && full_n) {
-        const uint16_t *src = p.B[b] + kr * p.ldb[b] + n0;
-        const uint4 v0 = *reinterpret_cast<const uint4 *>(src);
-        const uint4 v1 = *reinterpret_cast<const uint4 *>(src + 8);
-        q[0] = v0.x; q[1] = v0.y; q[2] = v0.z; q[3] = v0.w;
-        q[4] = v1.x; q[5] = v1.y; q[6] = v1.z; q[7] = v1.w;
-      } else {
-        const bool kok = kr < p.K;
-        const uint16_t *src = p.B[b] + (kok ? kr : 0) * p.ldb[b] + n0;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const uint32_t lo16 = (kok && n0 + 2 * i < p.N) ? src[2 * i] : 0u;
-          const uint32_t hi16 = (kok && n0 + 2 * i + 1 < p.N) ? src[2 * i + 1] : 0u;
-          q[i] = lo16 | (hi16 << 16);
-        }
-      }
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        slab[wave][b][(2 * i) * kTStride + lane] = (uint16_t)(q[i] & 0xffff);
-        slab[wave][b][(2 * i + 1) * kTStride + lane] = (uint16_t)(q[i] >> 16);
+        slab[wave][b][(2 * i) * kTStride + lane] = (uint16_t)(q[b][i] & 0xffff);
+        slab[wave][b][(2 * i + 1) * kTStride + lane] = (uint16_t)(q[b][i] >> 16);
       }
-    }
     wave_lds_sync();  // this wave's slab writes land before its lanes read them
-
     f32x4 acc[NB][MT];
 #pragma unroll
     for (int b = 0; b < NB; ++b)
@@ -265,22 +378,15 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_nn(GemmParams p) {
       for (int t = 0; t < MT; ++t) acc[b][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      if (!full_leaf && kb + 32 * s >= p.K) break;  // all-zero block: accumulator unchanged
-      const int64_t k = kb + 32 * s + 8 * g4;
-      bf16x8 wf[NB], xf[NB][MT];
+      if (partial && kb + 32 * s >= p.K) break;  // all-zero block: accumulator unchanged
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
-        wf[b] = *reinterpret_cast<const bf16x8 *>(&slab[wave][b][r16 * kTStride + 32 * s + 8 * g4]);
+        const bf16x8 wf = *reinterpret_cast<const bf16x8 *>(&slab[wave][b][r16 * kTStride + 32 * s + 8 * g4]);
 #pragma unroll
-        for (int t = 0; t < MT; ++t) xf[b][t] = full_leaf ? load_frag(arow[b][t], k) : load_frag_tail(arow[b][t], k, p.K);
+        for (int t = 0; t < MT; ++t) acc[b][t] = mfma16(wf, x.v[b][t][s], acc[b][t]);
       }
-#pragma unroll
-      for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int t = 0; t < MT; ++t) acc[b][t] = mfma16(wf[b], xf[b][t], acc[b][t]);
     }
     wave_lds_sync();  // slab reads done before the next leaf overwrites it
-
     uint32_t v[NP];
 #pragma unroll
     for (int b = 0; b < NB; ++b)
@@ -290,6 +396,53 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_nn(GemmParams p) {
         v[(b * MT + t) * 2 + 1] = pack_rne(acc[b][t][2], acc[b][t][3]);
       }
     tree_push<NP>(st, v, root, nl, j);
+  };
+
+  if (full_n) {
+    // Weight rows and activation fragments are fetched D leaves ahead, at the
+    // same distance, into a ring where leaf j lives in slot j % P; the loop
+    // issues them unconditionally (clamped indices) so that waits stay partial.
+    constexpr int P = 4, D = 3;
+    uint32_t qb[P][NB][8];
+    XF xb[P];
+    const int last = lo + nfull - 1;
+    if (nfull > 0) {
+#pragma unroll
+      for (int i = 0; i < D; ++i) {
+        fetch_fast(min(lo + i, last), qb[i]);
+        load_x(min(lo + i, last), xb[i]);
+      }
+    }
+    const int ngroups = nfull / P;
+    for (int gi = 0; gi < ngroups; ++gi) {
+#pragma unroll
+      for (int h = 0; h < P; ++h) {
+        const int j = gi * P + h;
+        fetch_fast(min(lo + j + D, last), qb[(h + D) % P]);
+        load_x(min(lo + j + D, last), xb[(h + D) % P]);
+        leaf_body(j, qb[h], xb[h], false);
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < P - 1; ++h) {
+      const int j = ngroups * P + h;
+      if (j < nfull) leaf_body(j, qb[h], xb[h], false);
+    }
+  } else {
+    for (int j = 0; j < nfull; ++j) {
+      uint32_t q[NB][8];
+      XF x;
+      fetch_slow(lo + j, q);
+      load_x(lo + j, x);
+      leaf_body(j, q, x, false);
+    }
+  }
+  if (tail) {
+    uint32_t q[NB][8];
+    XF x;
+    fetch_slow(hi - 1, q);
+    load_x_tail(hi - 1, x);
+    leaf_body(nl - 1, q, x, true);
   }
 
   if (!wg_combine<NP, WAVES>(root, dyn_lds, stack_words, wave, lane)) return;
@@ -300,8 +453,13 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_nn(GemmParams p) {
     const int64_t m = m0 + 16 * t + r16;
     if constexpr (EPI == EPI_STORE) {
 #pragma unroll
-      for (int b = 0; b < NB; ++b)
-        store4(p.C[b], p.ldc[b], m, n, p.M, p.N, root[(b * MT + t) * 2], root[(b * MT + t) * 2 + 1]);
+      for (int b = 0; b < NB; ++b) {
+        if (p.ksplit_depth > 0)
+          store4(p.part + ((int64_t)b * (1 << p.ksplit_depth) + ks) * p.part_stride, p.ldp, m, n, p.M, p.N,
+                 root[(b * MT + t) * 2], root[(b * MT + t) * 2 + 1]);
+        else
+          store4(p.C[b], p.ldc[b], m, n, p.M, p.N, root[(b * MT + t) * 2], root[(b * MT + t) * 2 + 1]);
+      }
     } else if constexpr (EPI == EPI_DSILU) {
       // dA at (m, n = i) with the saved g, u: dU = bf16(dA s), dG = bf16((dA u) s'),
       // a = bf16(s u); written row-major [M, I] and transposed [I, M].
@@ -336,6 +494,95 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_nn(GemmParams p) {
   }
 }
 
+// ------------------------------------------------------------------ one leaf
+
+// C_b[m][n] = bf16( leaf(A_b[m,:] . B[n,:]) ) for K <= 64: a single leaf, so
+// no tree node; this is the weight-gradient shape (K = tokens) and is bound by
+// its output writes.  A workgroup of 4 waves owns 64 m-rows x 128 n-columns;
+// wave w computes m-rows 16w..16w+15 against all 128 columns (the B fragments
+// are shared by the NB products), stages each 16 x 128 BF16 result in LDS and
+// stores it as whole 256-byte row segments.
+constexpr int kShortN = 128, kShortStride = kShortN + 8;
+
+template <int NB>
+__global__ __launch_bounds__(256) void k_gemm_short(GemmParams p) {
+  __shared__ __attribute__((aligned(16))) uint16_t stage[4][16 * kShortStride];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int r16 = lane & 15, g4 = lane >> 4;
+  const int64_t n0 = (int64_t)xcd_tile(blockIdx.x, gridDim.x) * kShortN;
+  const int64_t m0 = (int64_t)blockIdx.y * 64 + 16 * wave;
+
+  const int64_t mrow = m0 + r16 < p.M ? m0 + r16 : p.M - 1;  // clamped rows are never stored
+  const uint16_t *arow[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) arow[b] = p.A[b] + mrow * p.lda[b];
+  const uint16_t *brow[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const int64_t n = n0 + 16 * c + r16 < p.N ? n0 + 16 * c + r16 : p.N - 1;
+    brow[c] = p.B[0] + n * p.ldb[0];
+  }
+
+  f32x4 acc[NB][8];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[b][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < 2; ++s) {
+    if (32 * s >= p.K) break;  // all-zero block: the accumulator is unchanged
+    const int64_t k = 32 * s + 8 * g4;
+    bf16x8 xa[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) xa[b] = load_frag_tail(arow[b], k, p.K);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const bf16x8 w = load_frag_tail(brow[c], k, p.K);
+#pragma unroll
+      for (int b = 0; b < NB; ++b) acc[b][c] = mfma16(w, xa[b], acc[b][c]);
+    }
+  }
+
+  uint16_t *st = stage[wave];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    // lane holds C[m0 + r16][n0 + 16c + 4 g4 + (0..3)]
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const uint2 v = make_uint2(pack_rne(acc[b][c][0], acc[b][c][1]), pack_rne(acc[b][c][2], acc[b][c][3]));
+      *reinterpret_cast<uint2 *>(&st[r16 * kShortStride + 16 * c + 4 * g4]) = v;
+    }
+    wave_lds_sync();
+    // 16 rows x 256 bytes: lane l writes row (l >> 4) + 4i, bytes 16 (l & 15) .. +16
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = (lane >> 4) + 4 * i;
+      const int col = 8 * (lane & 15);
+      const int64_t m = m0 + row, n = n0 + col;
+      if (m < p.M) {
+        uint16_t *dst = p.C[b] + m * p.ldc[b] + n;
+        const uint4 v = *reinterpret_cast<const uint4 *>(&st[row * kShortStride + col]);
+        if (n + 8 <= p.N) {
+          *reinterpret_cast<uint4 *>(dst) = v;
+        } else {
+          const uint32_t q[4] = {v.x, v.y, v.z, v.w};
+          for (int e = 0; e < 8 && n + e < p.N; ++e) dst[e] = (uint16_t)(q[e >> 1] >> (16 * (e & 1)));
+        }
+      }
+    }
+    wave_lds_sync();  // the stage is reused by the next product
+  }
+}
+
+hipError_t launch_gemm_short(int nb, GemmParams p, hipStream_t stream) {
+  dim3 grid((unsigned)((p.N + kShortN - 1) / kShortN), (unsigned)((p.M + 63) / 64));
+  if (nb == 1)
+    hipLaunchKernelGGL((k_gemm_short<1>), grid, dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL((k_gemm_short<2>), grid, dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------------ launch
 
 #define DGF_DISPATCH_WAVES(KERNEL, NB, MT, EPI)                                                             \
@@ -353,7 +600,7 @@ hipError_t launch_gemm(int layout, int nb, int epi, GemmParams p, int waves, hip
   const int mt = p.M <= 16 ? 1 : 2;
   const int64_t tiles_n = (p.N + 15) / 16;
   const int64_t tiles_m = (p.M + 16 * mt - 1) / (16 * mt);
-  dim3 grid((unsigned)tiles_n, (unsigned)tiles_m);
+  dim3 grid((unsigned)tiles_n, (unsigned)tiles_m, (unsigned)(1 << p.ksplit_depth));
   if (layout == DGF_LAYOUT_NT) {
     if (nb == 1 && epi == EPI_STORE) {
       if (mt == 1) { DGF_DISPATCH_WAVES(k_gemm_nt, 1, 1, EPI_STORE) } else { DGF_DISPATCH_WAVES(k_gemm_nt, 1, 2, EPI_STORE) }

@@ -20,6 +20,9 @@ struct GemmParams {
   int64_t M, N, K;
   int L;                 // leaves = ceil(K / 64)
   int stack_slots;       // LDS tree-stack slots per wave (>= 1, >= a wave subtree's depth)
+  int ksplit_depth;      // the K leaves are split over 2^ksplit_depth workgroups (grid.z)
+  uint16_t *part;        // ksplit_depth > 0: partial roots [NB][2^ksplit_depth][M][ldp]
+  int64_t ldp, part_stride;
   int shared_a;          // NB = 2 with A[1] == A[0]
   // EPI_ACT: a = bf16(silu(C0) * C1)
   uint16_t *act_out;
@@ -34,11 +37,17 @@ struct GemmParams {
 };
 
 hipError_t launch_gemm(int layout, int nb, int epi, GemmParams p, int waves, hipStream_t stream);
+// NT, EPI_STORE, K <= 64 (one leaf), B shared by the NB products
+hipError_t launch_gemm_short(int nb, GemmParams p, hipStream_t stream);
 
 hipError_t launch_act_fwd(const uint16_t *g, const uint16_t *u, uint16_t *a, int64_t n, hipStream_t s);
 hipError_t launch_act_bwd(const uint16_t *da, const uint16_t *g, const uint16_t *u, uint16_t *dg, uint16_t *du,
                           uint16_t *a, int64_t n, hipStream_t s);
 hipError_t launch_combine(const uint16_t *const *parts, int S, uint16_t *out, int64_t n, hipStream_t s);
+// out [M, N] (ldo) = balanced combine over S partials part[s] [M, N] (ldp),
+// part[s] = part + s * part_stride
+hipError_t launch_combine_2d(const uint16_t *part, int64_t part_stride, int64_t ldp, int S, uint16_t *out, int64_t ldo,
+                             int64_t M, int64_t N, hipStream_t s);
 // dx [M, N] = bf16(G + U) per element (the gate lane first), row-major with leading dims
 hipError_t launch_add_lanes(const uint16_t *G, int64_t ldg, const uint16_t *U, int64_t ldu, uint16_t *dx,
                             int64_t lddx, int64_t M, int64_t N, hipStream_t s);
