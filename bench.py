@@ -104,7 +104,7 @@ def main():
     torch.cuda.synchronize()
     print("[bench] warmup done", file=sys.stderr, flush=True)
 
-    timer = dgf.KernelTimer(max_kernels=16 * args.steps + 16)
+    timer = dgf.KernelTimer(max_kernels=32 * args.steps + 64)
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()

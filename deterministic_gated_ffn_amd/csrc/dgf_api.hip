@@ -40,7 +40,7 @@ struct Prof {
   hipEvent_t *ev = nullptr;
   int pairs = 0;
   int used = 0;
-  const char *names[256] = {};
+  const char *names[4096] = {};
 };
 thread_local Prof g_prof;
 
@@ -55,7 +55,7 @@ hipError_t timed(hipStream_t s, const char *name, F &&launch) {
   hipError_t e = launch();
   if (rec && e == hipSuccess) e = hipEventRecord(g_prof.ev[2 * k + 1], s);
   if (g_prof.ev) {
-    if (k < 256) g_prof.names[k] = name;
+    if (k < 4096) g_prof.names[k] = name;
     g_prof.used = k + 1;
   }
   return e;
@@ -104,52 +104,131 @@ GemmParams blank() {
   return p;
 }
 
-// Launch shape of one tree GEMM.  A workgroup holds at most 8 waves; the grid
-// aims at every workgroup being resident at once (no second round of
-// workgroups) with at least 6 waves per CU on 256 CUs.  `per_cu` is the waves
-// a CU holds for the kernel variant (register-bound).  Narrow outputs (few
-// 16-column tiles) split the K leaves over 2, 4 or 8 workgroups (each a
-// subtree), whose roots a combine kernel joins; only plain-store GEMMs do so.
+// Launch shape of one tree GEMM.  A wave owns 16 RT output columns (RT from
+// gemm_row_tiles) and 16 MT tokens; a workgroup holds 1, 2 or 4 waves, each on
+// its own subtree of the K leaves, and plain-store GEMMs may further split K
+// over 2..16 workgroups (subtrees one level deeper each), whose roots a
+// combine kernel joins.  A shape is scored by the waves it launches, capped
+// at what 256 CUs hold at once (8 waves per CU by registers, fewer when the
+// workgroup's LDS, 64 KB at most, leaves room for fewer workgroups in a CU's
+// 160 KB); the best score wins, then fewer K pieces, then more waves per
+// workgroup.
 struct Plan {
   int waves = 1, kdepth = 0, slots = 1;
   size_t lds = 0;
 };
 
 constexpr int64_t kCUs = 256;
+constexpr size_t kMaxLds = 64 * 1024;
 
 Plan plan_gemm(int layout, int nb, int epi, int64_t M, int64_t N, int64_t K) {
-  Plan pl;
-  if (layout == DGF_LAYOUT_NT && epi == EPI_STORE && K <= 64) return pl;  // the one-leaf kernel
+  Plan best;
+  if (layout == DGF_LAYOUT_NT && epi == EPI_STORE && K <= 64) return best;  // the one-leaf kernel
   const int L = leaves(K);
   const int mt = M <= 16 ? 1 : 2;
-  const int64_t tiles = ((N + 15) / 16) * ((M + 16 * mt - 1) / (16 * mt));
-  const int64_t per_cu = (nb == 2 && mt == 2) ? 8 : 12;
-  const int64_t capacity = per_cu * kCUs;
-  pl.waves = 1;
-  while (pl.waves * 2 <= 8 && pl.waves * 2 <= L && tiles * pl.waves * 2 <= capacity) pl.waves *= 2;
-  if (epi == EPI_STORE)
-    while (pl.kdepth < 3 && tiles * (pl.waves << pl.kdepth) < 6 * kCUs &&
-           tiles * (pl.waves << (pl.kdepth + 1)) <= capacity && (L >> (pl.kdepth + 1)) >= 4 * pl.waves)
-      ++pl.kdepth;
-  const int depth = pl.kdepth + tree_depth(pl.waves);
-  const int per_wave = (L + (1 << depth) - 1) >> depth;  // largest subtree at that depth
-  pl.slots = tree_depth(per_wave) > 1 ? tree_depth(per_wave) : 1;
-  pl.lds = (size_t)pl.waves * pl.slots * (nb * mt * 2) * 64 * 4 +
-           (layout == DGF_LAYOUT_NN ? (size_t)pl.waves * nb * 16 * 72 * 2 : 0);
-  return pl;
+  const int rt = gemm_row_tiles(layout, nb, epi);
+  const int np = nb * rt * mt * 2;
+  const int64_t tiles = ((N + 16 * rt - 1) / (16 * rt)) * ((M + 16 * mt - 1) / (16 * mt));
+  const size_t slab = layout == DGF_LAYOUT_NN ? (size_t)nb * 16 * rt * 64 * 2 : 0;
+  const int max_kdepth = epi == EPI_STORE ? 4 : 0;
+  constexpr size_t kCuLds = 160 * 1024;
+  int64_t best_score = -1;
+  for (int kd = 0; kd <= max_kdepth; ++kd) {
+    for (int waves = 4; waves >= 1; waves >>= 1) {
+      const int depth = kd + tree_depth(waves);
+      if ((1 << depth) > (L > 0 ? L : 1)) continue;  // every wave keeps at least one leaf
+      const int per_wave = (L + (1 << depth) - 1) >> depth;  // largest subtree at that depth
+      Plan pl;
+      pl.waves = waves;
+      pl.kdepth = kd;
+      pl.slots = tree_depth(per_wave) > 1 ? tree_depth(per_wave) : 1;
+      pl.lds = (size_t)waves * ((size_t)pl.slots * np * 64 * 4 + slab);
+      if (pl.lds > kMaxLds) continue;
+      int64_t per_cu = (int64_t)(kCuLds / (pl.lds > 0 ? pl.lds : 1)) * waves;
+      if (per_cu > 8) per_cu = 8;
+      const int64_t total = tiles * ((int64_t)waves << kd);
+      const int64_t score = total < per_cu * kCUs ? total : per_cu * kCUs;
+      if (score > best_score) {
+        best_score = score;
+        best = pl;
+      }
+    }
+  }
+  if (best_score < 0) {  // nothing fits: report the smallest shape's LDS
+    const int per_wave = L > 0 ? L : 1;
+    best.slots = tree_depth(per_wave) > 1 ? tree_depth(per_wave) : 1;
+    best.lds = (size_t)best.slots * np * 64 * 4 + slab;
+  }
+  return best;
 }
 
-// Workspace bytes for the K-split partial roots of one GEMM (0 without a split).
+// Launch shape of the weight-streaming kernel (dgf_xs.hip): up to 8 waves per
+// workgroup, the K tree cut at the smallest depth kd that leaves every wave
+// at most 4 leaves (or up to two levels deeper when that spreads the output
+// tiles more evenly over 256 CUs), and G workgroups per (token tile, product,
+// K piece), each looping over ceil(tiles / G) output tiles.  The cost
+// compared is the weight bytes of the busiest CU plus the partial roots'
+// write and read spread over all CUs.  waves = 0: not applicable (more than
+// 32 K pieces would be needed).
+struct XsPlan {
+  int waves = 0, kd = 0, groups = 0;
+  size_t lds = 0;
+};
+
+XsPlan plan_xs(int layout, int nb, int64_t M, int64_t N, int64_t K) {
+  XsPlan best;
+  const int L = leaves(K);
+  if (L == 0 || M == 0 || N == 0) return best;
+  const int mt = M <= 16 ? 1 : 2;
+  int waves = 8;
+  while (waves > L) waves >>= 1;
+  const int dw = tree_depth(waves);
+  int kd_min = 0;
+  while (((L + (1 << (kd_min + dw)) - 1) >> (kd_min + dw)) > 4) ++kd_min;
+  if (kd_min > 5) return best;
+  const int64_t cols = xs_tile_cols(layout, mt);
+  const int64_t tiles_n = (N + cols - 1) / cols, tiles_m = (M + 16 * mt - 1) / (16 * mt);
+  if (tiles_m > 65535) return best;
+  double best_cost = 0;
+  for (int kd = kd_min; kd <= kd_min + 2 && kd <= 5 && (1 << (kd + dw)) <= L; ++kd) {
+    const int64_t per_piece = tiles_m * nb * ((int64_t)1 << kd);  // (token tile, product, K piece)
+    int64_t T = (tiles_n * per_piece + kCUs - 1) / kCUs;
+    if (T < 1) T = 1;
+    const int64_t G = (tiles_n + T - 1) / T;
+    const int64_t tiles_per_wg = (tiles_n + G - 1) / G;
+    const int64_t rounds = (G * per_piece + kCUs - 1) / kCUs;
+    const int64_t leaves_per_wave = (L + (1 << (kd + dw)) - 1) >> (kd + dw);
+    const double cost = (double)rounds * tiles_per_wg * leaves_per_wave * waves * cols * 64 * 2 +
+                        (kd > 0 ? 2.0 * nb * ((int64_t)1 << kd) * M * round8(N) * 2 / kCUs : 0.0);
+    if (best.waves == 0 || cost < best_cost) {
+      best_cost = cost;
+      best.waves = waves;
+      best.kd = kd;
+      best.groups = (int)G;
+      best.lds = xs_lds_bytes(layout, mt, waves);
+    }
+  }
+  return best;
+}
+
+// Workspace bytes for the partial roots of one GEMM (0 when it needs none).
 size_t partial_bytes(int layout, int nb, int epi, int64_t M, int64_t N, int64_t K) {
+  if (M == 0 || N == 0) return 0;
+  if (layout == DGF_LAYOUT_NT && epi == EPI_STORE && K <= 64) return 0;  // the one-leaf kernel
+  const XsPlan xp = plan_xs(layout, nb, M, N, K);
+  if (xp.waves > 0) {
+    if (xp.kd == 0 && epi == EPI_STORE) return 0;
+    return round256((size_t)nb * ((size_t)1 << xp.kd) * M * round8(N) * 2);
+  }
   const Plan pl = plan_gemm(layout, nb, epi, M, N, K);
-  if (pl.kdepth == 0 || M == 0 || N == 0) return 0;
+  if (pl.kdepth == 0) return 0;
   return round256((size_t)nb * ((size_t)1 << pl.kdepth) * M * round8(N) * 2);
 }
 
 // One tree GEMM: the MFMA kernel, then (K split) the combine of the partials.
 // `partials` must hold partial_bytes() of workspace.
 dgf_status run_gemm(int layout, int nb, int epi, GemmParams p, hipStream_t s, const char *what,
-                    uint16_t *partials = nullptr) {
+                    uint16_t *partials = nullptr, const char *join_what = "K-piece join") {
   if (p.M == 0 || p.N == 0) return DGF_OK;
   if ((p.M + 31) / 32 > 65535 || (p.N + 15) / 16 > 0x7fffffff)
     return fail(DGF_EUNSUPPORTED, "%s: %lld x %lld output exceeds the launch grid", what, (long long)p.M, (long long)p.N);
@@ -157,10 +236,30 @@ dgf_status run_gemm(int layout, int nb, int epi, GemmParams p, hipStream_t s, co
   if (layout == DGF_LAYOUT_NT && epi == EPI_STORE && p.K <= 64 && (nb == 1 || p.B[1] == p.B[0]) &&
       (p.M + 63) / 64 <= 65535)
     return hip_check(timed(s, what, [&] { return launch_gemm_short(nb, p, s); }), what);
+  const XsPlan xp = plan_xs(layout, nb, p.M, p.N, p.K);
+  if (xp.waves > 0) {
+    p.ksplit_depth = xp.kd;
+    const bool joined = xp.kd > 0 || epi != EPI_STORE;  // roots go through the combine kernel
+    p.to_part = joined ? 1 : 0;
+    if (!joined)
+      for (int b = 0; b < nb; ++b)
+        if (!p.C[b]) return fail(DGF_EINVAL, "%s: product %d has no output", what, b);
+    if (joined) {
+      if (!partials) return fail(DGF_EWORKSPACE, "%s: no workspace for the partial roots", what);
+      p.part = partials;
+      p.ldp = round8(p.N);
+      p.part_stride = p.M * p.ldp;
+    }
+    DGF_TRY(hip_check(timed(s, what, [&] { return launch_xs(layout, p, nb, xp.waves, xp.groups, s); }), what));
+    if (joined)
+      DGF_TRY(hip_check(timed(s, join_what, [&] { return launch_combine_epi(epi, nb, p, s); }), join_what));
+    return DGF_OK;
+  }
+  if (epi == EPI_DX) return fail(DGF_EUNSUPPORTED, "%s: K=%lld is too deep for the lane kernel", what, (long long)p.K);
   const Plan pl = plan_gemm(layout, nb, epi, p.M, p.N, p.K);
   p.stack_slots = pl.slots;
   p.ksplit_depth = pl.kdepth;
-  if (pl.lds > 64 * 1024)
+  if (pl.lds > kMaxLds)
     return fail(DGF_EUNSUPPORTED, "%s: K=%lld needs %zu bytes of LDS for the tree stack", what, (long long)p.K, pl.lds);
   if (pl.kdepth > 0) {
     if (!partials) return fail(DGF_EWORKSPACE, "%s: no workspace for the K-split partials", what);
@@ -208,11 +307,20 @@ struct Carve {
   }
 };
 
+// The dX lanes run as one two-product kernel with the ordered add in its join
+// when the weight-streaming kernel applies, else as two GEMMs and an add.
+bool dx_fused(int64_t M, int64_t H, int64_t I) { return plan_xs(DGF_LAYOUT_NN, 2, M, H, I).waves > 0; }
+
 size_t bwd_partials(int64_t M, int64_t H, int64_t I) {
-  size_t a = partial_bytes(DGF_LAYOUT_NN, 1, EPI_STORE, M, H, I);             // dX lanes
-  size_t b = partial_bytes(DGF_LAYOUT_NT, 2, EPI_STORE, I, H, M);             // dW_gate, dW_up
-  size_t c = partial_bytes(DGF_LAYOUT_NT, 1, EPI_STORE, H, I, M);             // dW_down
-  return a > b ? (a > c ? a : c) : (b > c ? b : c);
+  const size_t sizes[4] = {
+      partial_bytes(DGF_LAYOUT_NN, 1, EPI_DSILU, M, I, H),                                       // dA
+      dx_fused(M, H, I) ? partial_bytes(DGF_LAYOUT_NN, 2, EPI_DX, M, H, I)
+                        : partial_bytes(DGF_LAYOUT_NN, 1, EPI_STORE, M, H, I),                   // dX lanes
+      partial_bytes(DGF_LAYOUT_NT, 2, EPI_STORE, I, H, M),                                       // dW_gate, dW_up
+      partial_bytes(DGF_LAYOUT_NT, 1, EPI_STORE, H, I, M)};                                      // dW_down
+  size_t m = 0;
+  for (size_t v : sizes) m = v > m ? v : m;
+  return m;
 }
 
 size_t bwd_ws_bytes(int64_t M, int64_t H, int64_t I) {
@@ -225,8 +333,10 @@ size_t bwd_ws_bytes(int64_t M, int64_t H, int64_t I) {
 }
 
 size_t fwd_ws_bytes(int64_t M, int64_t H, int64_t I) {
-  return round256((size_t)M * round8(I) * 2)                     // a [M, I]
-         + partial_bytes(DGF_LAYOUT_NT, 1, EPI_STORE, M, H, I);  // down-projection partial roots
+  const size_t gu = partial_bytes(DGF_LAYOUT_NT, 2, EPI_ACT, M, I, H);  // gate/up partial roots
+  const size_t dn = partial_bytes(DGF_LAYOUT_NT, 1, EPI_STORE, M, H, I);  // down-projection partial roots
+  return round256((size_t)M * round8(I) * 2)  // a [M, I]
+         + (gu > dn ? gu : dn);               // the gate/up roots are joined before the down GEMM starts
 }
 
 size_t gemm_ws_bytes(int layout, int64_t M, int64_t N, int64_t K) {
@@ -265,7 +375,7 @@ int dgf_profile_end(void) {
 }
 
 const char *dgf_profile_name(int k) {
-  if (k < 0 || k >= 256 || k >= g_prof.used || !g_prof.names[k]) return "";
+  if (k < 0 || k >= 4096 || k >= g_prof.used || !g_prof.names[k]) return "";
   return g_prof.names[k];
 }
 
@@ -314,7 +424,7 @@ dgf_status dgf_ffn_fwd(const void *x, int64_t ldx, const void *w_gate, int64_t l
   p.act_out = a;
   p.ld_act = lda_;
   p.M = M; p.N = I; p.K = H;
-  DGF_TRY(run_gemm(DGF_LAYOUT_NT, 2, EPI_ACT, p, s, "gate/up tree GEMM"));
+  DGF_TRY(run_gemm(DGF_LAYOUT_NT, 2, EPI_ACT, p, s, "gate/up tree GEMM", partials, "gate/up join + act"));
 
   GemmParams q = blank();
   q.A[0] = a;
@@ -324,7 +434,7 @@ dgf_status dgf_ffn_fwd(const void *x, int64_t ldx, const void *w_gate, int64_t l
   q.C[0] = (uint16_t *)y;
   q.ldc[0] = ldy;
   q.M = M; q.N = H; q.K = I;
-  DGF_TRY(run_gemm(DGF_LAYOUT_NT, 1, EPI_STORE, q, s, "down tree GEMM", partials));
+  DGF_TRY(run_gemm(DGF_LAYOUT_NT, 1, EPI_STORE, q, s, "down tree GEMM", partials, "down join"));
   return ok();
 }
 
@@ -388,29 +498,42 @@ dgf_status dgf_ffn_bwd(const void *dy, int64_t lddy, const void *x, int64_t ldx,
   p.ld_gu = ld_gu;
   p.dG = dG; p.dU = dU; p.a_rm = nullptr; p.ld_d = ld_d;
   p.dGT = dGT; p.dUT = dUT; p.aT = aT; p.ld_t = Mp;
-  DGF_TRY(run_gemm(DGF_LAYOUT_NN, 1, EPI_DSILU, p, s, "dA tree GEMM"));
+  DGF_TRY(run_gemm(DGF_LAYOUT_NN, 1, EPI_DSILU, p, s, "dA tree GEMM", partials, "dA join + dsilu"));
 
-  // dX lanes G = T_I(dG W_gate), U = T_I(dU W_up), each its own tree GEMM
-  // (written to the caller's lane buffers when given, else to the workspace)
-  uint16_t *G = dx_gate_lane ? (uint16_t *)dx_gate_lane : Gw;
-  uint16_t *U = dx_up_lane ? (uint16_t *)dx_up_lane : Uw;
-  const int64_t ldG = dx_gate_lane ? lddx : ld_lane, ldU = dx_up_lane ? lddx : ld_lane;
-  for (int lane_i = 0; lane_i < 2; ++lane_i) {
+  // dX lanes G = T_I(dG W_gate), U = T_I(dU W_up) and dX = bf16(G + U), the
+  // gate lane first: one two-product GEMM whose join does the ordered add
+  // (lanes kept when the caller asks for them), or two GEMMs and an add
+  if (dx_fused(M, H, I)) {
     GemmParams q = blank();
-    q.A[0] = lane_i == 0 ? dG : dU;
-    q.lda[0] = ld_d;
-    q.B[0] = (const uint16_t *)(lane_i == 0 ? w_gate : w_up);
-    q.ldb[0] = lane_i == 0 ? ld_wg : ld_wu;
-    q.C[0] = lane_i == 0 ? G : U;
-    q.ldc[0] = lane_i == 0 ? ldG : ldU;
+    q.A[0] = dG; q.A[1] = dU;
+    q.lda[0] = q.lda[1] = ld_d;
+    q.B[0] = (const uint16_t *)w_gate; q.ldb[0] = ld_wg;
+    q.B[1] = (const uint16_t *)w_up; q.ldb[1] = ld_wu;
+    q.C[0] = (uint16_t *)dx_gate_lane; q.C[1] = (uint16_t *)dx_up_lane;
+    q.ldc[0] = q.ldc[1] = lddx;
+    q.dx = (uint16_t *)dx; q.lddx = lddx;
     q.M = M; q.N = H; q.K = I;
-    DGF_TRY(run_gemm(DGF_LAYOUT_NN, 1, EPI_STORE, q, s, lane_i == 0 ? "dX gate-lane tree GEMM" : "dX up-lane tree GEMM",
-                     partials));
+    DGF_TRY(run_gemm(DGF_LAYOUT_NN, 2, EPI_DX, q, s, "dX lanes tree GEMM", partials, "dX join + lane add"));
+  } else {
+    uint16_t *G = dx_gate_lane ? (uint16_t *)dx_gate_lane : Gw;
+    uint16_t *U = dx_up_lane ? (uint16_t *)dx_up_lane : Uw;
+    const int64_t ldG = dx_gate_lane ? lddx : ld_lane, ldU = dx_up_lane ? lddx : ld_lane;
+    for (int lane_i = 0; lane_i < 2; ++lane_i) {
+      GemmParams q = blank();
+      q.A[0] = lane_i == 0 ? dG : dU;
+      q.lda[0] = ld_d;
+      q.B[0] = (const uint16_t *)(lane_i == 0 ? w_gate : w_up);
+      q.ldb[0] = lane_i == 0 ? ld_wg : ld_wu;
+      q.C[0] = lane_i == 0 ? G : U;
+      q.ldc[0] = lane_i == 0 ? ldG : ldU;
+      q.M = M; q.N = H; q.K = I;
+      DGF_TRY(run_gemm(DGF_LAYOUT_NN, 1, EPI_STORE, q, s, lane_i == 0 ? "dX gate-lane tree GEMM" : "dX up-lane tree GEMM",
+                       partials));
+    }
+    if (dx)
+      DGF_TRY(hip_check(timed(s, "dX ordered add", [&] { return launch_add_lanes(G, ldG, U, ldU, (uint16_t *)dx, lddx, M, H, s); }),
+                        "dX ordered add"));
   }
-  // dX = bf16(G + U): the ordered add, gate lane first
-  if (dx)
-    DGF_TRY(hip_check(timed(s, "dX ordered add", [&] { return launch_add_lanes(G, ldG, U, ldU, (uint16_t *)dx, lddx, M, H, s); }),
-                      "dX ordered add"));
 
   // dW_gate = T_M(dG^T x), dW_up = T_M(dU^T x): NT over the transposed operands
   GemmParams w = blank();

@@ -43,6 +43,110 @@ __global__ __launch_bounds__(kThreads) void k_act_bwd(const uint16_t *da, const 
   }
 }
 
+// ------------------------------------------------------------------ K-piece join + epilogue
+
+// The 2^kd partial roots of product b at row m, columns c .. c+7, joined with
+// the balanced top of the tree (pairs of neighbours, level by level).  The
+// partial rows are padded to a multiple of 8 columns, so the 16-byte loads
+// stay inside the buffer; columns past N are never stored.
+template <int S>
+__device__ __forceinline__ void join8(const GemmParams &p, int b, int64_t m, int64_t c, uint32_t (&r)[4]) {
+  const uint16_t *base = p.part + (int64_t)b * S * p.part_stride + m * p.ldp + c;
+  uint32_t v[S][4];
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const uint4 q = *reinterpret_cast<const uint4 *>(base + s * p.part_stride);
+    v[s][0] = q.x; v[s][1] = q.y; v[s][2] = q.z; v[s][3] = q.w;
+  }
+#pragma unroll
+  for (int width = S; width > 1; width >>= 1)
+#pragma unroll
+    for (int j = 0; j < width / 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[j][q] = node2(v[2 * j][q], v[2 * j + 1][q]);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) r[q] = v[0][q];
+}
+
+__device__ __forceinline__ uint16_t half_of(const uint32_t (&r)[4], int e) {
+  return (uint16_t)(r[e >> 1] >> (16 * (e & 1)));
+}
+
+// 8 BF16 values to dst[0..8), or the first N - c of them.
+__device__ __forceinline__ void store8(uint16_t *dst, int64_t c, int64_t N, const uint32_t (&r)[4]) {
+  if (c + 8 <= N) {
+    *reinterpret_cast<uint4 *>(dst) = make_uint4(r[0], r[1], r[2], r[3]);
+  } else {
+    for (int e = 0; c + e < N; ++e) dst[e] = half_of(r, e);
+  }
+}
+
+template <int S, int EPI>
+__global__ __launch_bounds__(kThreads) void k_combine_epi(GemmParams p) {
+  const int64_t chunks = (p.N + 7) / 8;
+  const int b = blockIdx.y;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < p.M * chunks; i += (int64_t)gridDim.x * kThreads) {
+    const int64_t m = i / chunks, c = (i % chunks) * 8;
+    uint32_t r0[4];
+    join8<S>(p, EPI == EPI_STORE ? b : 0, m, c, r0);
+    if constexpr (EPI == EPI_STORE) {
+      store8(p.C[b] + m * p.ldc[b] + c, c, p.N, r0);
+    } else if constexpr (EPI == EPI_ACT) {
+      // gate product 0, up product 1: a = bf16(silu(g) u)
+      uint32_t r1[4], a[4];
+      join8<S>(p, 1, m, c, r1);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float g0 = bf_lo(r0[q]), g1 = bf_hi(r0[q]);
+        const float u0 = bf_lo(r1[q]), u1 = bf_hi(r1[q]);
+        const float s0 = g0 * sigma_f(g0), s1 = g1 * sigma_f(g1);
+        a[q] = pack_rne(s0 * u0, s1 * u1);
+      }
+      store8(p.act_out + m * p.ld_act + c, c, p.N, a);
+      if (p.C[0]) store8(p.C[0] + m * p.ldc[0] + c, c, p.N, r0);
+      if (p.C[1]) store8(p.C[1] + m * p.ldc[1] + c, c, p.N, r1);
+    } else if constexpr (EPI == EPI_DSILU) {
+      // dA with the saved g, u: dU = bf16(dA s), dG = bf16((dA u) s'), a = bf16(s u),
+      // written row-major [M, N] and transposed [N, M]
+      uint32_t dg[4] = {0, 0, 0, 0}, du[4] = {0, 0, 0, 0}, av[4] = {0, 0, 0, 0};
+      const int n_here = c + 8 <= p.N ? 8 : (int)(p.N - c);
+      for (int e = 0; e < n_here; ++e) {
+        const float da = bf2f(half_of(r0, e));
+        const float g = bf2f(p.sg[m * p.ld_gu + c + e]);
+        const float u = bf2f(p.su[m * p.ld_gu + c + e]);
+        const float sg = sigma_f(g);
+        const float s = g * sg;
+        const float one_m = 1.0f - sg;
+        const float tt = g * one_m;
+        const float onep = 1.0f + tt;
+        const float ds = sg * onep;
+        const uint32_t duv = f2bf(da * s);
+        const float dau = da * u;
+        const uint32_t dgv = f2bf(dau * ds);
+        const uint32_t aa = f2bf(s * u);
+        dg[e >> 1] |= dgv << (16 * (e & 1));
+        du[e >> 1] |= duv << (16 * (e & 1));
+        av[e >> 1] |= aa << (16 * (e & 1));
+        if (p.dGT) p.dGT[(c + e) * p.ld_t + m] = (uint16_t)dgv;
+        if (p.dUT) p.dUT[(c + e) * p.ld_t + m] = (uint16_t)duv;
+        if (p.aT) p.aT[(c + e) * p.ld_t + m] = (uint16_t)aa;
+      }
+      if (p.dG) store8(p.dG + m * p.ld_d + c, c, p.N, dg);
+      if (p.dU) store8(p.dU + m * p.ld_d + c, c, p.N, du);
+      if (p.a_rm) store8(p.a_rm + m * p.ld_d + c, c, p.N, av);
+    } else if constexpr (EPI == EPI_DX) {
+      // dx = bf16(G + U), the gate lane first
+      uint32_t r1[4], d[4];
+      join8<S>(p, 1, m, c, r1);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) d[q] = node2(r0[q], r1[q]);
+      if (p.dx) store8(p.dx + m * p.lddx + c, c, p.N, d);
+      if (p.C[0]) store8(p.C[0] + m * p.ldc[0] + c, c, p.N, r0);
+      if (p.C[1]) store8(p.C[1] + m * p.ldc[1] + c, c, p.N, r1);
+    }
+  }
+}
+
 struct Parts {
   const uint16_t *p[8];
 };
@@ -205,7 +309,9 @@ hipError_t launch_combine_2d(const uint16_t *part, int64_t part_stride, int64_t 
     case 1: hipLaunchKernelGGL(k_combine_2d<1>, g, dim3(kThreads), 0, s, part, part_stride, ldp, out, ldo, M, N); break;
     case 2: hipLaunchKernelGGL(k_combine_2d<2>, g, dim3(kThreads), 0, s, part, part_stride, ldp, out, ldo, M, N); break;
     case 4: hipLaunchKernelGGL(k_combine_2d<4>, g, dim3(kThreads), 0, s, part, part_stride, ldp, out, ldo, M, N); break;
-    default: hipLaunchKernelGGL(k_combine_2d<8>, g, dim3(kThreads), 0, s, part, part_stride, ldp, out, ldo, M, N); break;
+    case 8: hipLaunchKernelGGL(k_combine_2d<8>, g, dim3(kThreads), 0, s, part, part_stride, ldp, out, ldo, M, N); break;
+    case 16: hipLaunchKernelGGL(k_combine_2d<16>, g, dim3(kThreads), 0, s, part, part_stride, ldp, out, ldo, M, N); break;
+    default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
@@ -221,6 +327,33 @@ hipError_t launch_transpose(const uint16_t *src, int64_t lds_, int64_t R, int64_
   const dim3 g((unsigned)((C + 63) / 64), (unsigned)((R + 63) / 64));
   hipLaunchKernelGGL(k_transpose, g, dim3(kThreads), 0, s, src, lds_, R, C, dst, ldd);
   return hipGetLastError();
+}
+
+
+template <int EPI>
+hipError_t launch_combine_epi_s(int S, int nb, GemmParams p, hipStream_t s) {
+  const dim3 g(grid_for(p.M * ((p.N + 7) / 8), 1), EPI == EPI_STORE ? nb : 1);
+  switch (S) {
+    case 1: hipLaunchKernelGGL((k_combine_epi<1, EPI>), g, dim3(kThreads), 0, s, p); break;
+    case 2: hipLaunchKernelGGL((k_combine_epi<2, EPI>), g, dim3(kThreads), 0, s, p); break;
+    case 4: hipLaunchKernelGGL((k_combine_epi<4, EPI>), g, dim3(kThreads), 0, s, p); break;
+    case 8: hipLaunchKernelGGL((k_combine_epi<8, EPI>), g, dim3(kThreads), 0, s, p); break;
+    case 16: hipLaunchKernelGGL((k_combine_epi<16, EPI>), g, dim3(kThreads), 0, s, p); break;
+    case 32: hipLaunchKernelGGL((k_combine_epi<32, EPI>), g, dim3(kThreads), 0, s, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_epi(int epi, int nb, GemmParams p, hipStream_t s) {
+  const int S = 1 << p.ksplit_depth;
+  switch (epi) {
+    case EPI_STORE: return launch_combine_epi_s<EPI_STORE>(S, nb, p, s);
+    case EPI_ACT: return launch_combine_epi_s<EPI_ACT>(S, nb, p, s);
+    case EPI_DSILU: return launch_combine_epi_s<EPI_DSILU>(S, nb, p, s);
+    case EPI_DX: return launch_combine_epi_s<EPI_DX>(S, nb, p, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace dgf

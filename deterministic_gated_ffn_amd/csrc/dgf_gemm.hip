@@ -72,23 +72,25 @@ __device__ __forceinline__ bf16x8 load_frag_nt(const uint16_t *row, int64_t k) {
 // ------------------------------------------------------------------ NT
 
 // C_b[m][n] = T_K( A_b[m,:] . B_b[n,:] ), b < NB; A_b [M,K] and B_b [N,K] both
-// K-contiguous.  Weight and activation fragments are loaded D leaves ahead of
-// the MFMAs that use them, both at the same distance: loads complete in issue
-// order, so an activation load issued after a weight load would otherwise make
-// the wait for it also wait for that younger weight load.
-template <int NB, int MT, int WAVES, int EPI>
+// K-contiguous.  A wave owns RT tiles of 16 weight rows per product (16 RT
+// output columns n) and 16 MT tokens, so every activation fragment it loads
+// feeds NB RT MFMAs.  Weight and activation fragments are loaded D leaves
+// ahead of the MFMAs that use them, both at the same distance: loads complete
+// in issue order, so an activation load issued after a weight load would
+// otherwise make the wait for it also wait for that younger weight load.
+template <int NB, int RT, int MT, int WAVES, int EPI>
 __global__ __launch_bounds__(WAVES * 64) void k_gemm_nt(GemmParams p) {
   constexpr bool SHARED_A = (EPI == EPI_ACT);  // gate and up share the activation operand
   constexpr int NA = SHARED_A ? 1 : NB;
-  constexpr int NP = NB * MT * 2;
+  constexpr int NP = NB * RT * MT * 2;
   constexpr int DW = log2i<WAVES>();
-  constexpr int P = 4, D = 3;  // ring of fragment buffers and prefetch distance (leaves)
+  constexpr int P = NB * RT * MT >= 8 ? 2 : NB * RT * MT >= 4 ? 3 : 4, D = P - 1;  // ring slots, prefetch distance (leaves)
   extern __shared__ __attribute__((aligned(16))) uint32_t dyn_lds[];
   const int stack_words = p.stack_slots * NP * 64;  // per wave
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t n0 = (int64_t)xcd_tile(blockIdx.x, gridDim.x) * 16;
+  const int64_t n0 = (int64_t)xcd_tile(blockIdx.x, gridDim.x) * (16 * RT);
   const int64_t m0 = (int64_t)blockIdx.y * (16 * MT);
   const int ks = blockIdx.z;
   const int r16 = lane & 15, g4 = lane >> 4;
@@ -102,12 +104,13 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_nt(GemmParams p) {
   // Rows past N and tokens past M read a valid row instead (clamped); their
   // MFMA outputs are never stored, and every output depends only on its own
   // weight row and token.
-  const uint16_t *brow[NB];
+  const uint16_t *brow[NB][RT];
   const uint16_t *arow[NA][MT];
-  {
-    const int64_t n = n0 + r16 < p.N ? n0 + r16 : p.N - 1;
 #pragma unroll
-    for (int b = 0; b < NB; ++b) brow[b] = p.B[b] + n * p.ldb[b] + 8 * g4;
+  for (int rt = 0; rt < RT; ++rt) {
+    const int64_t n = n0 + 16 * rt + r16 < p.N ? n0 + 16 * rt + r16 : p.N - 1;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) brow[b][rt] = p.B[b] + n * p.ldb[b] + 8 * g4;
   }
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
@@ -116,14 +119,16 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_nt(GemmParams p) {
     for (int a = 0; a < NA; ++a) arow[a][t] = p.A[a] + m * p.lda[a] + 8 * g4;
   }
 
-  struct WF { bf16x8 v[NB][2]; };
+  struct WF { bf16x8 v[NB][RT][2]; };
   struct XF { bf16x8 v[NA][MT][2]; };
   auto load_w = [&](int leaf, WF &w) {
     const int64_t k = (int64_t)leaf * kLeaf;
 #pragma unroll
-    for (int b = 0; b < NB; ++b)
+    for (int s = 0; s < 2; ++s)
 #pragma unroll
-      for (int s = 0; s < 2; ++s) w.v[b][s] = load_frag_nt(brow[b], k + 32 * s);
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) w.v[b][rt][s] = load_frag_nt(brow[b][rt], k + 32 * s);
   };
   auto load_x = [&](int leaf, XF &x) {
     const int64_t k = (int64_t)leaf * kLeaf;
@@ -140,16 +145,33 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_nt(GemmParams p) {
 #pragma unroll
   for (int q = 0; q < NP; ++q) root[q] = 0;
 
-  auto finish_leaf = [&](f32x4 (&acc)[NB][MT], int j) {
+  // pack a leaf's accumulators (index ((b RT + rt) MT + t) 2 + h) and push them
+  auto finish_leaf = [&](f32x4 (&acc)[NB][RT][MT], int j) {
     uint32_t v[NP];
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
-      for (int t = 0; t < MT; ++t) {
-        v[(b * MT + t) * 2 + 0] = pack_rne(acc[b][t][0], acc[b][t][1]);
-        v[(b * MT + t) * 2 + 1] = pack_rne(acc[b][t][2], acc[b][t][3]);
-      }
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+          const int q = ((b * RT + rt) * MT + t) * 2;
+          v[q + 0] = pack_rne(acc[b][rt][t][0], acc[b][rt][t][1]);
+          v[q + 1] = pack_rne(acc[b][rt][t][2], acc[b][rt][t][3]);
+        }
     tree_push<NP>(st, v, root, nl, j);
+  };
+  auto leaf_mfma = [&](const WF &w, const XF &x, int j) {
+    f32x4 acc[NB][RT][MT];
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+          acc[b][rt][t] = mfma16(w.v[b][rt][0], x.v[SHARED_A ? 0 : b][t][0], f32x4{0.f, 0.f, 0.f, 0.f});
+          acc[b][rt][t] = mfma16(w.v[b][rt][1], x.v[SHARED_A ? 0 : b][t][1], acc[b][rt][t]);
+        }
+    finish_leaf(acc, j);
   };
 
   // Ring of P fragment buffers: leaf j lives in slot j % P.  The main loop
@@ -173,49 +195,31 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_nt(GemmParams p) {
       const int j = gi * P + q;
       load_w(min(lo + j + D, last), wb[(q + D) % P]);
       load_x(min(lo + j + D, last), xb[(q + D) % P]);
-      f32x4 acc[NB][MT];
-#pragma unroll
-      for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int t = 0; t < MT; ++t) {
-          acc[b][t] = mfma16(wb[q].v[b][0], xb[q].v[SHARED_A ? 0 : b][t][0], f32x4{0.f, 0.f, 0.f, 0.f});
-          acc[b][t] = mfma16(wb[q].v[b][1], xb[q].v[SHARED_A ? 0 : b][t][1], acc[b][t]);
-        }
-      finish_leaf(acc, j);
+      leaf_mfma(wb[q], xb[q], j);
     }
   }
   // the remaining nfull % P (< P, so <= D) leaves are already in the ring
 #pragma unroll
   for (int q = 0; q < P - 1; ++q) {
     const int j = ngroups * P + q;
-    if (j < nfull) {
-      f32x4 acc[NB][MT];
-#pragma unroll
-      for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int t = 0; t < MT; ++t) {
-          acc[b][t] = mfma16(wb[q].v[b][0], xb[q].v[SHARED_A ? 0 : b][t][0], f32x4{0.f, 0.f, 0.f, 0.f});
-          acc[b][t] = mfma16(wb[q].v[b][1], xb[q].v[SHARED_A ? 0 : b][t][1], acc[b][t]);
-        }
-      finish_leaf(acc, j);
-    }
+    if (j < nfull) leaf_mfma(wb[q], xb[q], j);
   }
 
   if (tail) {
     // the partial last leaf: zeros past K; an all-zero block leaves the
     // accumulator unchanged, so a half past K is skipped
     const int64_t kb = (int64_t)(hi - 1) * kLeaf;
-    f32x4 acc[NB][MT];
+    f32x4 acc[NB][RT][MT];
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
-      for (int t = 0; t < MT; ++t) acc[b][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int t = 0; t < MT; ++t) acc[b][rt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int s = 0; s < 2; ++s) {
       if (kb + 32 * s >= p.K) break;
       const int64_t k = kb + 32 * s;
-      bf16x8 wf[NB], xf[NA][MT];
-#pragma unroll
-      for (int b = 0; b < NB; ++b) wf[b] = load_frag_tail(brow[b], k, p.K - 8 * g4);
+      bf16x8 xf[NA][MT];
 #pragma unroll
       for (int a = 0; a < NA; ++a)
 #pragma unroll
@@ -223,45 +227,54 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_nt(GemmParams p) {
 #pragma unroll
       for (int b = 0; b < NB; ++b)
 #pragma unroll
-        for (int t = 0; t < MT; ++t) acc[b][t] = mfma16(wf[b], xf[SHARED_A ? 0 : b][t], acc[b][t]);
+        for (int rt = 0; rt < RT; ++rt) {
+          const bf16x8 wf = load_frag_tail(brow[b][rt], k, p.K - 8 * g4);
+#pragma unroll
+          for (int t = 0; t < MT; ++t) acc[b][rt][t] = mfma16(wf, xf[SHARED_A ? 0 : b][t], acc[b][rt][t]);
+        }
     }
     finish_leaf(acc, nl - 1);
   }
 
   if (!wg_combine<NP, WAVES>(root, dyn_lds, stack_words, wave, lane)) return;
 
-  const int64_t n = n0 + 4 * g4;
 #pragma unroll
-  for (int t = 0; t < MT; ++t) {
-    const int64_t m = m0 + 16 * t + r16;
-    if constexpr (EPI == EPI_STORE) {
+  for (int rt = 0; rt < RT; ++rt) {
+    const int64_t n = n0 + 16 * rt + 4 * g4;
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        if (p.ksplit_depth > 0)
-          store4(p.part + ((int64_t)b * (1 << p.ksplit_depth) + ks) * p.part_stride, p.ldp, m, n, p.M, p.N,
-                 root[(b * MT + t) * 2], root[(b * MT + t) * 2 + 1]);
-        else
-          store4(p.C[b], p.ldc[b], m, n, p.M, p.N, root[(b * MT + t) * 2], root[(b * MT + t) * 2 + 1]);
-      }
-    } else if constexpr (EPI == EPI_ACT) {
-      // gate (b = 0) and up (b = 1) of the same (m, n): a = bf16(silu(g) u)
-      uint32_t ap[2];
+    for (int t = 0; t < MT; ++t) {
+      const int64_t m = m0 + 16 * t + r16;
+      if constexpr (EPI == EPI_STORE) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const uint32_t gp = root[(0 * MT + t) * 2 + h], up = root[(1 * MT + t) * 2 + h];
-        float a2[2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const float g = e ? bf_hi(gp) : bf_lo(gp);
-          const float u = e ? bf_hi(up) : bf_lo(up);
-          const float s = g * sigma_f(g);
-          a2[e] = s * u;
+        for (int b = 0; b < NB; ++b) {
+          const int q = ((b * RT + rt) * MT + t) * 2;
+          if (p.ksplit_depth > 0)
+            store4(p.part + ((int64_t)b * (1 << p.ksplit_depth) + ks) * p.part_stride, p.ldp, m, n, p.M, p.N,
+                   root[q], root[q + 1]);
+          else
+            store4(p.C[b], p.ldc[b], m, n, p.M, p.N, root[q], root[q + 1]);
         }
-        ap[h] = pack_rne(a2[0], a2[1]);
+      } else if constexpr (EPI == EPI_ACT) {
+        // gate (b = 0) and up (b = 1) of the same (m, n): a = bf16(silu(g) u)
+        const int qg = ((0 * RT + rt) * MT + t) * 2, qu = ((1 * RT + rt) * MT + t) * 2;
+        uint32_t ap[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint32_t gp = root[qg + h], up = root[qu + h];
+          float a2[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const float g = e ? bf_hi(gp) : bf_lo(gp);
+            const float u = e ? bf_hi(up) : bf_lo(up);
+            const float s = g * sigma_f(g);
+            a2[e] = s * u;
+          }
+          ap[h] = pack_rne(a2[0], a2[1]);
+        }
+        store4(p.act_out, p.ld_act, m, n, p.M, p.N, ap[0], ap[1]);
+        if (p.C[0]) store4(p.C[0], p.ldc[0], m, n, p.M, p.N, root[qg], root[qg + 1]);
+        if (p.C[1]) store4(p.C[1], p.ldc[1], m, n, p.M, p.N, root[qu], root[qu + 1]);
       }
-      store4(p.act_out, p.ld_act, m, n, p.M, p.N, ap[0], ap[1]);
-      if (p.C[0]) store4(p.C[0], p.ldc[0], m, n, p.M, p.N, root[(0 * MT + t) * 2], root[(0 * MT + t) * 2 + 1]);
-      if (p.C[1]) store4(p.C[1], p.ldc[1], m, n, p.M, p.N, root[(1 * MT + t) * 2], root[(1 * MT + t) * 2 + 1]);
     }
   }
 }
@@ -269,25 +282,34 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_nt(GemmParams p) {
 // ------------------------------------------------------------------ NN
 
 // C_b[m][n] = T_K( A_b[m,:] . B_b[:,n] ); A_b [M,K] K-contiguous, B_b [K,N]
-// N-contiguous.  Each wave transposes its 64 x 16 weight slab of every leaf
-// through its own LDS region so that the MFMA A operand is K-contiguous; the
-// next leaf's slab rows are loaded while the current leaf computes.
-constexpr int kTStride = 72;  // padded K stride of a transposed slab (elements)
+// N-contiguous.  A wave owns 16 RT output columns; per leaf it loads the 64 x
+// 16 RT weight slab as whole row segments (2 RT lanes of 16 bytes per row) and
+// transposes it through its own LDS region so that the MFMA A operand is
+// K-contiguous.  The slab keeps column n's 64 K values in one 128-byte row
+// whose 16-byte chunks are permuted by XOR with swz(n), so that both the
+// transposing 2-byte writes and the 16-byte operand reads spread over the
+// banks.
+__device__ __forceinline__ int slab_swz(int n) { return (n ^ (n >> 3)) & 7; }
 
-template <int NB, int MT, int WAVES, int EPI>
+template <int NB, int RT, int MT, int WAVES, int EPI>
 __global__ __launch_bounds__(WAVES * 64) void k_gemm_nn(GemmParams p) {
-  constexpr int NP = NB * MT * 2;
+  constexpr int NP = NB * RT * MT * 2;
   constexpr int DW = log2i<WAVES>();
-  __shared__ __attribute__((aligned(16))) uint16_t slab[WAVES][NB][16 * kTStride];
+  constexpr int NI = 2 * RT;           // 16-byte loads per lane per leaf and product
+  constexpr int ROWS = 32 / RT;        // slab rows per load instruction
+  constexpr int P = NB * RT * MT >= 8 ? 2 : NB * RT * MT >= 4 ? 3 : 4, D = P - 1;
+  __shared__ __attribute__((aligned(16))) uint16_t slab[WAVES][NB][16 * RT * 64];
   extern __shared__ __attribute__((aligned(16))) uint32_t dyn_lds[];
   const int stack_words = p.stack_slots * NP * 64;  // per wave
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t n0 = (int64_t)xcd_tile(blockIdx.x, gridDim.x) * 16;
+  const int64_t n0 = (int64_t)xcd_tile(blockIdx.x, gridDim.x) * (16 * RT);
   const int64_t m0 = (int64_t)blockIdx.y * (16 * MT);
   const int ks = blockIdx.z;
   const int r16 = lane & 15, g4 = lane >> 4;
+  // this lane's place in a load instruction: slab row lrow (+ ROWS i), columns 8 lcol .. 8 lcol + 7
+  const int lrow = lane / NI, lcol = lane % NI;
 
   int lo, hi;
   subtree_range(p.L, p.ksplit_depth + DW, (ks << DW) | wave, lo, hi);
@@ -300,38 +322,41 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_nn(GemmParams p) {
 #pragma unroll
     for (int b = 0; b < NB; ++b) arow[b][t] = p.A[b] + m * p.lda[b];
   }
-  const bool full_n = n0 + 16 <= p.N;
+  const bool full_n = n0 + 16 * RT <= p.N;
   const bool tail = (int64_t)hi * kLeaf > p.K;  // this wave owns the partial last leaf
   const int nfull = tail ? nl - 1 : nl;
 
-  // lane l fetches weight row leaf*64 + l, columns n0..n0+15: two 16-byte
-  // pieces (full leaf, full column tile) or element by element with zeros
-  // outside the matrix
-  auto fetch_fast = [&](int leaf, uint32_t (&q)[NB][8]) {
-    const int64_t kr = (int64_t)leaf * kLeaf + lane;
-    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  struct QF { u32x4 v[NB][NI]; };
+  // full leaf, full column tile: 16-byte row pieces
+  auto fetch_fast = [&](int leaf, QF &q) {
+    const int64_t kr = (int64_t)leaf * kLeaf + lrow;
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const uint16_t *src = p.B[b] + kr * p.ldb[b] + n0;
-      const u32x4 v0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src));
-      const u32x4 v1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src + 8));
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) { q[b][i] = v0[i]; q[b][4 + i] = v1[i]; }
-    }
+      for (int i = 0; i < NI; ++i)
+        q.v[b][i] = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4 *>(p.B[b] + (kr + ROWS * i) * p.ldb[b] + n0 + 8 * lcol));
   };
-  auto fetch_slow = [&](int leaf, uint32_t (&q)[NB][8]) {
-    const int64_t kr = (int64_t)leaf * kLeaf + lane;
-    const bool kok = kr < p.K;
+  // element by element with zeros outside the matrix
+  auto fetch_slow = [&](int leaf, QF &q) {
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const uint16_t *src = p.B[b] + (kok ? kr : 0) * p.ldb[b] + n0;
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t lo16 = (kok && n0 + 2 * i < p.N) ? src[2 * i] : 0u;
-        const uint32_t hi16 = (kok && n0 + 2 * i + 1 < p.N) ? src[2 * i + 1] : 0u;
-        q[b][i] = lo16 | (hi16 << 16);
+      for (int i = 0; i < NI; ++i) {
+        const int64_t kr = (int64_t)leaf * kLeaf + lrow + ROWS * i;
+        const bool kok = kr < p.K;
+        const uint16_t *src = p.B[b] + (kok ? kr : 0) * p.ldb[b] + n0 + 8 * lcol;
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int64_t n = n0 + 8 * lcol + 2 * e;
+          const uint32_t lo16 = (kok && n < p.N) ? src[2 * e] : 0u;
+          const uint32_t hi16 = (kok && n + 1 < p.N) ? src[2 * e + 1] : 0u;
+          w[e] = lo16 | (hi16 << 16);
+        }
+        q.v[b][i] = u32x4{w[0], w[1], w[2], w[3]};
       }
-    }
   };
 
   TreeStack<NP> st{dyn_lds + wave * stack_words + lane};
@@ -360,41 +385,55 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_nn(GemmParams p) {
         for (int s = 0; s < 2; ++s) x.v[b][t][s] = load_frag_tail(arow[b][t], kb + 32 * s + 8 * g4, p.K);
   };
 
-  // stage the slab, transpose through LDS, two MFMA halves, then the tree
-  auto leaf_body = [&](int j, const uint32_t (&q)[NB][8], const XF &x, bool partial) {
+  // stage the slab transposed, two MFMA halves per column tile, then the tree
+  auto leaf_body = [&](int j, const QF &q, const XF &x, bool partial) {
     const int64_t kb = (int64_t)(lo + j) * kLeaf;
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        slab[wave][b][(2 * i) * kTStride + lane] = (uint16_t)(q[b][i] & 0xffff);
-        slab[wave][b][(2 * i + 1) * kTStride + lane] = (uint16_t)(q[b][i] >> 16);
+      for (int i = 0; i < NI; ++i) {
+        const int k = lrow + ROWS * i;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int n = 8 * lcol + e;
+          const uint32_t w = q.v[b][i][e >> 1];
+          slab[wave][b][n * 64 + 8 * ((k >> 3) ^ slab_swz(n)) + (k & 7)] = (uint16_t)((e & 1) ? (w >> 16) : w);
+        }
       }
     wave_lds_sync();  // this wave's slab writes land before its lanes read them
-    f32x4 acc[NB][MT];
+    f32x4 acc[NB][RT][MT];
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
-      for (int t = 0; t < MT; ++t) acc[b][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int t = 0; t < MT; ++t) acc[b][rt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       if (partial && kb + 32 * s >= p.K) break;  // all-zero block: accumulator unchanged
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const bf16x8 wf = *reinterpret_cast<const bf16x8 *>(&slab[wave][b][r16 * kTStride + 32 * s + 8 * g4]);
+      for (int b = 0; b < NB; ++b)
 #pragma unroll
-        for (int t = 0; t < MT; ++t) acc[b][t] = mfma16(wf, x.v[b][t][s], acc[b][t]);
-      }
+        for (int rt = 0; rt < RT; ++rt) {
+          const int n = 16 * rt + r16;
+          const bf16x8 wf =
+              *reinterpret_cast<const bf16x8 *>(&slab[wave][b][n * 64 + 8 * ((4 * s + g4) ^ slab_swz(n))]);
+#pragma unroll
+          for (int t = 0; t < MT; ++t) acc[b][rt][t] = mfma16(wf, x.v[b][t][s], acc[b][rt][t]);
+        }
     }
     wave_lds_sync();  // slab reads done before the next leaf overwrites it
     uint32_t v[NP];
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
-      for (int t = 0; t < MT; ++t) {
-        v[(b * MT + t) * 2 + 0] = pack_rne(acc[b][t][0], acc[b][t][1]);
-        v[(b * MT + t) * 2 + 1] = pack_rne(acc[b][t][2], acc[b][t][3]);
-      }
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+          const int qi = ((b * RT + rt) * MT + t) * 2;
+          v[qi + 0] = pack_rne(acc[b][rt][t][0], acc[b][rt][t][1]);
+          v[qi + 1] = pack_rne(acc[b][rt][t][2], acc[b][rt][t][3]);
+        }
     tree_push<NP>(st, v, root, nl, j);
   };
 
@@ -402,8 +441,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_nn(GemmParams p) {
     // Weight rows and activation fragments are fetched D leaves ahead, at the
     // same distance, into a ring where leaf j lives in slot j % P; the loop
     // issues them unconditionally (clamped indices) so that waits stay partial.
-    constexpr int P = 4, D = 3;
-    uint32_t qb[P][NB][8];
+    QF qb[P];
     XF xb[P];
     const int last = lo + nfull - 1;
     if (nfull > 0) {
@@ -430,7 +468,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_nn(GemmParams p) {
     }
   } else {
     for (int j = 0; j < nfull; ++j) {
-      uint32_t q[NB][8];
+      QF q;
       XF x;
       fetch_slow(lo + j, q);
       load_x(lo + j, x);
@@ -438,7 +476,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_nn(GemmParams p) {
     }
   }
   if (tail) {
-    uint32_t q[NB][8];
+    QF q;
     XF x;
     fetch_slow(hi - 1, q);
     load_x_tail(hi - 1, x);
@@ -447,47 +485,52 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_nn(GemmParams p) {
 
   if (!wg_combine<NP, WAVES>(root, dyn_lds, stack_words, wave, lane)) return;
 
-  const int64_t n = n0 + 4 * g4;
 #pragma unroll
-  for (int t = 0; t < MT; ++t) {
-    const int64_t m = m0 + 16 * t + r16;
-    if constexpr (EPI == EPI_STORE) {
+  for (int rt = 0; rt < RT; ++rt) {
+    const int64_t n = n0 + 16 * rt + 4 * g4;
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        if (p.ksplit_depth > 0)
-          store4(p.part + ((int64_t)b * (1 << p.ksplit_depth) + ks) * p.part_stride, p.ldp, m, n, p.M, p.N,
-                 root[(b * MT + t) * 2], root[(b * MT + t) * 2 + 1]);
-        else
-          store4(p.C[b], p.ldc[b], m, n, p.M, p.N, root[(b * MT + t) * 2], root[(b * MT + t) * 2 + 1]);
-      }
-    } else if constexpr (EPI == EPI_DSILU) {
-      // dA at (m, n = i) with the saved g, u: dU = bf16(dA s), dG = bf16((dA u) s'),
-      // a = bf16(s u); written row-major [M, I] and transposed [I, M].
-      if (m < p.M) {
+    for (int t = 0; t < MT; ++t) {
+      const int64_t m = m0 + 16 * t + r16;
+      if constexpr (EPI == EPI_STORE) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int64_t i = n + r;
-          if (i >= p.N) break;
-          const uint32_t pr = root[t * 2 + (r >> 1)];
-          const float da = (r & 1) ? bf_hi(pr) : bf_lo(pr);
-          const float g = bf2f(p.sg[m * p.ld_gu + i]);
-          const float u = bf2f(p.su[m * p.ld_gu + i]);
-          const float sg = sigma_f(g);
-          const float s = g * sg;
-          const float one_m = 1.0f - sg;
-          const float tt = g * one_m;
-          const float onep = 1.0f + tt;
-          const float ds = sg * onep;
-          const uint16_t du = f2bf(da * s);
-          const float dau = da * u;
-          const uint16_t dg = f2bf(dau * ds);
-          const uint16_t a = f2bf(s * u);
-          if (p.dG) p.dG[m * p.ld_d + i] = dg;
-          if (p.dU) p.dU[m * p.ld_d + i] = du;
-          if (p.dGT) p.dGT[i * p.ld_t + m] = dg;
-          if (p.dUT) p.dUT[i * p.ld_t + m] = du;
-          if (p.aT) p.aT[i * p.ld_t + m] = a;
-          if (p.a_rm) p.a_rm[m * p.ld_d + i] = a;
+        for (int b = 0; b < NB; ++b) {
+          const int q = ((b * RT + rt) * MT + t) * 2;
+          if (p.ksplit_depth > 0)
+            store4(p.part + ((int64_t)b * (1 << p.ksplit_depth) + ks) * p.part_stride, p.ldp, m, n, p.M, p.N,
+                   root[q], root[q + 1]);
+          else
+            store4(p.C[b], p.ldc[b], m, n, p.M, p.N, root[q], root[q + 1]);
+        }
+      } else if constexpr (EPI == EPI_DSILU) {
+        // dA at (m, n = i) with the saved g, u: dU = bf16(dA s), dG = bf16((dA u) s'),
+        // a = bf16(s u); written row-major [M, I] and transposed [I, M].
+        if (m < p.M) {
+          const int q = (rt * MT + t) * 2;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int64_t i = n + r;
+            if (i >= p.N) break;
+            const uint32_t pr = root[q + (r >> 1)];
+            const float da = (r & 1) ? bf_hi(pr) : bf_lo(pr);
+            const float g = bf2f(p.sg[m * p.ld_gu + i]);
+            const float u = bf2f(p.su[m * p.ld_gu + i]);
+            const float sg = sigma_f(g);
+            const float s = g * sg;
+            const float one_m = 1.0f - sg;
+            const float tt = g * one_m;
+            const float onep = 1.0f + tt;
+            const float ds = sg * onep;
+            const uint16_t du = f2bf(da * s);
+            const float dau = da * u;
+            const uint16_t dg = f2bf(dau * ds);
+            const uint16_t a = f2bf(s * u);
+            if (p.dG) p.dG[m * p.ld_d + i] = dg;
+            if (p.dU) p.dU[m * p.ld_d + i] = du;
+            if (p.dGT) p.dGT[i * p.ld_t + m] = dg;
+            if (p.dUT) p.dUT[i * p.ld_t + m] = du;
+            if (p.aT) p.aT[i * p.ld_t + m] = a;
+            if (p.a_rm) p.a_rm[m * p.ld_d + i] = a;
+          }
         }
       }
     }
@@ -585,40 +628,42 @@ hipError_t launch_gemm_short(int nb, GemmParams p, hipStream_t stream) {
 
 // ------------------------------------------------------------------ launch
 
-#define DGF_DISPATCH_WAVES(KERNEL, NB, MT, EPI)                                                             \
+#define DGF_DISPATCH_WAVES(KERNEL, NB, RT, MT, EPI)                                                         \
   {                                                                                                         \
-    const size_t shm = (size_t)waves * p.stack_slots * (NB * MT * 2) * 64 * 4;                              \
+    const size_t shm = (size_t)waves * p.stack_slots * (NB * RT * MT * 2) * 64 * 4;                         \
     switch (waves) {                                                                                        \
-      case 1: hipLaunchKernelGGL((KERNEL<NB, MT, 1, EPI>), grid, dim3(64), shm, stream, p); break;          \
-      case 2: hipLaunchKernelGGL((KERNEL<NB, MT, 2, EPI>), grid, dim3(128), shm, stream, p); break;         \
-      case 4: hipLaunchKernelGGL((KERNEL<NB, MT, 4, EPI>), grid, dim3(256), shm, stream, p); break;         \
-      default: hipLaunchKernelGGL((KERNEL<NB, MT, 8, EPI>), grid, dim3(512), shm, stream, p); break;        \
+      case 1: hipLaunchKernelGGL((KERNEL<NB, RT, MT, 1, EPI>), grid, dim3(64), shm, stream, p); break;      \
+      case 2: hipLaunchKernelGGL((KERNEL<NB, RT, MT, 2, EPI>), grid, dim3(128), shm, stream, p); break;     \
+      default: hipLaunchKernelGGL((KERNEL<NB, RT, MT, 4, EPI>), grid, dim3(256), shm, stream, p); break;    \
     }                                                                                                       \
   }
 
+#define DGF_DISPATCH_MT(KERNEL, NB, RT, EPI)                   \
+  {                                                            \
+    if (mt == 1) DGF_DISPATCH_WAVES(KERNEL, NB, RT, 1, EPI)    \
+    else DGF_DISPATCH_WAVES(KERNEL, NB, RT, 2, EPI)            \
+  }
+
+int gemm_row_tiles(int layout, int nb, int epi) {
+  if (layout == DGF_LAYOUT_NT) return nb == 2 ? 2 : 4;
+  return epi == EPI_DSILU ? 2 : 4;
+}
+
 hipError_t launch_gemm(int layout, int nb, int epi, GemmParams p, int waves, hipStream_t stream) {
   const int mt = p.M <= 16 ? 1 : 2;
-  const int64_t tiles_n = (p.N + 15) / 16;
+  const int rt = gemm_row_tiles(layout, nb, epi);
+  const int64_t tiles_n = (p.N + 16 * rt - 1) / (16 * rt);
   const int64_t tiles_m = (p.M + 16 * mt - 1) / (16 * mt);
   dim3 grid((unsigned)tiles_n, (unsigned)tiles_m, (unsigned)(1 << p.ksplit_depth));
   if (layout == DGF_LAYOUT_NT) {
-    if (nb == 1 && epi == EPI_STORE) {
-      if (mt == 1) { DGF_DISPATCH_WAVES(k_gemm_nt, 1, 1, EPI_STORE) } else { DGF_DISPATCH_WAVES(k_gemm_nt, 1, 2, EPI_STORE) }
-    } else if (nb == 2 && epi == EPI_STORE) {
-      if (mt == 1) { DGF_DISPATCH_WAVES(k_gemm_nt, 2, 1, EPI_STORE) } else { DGF_DISPATCH_WAVES(k_gemm_nt, 2, 2, EPI_STORE) }
-    } else if (nb == 2 && epi == EPI_ACT) {
-      if (mt == 1) { DGF_DISPATCH_WAVES(k_gemm_nt, 2, 1, EPI_ACT) } else { DGF_DISPATCH_WAVES(k_gemm_nt, 2, 2, EPI_ACT) }
-    } else {
-      return hipErrorInvalidValue;
-    }
+    if (nb == 1 && epi == EPI_STORE) DGF_DISPATCH_MT(k_gemm_nt, 1, 4, EPI_STORE)
+    else if (nb == 2 && epi == EPI_STORE) DGF_DISPATCH_MT(k_gemm_nt, 2, 2, EPI_STORE)
+    else if (nb == 2 && epi == EPI_ACT) DGF_DISPATCH_MT(k_gemm_nt, 2, 2, EPI_ACT)
+    else return hipErrorInvalidValue;
   } else {
-    if (nb == 1 && epi == EPI_STORE) {
-      if (mt == 1) { DGF_DISPATCH_WAVES(k_gemm_nn, 1, 1, EPI_STORE) } else { DGF_DISPATCH_WAVES(k_gemm_nn, 1, 2, EPI_STORE) }
-    } else if (nb == 1 && epi == EPI_DSILU) {
-      if (mt == 1) { DGF_DISPATCH_WAVES(k_gemm_nn, 1, 1, EPI_DSILU) } else { DGF_DISPATCH_WAVES(k_gemm_nn, 1, 2, EPI_DSILU) }
-    } else {
-      return hipErrorInvalidValue;
-    }
+    if (nb == 1 && epi == EPI_STORE) DGF_DISPATCH_MT(k_gemm_nn, 1, 4, EPI_STORE)
+    else if (nb == 1 && epi == EPI_DSILU) DGF_DISPATCH_MT(k_gemm_nn, 1, 2, EPI_DSILU)
+    else return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }

@@ -7,7 +7,7 @@
 namespace dgf {
 
 enum { DGF_LAYOUT_NT = 0, DGF_LAYOUT_NN = 1 };
-enum { EPI_STORE = 0, EPI_ACT = 1, EPI_DSILU = 2 };
+enum { EPI_STORE = 0, EPI_ACT = 1, EPI_DSILU = 2, EPI_DX = 3 };
 
 // Arguments of one tree-GEMM launch (two products when NB = 2).
 struct GemmParams {
@@ -21,7 +21,8 @@ struct GemmParams {
   int L;                 // leaves = ceil(K / 64)
   int stack_slots;       // LDS tree-stack slots per wave (>= 1, >= a wave subtree's depth)
   int ksplit_depth;      // the K leaves are split over 2^ksplit_depth workgroups (grid.z)
-  uint16_t *part;        // ksplit_depth > 0: partial roots [NB][2^ksplit_depth][M][ldp]
+  uint16_t *part;        // ksplit_depth > 0 (or to_part): partial roots [NB][2^ksplit_depth][M][ldp]
+  int to_part;           // weight-streaming kernel: roots go to `part` (joined by the combine kernel)
   int64_t ldp, part_stride;
   int shared_a;          // NB = 2 with A[1] == A[0]
   // EPI_ACT: a = bf16(silu(C0) * C1)
@@ -34,8 +35,24 @@ struct GemmParams {
   int64_t ld_d;
   uint16_t *dGT, *dUT, *aT;
   int64_t ld_t;
+  // EPI_DX (combine only): dx = bf16(G + U) of the two lanes; C[0], C[1] keep the lanes when set
+  uint16_t *dx;
+  int64_t lddx;
 };
 
+// Weight-streaming tree GEMM with stationary activations (dgf_xs.hip):
+// EPI_STORE products b < nb (grid.z = nb << ksplit_depth), each wave owning
+// at most 4 leaves; roots go to C[b] (ksplit_depth = 0) or to the partials.
+int xs_tile_cols(int layout, int mt);
+size_t xs_lds_bytes(int layout, int mt, int waves);
+hipError_t launch_xs(int layout, GemmParams p, int nb, int waves, int groups, hipStream_t stream);
+// Join the 2^ksplit_depth partial roots of each product and apply the
+// epilogue (STORE: C[b] for b < nb; ACT: a (and g, u in C[0], C[1]) from the
+// gate and up products; DSILU: dG, dU, a from dA; DX: dx from the G and U lanes).
+hipError_t launch_combine_epi(int epi, int nb, GemmParams p, hipStream_t stream);
+
+// Output row tiles of 16 per wave of the NT / NN tree GEMM kernel variants.
+int gemm_row_tiles(int layout, int nb, int epi);
 hipError_t launch_gemm(int layout, int nb, int epi, GemmParams p, int waves, hipStream_t stream);
 // NT, EPI_STORE, K <= 64 (one leaf), B shared by the NB products
 hipError_t launch_gemm_short(int nb, GemmParams p, hipStream_t stream);

@@ -1,0 +1,463 @@
+// Weight-streaming tree GEMMs with stationary activations (gfx950).
+//
+// C_b[m][n] = T_K( A_b[m,:] . W_b[n or :, :] ) for the FFN's thin products:
+// few tokens m, a large weight W_b that is read from HBM exactly once.
+//
+// Work split.  The canonical midpoint tree over the L = ceil(K/64) leaves is
+// cut at depth kd into 2^kd K pieces (grid.z, times the batched products b),
+// and each piece again at depth log2(WAVES) into one subtree of at most 4
+// leaves per wave.  A wave loads the activation fragments of its leaves once
+// and keeps them in registers while it walks over a contiguous range of
+// output tiles (16 RT columns each): per tile it streams its leaves' weight
+// rows (NT: 16 RT rows x 64 K per leaf) or weight slab (NN: 64 K rows x 16 RT
+// columns per leaf, in two halves of 32 rows, transposed through LDS),
+// reduces the leaves with the subtree's fixed shape in registers and parks
+// the subtree root in LDS.  After a workgroup barrier the WAVES roots of the
+// tile are joined with the balanced top of the piece's subtree, each wave
+// taking one 16 x 16 block of the tile, and the piece root is stored: to the
+// caller's output (kd = 0, plain store), else to a partial buffer that a
+// combine kernel joins with the top kd levels of the tree and the epilogue
+// (RL-Kernel PR #325, section "Design": contiguous K pieces are subtrees of
+// the one canonical tree, so any cut reproduces the unsharded result).
+//
+// Every weight byte is read once per token tile; the activation operand is
+// read once per wave instead of once per leaf and tile, which is what bounds
+// a thin tree GEMM that reloads it.  An NN wave reads whole 128-byte row
+// segments (64 columns); with 32 columns two CUs would each fetch half of
+// every line.
+#include "dgf_device.hpp"
+#include "dgf_kernels.hpp"
+
+namespace dgf {
+namespace {
+
+constexpr int kMaxNL = 4;    // leaves per wave
+constexpr int kXsWaves = 8;  // waves per workgroup (at most)
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-column tiles per output tile.  NT: 4 (64 columns) for one token tile, 2
+// for two, which keeps a wave's registers (stationary activations, two leaves
+// of weights in flight, the pending subtree values) within the 256 that let
+// two waves share a SIMD.  NN: always 4, streamed in half leaves.
+template <int LAYOUT, int MT>
+constexpr int rt_of() {
+  return LAYOUT == DGF_LAYOUT_NN ? 4 : (MT == 1 ? 4 : 2);
+}
+
+__device__ __forceinline__ int xs_swz(int n) { return (n ^ (n >> 3)) & 7; }
+
+// One streaming unit of weights: NT a whole leaf, NN half a leaf.
+template <int LAYOUT, int RT>
+struct WFrag;
+template <int RT>
+struct WFrag<DGF_LAYOUT_NT, RT> {
+  bf16x8 v[RT][2];  // rows 16 rt + r16, K half h
+};
+template <int RT>
+struct WFrag<DGF_LAYOUT_NN, RT> {
+  u32x4 v[RT];  // slab rows 32 S + lrow + (32 / RT) i, columns 8 lcol .. 8 lcol + 7
+};
+
+template <int MT>
+struct XFrag {
+  bf16x8 v[kMaxNL][MT][2];
+};
+
+// Static-shape post-order reduction of a wave's nl <= 4 leaves (midpoint
+// tree: 3 leaves split 1 | 2, 4 leaves split 2 | 2).  v holds leaf J of the
+// tile on entry and, after the last leaf, the subtree root.
+template <int NP, int J>
+__device__ __forceinline__ void leaf_reduce(int nl, uint32_t (&v)[NP], uint32_t (&s0)[NP], uint32_t (&s1)[NP]) {
+  if (nl == 2) {
+    if constexpr (J == 0) {
+#pragma unroll
+      for (int q = 0; q < NP; ++q) s0[q] = v[q];
+    } else if constexpr (J == 1) {
+#pragma unroll
+      for (int q = 0; q < NP; ++q) v[q] = node2(s0[q], v[q]);
+    }
+  } else if (nl == 3) {
+    if constexpr (J == 0) {
+#pragma unroll
+      for (int q = 0; q < NP; ++q) s0[q] = v[q];
+    } else if constexpr (J == 1) {
+#pragma unroll
+      for (int q = 0; q < NP; ++q) s1[q] = v[q];
+    } else if constexpr (J == 2) {
+#pragma unroll
+      for (int q = 0; q < NP; ++q) v[q] = node2(s0[q], node2(s1[q], v[q]));
+    }
+  } else if (nl == 4) {
+    if constexpr (J == 0) {
+#pragma unroll
+      for (int q = 0; q < NP; ++q) s0[q] = v[q];
+    } else if constexpr (J == 1) {
+#pragma unroll
+      for (int q = 0; q < NP; ++q) s0[q] = node2(s0[q], v[q]);
+    } else if constexpr (J == 2) {
+#pragma unroll
+      for (int q = 0; q < NP; ++q) s1[q] = v[q];
+    } else if constexpr (J == 3) {
+#pragma unroll
+      for (int q = 0; q < NP; ++q) v[q] = node2(s0[q], node2(s1[q], v[q]));
+    }
+  }
+}
+
+template <int LAYOUT, int MT>
+struct XsWave {
+  static constexpr bool NN = LAYOUT == DGF_LAYOUT_NN;
+  static constexpr int RT = rt_of<LAYOUT, MT>();
+  static constexpr int NP = RT * MT * 2;  // packed BF16 pairs per lane: index (rt MT + t) 2 + h
+  static constexpr int NI = 2 * RT;       // NN: lanes per slab row (16 bytes each)
+  static constexpr int ROWS = 32 / RT;    // NN: slab rows per load instruction
+  static constexpr int COLS = 16 * RT;    // output columns per tile
+  using WF = WFrag<LAYOUT, RT>;
+
+  const GemmParams &p;
+  uint32_t *roots;   // LDS [2][waves][NP][64]
+  uint16_t *slab;    // LDS, this wave's COLS x 64 transpose slab (NN)
+  int waves, wave, lane, r16, g4;
+  int b, lo, nl;
+  bool tail;
+  int64_t m0;
+  int tiles_n, t0, T;  // this workgroup's tiles: t0 .. t0 + T - 1
+  const uint16_t *W;
+  int64_t ldw;
+  uint16_t *out;
+  int64_t ldo;
+
+  __device__ __forceinline__ int tile_at(int i) const { return t0 + (i < T ? i : T - 1); }
+
+  // Weights of unit (tile i clamped, leaf lo + j, half s): NT the whole leaf
+  // (s ignored), NN rows 32 s .. 32 s + 31 of the leaf's slab.
+  __device__ __forceinline__ void load_unit(int i, int j, int s, WF &w) const {
+    const int64_t n0 = (int64_t)tile_at(i) * COLS;
+    const int64_t kb = (int64_t)(lo + j) * kLeaf;
+    if constexpr (!NN) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        // rows past N read the last row (their outputs are never stored)
+        const int64_t n = n0 + 16 * rt + r16 < p.N ? n0 + 16 * rt + r16 : p.N - 1;
+        const uint16_t *row = W + n * ldw + kb + 8 * g4;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          w.v[rt][h] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8 *>(row + 32 * h));
+      }
+    } else {
+      // 16-byte pieces of whole rows; a piece starting past N reads the last
+      // in-row piece instead (the leading dimension is a multiple of 8, and
+      // each output column depends on its own weight column only)
+      const int lrow = lane / NI, lcol = lane % NI;
+      const int64_t c0 = n0 + 8 * lcol;
+      const int64_t nlast = ((p.N + 7) & ~(int64_t)7) - 8;
+      const int64_t c = c0 <= nlast ? c0 : nlast;
+      const uint16_t *base = W + (kb + 32 * s + lrow) * ldw + c;
+#pragma unroll
+      for (int i2 = 0; i2 < RT; ++i2)
+        w.v[i2] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(base + (int64_t)ROWS * i2 * ldw));
+    }
+  }
+
+  // The same for the partial last leaf: zeros past K.
+  __device__ __forceinline__ void load_unit_tail(int i, int j, int s, WF &w) const {
+    const int64_t n0 = (int64_t)tile_at(i) * COLS;
+    const int64_t kb = (int64_t)(lo + j) * kLeaf;
+    if constexpr (!NN) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const int64_t n = n0 + 16 * rt + r16 < p.N ? n0 + 16 * rt + r16 : p.N - 1;
+        const uint16_t *row = W + n * ldw;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) w.v[rt][h] = load_frag_tail(row, kb + 32 * h + 8 * g4, p.K);
+      }
+    } else {
+      // rows past K read row K-1 and are zeroed
+      const int lrow = lane / NI, lcol = lane % NI;
+      const int64_t c0 = n0 + 8 * lcol;
+      const int64_t nlast = ((p.N + 7) & ~(int64_t)7) - 8;
+      const int64_t c = c0 <= nlast ? c0 : nlast;
+#pragma unroll
+      for (int i2 = 0; i2 < RT; ++i2) {
+        const int64_t k = kb + 32 * s + lrow + ROWS * i2;
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(W + (k < p.K ? k : p.K - 1) * ldw + c);
+        w.v[i2] = k < p.K ? v : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  }
+
+  __device__ __forceinline__ void pack(const f32x4 (&acc)[RT][MT], uint32_t (&v)[NP]) const {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        v[(rt * MT + t) * 2 + 0] = pack_rne(acc[rt][t][0], acc[rt][t][1]);
+        v[(rt * MT + t) * 2 + 1] = pack_rne(acc[rt][t][2], acc[rt][t][3]);
+      }
+  }
+
+  // NT: both K halves of a leaf (the second unless `half1` is false: an
+  // all-zero block leaves the sum unchanged), packed to BF16.
+  __device__ __forceinline__ void leaf_nt(const WF &w, const bf16x8 (&x)[MT][2], bool half1, uint32_t (&v)[NP]) const {
+    f32x4 acc[RT][MT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        acc[rt][t] = mfma16(w.v[rt][0], x[t][0], f32x4{0.f, 0.f, 0.f, 0.f});
+        if (half1) acc[rt][t] = mfma16(w.v[rt][1], x[t][1], acc[rt][t]);
+      }
+    pack(acc, v);
+  }
+
+  // NN: half S of a leaf.  The 32 slab rows go to LDS transposed (element
+  // (k, n) at n*64 + 8 ((k>>3) ^ swz(n)) + (k&7)); this lane's rows are
+  // k = 32 S + lrow + ROWS i2 of columns n = 8 lcol + e, whose chunk
+  // (k>>3) ^ swz(n) is c ^ lx with c = ((32 S + ROWS i2) / 8) ^ e and
+  // lx = (lrow>>3) ^ lcol: eight base addresses plus the immediate 64 e.
+  template <int S>
+  __device__ __forceinline__ void half_nn(const WF &w, const bf16x8 (&x)[MT][2], f32x4 (&acc)[RT][MT]) const {
+    const int lrow = lane / NI, lcol = lane % NI;
+    const int lx = (lrow >> 3) ^ lcol;
+    uint16_t *wp[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) wp[c] = slab + 8 * lcol * 64 + (lrow & 7) + 8 * (c ^ lx);
+#pragma unroll
+    for (int i2 = 0; i2 < RT; ++i2)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t word = w.v[i2][e >> 1];
+        wp[((32 * S + ROWS * i2) >> 3) ^ e][64 * e] = (uint16_t)((e & 1) ? (word >> 16) : word);
+      }
+    wave_lds_sync();  // this wave's slab writes land before its lanes read them
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const int n = 16 * rt + r16;
+      const bf16x8 wf = *reinterpret_cast<const bf16x8 *>(&slab[n * 64 + 8 * ((4 * S + g4) ^ xs_swz(n))]);
+#pragma unroll
+      for (int t = 0; t < MT; ++t) acc[rt][t] = mfma16(wf, x[t][S], S == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[rt][t]);
+    }
+    wave_lds_sync();  // slab reads done before the next unit overwrites it
+  }
+
+  // Park this wave's subtree root of tile i, then (after the barrier) join the
+  // WAVES roots for one 16 x 16 block per wave and store it.
+  __device__ __forceinline__ void finish_tile(int i, const uint32_t (&root)[NP]) const {
+    uint32_t *buf = roots + (size_t)(i & 1) * waves * NP * 64;
+#pragma unroll
+    for (int q = 0; q < NP; ++q) buf[(wave * NP + q) * 64 + lane] = root[q];
+    __syncthreads();
+    const int64_t n0 = (int64_t)tile_at(i) * COLS;
+    for (int blk = wave; blk < RT * MT; blk += waves) {
+      uint32_t r[kXsWaves][2];
+#pragma unroll
+      for (int w2 = 0; w2 < kXsWaves; ++w2)
+        if (w2 < waves) {
+          r[w2][0] = buf[(w2 * NP + 2 * blk + 0) * 64 + lane];
+          r[w2][1] = buf[(w2 * NP + 2 * blk + 1) * 64 + lane];
+        }
+#pragma unroll
+      for (int width = kXsWaves; width > 1; width >>= 1) {
+        if (width <= waves) {
+#pragma unroll
+          for (int k2 = 0; k2 < width / 2; ++k2) {
+            r[k2][0] = node2(r[2 * k2][0], r[2 * k2 + 1][0]);
+            r[k2][1] = node2(r[2 * k2][1], r[2 * k2 + 1][1]);
+          }
+        }
+      }
+      const int rt = blk / MT, t = blk % MT;
+      const int64_t m = m0 + 16 * t + r16, n = n0 + 16 * rt + 4 * g4;
+      if (m < p.M) {
+        uint16_t *dst = out + m * ldo + n;
+        if (n + 3 < p.N) {
+          *reinterpret_cast<uint2 *>(dst) = make_uint2(r[0][0], r[0][1]);
+        } else {
+          const uint16_t h4[4] = {(uint16_t)(r[0][0] & 0xffff), (uint16_t)(r[0][0] >> 16), (uint16_t)(r[0][1] & 0xffff),
+                                  (uint16_t)(r[0][1] >> 16)};
+          for (int e = 0; e < 4; ++e)
+            if (n + e < p.N) dst[e] = h4[e];
+        }
+      }
+    }
+  }
+
+  // Units U.. of one tile.  Unit U is leaf U (NT) or half U % 2 of leaf U / 2
+  // (NN); each first issues the loads of the next unit (of this tile, or the
+  // first of tile i + 1) into the other ring slot.  NT slot: (Q NF + U) % 2
+  // for the tile in position Q of its pair; NN slot: the half.
+  template <int NF, int Q, int U>
+  __device__ __forceinline__ void units(int i, WF (&ring)[2], const XFrag<MT> &xs, f32x4 (&acc)[RT][MT],
+                                        uint32_t (&v)[NP], uint32_t (&s0)[NP], uint32_t (&s1)[NP]) const {
+    constexpr int UN = NN ? 2 * NF : NF;
+    if constexpr (U < UN) {
+      constexpr int J = NN ? U / 2 : U, S = NN ? U % 2 : 0;
+      constexpr int slot = NN ? S : (Q * NF + U) % 2;
+      if constexpr (U + 1 < UN)
+        load_unit(i, NN ? (U + 1) / 2 : U + 1, NN ? (U + 1) % 2 : 0, ring[slot ^ 1]);
+      else
+        load_unit(i + 1, 0, 0, ring[slot ^ 1]);
+      // keep the prefetch ahead of this unit's MFMAs: the scheduler would
+      // otherwise sink the loads next to their use and serialise the stream
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (!NN) {
+        leaf_nt(ring[slot], xs.v[J], true, v);
+        leaf_reduce<NP, J>(nl, v, s0, s1);
+      } else {
+        half_nn<S>(ring[slot], xs.v[J], acc);
+        if constexpr (S == 1) {
+          pack(acc, v);
+          leaf_reduce<NP, J>(nl, v, s0, s1);
+        }
+      }
+      units<NF, Q, U + 1>(i, ring, xs, acc, v, s0, s1);
+    }
+  }
+
+  // One tile (index i) of a wave with NF full leaves (+ the partial last leaf
+  // when `tail`, loaded without prefetch).
+  template <int NF, int Q>
+  __device__ __forceinline__ void tile(int i, WF (&ring)[2], const XFrag<MT> &xs) const {
+    uint32_t s0[NP], s1[NP], v[NP];
+    f32x4 acc[RT][MT];
+#pragma unroll
+    for (int q = 0; q < NP; ++q) v[q] = s0[q] = s1[q] = 0;
+    units<NF, Q, 0>(i, ring, xs, acc, v, s0, s1);
+    if constexpr (NF < kMaxNL) {
+      if (tail) {
+        const int64_t kb = (int64_t)(lo + NF) * kLeaf;
+        const bool half1 = kb + 32 < p.K;  // an all-zero block leaves the sum unchanged
+        WF wt;
+        if constexpr (!NN) {
+          load_unit_tail(i, NF, 0, wt);
+          leaf_nt(wt, xs.v[NF], half1, v);
+        } else {
+          load_unit_tail(i, NF, 0, wt);
+          half_nn<0>(wt, xs.v[NF], acc);
+          if (half1) {
+            load_unit_tail(i, NF, 1, wt);
+            half_nn<1>(wt, xs.v[NF], acc);
+          }
+          pack(acc, v);
+        }
+        leaf_reduce<NP, NF>(nl, v, s0, s1);
+      }
+    }
+    finish_tile(i, v);
+  }
+
+  template <int NF>
+  __device__ __forceinline__ void run() const {
+    if (T <= 0) return;  // no tile for this workgroup (the same for all its waves)
+    // stationary activation fragments of this wave's leaves (rows past M clamped)
+    XFrag<MT> xs;
+    const uint16_t *arow[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      const int64_t m = m0 + 16 * t + r16 < p.M ? m0 + 16 * t + r16 : p.M - 1;
+      arow[t] = p.A[b] + m * p.lda[b];
+    }
+#pragma unroll
+    for (int j = 0; j < kMaxNL; ++j)
+#pragma unroll
+      for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const int64_t k = (int64_t)(lo + j) * kLeaf + 32 * s + 8 * g4;
+          if (j < NF)
+            xs.v[j][t][s] = load_frag(arow[t], k);
+          else if (j == NF && tail)
+            xs.v[j][t][s] = load_frag_tail(arow[t], k, p.K);
+          else
+            xs.v[j][t][s] = bf16x8{};
+        }
+    WF ring[2];
+    if constexpr (NF > 0) load_unit(0, 0, 0, ring[0]);
+    for (int i = 0; i < T; i += 2) {
+      tile<NF, 0>(i, ring, xs);
+      if (i + 1 < T) tile<NF, 1>(i + 1, ring, xs);
+    }
+  }
+};
+
+template <int LAYOUT, int MT>
+__global__ __launch_bounds__(kXsWaves * 64) void k_xs(GemmParams p) {
+  extern __shared__ __attribute__((aligned(16))) uint32_t xs_lds[];
+  using Wv = XsWave<LAYOUT, MT>;
+  const int waves = blockDim.x >> 6;
+  const int dw = __builtin_ctz(waves);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int kd = p.ksplit_depth;
+  const int b = blockIdx.z >> kd, piece = blockIdx.z & ((1 << kd) - 1);
+  int lo, hi;
+  subtree_range(p.L, kd + dw, (piece << dw) | wave, lo, hi);
+  const int tiles_n = (int)((p.N + Wv::COLS - 1) / Wv::COLS);
+  // contiguous tile ranges: workgroup g takes tiles g*per .. g*per + per - 1
+  const int per = (tiles_n + (int)gridDim.x - 1) / (int)gridDim.x;
+  const int t0 = (int)blockIdx.x * per;
+  const int T = t0 < tiles_n ? min(per, tiles_n - t0) : 0;
+  Wv w{p,
+       xs_lds,
+       reinterpret_cast<uint16_t *>(xs_lds + (size_t)2 * waves * Wv::NP * 64) + (size_t)wave * Wv::COLS * 64,
+       waves,
+       wave,
+       lane,
+       lane & 15,
+       lane >> 4,
+       b,
+       lo,
+       hi - lo,
+       (int64_t)hi * kLeaf > p.K,
+       (int64_t)blockIdx.y * 16 * MT,
+       tiles_n,
+       t0,
+       T,
+       p.B[b],
+       p.ldb[b],
+       p.to_part ? p.part + ((int64_t)b * (1 << kd) + piece) * p.part_stride : p.C[b],
+       p.to_part ? p.ldp : p.ldc[b]};
+  switch (w.nl - (w.tail ? 1 : 0)) {
+    case 0: w.template run<0>(); break;
+    case 1: w.template run<1>(); break;
+    case 2: w.template run<2>(); break;
+    case 3: w.template run<3>(); break;
+    default: w.template run<4>(); break;
+  }
+}
+
+}  // namespace
+
+int xs_tile_cols(int layout, int mt) {
+  if (layout == DGF_LAYOUT_NN) return 16 * rt_of<DGF_LAYOUT_NN, 1>();
+  return 16 * (mt == 1 ? rt_of<DGF_LAYOUT_NT, 1>() : rt_of<DGF_LAYOUT_NT, 2>());
+}
+
+size_t xs_lds_bytes(int layout, int mt, int waves) {
+  const size_t cols = (size_t)xs_tile_cols(layout, mt);
+  const size_t np = cols / 16 * mt * 2;
+  return 2 * (size_t)waves * np * 64 * 4 + (layout == DGF_LAYOUT_NN ? (size_t)waves * cols * 64 * 2 : 0);
+}
+
+hipError_t launch_xs(int layout, GemmParams p, int nb, int waves, int groups, hipStream_t stream) {
+  const int mt = p.M <= 16 ? 1 : 2;
+  const int64_t tiles_m = (p.M + 16 * mt - 1) / (16 * mt);
+  const dim3 grid((unsigned)groups, (unsigned)tiles_m, (unsigned)(nb << p.ksplit_depth));
+  const dim3 block((unsigned)(64 * waves));
+  const size_t shm = xs_lds_bytes(layout, mt, waves);
+  if (layout == DGF_LAYOUT_NT) {
+    if (mt == 1)
+      hipLaunchKernelGGL((k_xs<DGF_LAYOUT_NT, 1>), grid, block, shm, stream, p);
+    else
+      hipLaunchKernelGGL((k_xs<DGF_LAYOUT_NT, 2>), grid, block, shm, stream, p);
+  } else {
+    if (mt == 1)
+      hipLaunchKernelGGL((k_xs<DGF_LAYOUT_NN, 1>), grid, block, shm, stream, p);
+    else
+      hipLaunchKernelGGL((k_xs<DGF_LAYOUT_NN, 2>), grid, block, shm, stream, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dgf
