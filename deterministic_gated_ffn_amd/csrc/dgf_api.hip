@@ -214,7 +214,7 @@ XsPlan plan_xs(int layout, int nb, int64_t M, int64_t N, int64_t K) {
 // Workspace bytes for the partial roots of one GEMM (0 when it needs none).
 size_t partial_bytes(int layout, int nb, int epi, int64_t M, int64_t N, int64_t K) {
   if (M == 0 || N == 0) return 0;
-  if (layout == DGF_LAYOUT_NT && epi == EPI_STORE && K <= 64) return 0;  // the one-leaf kernel
+  if ((layout == DGF_LAYOUT_NT || layout == DGF_LAYOUT_TN) && epi == EPI_STORE && K <= 64) return 0;  // one-leaf kernels
   const XsPlan xp = plan_xs(layout, nb, M, N, K);
   if (xp.waves > 0) {
     if (xp.kd == 0 && epi == EPI_STORE) return 0;
@@ -233,6 +233,11 @@ dgf_status run_gemm(int layout, int nb, int epi, GemmParams p, hipStream_t s, co
   if ((p.M + 31) / 32 > 65535 || (p.N + 15) / 16 > 0x7fffffff)
     return fail(DGF_EUNSUPPORTED, "%s: %lld x %lld output exceeds the launch grid", what, (long long)p.M, (long long)p.N);
   p.L = leaves(p.K);
+  if (layout == DGF_LAYOUT_TN) {
+    if (epi != EPI_STORE || p.K > 64 || (nb == 2 && p.B[1] != p.B[0]) || (p.M + 63) / 64 > 65535)
+      return fail(DGF_EUNSUPPORTED, "%s: the TN kernel takes one leaf (K <= 64) and a shared B", what);
+    return hip_check(timed(s, what, [&] { return launch_gemm_tn1(nb, p, s); }), what);
+  }
   if (layout == DGF_LAYOUT_NT && epi == EPI_STORE && p.K <= 64 && (nb == 1 || p.B[1] == p.B[0]) &&
       (p.M + 63) / 64 <= 65535)
     return hip_check(timed(s, what, [&] { return launch_gemm_short(nb, p, s); }), what);
@@ -311,13 +316,18 @@ struct Carve {
 // when the weight-streaming kernel applies, else as two GEMMs and an add.
 bool dx_fused(int64_t M, int64_t H, int64_t I) { return plan_xs(DGF_LAYOUT_NN, 2, M, H, I).waves > 0; }
 
+// The weight gradients (K = M tokens) read the row-major operands directly
+// when the tokens fit one leaf; more tokens go through transposed copies and
+// the NT tree GEMM.
+bool dw_direct(int64_t M) { return M <= 64; }
+
 size_t bwd_partials(int64_t M, int64_t H, int64_t I) {
   const size_t sizes[4] = {
       partial_bytes(DGF_LAYOUT_NN, 1, EPI_DSILU, M, I, H),                                       // dA
       dx_fused(M, H, I) ? partial_bytes(DGF_LAYOUT_NN, 2, EPI_DX, M, H, I)
                         : partial_bytes(DGF_LAYOUT_NN, 1, EPI_STORE, M, H, I),                   // dX lanes
-      partial_bytes(DGF_LAYOUT_NT, 2, EPI_STORE, I, H, M),                                       // dW_gate, dW_up
-      partial_bytes(DGF_LAYOUT_NT, 1, EPI_STORE, H, I, M)};                                      // dW_down
+      dw_direct(M) ? 0 : partial_bytes(DGF_LAYOUT_NT, 2, EPI_STORE, I, H, M),                    // dW_gate, dW_up
+      dw_direct(M) ? 0 : partial_bytes(DGF_LAYOUT_NT, 1, EPI_STORE, H, I, M)};                   // dW_down
   size_t m = 0;
   for (size_t v : sizes) m = v > m ? v : m;
   return m;
@@ -325,11 +335,12 @@ size_t bwd_partials(int64_t M, int64_t H, int64_t I) {
 
 size_t bwd_ws_bytes(int64_t M, int64_t H, int64_t I) {
   const int64_t Mp = round8(M);
-  return round256((size_t)M * round8(I) * 2) * 2     // dG, dU row-major [M, I] (ld = I rounded to 8)
-         + round256((size_t)I * Mp * 2) * 3          // dG^T, dU^T, a^T [I, Mp]
-         + round256((size_t)H * Mp * 2) * 2          // x^T, dY^T [H, Mp]
-         + round256((size_t)M * round8(H) * 2) * 2   // the dX lanes G, U [M, H]
-         + bwd_partials(M, H, I);                    // K-split partial roots
+  return round256((size_t)M * round8(I) * 2) * 3                    // dG, dU, a row-major [M, I] (ld = I rounded to 8)
+         + (dw_direct(M) ? 0
+                         : round256((size_t)I * Mp * 2) * 3         // dG^T, dU^T, a^T [I, Mp]
+                               + round256((size_t)H * Mp * 2) * 2)  // x^T, dY^T [H, Mp]
+         + round256((size_t)M * round8(H) * 2) * 2                  // the dX lanes G, U [M, H]
+         + bwd_partials(M, H, I);                                   // K-split partial roots
 }
 
 size_t fwd_ws_bytes(int64_t M, int64_t H, int64_t I) {
@@ -343,6 +354,7 @@ size_t gemm_ws_bytes(int layout, int64_t M, int64_t N, int64_t K) {
   const int lay = layout == DGF_NN ? DGF_LAYOUT_NN : DGF_LAYOUT_NT;
   size_t b = partial_bytes(lay, 1, EPI_STORE, M, N, K);
   if (layout != DGF_TN) return b;
+  if (K <= 64) return 0;  // the one-leaf TN kernel reads the operands in place
   const int64_t Kp = round8(K);
   return round256((size_t)M * Kp * 2) + round256((size_t)N * Kp * 2) + b;
 }
@@ -474,17 +486,23 @@ dgf_status dgf_ffn_bwd(const void *dy, int64_t lddy, const void *x, int64_t ldx,
   const int64_t Mp = round8(M);
   Carve cv{(char *)ws, 0};
   const int64_t ld_d = round8(I);
-  uint16_t *dG = cv.take((size_t)M * ld_d), *dU = cv.take((size_t)M * ld_d);
-  uint16_t *dGT = cv.take((size_t)I * Mp), *dUT = cv.take((size_t)I * Mp), *aT = cv.take((size_t)I * Mp);
-  uint16_t *xT = cv.take((size_t)H * Mp), *dYT = cv.take((size_t)H * Mp);
+  const bool direct = dw_direct(M);
+  uint16_t *dG = cv.take((size_t)M * ld_d), *dU = cv.take((size_t)M * ld_d), *a_rm = cv.take((size_t)M * ld_d);
+  uint16_t *dGT = nullptr, *dUT = nullptr, *aT = nullptr, *xT = nullptr, *dYT = nullptr;
+  if (!direct) {
+    dGT = cv.take((size_t)I * Mp); dUT = cv.take((size_t)I * Mp); aT = cv.take((size_t)I * Mp);
+    xT = cv.take((size_t)H * Mp); dYT = cv.take((size_t)H * Mp);
+  }
   const int64_t ld_lane = round8(H);
   uint16_t *Gw = cv.take((size_t)M * ld_lane), *Uw = cv.take((size_t)M * ld_lane);
   uint16_t *partials = (uint16_t *)((char *)ws + cv.used);
 
-  DGF_TRY(hip_check(timed(s, "transpose x", [&] { return launch_transpose((const uint16_t *)x, ldx, M, H, xT, Mp, s); }),
-                    "transpose x"));
-  DGF_TRY(hip_check(timed(s, "transpose dY", [&] { return launch_transpose((const uint16_t *)dy, lddy, M, H, dYT, Mp, s); }),
-                    "transpose dY"));
+  if (!direct) {
+    DGF_TRY(hip_check(timed(s, "transpose x", [&] { return launch_transpose((const uint16_t *)x, ldx, M, H, xT, Mp, s); }),
+                      "transpose x"));
+    DGF_TRY(hip_check(timed(s, "transpose dY", [&] { return launch_transpose((const uint16_t *)dy, lddy, M, H, dYT, Mp, s); }),
+                      "transpose dY"));
+  }
 
   // dA = T_H(dY W_down) with the dsilu epilogue
   GemmParams p = blank();
@@ -496,8 +514,8 @@ dgf_status dgf_ffn_bwd(const void *dy, int64_t lddy, const void *x, int64_t ldx,
   p.sg = (const uint16_t *)g;
   p.su = (const uint16_t *)u;
   p.ld_gu = ld_gu;
-  p.dG = dG; p.dU = dU; p.a_rm = nullptr; p.ld_d = ld_d;
-  p.dGT = dGT; p.dUT = dUT; p.aT = aT; p.ld_t = Mp;
+  p.dG = dG; p.dU = dU; p.a_rm = a_rm; p.ld_d = ld_d;
+  p.dGT = dGT; p.dUT = dUT; p.aT = aT; p.ld_t = Mp;  // transposed copies only without the direct dW kernel
   DGF_TRY(run_gemm(DGF_LAYOUT_NN, 1, EPI_DSILU, p, s, "dA tree GEMM", partials, "dA join + dsilu"));
 
   // dX lanes G = T_I(dG W_gate), U = T_I(dU W_up) and dX = bf16(G + U), the
@@ -535,24 +553,34 @@ dgf_status dgf_ffn_bwd(const void *dy, int64_t lddy, const void *x, int64_t ldx,
                         "dX ordered add"));
   }
 
-  // dW_gate = T_M(dG^T x), dW_up = T_M(dU^T x): NT over the transposed operands
+  // dW_gate = T_M(dG^T x), dW_up = T_M(dU^T x); dW_down = T_M(dY^T a): one
+  // leaf over the row-major operands, or NT over the transposed copies
   GemmParams w = blank();
-  w.A[0] = dGT; w.A[1] = dUT;
-  w.lda[0] = w.lda[1] = Mp;
-  w.B[0] = w.B[1] = xT;
-  w.ldb[0] = w.ldb[1] = Mp;
   w.C[0] = (uint16_t *)dw_gate; w.ldc[0] = ld_dwg;
   w.C[1] = (uint16_t *)dw_up; w.ldc[1] = ld_dwu;
   w.M = I; w.N = H; w.K = M;
-  DGF_TRY(run_gemm(DGF_LAYOUT_NT, 2, EPI_STORE, w, s, "dW_gate/dW_up tree GEMM", partials));
-
-  // dW_down = T_M(dY^T a)
   GemmParams v = blank();
-  v.A[0] = dYT; v.lda[0] = Mp;
-  v.B[0] = aT; v.ldb[0] = Mp;
   v.C[0] = (uint16_t *)dw_down; v.ldc[0] = ld_dwd;
   v.M = H; v.N = I; v.K = M;
-  DGF_TRY(run_gemm(DGF_LAYOUT_NT, 1, EPI_STORE, v, s, "dW_down tree GEMM", partials));
+  if (direct) {
+    w.A[0] = dG; w.A[1] = dU;
+    w.lda[0] = w.lda[1] = ld_d;
+    w.B[0] = w.B[1] = (const uint16_t *)x;
+    w.ldb[0] = w.ldb[1] = ldx;
+    DGF_TRY(run_gemm(DGF_LAYOUT_TN, 2, EPI_STORE, w, s, "dW_gate/dW_up tree GEMM"));
+    v.A[0] = (const uint16_t *)dy; v.lda[0] = lddy;
+    v.B[0] = a_rm; v.ldb[0] = ld_d;
+    DGF_TRY(run_gemm(DGF_LAYOUT_TN, 1, EPI_STORE, v, s, "dW_down tree GEMM"));
+  } else {
+    w.A[0] = dGT; w.A[1] = dUT;
+    w.lda[0] = w.lda[1] = Mp;
+    w.B[0] = w.B[1] = xT;
+    w.ldb[0] = w.ldb[1] = Mp;
+    DGF_TRY(run_gemm(DGF_LAYOUT_NT, 2, EPI_STORE, w, s, "dW_gate/dW_up tree GEMM", partials));
+    v.A[0] = dYT; v.lda[0] = Mp;
+    v.B[0] = aT; v.ldb[0] = Mp;
+    DGF_TRY(run_gemm(DGF_LAYOUT_NT, 1, EPI_STORE, v, s, "dW_down tree GEMM", partials));
+  }
   return ok();
 }
 
@@ -604,7 +632,11 @@ dgf_status dgf_gemm_tree(int layout, const void *A, int64_t lda, const void *B, 
   p.M = M; p.N = N; p.K = K;
   p.C[0] = (uint16_t *)C;
   p.ldc[0] = ldc;
-  if (layout == DGF_TN) {
+  if (layout == DGF_TN && K <= 64) {
+    p.A[0] = (const uint16_t *)A; p.lda[0] = lda;
+    p.B[0] = (const uint16_t *)B; p.ldb[0] = ldb;
+    DGF_TRY(run_gemm(DGF_LAYOUT_TN, 1, EPI_STORE, p, s, "TN tree GEMM"));
+  } else if (layout == DGF_TN) {
     const int64_t Kp = round8(K);
     Carve cv{(char *)ws, 0};
     uint16_t *AT = cv.take((size_t)M * Kp), *BT = cv.take((size_t)N * Kp);

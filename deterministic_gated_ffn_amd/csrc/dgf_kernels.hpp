@@ -6,7 +6,7 @@
 
 namespace dgf {
 
-enum { DGF_LAYOUT_NT = 0, DGF_LAYOUT_NN = 1 };
+enum { DGF_LAYOUT_NT = 0, DGF_LAYOUT_NN = 1, DGF_LAYOUT_TN = 2 };
 enum { EPI_STORE = 0, EPI_ACT = 1, EPI_DSILU = 2, EPI_DX = 3 };
 
 // Arguments of one tree-GEMM launch (two products when NB = 2).
@@ -56,6 +56,8 @@ int gemm_row_tiles(int layout, int nb, int epi);
 hipError_t launch_gemm(int layout, int nb, int epi, GemmParams p, int waves, hipStream_t stream);
 // NT, EPI_STORE, K <= 64 (one leaf), B shared by the NB products
 hipError_t launch_gemm_short(int nb, GemmParams p, hipStream_t stream);
+// TN, EPI_STORE, K <= 64 (one leaf): A_b [K][M] and B [K][N] row-major, B shared by the NB products
+hipError_t launch_gemm_tn1(int nb, GemmParams p, hipStream_t stream);
 
 hipError_t launch_act_fwd(const uint16_t *g, const uint16_t *u, uint16_t *a, int64_t n, hipStream_t s);
 hipError_t launch_act_bwd(const uint16_t *da, const uint16_t *g, const uint16_t *u, uint16_t *dg, uint16_t *du,

@@ -9,8 +9,10 @@
 // leaves per wave.  A wave loads the activation fragments of its leaves once
 // and keeps them in registers while it walks over a contiguous range of
 // output tiles (16 RT columns each): per tile it streams its leaves' weight
-// rows (NT: 16 RT rows x 64 K per leaf) or weight slab (NN: 64 K rows x 16 RT
-// columns per leaf, in two halves of 32 rows, transposed through LDS),
+// rows (NT: 16 RT rows x 64 K per leaf, staged through LDS so that every load
+// instruction reads whole 128-byte row segments) or weight slab (NN: 64 K
+// rows x 16 RT columns per leaf, in two halves of 32 rows, transposed through
+// LDS),
 // reduces the leaves with the subtree's fixed shape in registers and parks
 // the subtree root in LDS.  After a workgroup barrier the WAVES roots of the
 // tile are joined with the balanced top of the piece's subtree, each wave
@@ -52,7 +54,7 @@ template <int LAYOUT, int RT>
 struct WFrag;
 template <int RT>
 struct WFrag<DGF_LAYOUT_NT, RT> {
-  bf16x8 v[RT][2];  // rows 16 rt + r16, K half h
+  u32x4 v[2 * RT];  // rows 8 i + lane / 8, 16-byte K chunk lane % 8 of the leaf
 };
 template <int RT>
 struct WFrag<DGF_LAYOUT_NN, RT> {
@@ -113,11 +115,14 @@ struct XsWave {
   static constexpr int NI = 2 * RT;       // NN: lanes per slab row (16 bytes each)
   static constexpr int ROWS = 32 / RT;    // NN: slab rows per load instruction
   static constexpr int COLS = 16 * RT;    // output columns per tile
+  // ring slots of weight units (prefetch distance PR - 1 units); a third slot
+  // measured no faster
+  static constexpr int PR = 2;
   using WF = WFrag<LAYOUT, RT>;
 
   const GemmParams &p;
   uint32_t *roots;   // LDS [2][waves][NP][64]
-  uint16_t *slab;    // LDS, this wave's COLS x 64 transpose slab (NN)
+  uint16_t *slab;    // LDS, this wave's COLS x 64 staging slab
   int waves, wave, lane, r16, g4;
   int b, lo, nl;
   bool tail;
@@ -136,14 +141,12 @@ struct XsWave {
     const int64_t n0 = (int64_t)tile_at(i) * COLS;
     const int64_t kb = (int64_t)(lo + j) * kLeaf;
     if constexpr (!NN) {
+      // whole 128-byte row segments: 8 rows per instruction; rows past N read
+      // the last row (their outputs are never stored)
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        // rows past N read the last row (their outputs are never stored)
-        const int64_t n = n0 + 16 * rt + r16 < p.N ? n0 + 16 * rt + r16 : p.N - 1;
-        const uint16_t *row = W + n * ldw + kb + 8 * g4;
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-          w.v[rt][h] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8 *>(row + 32 * h));
+      for (int i2 = 0; i2 < 2 * RT; ++i2) {
+        const int64_t n = n0 + 8 * i2 + (lane >> 3) < p.N ? n0 + 8 * i2 + (lane >> 3) : p.N - 1;
+        w.v[i2] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(W + n * ldw + kb + 8 * (lane & 7)));
       }
     } else {
       // 16-byte pieces of whole rows; a piece starting past N reads the last
@@ -166,11 +169,9 @@ struct XsWave {
     const int64_t kb = (int64_t)(lo + j) * kLeaf;
     if constexpr (!NN) {
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        const int64_t n = n0 + 16 * rt + r16 < p.N ? n0 + 16 * rt + r16 : p.N - 1;
-        const uint16_t *row = W + n * ldw;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) w.v[rt][h] = load_frag_tail(row, kb + 32 * h + 8 * g4, p.K);
+      for (int i2 = 0; i2 < 2 * RT; ++i2) {
+        const int64_t n = n0 + 8 * i2 + (lane >> 3) < p.N ? n0 + 8 * i2 + (lane >> 3) : p.N - 1;
+        w.v[i2] = __builtin_bit_cast(u32x4, load_frag_tail(W + n * ldw, kb + 8 * (lane & 7), p.K));
       }
     } else {
       // rows past K read row K-1 and are zeroed
@@ -198,16 +199,29 @@ struct XsWave {
   }
 
   // NT: both K halves of a leaf (the second unless `half1` is false: an
-  // all-zero block leaves the sum unchanged), packed to BF16.
+  // all-zero block leaves the sum unchanged), packed to BF16.  The rows pass
+  // through this wave's LDS slab: row r's 16-byte chunk c at r*64 + 8 (c ^ (r&7)),
+  // which keeps both the row-wise writes and the MFMA-layout reads (lane:
+  // row 16 rt + r16, chunk 4 h + g4) on distinct banks.
   __device__ __forceinline__ void leaf_nt(const WF &w, const bf16x8 (&x)[MT][2], bool half1, uint32_t (&v)[NP]) const {
+    const int wr = lane >> 3, wc = lane & 7;
+#pragma unroll
+    for (int i2 = 0; i2 < 2 * RT; ++i2)
+      *reinterpret_cast<u32x4 *>(&slab[(8 * i2 + wr) * 64 + 8 * (wc ^ wr)]) = w.v[i2];
+    wave_lds_sync();  // this wave's slab writes land before its lanes read them
     f32x4 acc[RT][MT];
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
+    for (int rt = 0; rt < RT; ++rt) {
+      const int r = 16 * rt + r16;
+      const bf16x8 w0 = *reinterpret_cast<const bf16x8 *>(&slab[r * 64 + 8 * ((0 + g4) ^ (r & 7))]);
+      const bf16x8 w1 = *reinterpret_cast<const bf16x8 *>(&slab[r * 64 + 8 * ((4 + g4) ^ (r & 7))]);
 #pragma unroll
       for (int t = 0; t < MT; ++t) {
-        acc[rt][t] = mfma16(w.v[rt][0], x[t][0], f32x4{0.f, 0.f, 0.f, 0.f});
-        if (half1) acc[rt][t] = mfma16(w.v[rt][1], x[t][1], acc[rt][t]);
+        acc[rt][t] = mfma16(w0, x[t][0], f32x4{0.f, 0.f, 0.f, 0.f});
+        if (half1) acc[rt][t] = mfma16(w1, x[t][1], acc[rt][t]);
       }
+    }
+    wave_lds_sync();  // slab reads done before the next leaf overwrites it
     pack(acc, v);
   }
 
@@ -284,20 +298,19 @@ struct XsWave {
   }
 
   // Units U.. of one tile.  Unit U is leaf U (NT) or half U % 2 of leaf U / 2
-  // (NN); each first issues the loads of the next unit (of this tile, or the
-  // first of tile i + 1) into the other ring slot.  NT slot: (Q NF + U) % 2
-  // for the tile in position Q of its pair; NN slot: the half.
+  // (NN).  Tiles run in groups of PR; unit U of the group's tile Q has group
+  // index g = Q UN + U and lives in ring slot g % PR, and each unit first
+  // issues the loads of unit g + PR - 1 (possibly of a later tile) into its slot.
   template <int NF, int Q, int U>
-  __device__ __forceinline__ void units(int i, WF (&ring)[2], const XFrag<MT> &xs, f32x4 (&acc)[RT][MT],
+  __device__ __forceinline__ void units(int i, WF (&ring)[PR], const XFrag<MT> &xs, f32x4 (&acc)[RT][MT],
                                         uint32_t (&v)[NP], uint32_t (&s0)[NP], uint32_t (&s1)[NP]) const {
     constexpr int UN = NN ? 2 * NF : NF;
     if constexpr (U < UN) {
       constexpr int J = NN ? U / 2 : U, S = NN ? U % 2 : 0;
-      constexpr int slot = NN ? S : (Q * NF + U) % 2;
-      if constexpr (U + 1 < UN)
-        load_unit(i, NN ? (U + 1) / 2 : U + 1, NN ? (U + 1) % 2 : 0, ring[slot ^ 1]);
-      else
-        load_unit(i + 1, 0, 0, ring[slot ^ 1]);
+      constexpr int g = Q * UN + U, slot = g % PR;
+      constexpr int nx = U + PR - 1;  // the unit to prefetch, counted from this tile's unit 0
+      constexpr int nu = nx % UN;
+      load_unit(i + nx / UN, NN ? nu / 2 : nu, NN ? nu % 2 : 0, ring[(g + PR - 1) % PR]);
       // keep the prefetch ahead of this unit's MFMAs: the scheduler would
       // otherwise sink the loads next to their use and serialise the stream
       __builtin_amdgcn_sched_barrier(0);
@@ -318,7 +331,7 @@ struct XsWave {
   // One tile (index i) of a wave with NF full leaves (+ the partial last leaf
   // when `tail`, loaded without prefetch).
   template <int NF, int Q>
-  __device__ __forceinline__ void tile(int i, WF (&ring)[2], const XFrag<MT> &xs) const {
+  __device__ __forceinline__ void tile(int i, WF (&ring)[PR], const XFrag<MT> &xs) const {
     uint32_t s0[NP], s1[NP], v[NP];
     f32x4 acc[RT][MT];
 #pragma unroll
@@ -372,11 +385,20 @@ struct XsWave {
           else
             xs.v[j][t][s] = bf16x8{};
         }
-    WF ring[2];
-    if constexpr (NF > 0) load_unit(0, 0, 0, ring[0]);
-    for (int i = 0; i < T; i += 2) {
+    WF ring[PR];
+    if constexpr (NF > 0) {
+      constexpr int UN = NN ? 2 * NF : NF;
+#pragma unroll
+      for (int g = 0; g < PR - 1; ++g) {
+        const int u = g % UN;
+        load_unit(g / UN, NN ? u / 2 : u, NN ? u % 2 : 0, ring[g]);
+      }
+    }
+    for (int i = 0; i < T; i += PR) {
       tile<NF, 0>(i, ring, xs);
       if (i + 1 < T) tile<NF, 1>(i + 1, ring, xs);
+      if constexpr (PR > 2)
+        if (i + 2 < T) tile<NF, 2>(i + 2, ring, xs);
     }
   }
 };
@@ -437,7 +459,7 @@ int xs_tile_cols(int layout, int mt) {
 size_t xs_lds_bytes(int layout, int mt, int waves) {
   const size_t cols = (size_t)xs_tile_cols(layout, mt);
   const size_t np = cols / 16 * mt * 2;
-  return 2 * (size_t)waves * np * 64 * 4 + (layout == DGF_LAYOUT_NN ? (size_t)waves * cols * 64 * 2 : 0);
+  return 2 * (size_t)waves * np * 64 * 4 + (size_t)waves * cols * 64 * 2;
 }
 
 hipError_t launch_xs(int layout, GemmParams p, int nb, int waves, int groups, hipStream_t stream) {

@@ -146,7 +146,9 @@ dgf_status dgf_tree_combine(const void *const *parts, int S, void *out, int64_t 
  *   layout DGF_NT: A [M,K] (lda) times B [N,K] (ldb) transposed,
  *   layout DGF_NN: A [M,K] (lda) times B [K,N] (ldb),
  *   layout DGF_TN: A [K,M] (lda) transposed times B [K,N] (ldb).
- * K = 0 writes zeros.  Workspace: dgf_gemm_tree_workspace(layout,M,N,K) bytes.
+ * K = 0 writes zeros.  Workspace: dgf_gemm_tree_workspace(layout,M,N,K) bytes
+ * (0 when none is needed, e.g. DGF_TN with K <= 64, which reads A and B in
+ * place; a NULL ws is then accepted).
  */
 enum { DGF_NT = 0, DGF_NN = 1, DGF_TN = 2 };
 size_t dgf_gemm_tree_workspace(int layout, int64_t M, int64_t N, int64_t K);

@@ -48,7 +48,8 @@ def test_workspace_queries(lib):
     assert lib.dgf_ffn_fwd_workspace(32, 4096, 12288) >= 32 * 12288 * 2
     assert lib.dgf_ffn_bwd_workspace(32, 4096, 12288) >= 32 * 12288 * 2 * 5
     assert lib.dgf_gemm_tree_workspace(binding.DGF_NT, 4, 4, 4) == 0
-    assert lib.dgf_gemm_tree_workspace(binding.DGF_TN, 4, 4, 4) > 0
+    assert lib.dgf_gemm_tree_workspace(binding.DGF_TN, 4, 4, 4) == 0  # one leaf: operands read in place
+    assert lib.dgf_gemm_tree_workspace(binding.DGF_TN, 4, 4, 100) > 0  # transposed copies
 
 
 FAKE = 1 << 20  # a 16-byte aligned stand-in address; never dereferenced by these calls
@@ -109,7 +110,8 @@ def test_combine_validation(lib):
 def test_gemm_validation(lib):
     assert lib.dgf_gemm_tree(7, FAKE, 8, FAKE, 8, FAKE, 8, 4, 4, 4, None, 0, None) == 1
     assert lib.dgf_gemm_tree(binding.DGF_NT, FAKE, 8, FAKE, 8, FAKE, 8, 0, 4, 4, None, 0, None) == 0
-    assert lib.dgf_gemm_tree(binding.DGF_TN, FAKE, 8, FAKE, 8, FAKE, 8, 4, 4, 4, None, 0, None) == 3
+    # TN past one leaf needs transposed copies in the workspace
+    assert lib.dgf_gemm_tree(binding.DGF_TN, FAKE, 8, FAKE, 8, FAKE, 8, 4, 4, 100, None, 0, None) == 3
     assert lib.dgf_gemm_tree(binding.DGF_NN, FAKE, 4, FAKE, 8, FAKE, 8, 4, 4, 8, None, 0, None) == 1
     assert lib.dgf_act_fwd(None, FAKE, FAKE, 10, None) == 1
     assert lib.dgf_act_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == 0
