@@ -56,6 +56,41 @@ def kernel_bytes(name: str, M: int) -> int | None:
     return table.get(name)
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ffn_train_step_M32_hbm_traffic.md")
+
+
+def sources_digest() -> str:
+    """sha256 over the kernel sources (name then bytes, sorted by path)."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "deterministic_gated_ffn_amd", "csrc")
+    for path in sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.hpp"))):
+        h.update(os.path.basename(path).encode())
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel: str) -> int | None:
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    summary, or None when it has no figure or the kernel sources changed since."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    figures, digest = {}, None
+    for line in text.splitlines():
+        if line.startswith("traffic: "):
+            name, _, value = line[len("traffic: "):].rpartition(" = ")
+            figures[name] = int(value)
+        elif line.startswith("sources_sha256: "):
+            digest = line.split(":", 1)[1].strip()
+    if digest != sources_digest():
+        return None
+    return figures.get(kernel)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -164,7 +199,8 @@ def main():
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1) if achieved else None,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4) if achieved else None,
-                     "bytes_per_launch": dom_bytes, "avg_launch_us": round(dom_us, 2), "traffic": None},
+                     "bytes_per_launch": dom_bytes, "avg_launch_us": round(dom_us, 2),
+                     "traffic": measured_traffic(dom)},
         "kernels": kernels,
         "kernels_note": "per-launch HIP events in a second region of the same K steps "
                         f"({ms_step_profiled * 1e3:.1f} us/step with the events)",
@@ -202,7 +238,7 @@ def main():
 
 def cpu_baseline(M: int) -> dict:
     """The CPU oracle on a bounded sample of the same step: the full M=32
-    forward, the full dA and dX, and 1/64 of the dW rows (scaled by 64)."""
+    forward, the full dA and dX, and 1/16 of the dW rows (scaled by 16)."""
     import numpy as np
 
     import oracle
@@ -223,7 +259,7 @@ def cpu_baseline(M: int) -> dict:
     U = oracle.gemm_tree(du, wu, "NN")
     oracle.tree_combine([G, U])
     t_dx = time.perf_counter() - t0
-    frac = 64
+    frac = 16
     t0 = time.perf_counter()
     oracle.gemm_tree(np.ascontiguousarray(dg[:, :I // frac]), x, "TN")
     oracle.gemm_tree(np.ascontiguousarray(du[:, :I // frac]), x, "TN")
