@@ -621,26 +621,30 @@ __global__ __launch_bounds__(256) void k_gemm_short(GemmParams p) {
 
 // C_b[r][c] = bf16( leaf( sum_k A_b[k][r] B[k][c] ) ) for K <= 64, straight
 // from row-major [k][features] operands: the weight gradients, k = tokens.
-// A workgroup of 4 waves owns 64 rows r x 128 columns c.  It copies the K x 64
-// and K x 128 operand tiles into LDS feature-major, with zeros past K (up to
-// the next multiple of 32: an all-zero block leaves the sum unchanged), past
-// M and past N; then every wave computes 16 rows x 128 columns and stores
-// them through LDS (the B tile's space, once all waves have read it) as whole
-// 256-byte row segments, as k_gemm_short does.
-constexpr int kTnK = 72;  // padded K stride of the feature-major LDS tiles
+// A workgroup of 4 waves owns 64 rows r and CT consecutive tiles of 128
+// columns c.  It copies the K x 64 A tile into LDS feature-major once, and
+// each K x 128 B tile in turn, with zeros past K (up to the next multiple of
+// 32: an all-zero block leaves the sum unchanged), past M and past N.  Every
+// wave computes 16 rows x 128 columns per tile and stores them through its
+// own LDS stage as whole 256-byte row segments; the next B tile's loads are
+// issued before those stores.
+constexpr int kTnTile = 128;
 
 template <int NB>
-__global__ __launch_bounds__(256) void k_gemm_tn1(GemmParams p) {
-  static_assert(4 * 16 * kShortStride <= kShortN * kTnK, "the store stage reuses the B tile");
-  __shared__ __attribute__((aligned(16))) uint16_t sA[NB][64 * kTnK];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[kShortN * kTnK];
+__global__ __launch_bounds__(256) void k_gemm_tn1(GemmParams p, int ct) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t tn_lds[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, g4 = lane >> 4;
-  const int64_t c0 = (int64_t)xcd_tile(blockIdx.x, gridDim.x) * kShortN;
-  const int64_t r0 = (int64_t)blockIdx.y * 64;
   const int K = (int)p.K;
   const int KH = (K + 31) / 32;  // MFMA K halves
   const int KP = 32 * KH;
+  const int ks = KP + 8;         // padded K stride of the feature-major tiles
+  const int km = KP / 8 - 1;     // K-chunk swizzle mask: chunks stay inside the row's KP elements
+  uint16_t *sA = tn_lds;                            // [NB][64][ks]
+  uint16_t *sB = sA + NB * 64 * ks;                 // [128][ks]
+  uint16_t *stage = sB + kTnTile * ks + wave * 16 * kShortStride;  // this wave's [16][kShortStride]
+  const int64_t r0 = (int64_t)blockIdx.y * 64;
+  const int64_t cbase = (int64_t)xcd_tile(blockIdx.x, gridDim.x) * kTnTile * ct;
 
   // 8 consecutive features f0 .. f0+7 of operand row k (zeros outside)
   auto load8 = [&](const uint16_t *src, int64_t ld, int k, int64_t f0, int64_t F, uint16_t (&v)[8]) {
@@ -655,88 +659,103 @@ __global__ __launch_bounds__(256) void k_gemm_tn1(GemmParams p) {
     }
   };
   // Eight consecutive threads read one 128-byte operand row; feature f = 8 cc + e
-  // of row k lands at LDS row f, position k ^ (8 (cc & 7)): 16-byte K chunks
+  // of row k lands at LDS row f, position k ^ (8 (cc & km)): 16-byte K chunks
   // permuted per feature group, which spreads the transposing writes over the
   // banks and keeps each MFMA operand read one aligned 16-byte chunk.
+  auto fill_b = [&](int64_t c0) {
+    for (int q = tid; q < KP * (kTnTile / 8); q += 256) {
+      const int k = q / (kTnTile / 8), cc = q % (kTnTile / 8);
+      uint16_t v[8];
+      load8(p.B[0], p.ldb[0], k, c0 + 8 * cc, p.N, v);
+      const int kk = k ^ (8 * (cc & km));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sB[(8 * cc + e) * ks + kk] = v[e];
+    }
+  };
   for (int q = tid; q < NB * KP * 8; q += 256) {
     const int b = q / (KP * 8), rem = q % (KP * 8), k = rem / 8, cc = rem % 8;
     uint16_t v[8];
     load8(p.A[b], p.lda[b], k, r0 + 8 * cc, p.M, v);
-    const int kk = k ^ (8 * cc);
+    const int kk = k ^ (8 * (cc & km));
 #pragma unroll
-    for (int e = 0; e < 8; ++e) sA[b][(8 * cc + e) * kTnK + kk] = v[e];
+    for (int e = 0; e < 8; ++e) sA[(b * 64 + 8 * cc + e) * ks + kk] = v[e];
   }
-  for (int q = tid; q < KP * (kShortN / 8); q += 256) {
-    const int k = q / (kShortN / 8), cc = q % (kShortN / 8);
-    uint16_t v[8];
-    load8(p.B[0], p.ldb[0], k, c0 + 8 * cc, p.N, v);
-    const int kk = k ^ (8 * (cc & 7));
-#pragma unroll
-    for (int e = 0; e < 8; ++e) sB[(8 * cc + e) * kTnK + kk] = v[e];
-  }
+  fill_b(cbase);
   __syncthreads();
 
-  f32x4 acc[NB][8];
-#pragma unroll
-  for (int b = 0; b < NB; ++b)
-#pragma unroll
-    for (int c = 0; c < 8; ++c) acc[b][c] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < KH; ++s) {
-    bf16x8 xa[NB];
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const int ra = 16 * wave + r16;
-      xa[b] = *reinterpret_cast<const bf16x8 *>(&sA[b][ra * kTnK + 8 * ((4 * s + g4) ^ ((ra >> 3) & 7))]);
-    }
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const int rb = 16 * c + r16;
-      const bf16x8 w = *reinterpret_cast<const bf16x8 *>(&sB[rb * kTnK + 8 * ((4 * s + g4) ^ ((rb >> 3) & 7))]);
-#pragma unroll
-      for (int b = 0; b < NB; ++b) acc[b][c] = mfma16(w, xa[b], acc[b][c]);
-    }
-  }
-
-  // all waves are done with the B tile before it becomes the store stage
-  __syncthreads();
   const int64_t m0 = r0 + 16 * wave;
-  uint16_t *st = sB + wave * 16 * kShortStride;
+  for (int c = 0; c < ct; ++c) {
+    const int64_t c0 = cbase + (int64_t)c * kTnTile;
+    if (c0 >= p.N) break;  // the same for every wave of the workgroup
+    f32x4 acc[NB][8];
 #pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    // lane holds C[m0 + r16][c0 + 16c + 4 g4 + (0..3)]
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const uint2 v = make_uint2(pack_rne(acc[b][c][0], acc[b][c][1]), pack_rne(acc[b][c][2], acc[b][c][3]));
-      *reinterpret_cast<uint2 *>(&st[r16 * kShortStride + 16 * c + 4 * g4]) = v;
-    }
-    wave_lds_sync();
-    // 16 rows x 256 bytes: lane l writes row (l >> 4) + 4i, bytes 16 (l & 15) .. +16
+      for (int t = 0; t < 8; ++t) acc[b][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < KH; ++s) {
+      bf16x8 xa[NB];
+      const int ra = 16 * wave + r16;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = (lane >> 4) + 4 * i;
-      const int col = 8 * (lane & 15);
-      const int64_t m = m0 + row, n = c0 + col;
-      if (m < p.M) {
-        uint16_t *dst = p.C[b] + m * p.ldc[b] + n;
-        const uint4 v = *reinterpret_cast<const uint4 *>(&st[row * kShortStride + col]);
-        if (n + 8 <= p.N) {
-          *reinterpret_cast<uint4 *>(dst) = v;
-        } else {
-          const uint32_t q[4] = {v.x, v.y, v.z, v.w};
-          for (int e = 0; e < 8 && n + e < p.N; ++e) dst[e] = (uint16_t)(q[e >> 1] >> (16 * (e & 1)));
-        }
+      for (int b = 0; b < NB; ++b)
+        xa[b] = *reinterpret_cast<const bf16x8 *>(&sA[(b * 64 + ra) * ks + 8 * ((4 * s + g4) ^ ((ra >> 3) & km))]);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int rb = 16 * t + r16;
+        const bf16x8 w = *reinterpret_cast<const bf16x8 *>(&sB[rb * ks + 8 * ((4 * s + g4) ^ ((rb >> 3) & km))]);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) acc[b][t] = mfma16(w, xa[b], acc[b][t]);
       }
     }
-    wave_lds_sync();  // the stage is reused by the next product
+    __syncthreads();  // every wave is done with this B tile
+    if (c + 1 < ct && c0 + kTnTile < p.N) fill_b(c0 + kTnTile);  // loads in flight during the stores below
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      // lane holds C[m0 + r16][c0 + 16t + 4 g4 + (0..3)]
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const uint2 v = make_uint2(pack_rne(acc[b][t][0], acc[b][t][1]), pack_rne(acc[b][t][2], acc[b][t][3]));
+        *reinterpret_cast<uint2 *>(&stage[r16 * kShortStride + 16 * t + 4 * g4]) = v;
+      }
+      wave_lds_sync();
+      // 16 rows x 256 bytes: lane l writes row (l >> 4) + 4i, bytes 16 (l & 15) .. +16
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = (lane >> 4) + 4 * i;
+        const int col = 8 * (lane & 15);
+        const int64_t m = m0 + row, n = c0 + col;
+        if (m < p.M) {
+          uint16_t *dst = p.C[b] + m * p.ldc[b] + n;
+          const uint4 v = *reinterpret_cast<const uint4 *>(&stage[row * kShortStride + col]);
+          if (n + 8 <= p.N) {
+            *reinterpret_cast<uint4 *>(dst) = v;
+          } else {
+            const uint32_t q[4] = {v.x, v.y, v.z, v.w};
+            for (int e = 0; e < 8 && n + e < p.N; ++e) dst[e] = (uint16_t)(q[e >> 1] >> (16 * (e & 1)));
+          }
+        }
+      }
+      wave_lds_sync();  // the stage is reused by the next product
+    }
+    __syncthreads();  // the next B tile is in LDS
   }
 }
 
+size_t tn1_lds_bytes(int nb, int64_t K) {
+  const int64_t ks = 32 * ((K + 31) / 32) + 8;
+  return (size_t)(nb * 64 + kTnTile) * ks * 2 + (size_t)4 * 16 * kShortStride * 2;
+}
+
 hipError_t launch_gemm_tn1(int nb, GemmParams p, hipStream_t stream) {
-  dim3 grid((unsigned)((p.N + kShortN - 1) / kShortN), (unsigned)((p.M + 63) / 64));
+  // column tiles per workgroup: as many as keep at least 4 workgroups per CU busy
+  const int64_t tiles_c = (p.N + kTnTile - 1) / kTnTile, tiles_r = (p.M + 63) / 64;
+  int ct = 1;
+  while (ct < 8 && tiles_c % (2 * ct) == 0 && (tiles_c / (2 * ct)) * tiles_r >= 4 * 256) ct *= 2;
+  dim3 grid((unsigned)((tiles_c + ct - 1) / ct), (unsigned)tiles_r);
+  const size_t shm = tn1_lds_bytes(nb, p.K);
   if (nb == 1)
-    hipLaunchKernelGGL((k_gemm_tn1<1>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((k_gemm_tn1<1>), grid, dim3(256), shm, stream, p, ct);
   else
-    hipLaunchKernelGGL((k_gemm_tn1<2>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((k_gemm_tn1<2>), grid, dim3(256), shm, stream, p, ct);
   return hipGetLastError();
 }
 

@@ -66,31 +66,31 @@ struct XFrag {
   bf16x8 v[kMaxNL][MT][2];
 };
 
-// Static-shape post-order reduction of a wave's nl <= 4 leaves (midpoint
+// Static-shape post-order reduction of a wave's NL <= 4 leaves (midpoint
 // tree: 3 leaves split 1 | 2, 4 leaves split 2 | 2).  v holds leaf J of the
 // tile on entry and, after the last leaf, the subtree root.
-template <int NP, int J>
-__device__ __forceinline__ void leaf_reduce(int nl, uint32_t (&v)[NP], uint32_t (&s0)[NP], uint32_t (&s1)[NP]) {
-  if (nl == 2) {
+template <int NP, int NL, int J>
+__device__ __forceinline__ void leaf_reduce(uint32_t (&v)[NP], uint32_t (&s0)[NP], uint32_t (&s1)[NP]) {
+  if constexpr (NL == 2) {
     if constexpr (J == 0) {
 #pragma unroll
       for (int q = 0; q < NP; ++q) s0[q] = v[q];
-    } else if constexpr (J == 1) {
+    } else {
 #pragma unroll
       for (int q = 0; q < NP; ++q) v[q] = node2(s0[q], v[q]);
     }
-  } else if (nl == 3) {
+  } else if constexpr (NL == 3) {
     if constexpr (J == 0) {
 #pragma unroll
       for (int q = 0; q < NP; ++q) s0[q] = v[q];
     } else if constexpr (J == 1) {
 #pragma unroll
       for (int q = 0; q < NP; ++q) s1[q] = v[q];
-    } else if constexpr (J == 2) {
+    } else {
 #pragma unroll
       for (int q = 0; q < NP; ++q) v[q] = node2(s0[q], node2(s1[q], v[q]));
     }
-  } else if (nl == 4) {
+  } else if constexpr (NL == 4) {
     if constexpr (J == 0) {
 #pragma unroll
       for (int q = 0; q < NP; ++q) s0[q] = v[q];
@@ -100,7 +100,7 @@ __device__ __forceinline__ void leaf_reduce(int nl, uint32_t (&v)[NP], uint32_t 
     } else if constexpr (J == 2) {
 #pragma unroll
       for (int q = 0; q < NP; ++q) s1[q] = v[q];
-    } else if constexpr (J == 3) {
+    } else {
 #pragma unroll
       for (int q = 0; q < NP; ++q) v[q] = node2(s0[q], node2(s1[q], v[q]));
     }
@@ -132,34 +132,39 @@ struct XsWave {
   int64_t ldw;
   uint16_t *out;
   int64_t ldo;
+  int64_t wbytes;  // bytes of W the loads may touch: N rows (NT) or K rows (NN) of ldw elements
 
   __device__ __forceinline__ int tile_at(int i) const { return t0 + (i < T ? i : T - 1); }
 
   // Weights of unit (tile i clamped, leaf lo + j, half s): NT the whole leaf
-  // (s ignored), NN rows 32 s .. 32 s + 31 of the leaf's slab.
-  __device__ __forceinline__ void load_unit(int i, int j, int s, WF &w) const {
+  // (s ignored), NN rows 32 s .. 32 s + 31 of the leaf's slab.  Buffer loads:
+  // the descriptor is rebased on the unit's first byte (scalar arithmetic)
+  // and every lane adds its fixed offset voff[i2], so a unit costs no vector
+  // address arithmetic.  Bytes past the matrix read as zero (the range check
+  // of the rebased descriptor): NT rows past N, NN rows past K.
+  __device__ __forceinline__ void load_unit(int i, int j, int s, WF &w, const uint32_t (&voff)[2 * RT]) const {
     const int64_t n0 = (int64_t)tile_at(i) * COLS;
     const int64_t kb = (int64_t)(lo + j) * kLeaf;
+    const int64_t base = NN ? ((kb + 32 * s) * ldw + n0) * 2 : (n0 * ldw + kb) * 2;
+    const int64_t left = wbytes - base;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)((const char *)W + base), (short)0, (int)(left > 0 ? (left < 0x7fffffff ? left : 0x7fffffff) : 0),
+        0x00020000);
+    constexpr int NL = NN ? RT : 2 * RT;
+#pragma unroll
+    for (int i2 = 0; i2 < NL; ++i2)
+      w.v[i2] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)voff[i2], 0, 2));
+  }
+
+  // per-lane byte offsets of the unit loads (relative to the unit's first byte)
+  __device__ __forceinline__ void unit_offsets(uint32_t (&voff)[2 * RT]) const {
     if constexpr (!NN) {
-      // whole 128-byte row segments: 8 rows per instruction; rows past N read
-      // the last row (their outputs are never stored)
 #pragma unroll
-      for (int i2 = 0; i2 < 2 * RT; ++i2) {
-        const int64_t n = n0 + 8 * i2 + (lane >> 3) < p.N ? n0 + 8 * i2 + (lane >> 3) : p.N - 1;
-        w.v[i2] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(W + n * ldw + kb + 8 * (lane & 7)));
-      }
+      for (int i2 = 0; i2 < 2 * RT; ++i2) voff[i2] = (uint32_t)(((8 * i2 + (lane >> 3)) * ldw + 8 * (lane & 7)) * 2);
     } else {
-      // 16-byte pieces of whole rows; a piece starting past N reads the last
-      // in-row piece instead (the leading dimension is a multiple of 8, and
-      // each output column depends on its own weight column only)
       const int lrow = lane / NI, lcol = lane % NI;
-      const int64_t c0 = n0 + 8 * lcol;
-      const int64_t nlast = ((p.N + 7) & ~(int64_t)7) - 8;
-      const int64_t c = c0 <= nlast ? c0 : nlast;
-      const uint16_t *base = W + (kb + 32 * s + lrow) * ldw + c;
 #pragma unroll
-      for (int i2 = 0; i2 < RT; ++i2)
-        w.v[i2] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(base + (int64_t)ROWS * i2 * ldw));
+      for (int i2 = 0; i2 < 2 * RT; ++i2) voff[i2] = (uint32_t)(((lrow + ROWS * i2) * ldw + 8 * lcol) * 2);
     }
   }
 
@@ -264,32 +269,37 @@ struct XsWave {
     __syncthreads();
     const int64_t n0 = (int64_t)tile_at(i) * COLS;
     for (int blk = wave; blk < RT * MT; blk += waves) {
+      // the balanced tree over 8 roots, level by level; with fewer waves the
+      // root is the level-log2(waves) node of the first group (roots past the
+      // last wave read the last wave's and are never selected)
       uint32_t r[kXsWaves][2];
 #pragma unroll
-      for (int w2 = 0; w2 < kXsWaves; ++w2)
-        if (w2 < waves) {
-          r[w2][0] = buf[(w2 * NP + 2 * blk + 0) * 64 + lane];
-          r[w2][1] = buf[(w2 * NP + 2 * blk + 1) * 64 + lane];
-        }
-#pragma unroll
-      for (int width = kXsWaves; width > 1; width >>= 1) {
-        if (width <= waves) {
-#pragma unroll
-          for (int k2 = 0; k2 < width / 2; ++k2) {
-            r[k2][0] = node2(r[2 * k2][0], r[2 * k2 + 1][0]);
-            r[k2][1] = node2(r[2 * k2][1], r[2 * k2 + 1][1]);
-          }
-        }
+      for (int w2 = 0; w2 < kXsWaves; ++w2) {
+        const int src = w2 < waves ? w2 : waves - 1;
+        r[w2][0] = buf[(src * NP + 2 * blk + 0) * 64 + lane];
+        r[w2][1] = buf[(src * NP + 2 * blk + 1) * 64 + lane];
       }
+      uint32_t l1[4][2], l2[2][2], l3[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int k2 = 0; k2 < 4; ++k2) l1[k2][h] = node2(r[2 * k2][h], r[2 * k2 + 1][h]);
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) l2[k2][h] = node2(l1[2 * k2][h], l1[2 * k2 + 1][h]);
+        l3[h] = node2(l2[0][h], l2[1][h]);
+      }
+      uint32_t o[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) o[h] = waves == 8 ? l3[h] : waves == 4 ? l2[0][h] : waves == 2 ? l1[0][h] : r[0][h];
       const int rt = blk / MT, t = blk % MT;
       const int64_t m = m0 + 16 * t + r16, n = n0 + 16 * rt + 4 * g4;
       if (m < p.M) {
         uint16_t *dst = out + m * ldo + n;
         if (n + 3 < p.N) {
-          *reinterpret_cast<uint2 *>(dst) = make_uint2(r[0][0], r[0][1]);
+          *reinterpret_cast<uint2 *>(dst) = make_uint2(o[0], o[1]);
         } else {
-          const uint16_t h4[4] = {(uint16_t)(r[0][0] & 0xffff), (uint16_t)(r[0][0] >> 16), (uint16_t)(r[0][1] & 0xffff),
-                                  (uint16_t)(r[0][1] >> 16)};
+          const uint16_t h4[4] = {(uint16_t)(o[0] & 0xffff), (uint16_t)(o[0] >> 16), (uint16_t)(o[1] & 0xffff),
+                                  (uint16_t)(o[1] >> 16)};
           for (int e = 0; e < 4; ++e)
             if (n + e < p.N) dst[e] = h4[e];
         }
@@ -301,67 +311,66 @@ struct XsWave {
   // (NN).  Tiles run in groups of PR; unit U of the group's tile Q has group
   // index g = Q UN + U and lives in ring slot g % PR, and each unit first
   // issues the loads of unit g + PR - 1 (possibly of a later tile) into its slot.
-  template <int NF, int Q, int U>
+  template <int NL, int NF, int Q, int U>
   __device__ __forceinline__ void units(int i, WF (&ring)[PR], const XFrag<MT> &xs, f32x4 (&acc)[RT][MT],
-                                        uint32_t (&v)[NP], uint32_t (&s0)[NP], uint32_t (&s1)[NP]) const {
+                                        uint32_t (&v)[NP], uint32_t (&s0)[NP], uint32_t (&s1)[NP],
+                                        const uint32_t (&voff)[2 * RT]) const {
     constexpr int UN = NN ? 2 * NF : NF;
     if constexpr (U < UN) {
       constexpr int J = NN ? U / 2 : U, S = NN ? U % 2 : 0;
       constexpr int g = Q * UN + U, slot = g % PR;
       constexpr int nx = U + PR - 1;  // the unit to prefetch, counted from this tile's unit 0
       constexpr int nu = nx % UN;
-      load_unit(i + nx / UN, NN ? nu / 2 : nu, NN ? nu % 2 : 0, ring[(g + PR - 1) % PR]);
+      load_unit(i + nx / UN, NN ? nu / 2 : nu, NN ? nu % 2 : 0, ring[(g + PR - 1) % PR], voff);
       // keep the prefetch ahead of this unit's MFMAs: the scheduler would
       // otherwise sink the loads next to their use and serialise the stream
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (!NN) {
         leaf_nt(ring[slot], xs.v[J], true, v);
-        leaf_reduce<NP, J>(nl, v, s0, s1);
+        leaf_reduce<NP, NL, J>(v, s0, s1);
       } else {
         half_nn<S>(ring[slot], xs.v[J], acc);
         if constexpr (S == 1) {
           pack(acc, v);
-          leaf_reduce<NP, J>(nl, v, s0, s1);
+          leaf_reduce<NP, NL, J>(v, s0, s1);
         }
       }
-      units<NF, Q, U + 1>(i, ring, xs, acc, v, s0, s1);
+      units<NL, NF, Q, U + 1>(i, ring, xs, acc, v, s0, s1, voff);
     }
   }
 
-  // One tile (index i) of a wave with NF full leaves (+ the partial last leaf
-  // when `tail`, loaded without prefetch).
-  template <int NF, int Q>
-  __device__ __forceinline__ void tile(int i, WF (&ring)[PR], const XFrag<MT> &xs) const {
+  // One tile (index i) of a wave with NL leaves, the last partial when TAIL
+  // (loaded without prefetch); NF = NL - TAIL go through the ring.
+  template <int NL, bool TAIL, int Q>
+  __device__ __forceinline__ void tile(int i, WF (&ring)[PR], const XFrag<MT> &xs, const uint32_t (&voff)[2 * RT]) const {
+    constexpr int NF = NL - (TAIL ? 1 : 0);
     uint32_t s0[NP], s1[NP], v[NP];
     f32x4 acc[RT][MT];
-#pragma unroll
-    for (int q = 0; q < NP; ++q) v[q] = s0[q] = s1[q] = 0;
-    units<NF, Q, 0>(i, ring, xs, acc, v, s0, s1);
-    if constexpr (NF < kMaxNL) {
-      if (tail) {
-        const int64_t kb = (int64_t)(lo + NF) * kLeaf;
-        const bool half1 = kb + 32 < p.K;  // an all-zero block leaves the sum unchanged
-        WF wt;
-        if constexpr (!NN) {
-          load_unit_tail(i, NF, 0, wt);
-          leaf_nt(wt, xs.v[NF], half1, v);
-        } else {
-          load_unit_tail(i, NF, 0, wt);
-          half_nn<0>(wt, xs.v[NF], acc);
-          if (half1) {
-            load_unit_tail(i, NF, 1, wt);
-            half_nn<1>(wt, xs.v[NF], acc);
-          }
-          pack(acc, v);
+    units<NL, NF, Q, 0>(i, ring, xs, acc, v, s0, s1, voff);
+    if constexpr (TAIL) {
+      const int64_t kb = (int64_t)(lo + NF) * kLeaf;
+      const bool half1 = kb + 32 < p.K;  // an all-zero block leaves the sum unchanged
+      WF wt;
+      if constexpr (!NN) {
+        load_unit_tail(i, NF, 0, wt);
+        leaf_nt(wt, xs.v[NF], half1, v);
+      } else {
+        load_unit_tail(i, NF, 0, wt);
+        half_nn<0>(wt, xs.v[NF], acc);
+        if (half1) {
+          load_unit_tail(i, NF, 1, wt);
+          half_nn<1>(wt, xs.v[NF], acc);
         }
-        leaf_reduce<NP, NF>(nl, v, s0, s1);
+        pack(acc, v);
       }
+      leaf_reduce<NP, NL, NF>(v, s0, s1);
     }
     finish_tile(i, v);
   }
 
-  template <int NF>
+  template <int NL, bool TAIL>
   __device__ __forceinline__ void run() const {
+    constexpr int NF = NL - (TAIL ? 1 : 0);
     if (T <= 0) return;  // no tile for this workgroup (the same for all its waves)
     // stationary activation fragments of this wave's leaves (rows past M clamped)
     XFrag<MT> xs;
@@ -372,33 +381,30 @@ struct XsWave {
       arow[t] = p.A[b] + m * p.lda[b];
     }
 #pragma unroll
-    for (int j = 0; j < kMaxNL; ++j)
+    for (int j = 0; j < NL; ++j)
 #pragma unroll
       for (int t = 0; t < MT; ++t)
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
           const int64_t k = (int64_t)(lo + j) * kLeaf + 32 * s + 8 * g4;
-          if (j < NF)
-            xs.v[j][t][s] = load_frag(arow[t], k);
-          else if (j == NF && tail)
-            xs.v[j][t][s] = load_frag_tail(arow[t], k, p.K);
-          else
-            xs.v[j][t][s] = bf16x8{};
+          xs.v[j][t][s] = (TAIL && j == NF) ? load_frag_tail(arow[t], k, p.K) : load_frag(arow[t], k);
         }
     WF ring[PR];
+    uint32_t voff[2 * RT];
+    unit_offsets(voff);
     if constexpr (NF > 0) {
       constexpr int UN = NN ? 2 * NF : NF;
 #pragma unroll
       for (int g = 0; g < PR - 1; ++g) {
         const int u = g % UN;
-        load_unit(g / UN, NN ? u / 2 : u, NN ? u % 2 : 0, ring[g]);
+        load_unit(g / UN, NN ? u / 2 : u, NN ? u % 2 : 0, ring[g], voff);
       }
     }
     for (int i = 0; i < T; i += PR) {
-      tile<NF, 0>(i, ring, xs);
-      if (i + 1 < T) tile<NF, 1>(i + 1, ring, xs);
+      tile<NL, TAIL, 0>(i, ring, xs, voff);
+      if (i + 1 < T) tile<NL, TAIL, 1>(i + 1, ring, xs, voff);
       if constexpr (PR > 2)
-        if (i + 2 < T) tile<NF, 2>(i + 2, ring, xs);
+        if (i + 2 < T) tile<NL, TAIL, 2>(i + 2, ring, xs, voff);
     }
   }
 };
@@ -439,13 +445,19 @@ __global__ __launch_bounds__(kXsWaves * 64) void k_xs(GemmParams p) {
        p.B[b],
        p.ldb[b],
        p.to_part ? p.part + ((int64_t)b * (1 << kd) + piece) * p.part_stride : p.C[b],
-       p.to_part ? p.ldp : p.ldc[b]};
-  switch (w.nl - (w.tail ? 1 : 0)) {
-    case 0: w.template run<0>(); break;
-    case 1: w.template run<1>(); break;
-    case 2: w.template run<2>(); break;
-    case 3: w.template run<3>(); break;
-    default: w.template run<4>(); break;
+       p.to_part ? p.ldp : p.ldc[b],
+       (LAYOUT == DGF_LAYOUT_NN ? p.K : p.N) * p.ldb[b] * 2};
+  // the wave's leaf count and whether it owns the partial last leaf, as
+  // compile-time shapes (nl is 1..4 by the launch plan)
+  switch (w.nl * 2 + (w.tail ? 1 : 0)) {
+    case 2: w.template run<1, false>(); break;
+    case 3: w.template run<1, true>(); break;
+    case 4: w.template run<2, false>(); break;
+    case 5: w.template run<2, true>(); break;
+    case 6: w.template run<3, false>(); break;
+    case 7: w.template run<3, true>(); break;
+    case 8: w.template run<4, false>(); break;
+    default: w.template run<4, true>(); break;
   }
 }
 
