@@ -344,7 +344,7 @@ size_t bwd_ws_bytes(int64_t M, int64_t H, int64_t I) {
 }
 
 size_t fwd_ws_bytes(int64_t M, int64_t H, int64_t I) {
-  const size_t gu = partial_bytes(DGF_LAYOUT_NT, 2, EPI_ACT, M, I, H);  // gate/up partial roots
+  const size_t gu = gu_act_applies(M, I, H) ? 0 : partial_bytes(DGF_LAYOUT_NT, 2, EPI_ACT, M, I, H);  // gate/up partial roots
   const size_t dn = partial_bytes(DGF_LAYOUT_NT, 1, EPI_STORE, M, H, I);  // down-projection partial roots
   return round256((size_t)M * round8(I) * 2)  // a [M, I]
          + (gu > dn ? gu : dn);               // the gate/up roots are joined before the down GEMM starts
@@ -422,21 +422,34 @@ dgf_status dgf_ffn_fwd(const void *x, int64_t ldx, const void *w_gate, int64_t l
   const int64_t lda_ = round8(I);
   uint16_t *partials = (uint16_t *)((char *)ws + cv.used);
 
-  GemmParams p = blank();
-  p.A[0] = p.A[1] = (const uint16_t *)x;
-  p.lda[0] = p.lda[1] = ldx;
-  p.shared_a = 1;
-  p.B[0] = (const uint16_t *)w_gate;
-  p.ldb[0] = ld_wg;
-  p.B[1] = (const uint16_t *)w_up;
-  p.ldb[1] = ld_wu;
-  p.C[0] = (uint16_t *)g_save;
-  p.C[1] = (uint16_t *)u_save;
-  p.ldc[0] = p.ldc[1] = ld_gu;
-  p.act_out = a;
-  p.ld_act = lda_;
-  p.M = M; p.N = I; p.K = H;
-  DGF_TRY(run_gemm(DGF_LAYOUT_NT, 2, EPI_ACT, p, s, "gate/up tree GEMM", partials, "gate/up join + act"));
+  if (gu_act_applies(M, I, H)) {
+    // one kernel: both projections over all of K per workgroup, then the activation
+    GuParams f;
+    memset(&f, 0, sizeof f);
+    f.x = (const uint16_t *)x; f.ldx = ldx;
+    f.w[0] = (const uint16_t *)w_gate; f.ldw[0] = ld_wg;
+    f.w[1] = (const uint16_t *)w_up; f.ldw[1] = ld_wu;
+    f.a = a; f.lda = lda_;
+    f.g = (uint16_t *)g_save; f.u = (uint16_t *)u_save; f.ldgu = ld_gu;
+    f.M = M; f.N = I; f.K = H; f.L = leaves(H);
+    DGF_TRY(hip_check(timed(s, "gate/up + act", [&] { return launch_gu_act(f, s); }), "gate/up + act"));
+  } else {
+    GemmParams p = blank();
+    p.A[0] = p.A[1] = (const uint16_t *)x;
+    p.lda[0] = p.lda[1] = ldx;
+    p.shared_a = 1;
+    p.B[0] = (const uint16_t *)w_gate;
+    p.ldb[0] = ld_wg;
+    p.B[1] = (const uint16_t *)w_up;
+    p.ldb[1] = ld_wu;
+    p.C[0] = (uint16_t *)g_save;
+    p.C[1] = (uint16_t *)u_save;
+    p.ldc[0] = p.ldc[1] = ld_gu;
+    p.act_out = a;
+    p.ld_act = lda_;
+    p.M = M; p.N = I; p.K = H;
+    DGF_TRY(run_gemm(DGF_LAYOUT_NT, 2, EPI_ACT, p, s, "gate/up tree GEMM", partials, "gate/up join + act"));
+  }
 
   GemmParams q = blank();
   q.A[0] = a;

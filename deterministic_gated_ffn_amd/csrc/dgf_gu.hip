@@ -1,0 +1,336 @@
+// Fused gate/up projection and activation for few tokens (gfx950).
+//
+// a[m][n] = bf16( silu(g) u ) with g = T_K(x[m,:] . W_gate[n,:]) and
+// u = T_K(x[m,:] . W_up[n,:]), both rounded to BF16 (the stage boundaries of
+// RL-Kernel PR #325, sections "Design" and "Operator test matrix").
+//
+// One workgroup of 8 waves owns whole output tiles of 16 columns and all K:
+// the canonical midpoint tree over the L <= 64 leaves is cut at depth 3 into
+// one subtree per wave (at most 8 leaves), the wave reduces its subtree with
+// the fixed post-order in registers, and after a workgroup barrier the 8
+// wave roots are joined with the balanced top three levels.  Gate and up of a
+// tile are reduced by the same workgroup one after the other, so the
+// activation is applied right there: no partial roots, no join kernel.
+//
+// The activation operand stays on chip for the whole kernel: the first NR
+// leaves of a wave's subtree in registers, the rest in the wave's own LDS
+// region (a wave reads only what it wrote, so no barrier guards it).  Weights
+// stream through the wave as whole 128-byte row segments (8 rows per load
+// instruction, buffer loads on a rebased descriptor) staged through a
+// swizzled LDS slab into the MFMA layout; each weight byte is read from HBM
+// once per 16-token tile.
+#include "dgf_device.hpp"
+#include "dgf_kernels.hpp"
+
+namespace dgf {
+namespace {
+
+constexpr int kGuWaves = 8;
+constexpr int kGuMaxNL = 8;  // leaves per wave (L <= 64)
+constexpr int kGuCols = 16;  // output columns per tile
+constexpr int kGuRing = 4;   // ring slots of weight units: PR - 1 units in flight per wave
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Depth D of leaf j in the midpoint tree over n leaves, and the number m of
+// right-child steps that end its root-to-leaf path (the merges it triggers).
+struct LeafPos {
+  int D, m;
+};
+constexpr LeafPos leaf_pos(int n, int j) {
+  int lo = 0, hi = n, D = 0, m = 0;
+  while (hi - lo > 1) {
+    const int mid = lo + (hi - lo) / 2;
+    if (j < mid) {
+      hi = mid;
+      m = 0;
+    } else {
+      lo = mid;
+      ++m;
+    }
+    ++D;
+  }
+  return LeafPos{D, m};
+}
+
+// Feed leaf J of an N-leaf subtree (N <= 8, so depth <= 3): merge it with the
+// pending left siblings its position closes, then park it at its depth; after
+// the last leaf v is the subtree root.
+template <int NP, int N, int J>
+__device__ __forceinline__ void push_leaf(uint32_t (&v)[NP], uint32_t (&st)[3][NP]) {
+  constexpr LeafPos lp = leaf_pos(N, J);
+#pragma unroll
+  for (int t = 0; t < lp.m; ++t)
+#pragma unroll
+    for (int q = 0; q < NP; ++q) v[q] = node2(st[lp.D - 1 - t][q], v[q]);
+  constexpr int d = lp.D - lp.m;
+  if constexpr (d > 0) {
+#pragma unroll
+    for (int q = 0; q < NP; ++q) st[d - 1][q] = v[q];
+  }
+}
+
+template <int MT>
+constexpr int nr_of() {
+  return MT == 1 ? kGuMaxNL : 5;  // activation leaves held in registers
+}
+
+template <int MT>
+struct GuLds {
+  // per wave: the LDS-resident activation fragments, then the weight slab
+  static constexpr int XL = kGuMaxNL - nr_of<MT>();
+  static constexpr size_t x_bytes = (size_t)XL * MT * 2 * 64 * 16;
+  static constexpr size_t slab_bytes = (size_t)kGuCols * 64 * 2;
+  static constexpr size_t roots_bytes = (size_t)2 * 2 * kGuWaves * (MT * 2) * 64 * 4;  // [parity][b][wave][NP][lane]
+  static constexpr size_t total = roots_bytes + kGuWaves * (x_bytes + slab_bytes);
+};
+
+template <int MT>
+struct GuWave {
+  static constexpr int NP = MT * 2;  // packed BF16 pairs per lane: index 2 t + h
+  static constexpr int NR = nr_of<MT>();
+  struct WF {
+    u32x4 v[2];  // rows 8 i2 + lane / 8 of the tile, 16-byte K chunk lane % 8 of the leaf
+  };
+
+  const GuParams &p;
+  uint32_t *roots;   // LDS [2][2][waves][NP][64]
+  u32x4 *xl;         // this wave's LDS activation fragments [XL][MT][2][64]
+  uint16_t *slab;    // this wave's 16 x 64 staging slab
+  int wave, lane, r16, g4;
+  int lo;
+  int64_t m0;
+  int t0, T;
+  int64_t wbytes[2];
+
+  __device__ __forceinline__ int64_t col0(int i) const { return (int64_t)(t0 + (i < T ? i : T - 1)) * kGuCols; }
+
+  // Weight unit (tile i, product b, leaf lo + j): 16 rows x 128 bytes.  Rows
+  // past N read as zero (range check of the rebased descriptor), and so does
+  // every row of a prefetch past this workgroup's last tile (an empty range:
+  // no memory request at all).
+  __device__ __forceinline__ void load_unit(int i, int b, int j, WF &w, const uint32_t (&voff)[2][2]) const {
+    const int64_t base = (col0(i) * p.ldw[b] + (int64_t)(lo + j) * kLeaf) * 2;
+    const int64_t left = i < T ? wbytes[b] - base : 0;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)((const char *)p.w[b] + base), (short)0,
+        (int)(left > 0 ? (left < 0x7fffffff ? left : 0x7fffffff) : 0), 0x00020000);
+#pragma unroll
+    for (int i2 = 0; i2 < 2; ++i2)
+      w.v[i2] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)voff[b][i2], 0, 2));
+  }
+
+  // Leaf J of product b: the 16 weight rows through the slab (row r's chunk c
+  // at r*64 + 8 (c ^ (r & 7)): conflict-free row writes and MFMA-layout
+  // reads), two MFMAs per token tile from a zero accumulator, packed to BF16.
+  template <int J>
+  __device__ __forceinline__ void leaf(const WF &w, const bf16x8 (&xr)[NR][MT][2], uint32_t (&v)[NP]) const {
+    const int wr = lane >> 3, wc = lane & 7;
+#pragma unroll
+    for (int i2 = 0; i2 < 2; ++i2) *reinterpret_cast<u32x4 *>(&slab[(8 * i2 + wr) * 64 + 8 * (wc ^ wr)]) = w.v[i2];
+    wave_lds_sync();
+    const bf16x8 w0 = *reinterpret_cast<const bf16x8 *>(&slab[r16 * 64 + 8 * ((0 + g4) ^ (r16 & 7))]);
+    const bf16x8 w1 = *reinterpret_cast<const bf16x8 *>(&slab[r16 * 64 + 8 * ((4 + g4) ^ (r16 & 7))]);
+    bf16x8 xf[MT][2];
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        if constexpr (J < NR)
+          xf[t][s] = xr[J][t][s];
+        else
+          xf[t][s] = __builtin_bit_cast(bf16x8, xl[((J - NR) * MT + t) * 2 * 64 + s * 64 + lane]);
+      }
+    f32x4 acc[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      acc[t] = mfma16(w0, xf[t][0], f32x4{0.f, 0.f, 0.f, 0.f});
+      acc[t] = mfma16(w1, xf[t][1], acc[t]);
+    }
+    wave_lds_sync();  // slab reads done before the next unit overwrites it
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      v[2 * t + 0] = pack_rne(acc[t][0], acc[t][1]);
+      v[2 * t + 1] = pack_rne(acc[t][2], acc[t][3]);
+    }
+  }
+
+  // Units U.. of one tile: unit U is leaf U % NL of product U / NL, in ring
+  // slot U % PR (PR divides the 2 NL units of a tile, so every tile starts in
+  // slot 0); each unit first issues the loads of the unit PR - 1 ahead
+  // (possibly of the next tile) into the slot the previous unit freed.
+  template <int NL, int PR, int U>
+  __device__ __forceinline__ void units(int i, WF (&ring)[PR], const bf16x8 (&xr)[NR][MT][2], uint32_t (&v)[NP],
+                                        uint32_t (&st)[3][NP], uint32_t (&rg)[NP], const uint32_t (&voff)[2][2]) const {
+    constexpr int UN = 2 * NL;
+    if constexpr (U < UN) {
+      constexpr int b = U / NL, J = U % NL;
+      constexpr int nx = U + PR - 1, nu = nx % UN;
+      load_unit(i + nx / UN, nu / NL, nu % NL, ring[nx % PR], voff);
+      __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of this unit's MFMAs
+      leaf<J>(ring[U % PR], xr, v);
+      push_leaf<NP, NL, J>(v, st);
+      if constexpr (J == NL - 1 && b == 0) {
+#pragma unroll
+        for (int q = 0; q < NP; ++q) rg[q] = v[q];
+      }
+      units<NL, PR, U + 1>(i, ring, xr, v, st, rg, voff);
+    }
+  }
+
+  // Park the gate and up roots of tile i, then (after the barrier) join the 8
+  // wave roots of each with the balanced top of the tree and apply the
+  // activation: wave t < MT takes token block t.
+  __device__ __forceinline__ void finish_tile(int i, const uint32_t (&rg)[NP], const uint32_t (&ru)[NP]) const {
+    uint32_t *buf = roots + (size_t)(i & 1) * 2 * kGuWaves * NP * 64;
+#pragma unroll
+    for (int q = 0; q < NP; ++q) {
+      buf[((0 * kGuWaves + wave) * NP + q) * 64 + lane] = rg[q];
+      buf[((1 * kGuWaves + wave) * NP + q) * 64 + lane] = ru[q];
+    }
+    __syncthreads();
+    if (wave >= MT) return;
+    const int t = wave;
+    uint32_t o[2][2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        uint32_t r[kGuWaves];
+#pragma unroll
+        for (int w2 = 0; w2 < kGuWaves; ++w2) r[w2] = buf[((b * kGuWaves + w2) * NP + 2 * t + h) * 64 + lane];
+        o[b][h] = node2(node2(node2(r[0], r[1]), node2(r[2], r[3])), node2(node2(r[4], r[5]), node2(r[6], r[7])));
+      }
+    uint32_t av[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const float ga = bf_lo(o[0][h]), gb = bf_hi(o[0][h]);
+      const float ua = bf_lo(o[1][h]), ub = bf_hi(o[1][h]);
+      const float sa = ga * sigma_f(ga), sb = gb * sigma_f(gb);
+      av[h] = pack_rne(sa * ua, sb * ub);
+    }
+    const int64_t m = m0 + 16 * t + r16, n = col0(i) + 4 * g4;
+    if (m >= p.M || n >= p.N) return;
+    auto put = [&](uint16_t *C, int64_t ldc, uint32_t lo2, uint32_t hi2) {
+      uint16_t *dst = C + m * ldc + n;
+      if (n + 3 < p.N) {
+        *reinterpret_cast<uint2 *>(dst) = make_uint2(lo2, hi2);
+      } else {
+        const uint16_t h4[4] = {(uint16_t)(lo2 & 0xffff), (uint16_t)(lo2 >> 16), (uint16_t)(hi2 & 0xffff),
+                                (uint16_t)(hi2 >> 16)};
+        for (int e = 0; e < 4; ++e)
+          if (n + e < p.N) dst[e] = h4[e];
+      }
+    };
+    put(p.a, p.lda, av[0], av[1]);
+    if (p.g) put(p.g, p.ldgu, o[0][0], o[0][1]);
+    if (p.u) put(p.u, p.ldgu, o[1][0], o[1][1]);
+  }
+
+  template <int NL>
+  __device__ __forceinline__ void run() const {
+    if (T <= 0) return;
+    // the first weight units go out before the activation loads: the stream
+    // starts while the activations arrive
+    uint32_t voff[2][2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int i2 = 0; i2 < 2; ++i2)
+        voff[b][i2] = (uint32_t)(((8 * i2 + (lane >> 3)) * p.ldw[b] + 8 * (lane & 7)) * 2);
+    constexpr int PR = (2 * NL) % kGuRing == 0 ? kGuRing : 2;
+    WF ring[PR];
+#pragma unroll
+    for (int g = 0; g < PR - 1; ++g) load_unit(g / (2 * NL), (g % (2 * NL)) / NL, g % NL, ring[g], voff);
+    // activation fragments of this wave's leaves: the first NR in registers,
+    // the rest in LDS (rows past M clamped to a valid row; never stored)
+    bf16x8 xr[NR][MT][2];
+    const uint16_t *arow[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      const int64_t m = m0 + 16 * t + r16 < p.M ? m0 + 16 * t + r16 : p.M - 1;
+      arow[t] = p.x + m * p.ldx;
+    }
+#pragma unroll
+    for (int j = 0; j < NL; ++j)
+#pragma unroll
+      for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const bf16x8 f = load_frag(arow[t], (int64_t)(lo + j) * kLeaf + 32 * s + 8 * g4);
+          if (j < NR)
+            xr[j < NR ? j : 0][t][s] = f;
+          else
+            xl[((j - NR) * MT + t) * 2 * 64 + s * 64 + lane] = __builtin_bit_cast(u32x4, f);
+        }
+    wave_lds_sync();
+    for (int i = 0; i < T; ++i) {
+      uint32_t v[NP], st[3][NP], rg[NP];
+      units<NL, PR, 0>(i, ring, xr, v, st, rg, voff);
+      finish_tile(i, rg, v);
+    }
+  }
+};
+
+template <int MT>
+__global__ __launch_bounds__(kGuWaves * 64) void k_gate_up_act(GuParams p) {
+  extern __shared__ __attribute__((aligned(16))) uint32_t gu_lds[];
+  using Wv = GuWave<MT>;
+  using Lay = GuLds<MT>;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int lo, hi;
+  subtree_range(p.L, 3, wave, lo, hi);
+  const int tiles_n = (int)((p.N + kGuCols - 1) / kGuCols);
+  const int per = (tiles_n + (int)gridDim.x - 1) / (int)gridDim.x;
+  const int t0 = (int)blockIdx.x * per;
+  const int T = t0 < tiles_n ? min(per, tiles_n - t0) : 0;
+  char *base = reinterpret_cast<char *>(gu_lds) + Lay::roots_bytes + (size_t)wave * (Lay::x_bytes + Lay::slab_bytes);
+  Wv w{p,
+       gu_lds,
+       reinterpret_cast<u32x4 *>(base),
+       reinterpret_cast<uint16_t *>(base + Lay::x_bytes),
+       wave,
+       lane,
+       lane & 15,
+       lane >> 4,
+       lo,
+       (int64_t)blockIdx.y * 16 * MT,
+       t0,
+       T,
+       {p.N * p.ldw[0] * 2, p.N * p.ldw[1] * 2}};
+  switch (hi - lo) {  // 1..8 by the launch conditions (8 <= L <= 64)
+    case 1: w.template run<1>(); break;
+    case 2: w.template run<2>(); break;
+    case 3: w.template run<3>(); break;
+    case 4: w.template run<4>(); break;
+    case 5: w.template run<5>(); break;
+    case 6: w.template run<6>(); break;
+    case 7: w.template run<7>(); break;
+    default: w.template run<8>(); break;
+  }
+}
+
+}  // namespace
+
+bool gu_act_applies(int64_t M, int64_t N, int64_t K) {
+  const int64_t L = K / kLeaf;
+  return M >= 1 && M <= 32 && N >= 1 && K % kLeaf == 0 && L >= kGuWaves && L <= kGuWaves * kGuMaxNL;
+}
+
+hipError_t launch_gu_act(const GuParams &p, hipStream_t stream) {
+  const int mt = p.M <= 16 ? 1 : 2;
+  const int64_t tiles_n = (p.N + kGuCols - 1) / kGuCols;
+  // one wave of workgroups over the 256 CUs (one workgroup per CU by LDS);
+  // each takes a contiguous run of ceil(tiles / groups) tiles
+  int64_t per = (tiles_n + 255) / 256;
+  const int64_t groups = (tiles_n + per - 1) / per;
+  const dim3 grid((unsigned)groups, 1u), block(kGuWaves * 64);
+  if (mt == 1)
+    hipLaunchKernelGGL(k_gate_up_act<1>, grid, block, GuLds<1>::total, stream, p);
+  else
+    hipLaunchKernelGGL(k_gate_up_act<2>, grid, block, GuLds<2>::total, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace dgf

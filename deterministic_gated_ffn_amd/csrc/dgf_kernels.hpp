@@ -51,6 +51,24 @@ hipError_t launch_xs(int layout, GemmParams p, int nb, int waves, int groups, hi
 // gate and up products; DSILU: dG, dU, a from dA; DX: dx from the G and U lanes).
 hipError_t launch_combine_epi(int epi, int nb, GemmParams p, hipStream_t stream);
 
+// Fused gate/up projection and activation (dgf_gu.hip): x [M, K], W_gate and
+// W_up [N, K], all K-contiguous; a = bf16(silu(g) u) [M, N], g and u kept
+// when non-null.  Applies to M <= 32 and K a multiple of 64 with 8..64 leaves.
+struct GuParams {
+  const uint16_t *x;
+  int64_t ldx;
+  const uint16_t *w[2];
+  int64_t ldw[2];
+  uint16_t *a;
+  int64_t lda;
+  uint16_t *g, *u;
+  int64_t ldgu;
+  int64_t M, N, K;
+  int L;
+};
+bool gu_act_applies(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gu_act(const GuParams &p, hipStream_t stream);
+
 // Output row tiles of 16 per wave of the NT / NN tree GEMM kernel variants.
 int gemm_row_tiles(int layout, int nb, int epi);
 hipError_t launch_gemm(int layout, int nb, int epi, GemmParams p, int waves, hipStream_t stream);

@@ -141,12 +141,14 @@ struct XsWave {
   // the descriptor is rebased on the unit's first byte (scalar arithmetic)
   // and every lane adds its fixed offset voff[i2], so a unit costs no vector
   // address arithmetic.  Bytes past the matrix read as zero (the range check
-  // of the rebased descriptor): NT rows past N, NN rows past K.
+  // of the rebased descriptor): NT rows past N, NN rows past K, and every
+  // byte of a prefetch past this workgroup's last tile (an empty range: no
+  // memory request at all).
   __device__ __forceinline__ void load_unit(int i, int j, int s, WF &w, const uint32_t (&voff)[2 * RT]) const {
     const int64_t n0 = (int64_t)tile_at(i) * COLS;
     const int64_t kb = (int64_t)(lo + j) * kLeaf;
     const int64_t base = NN ? ((kb + 32 * s) * ldw + n0) * 2 : (n0 * ldw + kb) * 2;
-    const int64_t left = wbytes - base;
+    const int64_t left = i < T ? wbytes - base : 0;
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         (void *)((const char *)W + base), (short)0, (int)(left > 0 ? (left < 0x7fffffff ? left : 0x7fffffff) : 0),
         0x00020000);

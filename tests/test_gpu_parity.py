@@ -211,7 +211,8 @@ def test_tiny_ffn_forward_backward_bitwise():
         assert fp64.rel_l2(inputs.bits(r[k]), fb[k]) <= 1e-2, k
 
 
-@pytest.mark.parametrize("M,H,I", [(1, 64, 64), (3, 128, 320), (20, 256, 768), (37, 200, 136), (64, 128, 256)])
+@pytest.mark.parametrize("M,H,I", [(1, 64, 64), (3, 128, 320), (20, 256, 768), (37, 200, 136), (64, 128, 256),
+                                   (5, 512, 200), (17, 960, 1000), (32, 2112, 136), (9, 4096, 40), (32, 576, 24)])
 def test_ffn_other_shapes_bitwise(M, H, I):
     rng = np.random.default_rng(M + H + I)
     x, dy = rnd(rng, (M, H)), rnd(rng, (M, H))
@@ -326,3 +327,46 @@ def test_bad_arguments_raise():
     with pytest.raises(dgf.DgfError) as e:
         dgf.ffn_fwd(x[:, 1:], w[:, 1:], w[:, 1:], wd[1:])  # misaligned views
     assert e.value.status == 1
+
+
+def test_long_sequence_sampled_vs_oracle(qwen_weights):
+    # M = 4096 tokens (8 sequences x 512), the compute-bound shape: the whole
+    # forward and backward run on the GPU; the oracle checks sampled token rows
+    # of g, u, y and dX (every output depends on its own token row only) and
+    # sampled I-slices of the weight gradients (dW_gate/dW_up rows and dW_down
+    # columns depend only on their slice of I, with K = all 4096 tokens).
+    (wg_c, wu_c, wd_c), (wg, wu, wd) = qwen_weights
+    M, H, I = 4096, 4096, 12288
+    x_c, dy_c = inputs.activations(M)
+    x, dy = x_c.cuda(), dy_c.cuda()
+    y, g, u = dgf.ffn_fwd(x, wg, wu, wd, training=True)
+    r = dgf.ffn_bwd(dy, x, g, u, wg, wu, wd)
+    torch.cuda.synchronize()
+    B = {k: inputs.bits(v) for k, v in (("x", x_c), ("dy", dy_c), ("wg", wg_c), ("wu", wu_c), ("wd", wd_c))}
+    rng = np.random.default_rng(4096)
+    ms = np.unique(np.concatenate([[0, 511, 512, 4095], rng.choice(M, 4, replace=False)]))
+    cols = np.unique(np.concatenate([[0, I - 1], rng.choice(I, 6, replace=False)]))
+    # token rows
+    o = oracle.ffn_fwd(B["x"][ms], B["wg"], B["wu"], B["wd"])
+    for k, t in (("g", g), ("u", u), ("y", y)):
+        assert_bitwise(inputs.bits(t)[ms], o[k], f"{k} rows")
+    ob = oracle.ffn_bwd(B["dy"][ms], B["x"][ms], o["g"], o["u"], B["wg"], B["wu"], B["wd"])
+    assert_bitwise(inputs.bits(r["dX"])[ms], ob["dX"], "dX rows")
+    # I-slices of the weight gradients
+    wg_s = np.ascontiguousarray(B["wg"][cols]); wu_s = np.ascontiguousarray(B["wu"][cols])
+    wd_s = np.ascontiguousarray(B["wd"][:, cols])
+    os_ = oracle.ffn_fwd(B["x"], wg_s, wu_s, wd_s)
+    obs = oracle.ffn_bwd(B["dy"], B["x"], os_["g"], os_["u"], wg_s, wu_s, wd_s)
+    assert_bitwise(inputs.bits(g)[:, cols], os_["g"], "g columns")
+    assert_bitwise(inputs.bits(r["dW_gate"])[cols], obs["dW_gate"], "dW_gate rows")
+    assert_bitwise(inputs.bits(r["dW_up"])[cols], obs["dW_up"], "dW_up rows")
+    assert_bitwise(inputs.bits(r["dW_down"])[:, cols], obs["dW_down"], "dW_down columns")
+    # float64 brute force on the same samples: relative L2 <= 1e-2
+    f = fp64.ffn_fwd(B["x"][ms], B["wg"], B["wu"], B["wd"])
+    assert fp64.rel_l2(inputs.bits(y)[ms], f["y"]) <= 1e-2
+    fb = fp64.ffn_bwd(B["dy"][ms], B["x"][ms], B["wg"], B["wu"], B["wd"])
+    assert fp64.rel_l2(inputs.bits(r["dX"])[ms], fb["dX"]) <= 1e-2
+    fs = fp64.ffn_bwd(B["dy"], B["x"], wg_s, wu_s, wd_s)
+    for k in ("dW_gate", "dW_up"):
+        assert fp64.rel_l2(inputs.bits(r[k])[cols], fs[k]) <= 1e-2, k
+    assert fp64.rel_l2(inputs.bits(r["dW_down"])[:, cols], fs["dW_down"]) <= 1e-2
