@@ -528,8 +528,12 @@ dgf_status dgf_ffn_bwd(const void *dy, int64_t lddy, const void *x, int64_t ldx,
   p.su = (const uint16_t *)u;
   p.ld_gu = ld_gu;
   p.dG = dG; p.dU = dU; p.a_rm = a_rm; p.ld_d = ld_d;
-  p.dGT = dGT; p.dUT = dUT; p.aT = aT; p.ld_t = Mp;  // transposed copies only without the direct dW kernel
   DGF_TRY(run_gemm(DGF_LAYOUT_NN, 1, EPI_DSILU, p, s, "dA tree GEMM", partials, "dA join + dsilu"));
+  if (!direct) {  // token-major copies for the weight-gradient GEMMs
+    DGF_TRY(hip_check(timed(s, "transpose dG", [&] { return launch_transpose(dG, ld_d, M, I, dGT, Mp, s); }), "transpose dG"));
+    DGF_TRY(hip_check(timed(s, "transpose dU", [&] { return launch_transpose(dU, ld_d, M, I, dUT, Mp, s); }), "transpose dU"));
+    DGF_TRY(hip_check(timed(s, "transpose a", [&] { return launch_transpose(a_rm, ld_d, M, I, aT, Mp, s); }), "transpose a"));
+  }
 
   // dX lanes G = T_I(dG W_gate), U = T_I(dU W_up) and dX = bf16(G + U), the
   // gate lane first: one two-product GEMM whose join does the ordered add

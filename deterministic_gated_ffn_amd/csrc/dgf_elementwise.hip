@@ -106,8 +106,7 @@ __global__ __launch_bounds__(kThreads) void k_combine_epi(GemmParams p) {
       if (p.C[0]) store8(p.C[0] + m * p.ldc[0] + c, c, p.N, r0);
       if (p.C[1]) store8(p.C[1] + m * p.ldc[1] + c, c, p.N, r1);
     } else if constexpr (EPI == EPI_DSILU) {
-      // dA with the saved g, u: dU = bf16(dA s), dG = bf16((dA u) s'), a = bf16(s u),
-      // written row-major [M, N] and transposed [N, M]
+      // dA with the saved g, u: dU = bf16(dA s), dG = bf16((dA u) s'), a = bf16(s u), row-major [M, N]
       uint32_t dg[4] = {0, 0, 0, 0}, du[4] = {0, 0, 0, 0}, av[4] = {0, 0, 0, 0};
       const int n_here = c + 8 <= p.N ? 8 : (int)(p.N - c);
       for (int e = 0; e < n_here; ++e) {
@@ -127,9 +126,6 @@ __global__ __launch_bounds__(kThreads) void k_combine_epi(GemmParams p) {
         dg[e >> 1] |= dgv << (16 * (e & 1));
         du[e >> 1] |= duv << (16 * (e & 1));
         av[e >> 1] |= aa << (16 * (e & 1));
-        if (p.dGT) p.dGT[(c + e) * p.ld_t + m] = (uint16_t)dgv;
-        if (p.dUT) p.dUT[(c + e) * p.ld_t + m] = (uint16_t)duv;
-        if (p.aT) p.aT[(c + e) * p.ld_t + m] = (uint16_t)aa;
       }
       if (p.dG) store8(p.dG + m * p.ld_d + c, c, p.N, dg);
       if (p.dU) store8(p.dU + m * p.ld_d + c, c, p.N, du);
@@ -243,19 +239,44 @@ __global__ __launch_bounds__(kThreads) void k_add_lanes(const uint16_t *G, int64
 }
 
 // dst [C, R] = src [R, C]^T through a 64 x 64 LDS tile.
+// dst [C, R] = transpose of src [R, C] in 64 x 64 tiles through LDS: 16-byte
+// row-segment loads and 16-byte column-segment stores (8 threads cover one
+// 128-byte segment), element by element only at ragged edges.  Both leading
+// dimensions are multiples of 8 elements and both bases 16-byte aligned.
 __global__ __launch_bounds__(kThreads) void k_transpose(const uint16_t *src, int64_t lds_, int64_t R, int64_t C,
                                                         uint16_t *dst, int64_t ldd) {
-  __shared__ uint16_t tile[64][65];
+  __shared__ __attribute__((aligned(16))) uint16_t tile[64][72];  // 144-byte rows: 16-byte aligned chunks
   const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int i = ty; i < 64; i += kThreads / 64) {
-    const int64_t r = r0 + i, c = c0 + tx;
-    tile[i][tx] = (r < R && c < C) ? src[r * lds_ + c] : (uint16_t)0;
+  const int t8 = threadIdx.x >> 3, cc = threadIdx.x & 7;
+  for (int j = 0; j < 64; j += kThreads / 8) {
+    const int r = t8 + j;
+    const int64_t gr = r0 + r, gc = c0 + 8 * cc;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (gr < R && gc + 8 <= C) {
+      v = *reinterpret_cast<const uint4 *>(src + gr * lds_ + gc);
+    } else if (gr < R) {
+      uint16_t h[8];
+      for (int e = 0; e < 8; ++e) h[e] = gc + e < C ? src[gr * lds_ + gc + e] : (uint16_t)0;
+      v = make_uint4(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16), h[4] | ((uint32_t)h[5] << 16),
+                     h[6] | ((uint32_t)h[7] << 16));
+    }
+    *reinterpret_cast<uint4 *>(&tile[r][8 * cc]) = v;
   }
   __syncthreads();
-  for (int i = ty; i < 64; i += kThreads / 64) {
-    const int64_t c = c0 + i, r = r0 + tx;
-    if (c < C && r < R) dst[c * ldd + r] = tile[tx][i];
+  for (int j = 0; j < 64; j += kThreads / 8) {
+    const int oc = t8 + j;  // source column = destination row within the tile
+    const int64_t drow = c0 + oc, dcol = r0 + 8 * cc;
+    if (drow >= C) continue;
+    uint16_t h[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) h[e] = tile[8 * cc + e][oc];
+    if (dcol + 8 <= R) {
+      *reinterpret_cast<uint4 *>(dst + drow * ldd + dcol) =
+          make_uint4(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16), h[4] | ((uint32_t)h[5] << 16),
+                     h[6] | ((uint32_t)h[7] << 16));
+    } else {
+      for (int e = 0; dcol + e < R; ++e) dst[drow * ldd + dcol + e] = h[e];
+    }
   }
 }
 

@@ -503,7 +503,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_nn(GemmParams p) {
         }
       } else if constexpr (EPI == EPI_DSILU) {
         // dA at (m, n = i) with the saved g, u: dU = bf16(dA s), dG = bf16((dA u) s'),
-        // a = bf16(s u); written row-major [M, I] and transposed [I, M].
+        // a = bf16(s u); written row-major [M, I].
         if (m < p.M) {
           const int q = (rt * MT + t) * 2;
 #pragma unroll
@@ -526,9 +526,6 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_nn(GemmParams p) {
             const uint16_t a = f2bf(s * u);
             if (p.dG) p.dG[m * p.ld_d + i] = dg;
             if (p.dU) p.dU[m * p.ld_d + i] = du;
-            if (p.dGT) p.dGT[i * p.ld_t + m] = dg;
-            if (p.dUT) p.dUT[i * p.ld_t + m] = du;
-            if (p.aT) p.aT[i * p.ld_t + m] = a;
             if (p.a_rm) p.a_rm[m * p.ld_d + i] = a;
           }
         }

@@ -28,13 +28,11 @@ struct GemmParams {
   // EPI_ACT: a = bf16(silu(C0) * C1)
   uint16_t *act_out;
   int64_t ld_act;
-  // EPI_DSILU: saved g, u [M, N]; outputs dG, dU, a row-major and transposed
+  // EPI_DSILU: saved g, u [M, N]; outputs dG, dU, a row-major
   const uint16_t *sg, *su;
   int64_t ld_gu;
   uint16_t *dG, *dU, *a_rm;
   int64_t ld_d;
-  uint16_t *dGT, *dUT, *aT;
-  int64_t ld_t;
   // EPI_DX (combine only): dx = bf16(G + U) of the two lanes; C[0], C[1] keep the lanes when set
   uint16_t *dx;
   int64_t lddx;
