@@ -23,6 +23,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense BF16 matrix peak, published
 METRIC = "FFN fwd & fwd+bwd µs + HBM GB/s, H=4096 I=12288 BF16 M=1/8/32"
 H, I = 4096, 12288
 BF = 2
@@ -46,6 +47,7 @@ def kernel_bytes(name: str, M: int) -> int | None:
     W = H * I * BF
     act_mi, act_mh = M * I * BF, M * H * BF
     table = {
+        "gate/up + act": 2 * W + act_mh + 3 * act_mi,            # W_gate, W_up, x -> g, u, a
         "gate/up tree GEMM": 2 * W + act_mh + 2 * act_mi,        # W_gate, W_up, x -> g, u
         "down tree GEMM": W + act_mi + act_mh,                    # W_down, a -> y
         "dA tree GEMM": W + act_mh + act_mi,                      # W_down, dY -> dA
@@ -59,36 +61,49 @@ def kernel_bytes(name: str, M: int) -> int | None:
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ffn_train_step_M32_hbm_traffic.md")
 
 
-def sources_digest() -> str:
-    """sha256 over the kernel sources (name then bytes, sorted by path)."""
-    import glob
+# the source file of each timed kernel; its digest and the shared headers'
+# digests must match the ones recorded with the counters
+KERNEL_SOURCE = {
+    "gate/up + act": "dgf_gu.hip",
+    "gate/up tree GEMM": "dgf_xs.hip",
+    "down tree GEMM": "dgf_xs.hip",
+    "dA tree GEMM": "dgf_xs.hip",
+    "dX lanes tree GEMM": "dgf_xs.hip",
+    "dW_gate/dW_up tree GEMM": "dgf_gemm.hip",
+    "dW_down tree GEMM": "dgf_gemm.hip",
+}
+SHARED_HEADERS = ("dgf_device.hpp", "dgf_kernels.hpp")
+
+
+def source_digest(name: str) -> str:
     import hashlib
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "deterministic_gated_ffn_amd", "csrc")
-    for path in sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.hpp"))):
-        h.update(os.path.basename(path).encode())
-        with open(path, "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()
+    with open(os.path.join(ROOT, "deterministic_gated_ffn_amd", "csrc", name), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
 
 
 def measured_traffic(kernel: str) -> int | None:
     """HBM bytes per launch of `kernel` from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
-    summary, or None when it has no figure or the kernel sources changed since."""
+    summary, or None when it has no figure or the kernel's source (or a shared
+    header) changed since the counters were taken."""
     try:
         text = open(TRAFFIC_FILE).read()
     except OSError:
         return None
-    figures, digest = {}, None
+    figures, digests = {}, {}
     for line in text.splitlines():
         if line.startswith("traffic: "):
             name, _, value = line[len("traffic: "):].rpartition(" = ")
             figures[name] = int(value)
-        elif line.startswith("sources_sha256: "):
-            digest = line.split(":", 1)[1].strip()
-    if digest != sources_digest():
+        elif line.startswith("source_sha256: "):
+            name, _, value = line[len("source_sha256: "):].rpartition(" = ")
+            digests[name] = value.strip()
+    src = KERNEL_SOURCE.get(kernel)
+    if src is None or kernel not in figures:
         return None
-    return figures.get(kernel)
+    for f in (src,) + SHARED_HEADERS:
+        if digests.get(f) != source_digest(f):
+            return None
+    return figures[kernel]
 
 
 def main():
@@ -230,10 +245,46 @@ def main():
         result["forward"] = fwd
         result["fwd_bwd_us"] = round(ms_step * 1e3, 2)
 
+    if not args.quick:
+        result["long_sequence"] = long_sequence(W[0])
+
     if not args.no_cpu_baseline and not args.quick:
         result["cpu_baseline"] = cpu_baseline(M)
 
     print(json.dumps(result), flush=True)
+
+
+def long_sequence(weights, M: int = 4096, steps: int = 5, warmup: int = 2) -> dict:
+    """The compute-bound shape: fwd+bwd at M=4096 tokens (8 sequences x 512),
+    timed over `steps` steps; 18 M H I flops per step (nine products)."""
+    import torch
+    from deterministic_gated_ffn_amd import binding as dgf
+    from deterministic_gated_ffn_amd import inputs
+
+    wg, wu, wd = weights
+    x_c, dy_c = inputs.activations(M)
+    x, dy = x_c.cuda(), dy_c.cuda()
+
+    def step():
+        y, g, u = dgf.ffn_fwd(x, wg, wu, wd, training=True)
+        return dgf.ffn_bwd(dy, x, g, u, wg, wu, wd)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    flops = 18 * M * H * I
+    tflops = flops / (ms * 1e-3) / 1e12
+    print(f"[bench] fwd+bwd M={M}: {ms:.3f} ms, {tflops:.1f} TFLOP/s", file=sys.stderr, flush=True)
+    return {"M": M, "ms_per_step": round(ms, 4), "flops_per_step": flops, "TFLOPs": round(tflops, 2),
+            "peak_TFLOPs": BF16_MFMA_PEAK_TFLOPS, "frac_mfma_peak": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
+            "steps": steps}
 
 
 def cpu_baseline(M: int) -> dict:
