@@ -371,3 +371,50 @@ def test_long_sequence_sampled_vs_oracle(qwen_weights):
     for k in ("dW_gate", "dW_up"):
         assert fp64.rel_l2(inputs.bits(r[k])[cols], fs[k]) <= 1e-2, k
     assert fp64.rel_l2(inputs.bits(r["dW_down"])[:, cols], fs["dW_down"]) <= 1e-2
+
+
+def test_token_shard_weight_gradients(qwen_weights):
+    # Token (context-parallel) shards of the weight gradients.  The pages
+    # gather whole token sequences before the weight-gradient GEMMs so that
+    # their K tree is the unsharded one (PR #325, section "Design").  K = M is
+    # the token axis, so 512-token shards of the M=4096 case are 8-leaf
+    # subtrees of that tree: per-shard backward passes combined with the
+    # balanced tree reproduce the unsharded weight gradients bit for bit.
+    _, (wg, wu, wd) = qwen_weights
+    M, S = 4096, 8
+    x, dy = (t.cuda() for t in inputs.activations(M))
+    y, g, u = dgf.ffn_fwd(x, wg, wu, wd, training=True)
+    full = dgf.ffn_bwd(dy, x, g, u, wg, wu, wd)
+    Ms = M // S
+    parts = {k: [] for k in ("dW_gate", "dW_up", "dW_down")}
+    for r in range(S):
+        sl = slice(r * Ms, (r + 1) * Ms)
+        br = dgf.ffn_bwd(dy[sl], x[sl], g[sl], u[sl], wg, wu, wd)
+        # dX rows are local to their tokens
+        assert (inputs.bits(br["dX"]) == inputs.bits(full["dX"][sl])).all()
+        for k in parts:
+            parts[k].append(br[k].contiguous())
+    for k, ps in parts.items():
+        got = dgf.tree_combine(ps)
+        torch.cuda.synchronize()
+        gb, rb = inputs.bits(got), inputs.bits(full[k].contiguous())
+        assert int((gb != rb).sum()) == 0, f"{k}: {(gb != rb).sum()} mismatches vs unsharded"
+
+
+def test_sub_leaf_token_shards_need_the_gather():
+    # Shards smaller than one 64-token leaf are not subtrees: combining their
+    # partial weight gradients rounds each part to BF16 on its own and differs
+    # from the unsharded leaf, which is why the tokens are gathered first
+    # (PR #325, section "Design"); the gathered tokens give the unsharded
+    # result.  Checked against the oracle.
+    rng = np.random.default_rng(7)
+    M, H, I = 32, 64, 48
+    dg, x = rnd(rng, (M, I)), rnd(rng, (M, H))
+    full = oracle.gemm_tree(dg, x, "TN")
+    parts = [oracle.gemm_tree(np.ascontiguousarray(dg[r * 8:(r + 1) * 8]), np.ascontiguousarray(x[r * 8:(r + 1) * 8]), "TN")
+             for r in range(4)]
+    combined = oracle.tree_combine(parts).reshape(full.shape)
+    assert (combined != full).sum() > 0  # per-shard rounding changes the result
+    got = dgf.gemm_tree("TN", dev(dg), dev(x))  # the gathered tokens: one leaf over all 32
+    torch.cuda.synchronize()
+    assert_bitwise(got, full, "gathered dW")
