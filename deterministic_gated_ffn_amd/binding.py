@@ -35,6 +35,7 @@ SIGNATURES = {
                          _P, _P, _P, _I64, _P, _I64, _P, _I64, _P, _I64,
                          _I64, _I64, _I64, _P, _SZ, _P]),
     "dgf_tree_combine": (_I, [ctypes.POINTER(_P), _I, _P, _I64, _P]),
+    "dgf_tree_combine_typed": (_I, [ctypes.POINTER(_P), _I, _P, _I64, _I, _P]),
     "dgf_gemm_tree_workspace": (_SZ, [_I, _I64, _I64, _I64]),
     "dgf_gemm_tree": (_I, [_I, _P, _I64, _P, _I64, _P, _I64, _I64, _I64, _I64, _P, _SZ, _P]),
     "dgf_act_fwd": (_I, [_P, _P, _P, _I64, _P]),
@@ -158,25 +159,37 @@ def ffn_bwd(dy, x, g, u, w_gate, w_up, w_down, lanes: bool = False, stream=None)
     return r
 
 
+DGF_BF16, DGF_FP16, DGF_FP32 = 0, 1, 2
+_COMBINE_DTYPES = {torch.bfloat16: DGF_BF16, torch.float16: DGF_FP16, torch.float32: DGF_FP32}
+
+
 def tree_combine(parts, out=None, stream=None):
-    """Balanced BF16 combine of S in {1,2,4,8} equally sized tensors (rank order)."""
+    """Balanced combine of S in {1,2,4,8} equally sized tensors (rank order);
+    BF16, FP16 or FP32, all parts of one dtype."""
     L = load()
     parts = list(parts)
     n = parts[0].numel()
+    dt = parts[0].dtype
+    if dt not in _COMBINE_DTYPES:
+        raise ValueError(f"tree_combine takes bfloat16, float16 or float32, not {dt}")
     for t in parts:
-        if t.dtype != torch.bfloat16 or not t.is_cuda or t.numel() != n or not t.is_contiguous():
-            raise ValueError("parts must be contiguous GPU bfloat16 tensors of one size")
+        if t.dtype != dt or not t.is_cuda or t.numel() != n or not t.is_contiguous():
+            raise ValueError("parts must be contiguous GPU tensors of one dtype and size")
     out = out if out is not None else torch.empty_like(parts[0])
     arr = (ctypes.c_void_p * len(parts))(*[t.data_ptr() for t in parts])
-    _check(L.dgf_tree_combine(arr, len(parts), out.data_ptr(), n, _stream(stream)), "dgf_tree_combine")
+    if dt == torch.bfloat16:
+        _check(L.dgf_tree_combine(arr, len(parts), out.data_ptr(), n, _stream(stream)), "dgf_tree_combine")
+    else:
+        _check(L.dgf_tree_combine_typed(arr, len(parts), out.data_ptr(), n, _COMBINE_DTYPES[dt], _stream(stream)),
+               "dgf_tree_combine_typed")
     return out
 
 
-def tree_combine_ptrs(ptrs, S: int, out_ptr: int, n: int, stream=None):
+def tree_combine_ptrs(ptrs, S: int, out_ptr: int, n: int, stream=None, dtype: int = DGF_BF16):
     """Raw-pointer form (offset or unaligned views)."""
     L = load()
     arr = (ctypes.c_void_p * len(ptrs))(*ptrs)
-    _check(L.dgf_tree_combine(arr, S, out_ptr, n, _stream(stream)), "dgf_tree_combine")
+    _check(L.dgf_tree_combine_typed(arr, S, out_ptr, n, dtype, _stream(stream)), "dgf_tree_combine_typed")
 
 
 def gemm_tree(layout: str, A, B, out=None, stream=None):

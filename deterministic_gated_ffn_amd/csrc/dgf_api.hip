@@ -618,6 +618,27 @@ dgf_status dgf_tree_combine(const void *const *parts, int S, void *out, int64_t 
   return ok();
 }
 
+dgf_status dgf_tree_combine_typed(const void *const *parts, int S, void *out, int64_t n, int dtype, void *stream) {
+  if (n < 0) return fail(DGF_EINVAL, "negative length %lld", (long long)n);
+  if (dtype != DGF_BF16 && dtype != DGF_FP16 && dtype != DGF_FP32) return fail(DGF_EINVAL, "unknown dtype %d", dtype);
+  if (!(S == 1 || S == 2 || S == 4 || S == 8)) return fail(DGF_EUNSUPPORTED, "S=%d: only 1, 2, 4 or 8 parts", S);
+  if (n == 0) return ok();
+  if (!parts) return fail(DGF_EINVAL, "parts is NULL");
+  if (!out) return fail(DGF_EINVAL, "out is NULL");
+  const uintptr_t align = dtype == DGF_FP32 ? 4 : 2;
+  for (int i = 0; i < S; ++i)
+    if (!parts[i]) return fail(DGF_EINVAL, "parts[%d] is NULL", i);
+  if (((uintptr_t)out & (align - 1)) != 0) return fail(DGF_EINVAL, "out is not %d-byte aligned", (int)align);
+  for (int i = 0; i < S; ++i)
+    if (((uintptr_t)parts[i] & (align - 1)) != 0) return fail(DGF_EINVAL, "parts[%d] is not %d-byte aligned", i, (int)align);
+  static_assert(DGF_BF16 == DGF_COMBINE_BF16 && DGF_FP16 == DGF_COMBINE_FP16 && DGF_FP32 == DGF_COMBINE_FP32,
+                "dtype codes");
+  hipStream_t s = (hipStream_t)stream;
+  DGF_TRY(hip_check(timed(s, "tree_combine", [&] { return launch_combine_typed(parts, S, out, n, dtype, s); }),
+                    "tree_combine"));
+  return ok();
+}
+
 size_t dgf_gemm_tree_workspace(int layout, int64_t M, int64_t N, int64_t K) {
   if (M <= 0 || N <= 0 || K <= 0) return 0;
   return gemm_ws_bytes(layout, M, N, K);

@@ -182,6 +182,79 @@ __global__ __launch_bounds__(kThreads) void k_combine_scalar(Parts parts, uint16
   }
 }
 
+// FP16 and FP32 parts: the same balanced rank tree; an FP16 node adds its two
+// children in FP32 and rounds the sum to FP16 (nearest even), an FP32 node is
+// one FP32 addition (PR #357, "Determinism and correctness").
+template <int DT>
+struct CElem;
+template <>
+struct CElem<DGF_COMBINE_FP16> {
+  using T = uint16_t;
+  static constexpr int PER16 = 8;
+  static __device__ __forceinline__ float ld(T v) { return (float)__builtin_bit_cast(_Float16, v); }
+  static __device__ __forceinline__ T rnd(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+};
+template <>
+struct CElem<DGF_COMBINE_FP32> {
+  using T = float;
+  static constexpr int PER16 = 4;
+  static __device__ __forceinline__ float ld(T v) { return v; }
+  static __device__ __forceinline__ T rnd(float f) { return f; }
+};
+
+struct PartsV {
+  const void *p[8];
+};
+
+template <int S, int DT>
+__device__ __forceinline__ typename CElem<DT>::T combine_el(const PartsV &parts, int64_t i) {
+  using E = CElem<DT>;
+  float r[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) r[s] = E::ld(reinterpret_cast<const typename E::T *>(parts.p[s])[i]);
+#pragma unroll
+  for (int width = S; width > 1; width >>= 1)
+#pragma unroll
+    for (int j = 0; j < width / 2; ++j) r[j] = E::ld(E::rnd(r[2 * j] + r[2 * j + 1]));
+  return E::rnd(r[0]);
+}
+
+// 16 bytes per thread and part (8 FP16 or 4 FP32 elements).
+template <int S, int DT>
+__global__ __launch_bounds__(kThreads) void k_combine_vec_t(PartsV parts, void *out, int64_t nvec) {
+  using E = CElem<DT>;
+  constexpr int P = E::PER16;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nvec; i += (int64_t)gridDim.x * kThreads) {
+    float r[S][P];
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const uint4 v = reinterpret_cast<const uint4 *>(parts.p[s])[i];
+      typename E::T el[P];
+      __builtin_memcpy(el, &v, 16);
+#pragma unroll
+      for (int e = 0; e < P; ++e) r[s][e] = E::ld(el[e]);
+    }
+#pragma unroll
+    for (int width = S; width > 1; width >>= 1)
+#pragma unroll
+      for (int j = 0; j < width / 2; ++j)
+#pragma unroll
+        for (int e = 0; e < P; ++e) r[j][e] = E::ld(E::rnd(r[2 * j][e] + r[2 * j + 1][e]));
+    typename E::T o[P];
+#pragma unroll
+    for (int e = 0; e < P; ++e) o[e] = E::rnd(r[0][e]);
+    uint4 v;
+    __builtin_memcpy(&v, o, 16);
+    reinterpret_cast<uint4 *>(out)[i] = v;
+  }
+}
+
+template <int S, int DT>
+__global__ __launch_bounds__(kThreads) void k_combine_scalar_t(PartsV parts, void *out, int64_t begin, int64_t n) {
+  for (int64_t i = begin + (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += (int64_t)gridDim.x * kThreads)
+    reinterpret_cast<typename CElem<DT>::T *>(out)[i] = combine_el<S, DT>(parts, i);
+}
+
 // out[m][n] = balanced combine over S partial roots (the top levels of the
 // tree above the workgroups' K pieces); 8 elements per thread.
 template <int S>
@@ -321,6 +394,47 @@ hipError_t launch_combine(const uint16_t *const *parts, int S, uint16_t *out, in
     }
   }
   return hipGetLastError();
+}
+
+template <int DT>
+hipError_t launch_combine_t(const void *const *parts, int S, void *out, int64_t n, hipStream_t s) {
+  constexpr int P = CElem<DT>::PER16;
+  PartsV pv{};
+  bool aligned = ((uintptr_t)out & 15) == 0;
+  for (int i = 0; i < S; ++i) {
+    pv.p[i] = parts[i];
+    aligned = aligned && (((uintptr_t)parts[i] & 15) == 0);
+  }
+  const int64_t nvec = aligned ? n / P : 0;
+  if (nvec > 0) {
+    const dim3 g(grid_for(nvec, 1));
+    switch (S) {
+      case 1: hipLaunchKernelGGL((k_combine_vec_t<1, DT>), g, dim3(kThreads), 0, s, pv, out, nvec); break;
+      case 2: hipLaunchKernelGGL((k_combine_vec_t<2, DT>), g, dim3(kThreads), 0, s, pv, out, nvec); break;
+      case 4: hipLaunchKernelGGL((k_combine_vec_t<4, DT>), g, dim3(kThreads), 0, s, pv, out, nvec); break;
+      default: hipLaunchKernelGGL((k_combine_vec_t<8, DT>), g, dim3(kThreads), 0, s, pv, out, nvec); break;
+    }
+  }
+  const int64_t begin = nvec * P;
+  if (begin < n) {
+    const dim3 g(grid_for(n - begin, 1));
+    switch (S) {
+      case 1: hipLaunchKernelGGL((k_combine_scalar_t<1, DT>), g, dim3(kThreads), 0, s, pv, out, begin, n); break;
+      case 2: hipLaunchKernelGGL((k_combine_scalar_t<2, DT>), g, dim3(kThreads), 0, s, pv, out, begin, n); break;
+      case 4: hipLaunchKernelGGL((k_combine_scalar_t<4, DT>), g, dim3(kThreads), 0, s, pv, out, begin, n); break;
+      default: hipLaunchKernelGGL((k_combine_scalar_t<8, DT>), g, dim3(kThreads), 0, s, pv, out, begin, n); break;
+    }
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_typed(const void *const *parts, int S, void *out, int64_t n, int dtype, hipStream_t s) {
+  switch (dtype) {
+    case DGF_COMBINE_BF16: return launch_combine((const uint16_t *const *)parts, S, (uint16_t *)out, n, s);
+    case DGF_COMBINE_FP16: return launch_combine_t<DGF_COMBINE_FP16>(parts, S, out, n, s);
+    case DGF_COMBINE_FP32: return launch_combine_t<DGF_COMBINE_FP32>(parts, S, out, n, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_combine_2d(const uint16_t *part, int64_t part_stride, int64_t ldp, int S, uint16_t *out, int64_t ldo,

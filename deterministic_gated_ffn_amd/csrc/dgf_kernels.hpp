@@ -79,6 +79,9 @@ hipError_t launch_act_fwd(const uint16_t *g, const uint16_t *u, uint16_t *a, int
 hipError_t launch_act_bwd(const uint16_t *da, const uint16_t *g, const uint16_t *u, uint16_t *dg, uint16_t *du,
                           uint16_t *a, int64_t n, hipStream_t s);
 hipError_t launch_combine(const uint16_t *const *parts, int S, uint16_t *out, int64_t n, hipStream_t s);
+// the same rank tree for BF16, FP16 or FP32 parts (dtype one of DGF_COMBINE_*)
+enum { DGF_COMBINE_BF16 = 0, DGF_COMBINE_FP16 = 1, DGF_COMBINE_FP32 = 2 };
+hipError_t launch_combine_typed(const void *const *parts, int S, void *out, int64_t n, int dtype, hipStream_t s);
 // out [M, N] (ldo) = balanced combine over S partials part[s] [M, N] (ldp),
 // part[s] = part + s * part_stride
 hipError_t launch_combine_2d(const uint16_t *part, int64_t part_stride, int64_t ldp, int S, uint16_t *out, int64_t ldo,

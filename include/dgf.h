@@ -139,6 +139,20 @@ dgf_status dgf_ffn_bwd(const void *dy, int64_t lddy,
 dgf_status dgf_tree_combine(const void *const *parts, int S, void *out, int64_t n, void *stream);
 
 /*
+ * The same fixed rank tree for other element types (PR #357, section
+ * "Determinism and correctness": FP32, FP16 and BF16 follow one rank tree).
+ * dtype DGF_BF16 is dgf_tree_combine; DGF_FP16: every node adds its two FP16
+ * children in FP32 and rounds the sum to FP16 (nearest even, IEEE subnormals
+ * kept, overflow to infinity); DGF_FP32: every node is one FP32 addition.
+ * parts/out as for dgf_tree_combine, holding n elements of the dtype; every
+ * pointer aligned to the element size (else DGF_EINVAL); 16-byte aligned
+ * buffers take the vector path (PR #357, section "Design").  Unknown dtype:
+ * DGF_EINVAL.
+ */
+enum { DGF_BF16 = 0, DGF_FP16 = 1, DGF_FP32 = 2 };
+dgf_status dgf_tree_combine_typed(const void *const *parts, int S, void *out, int64_t n, int dtype, void *stream);
+
+/*
  * Diagnostic entry points (stage isolation and shard emulation; the FFN
  * entry points above are composed of the same kernels).
  *

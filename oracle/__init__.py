@@ -55,6 +55,12 @@ def lib():
         L.oracle_gemm_tree.argtypes = [P, I64, I64, P, I64, I64, P, I64, I64, I64, I64]
         L.oracle_tree_combine.restype = ctypes.c_int
         L.oracle_tree_combine.argtypes = [ctypes.POINTER(P), ctypes.c_int, P, I64]
+        L.oracle_tree_combine_typed.restype = ctypes.c_int
+        L.oracle_tree_combine_typed.argtypes = [ctypes.POINTER(P), ctypes.c_int, P, I64, ctypes.c_int]
+        L.oracle_f16_to_f32.restype = ctypes.c_float
+        L.oracle_f16_to_f32.argtypes = [ctypes.c_uint16]
+        L.oracle_f32_to_f16.restype = ctypes.c_uint16
+        L.oracle_f32_to_f16.argtypes = [ctypes.c_float]
         for f in ("oracle_sigma", "oracle_silu", "oracle_dsilu"):
             getattr(L, f).restype = ctypes.c_float
             getattr(L, f).argtypes = [ctypes.c_float]
@@ -151,6 +157,32 @@ def tree_combine(parts) -> np.ndarray:
     if rc != 0:
         raise ValueError(f"unsupported part count {len(parts)}")
     return out
+
+
+_DTYPES = {"bf16": (0, np.uint16), "fp16": (1, np.uint16), "fp32": (2, np.float32)}
+
+
+def tree_combine_typed(parts, dtype: str) -> np.ndarray:
+    """The balanced rank tree over S parts in BF16, FP16 (bit patterns as
+    uint16) or FP32 (float32 arrays)."""
+    code, np_t = _DTYPES[dtype]
+    parts = [np.ascontiguousarray(np.asarray(p).astype(np_t, copy=False)).ravel() for p in parts]
+    n = parts[0].size
+    assert all(p.size == n for p in parts)
+    arr = (ctypes.c_void_p * len(parts))(*[p.ctypes.data for p in parts])
+    out = np.zeros(n, np_t)
+    rc = lib().oracle_tree_combine_typed(arr, len(parts), out.ctypes.data, n, code)
+    if rc != 0:
+        raise ValueError(f"unsupported part count {len(parts)} or dtype {dtype}")
+    return out
+
+
+def f16_to_f32(h: int) -> np.float32:
+    return np.float32(lib().oracle_f16_to_f32(int(h)))
+
+
+def f32_to_f16(x) -> int:
+    return int(lib().oracle_f32_to_f16(ctypes.c_float(float(x))))
 
 
 # ------------------------------------------------------------------ activation

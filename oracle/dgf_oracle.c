@@ -312,6 +312,95 @@ int oracle_tree_combine(const bf16_t *const *parts, int S, bf16_t *out, int64_t 
     return 0;
 }
 
+/* ------------------------------------------------------------ FP16 and FP32 combine */
+
+/* The same fixed rank tree in FP16 and FP32 (PR #357, "Determinism and
+ * correctness": FP32, FP16 and BF16 follow one rank tree).  An FP16 node adds
+ * its two children in FP32 and rounds the sum to FP16 (nearest even), as the
+ * BF16 node does; an FP32 node is one FP32 addition. */
+
+typedef uint16_t f16_t;
+
+/* IEEE binary16 -> FP32 (exact): sign, 5-bit exponent (bias 15), 10-bit
+ * fraction; exponent 0 holds subnormals (fraction * 2^-24). */
+static float f16_to_f32(f16_t h)
+{
+    int sign = (h >> 15) & 1, e = (h >> 10) & 0x1F, f = h & 0x3FF;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -24);
+    else if (e == 31)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexp((double)(f | 0x400), e - 25);
+    return (float)(sign ? -v : v);
+}
+
+/* FP32 -> IEEE binary16, round to nearest even.  The magnitude is split into
+ * the FP16 step q at its binade (2^(e-10) for normals, 2^-24 below 2^-14), the
+ * quotient |x| / q (exact in double) is rounded to an integer with ties to
+ * even, and the integer is re-encoded; 65520 and above overflow to infinity. */
+static f16_t f32_to_f16(float x)
+{
+    uint32_t u;
+    memcpy(&u, &x, 4);
+    f16_t sign = (f16_t)((u >> 16) & 0x8000u);
+    if (isnan(x)) return (f16_t)(sign | 0x7E00u);
+    double a = fabs((double)x);
+    if (a >= 65520.0) return (f16_t)(sign | 0x7C00u);
+    int e = a > 0 ? ilogb(a) : -25;          /* binade of |x| */
+    if (e < -14) e = -14;                     /* subnormal range shares the 2^-24 step */
+    double q = ldexp(1.0, e - 10);
+    double m = a / q;                         /* exact: a power-of-two divisor */
+    double r = floor(m), frac = m - r;
+    if (frac > 0.5 || (frac == 0.5 && fmod(r, 2.0) != 0.0)) r += 1.0;
+    /* r in [0, 2048]; 2048 carries into the next binade */
+    if (r >= 2048.0) { r = 1024.0; e += 1; }
+    if (e == -14 && r < 1024.0) return (f16_t)(sign | (f16_t)r);        /* subnormal (or zero) */
+    return (f16_t)(sign | (f16_t)((e + 15) << 10) | (f16_t)((int)r - 1024));
+}
+
+static f16_t node_add_f16(f16_t l, f16_t r)
+{
+    float s = f16_to_f32(l) + f16_to_f32(r);
+    return f32_to_f16(s);
+}
+
+static f16_t combine_range_f16(const f16_t *const *parts, int64_t i, int lo, int hi)
+{
+    if (hi - lo == 1) return parts[lo][i];
+    int mid = lo + (hi - lo) / 2;
+    return node_add_f16(combine_range_f16(parts, i, lo, mid), combine_range_f16(parts, i, mid, hi));
+}
+
+static float combine_range_f32(const float *const *parts, int64_t i, int lo, int hi)
+{
+    if (hi - lo == 1) return parts[lo][i];
+    int mid = lo + (hi - lo) / 2;
+    return combine_range_f32(parts, i, lo, mid) + combine_range_f32(parts, i, mid, hi);
+}
+
+/* dtype 0: BF16, 1: FP16, 2: FP32 (element bit patterns in and out) */
+int oracle_tree_combine_typed(const void *const *parts, int S, void *out, int64_t n, int dtype)
+{
+    if (!(S == 1 || S == 2 || S == 4 || S == 8)) return 2;
+    if (dtype == 0) return oracle_tree_combine((const bf16_t *const *)parts, S, (bf16_t *)out, n);
+    if (dtype == 1) {
+#pragma omp parallel for schedule(static)
+        for (int64_t i = 0; i < n; ++i) ((f16_t *)out)[i] = combine_range_f16((const f16_t *const *)parts, i, 0, S);
+        return 0;
+    }
+    if (dtype == 2) {
+#pragma omp parallel for schedule(static)
+        for (int64_t i = 0; i < n; ++i) ((float *)out)[i] = combine_range_f32((const float *const *)parts, i, 0, S);
+        return 0;
+    }
+    return 3;
+}
+
+float oracle_f16_to_f32(uint16_t h) { return f16_to_f32(h); }
+uint16_t oracle_f32_to_f16(float x) { return f32_to_f16(x); }
+
 /* ------------------------------------------------------------ activation */
 
 /* e = exp(-g) rounded once to FP32 (computed in double, then rounded). */

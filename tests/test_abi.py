@@ -27,7 +27,7 @@ def lib():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for required in ("dgf_ffn_fwd", "dgf_ffn_bwd", "dgf_tree_combine", "dgf_gemm_tree",
+    for required in ("dgf_ffn_fwd", "dgf_ffn_bwd", "dgf_tree_combine", "dgf_tree_combine_typed", "dgf_gemm_tree",
                      "dgf_act_fwd", "dgf_act_bwd", "dgf_last_error"):
         assert required in names
 
@@ -105,6 +105,18 @@ def test_combine_validation(lib):
     assert lib.dgf_tree_combine(arr8, 8, FAKE, -1, None) == 1
     arr2 = (ctypes.c_void_p * 2)(FAKE, None)
     assert lib.dgf_tree_combine(arr2, 2, FAKE, 10, None) == 1
+
+
+def test_typed_combine_validation(lib):
+    arr4 = (ctypes.c_void_p * 4)(*([FAKE] * 4))
+    assert lib.dgf_tree_combine_typed(arr4, 4, FAKE, 0, binding.DGF_FP32, None) == 0  # n = 0: no launch
+    assert lib.dgf_tree_combine_typed(arr4, 4, FAKE, 10, 7, None) == 1
+    assert b"dtype" in lib.dgf_last_error()
+    assert lib.dgf_tree_combine_typed(arr4, 3, FAKE, 10, binding.DGF_FP16, None) == 2
+    assert lib.dgf_tree_combine_typed(arr4, 4, FAKE + 2, 10, binding.DGF_FP32, None) == 1  # FP32 needs 4-byte alignment
+    assert b"aligned" in lib.dgf_last_error()
+    assert lib.dgf_tree_combine_typed(arr4, 4, FAKE + 1, 10, binding.DGF_FP16, None) == 1
+    assert lib.dgf_tree_combine_typed(arr4, 4, None, 10, binding.DGF_BF16, None) == 1
 
 
 def test_gemm_validation(lib):

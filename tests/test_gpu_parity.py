@@ -176,6 +176,41 @@ def test_tree_combine(S, n):
     assert_bitwise(p0[0], expect, f"combine in place S={S} n={n}")
 
 
+@pytest.mark.parametrize("dtype", ["fp16", "fp32"])
+@pytest.mark.parametrize("S", [1, 2, 4, 8])
+@pytest.mark.parametrize("n", [1, 5, 8, 1000, 4099])
+def test_tree_combine_fp16_fp32(dtype, S, n):
+    # the same rank tree in FP16 and FP32, against the oracle, bitwise; values
+    # over a wide exponent range (FP16 subnormals and overflow included)
+    rng = np.random.default_rng(S * 31 + n + (7 if dtype == "fp16" else 0))
+    tdt = torch.float16 if dtype == "fp16" else torch.float32
+    if dtype == "fp16":
+        parts = [(rng.standard_normal(n) * 2.0 ** rng.integers(-26, 11, n)).astype(np.float16) for _ in range(S)]
+        raw = [p.view(np.uint16) for p in parts]
+        expect = oracle.tree_combine_typed(raw, "fp16")
+        to_dev = lambda p: torch.from_numpy(p.view(np.int16).copy()).view(torch.float16).cuda()
+        bits_of = lambda t: t.detach().cpu().view(torch.int16).numpy().view(np.uint16)
+    else:
+        parts = [(rng.standard_normal(n) * 10.0 ** rng.integers(-30, 30, n)).astype(np.float32) for _ in range(S)]
+        raw = parts
+        expect = oracle.tree_combine_typed(raw, "fp32").view(np.uint32)
+        to_dev = lambda p: torch.from_numpy(p.copy()).cuda()
+        bits_of = lambda t: t.detach().cpu().numpy().view(np.uint32)
+    got = dgf.tree_combine([to_dev(p) for p in parts])
+    torch.cuda.synchronize()
+    assert (bits_of(got) == expect).all(), f"{dtype} S={S} n={n}: {(bits_of(got) != expect).sum()} mismatches"
+    # offset views (one element in): the element path, same arithmetic
+    bufs = [torch.zeros(n + 1, dtype=tdt, device="cuda") for _ in range(S)]
+    for b, p in zip(bufs, parts):
+        b[1:] = to_dev(p)
+    out = torch.zeros(n + 1, dtype=tdt, device="cuda")
+    es = bufs[0].element_size()
+    dgf.tree_combine_ptrs([b.data_ptr() + es for b in bufs], S, out.data_ptr() + es, n,
+                          dtype=dgf.DGF_FP16 if dtype == "fp16" else dgf.DGF_FP32)
+    torch.cuda.synchronize()
+    assert (bits_of(out[1:]) == expect).all(), f"{dtype} offset S={S} n={n}"
+
+
 def test_tree_combine_hand_worked_and_errors():
     one, a = 0x3F80, 0x3B80
     vals = np.array([one, a, a, a, a, a, a, a], np.uint16)

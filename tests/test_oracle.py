@@ -177,6 +177,112 @@ def test_tree_combine_hand_worked():
         c([one, a, a])
 
 
+# ------------------------------------------------------------ FP16 / FP32 combine
+def _all_f16_values():
+    """Every finite FP16 value as (bit pattern, exact Fraction), from the format's definition."""
+    from fractions import Fraction
+    out = []
+    for h in range(0x7C00):
+        e, f = h >> 10, h & 0x3FF
+        v = Fraction(f, 1 << 24) if e == 0 else Fraction(f + 1024, 1 << 10) * (Fraction(2) ** (e - 15))
+        out.append((h, v))
+    return out
+
+
+def _rne_f16(x, table):
+    """Nearest finite FP16 to the exact rational x, ties to the even bit pattern;
+    |x| past the overflow threshold (65520) gives infinity."""
+    import bisect
+    from fractions import Fraction
+    sign = 0x8000 if x < 0 else 0
+    a = abs(x)
+    if a >= 65520:
+        return sign | 0x7C00
+    vals = [v for _, v in table]
+    i = bisect.bisect_left(vals, a)
+    if i < len(vals) and vals[i] == a:
+        return sign | table[i][0]
+    lo, hi = table[i - 1], table[i]
+    dl, dh = a - lo[1], hi[1] - a
+    pick = lo if dl < dh else hi if dh < dl else (lo if lo[0] % 2 == 0 else hi)
+    return (sign | pick[0]) if pick[0] or not sign else sign
+
+
+def test_f16_conversions_against_the_format():
+    from fractions import Fraction
+    table = _all_f16_values()
+    # FP16 -> FP32 is exact for every finite value
+    for h, v in table[::37] + table[:40] + table[-40:]:
+        assert Fraction(float(oracle.f16_to_f32(h))) == v
+        assert Fraction(float(oracle.f16_to_f32(h | 0x8000))) == -v
+    # FP32 -> FP16 is nearest-even: midpoints between neighbours, random FP32 values, overflow
+    rng = np.random.default_rng(16)
+    xs = []
+    for (h0, v0), (h1, v1) in list(zip(table[:-1], table[1:]))[::53]:
+        xs.append((v0 + v1) / 2)                 # an exact tie
+        xs.append(v0 + (v1 - v0) / 3)
+    for x in xs:
+        if Fraction(float(np.float32(x))) != x:  # keep exactly representable FP32 inputs
+            continue
+        assert oracle.f32_to_f16(float(x)) == _rne_f16(x, table), x
+    for x in rng.standard_normal(2000).astype(np.float32) * np.float32(2.0) ** rng.integers(-30, 17, 2000):
+        assert oracle.f32_to_f16(float(x)) == _rne_f16(Fraction(float(x)), table), x
+    assert oracle.f32_to_f16(65519.0) == 0x7BFF and oracle.f32_to_f16(65520.0) == 0x7C00
+    assert oracle.f32_to_f16(-(2.0 ** -25)) == 0x8000  # ties to (negative) zero
+    assert oracle.f32_to_f16(np.float32(np.inf)) == 0x7C00
+
+
+def test_f16_node_is_the_correctly_rounded_sum():
+    # FP32 holds the sum of two FP16 values closely enough that rounding it to
+    # FP16 again equals rounding the exact sum once: checked on random pairs
+    # over the whole range, subnormals included, against exact rationals.
+    from fractions import Fraction
+    table = _all_f16_values()
+    byh = dict(table)
+    rng = np.random.default_rng(61)
+    for _ in range(3000):
+        ha, hb = (int(v) for v in rng.integers(0, 0x7C00, 2))
+        sa, sb = (int(v) for v in rng.integers(0, 2, 2))
+        x, y = byh[ha] * (-1 if sa else 1), byh[hb] * (-1 if sb else 1)
+        got = int(oracle.tree_combine_typed([np.array([ha | (sa << 15)], np.uint16),
+                                             np.array([hb | (sb << 15)], np.uint16)], "fp16")[0])
+        want = _rne_f16(x + y, table)
+        if x + y == 0:  # an exact zero sum is +0 in round-to-nearest
+            want = 0x8000 if (sa and sb) else 0
+        assert got == want, (hex(ha | (sa << 15)), hex(hb | (sb << 15)))
+
+
+def test_typed_combine_tree_order_hand_worked():
+    # FP16 spacing at 2048 is 2: 2048 + 1 ties to 2048.  The balanced tree
+    # (2048 + 1) + (1 + 1) = 2048 + 2 = 2050; a left fold would stay at 2048.
+    f16 = lambda v: np.array([v], np.float16).view(np.uint16)
+    got = oracle.tree_combine_typed([f16(2048.0), f16(1.0), f16(1.0), f16(1.0)], "fp16")
+    assert got.view(np.float16)[0] == np.float16(2050.0)
+    # FP32: 2^24 + 1 ties to 2^24; balanced (2^24 + 1) + (1 + 1) = 2^24 + 2
+    f32 = lambda v: np.array([v], np.float32)
+    got = oracle.tree_combine_typed([f32(2.0 ** 24), f32(1.0), f32(1.0), f32(1.0)], "fp32")
+    assert got[0] == np.float32(2.0 ** 24 + 2)
+    # eight parts: ((p0+p1)+(p2+p3))+((p4+p5)+(p6+p7)); with p0 = 2^24 and seven
+    # ones the pairs give 2^24, 2, 2, 2 -> (2^24 + 2) + 4 = 2^24 + 6
+    got = oracle.tree_combine_typed([f32(2.0 ** 24)] + [f32(1.0)] * 7, "fp32")
+    assert got[0] == np.float32(2.0 ** 24 + 6)
+    # BF16 through the typed entry equals the BF16 combine
+    one, a = 0x3F80, 0x3B80
+    vals = [np.array([v], np.uint16) for v in (one, a, a, a, a, a, a, a)]
+    assert int(oracle.tree_combine_typed(vals, "bf16")[0]) == 0x3F83
+
+
+def test_fp32_combine_matches_numpy_pairwise():
+    # FP32 nodes are IEEE additions: the tree equals numpy's float32 adds in the tree's order
+    rng = np.random.default_rng(32)
+    for S in (1, 2, 4, 8):
+        parts = [(rng.standard_normal(500) * 10.0 ** rng.integers(-6, 7, 500)).astype(np.float32) for _ in range(S)]
+        vals = list(parts)
+        while len(vals) > 1:
+            vals = [vals[2 * j] + vals[2 * j + 1] for j in range(len(vals) // 2)]
+        assert np.array_equal(oracle.tree_combine_typed(parts, "fp32"), vals[0])
+
+
 # ------------------------------------------------------------ activation
 def test_sigma_special_values():
     assert oracle.sigma(0.0) == 0.5
