@@ -211,10 +211,40 @@ XsPlan plan_xs(int layout, int nb, int64_t M, int64_t N, int64_t K) {
   return best;
 }
 
+// Launch shape of the tiled kernel (dgf_mm.hip) for many tokens: the K tree
+// cut at the smallest depth kd whose pieces split into at most 8 lower
+// subtrees of the kernel's maximum size.  kd = -1: not applicable.
+struct MmPlan {
+  int kd = -1, up = 0, nlh = 0;
+};
+
+constexpr int64_t kMmMinM = 128;  // one full 128-token tile: below it the weights stream
+
+MmPlan plan_mm(int layout, int64_t M, int64_t K) {
+  MmPlan pl;
+  if (layout != DGF_LAYOUT_NT || M < kMmMinM) return pl;
+  const int L = leaves(K);
+  for (int kd = 0; kd <= 5 && (1 << kd) <= L; ++kd) {
+    const int lmin = L >> kd, lmax = (L + (1 << kd) - 1) >> kd;  // piece sizes
+    const int up = mm_upper_levels(lmax);
+    if (up < 0 || (1 << up) > lmin) continue;
+    pl.kd = kd;
+    pl.up = up;
+    pl.nlh = (lmax + (1 << up) - 1) >> up;
+    return pl;
+  }
+  return pl;
+}
+
 // Workspace bytes for the partial roots of one GEMM (0 when it needs none).
 size_t partial_bytes(int layout, int nb, int epi, int64_t M, int64_t N, int64_t K) {
   if (M == 0 || N == 0) return 0;
   if ((layout == DGF_LAYOUT_NT || layout == DGF_LAYOUT_TN) && epi == EPI_STORE && K <= 64) return 0;  // one-leaf kernels
+  const MmPlan mp = plan_mm(layout, M, K);
+  if (mp.kd >= 0) {
+    if (mp.kd == 0 && epi == EPI_STORE) return 0;
+    return round256((size_t)nb * ((size_t)1 << mp.kd) * M * round8(N) * 2);
+  }
   const XsPlan xp = plan_xs(layout, nb, M, N, K);
   if (xp.waves > 0) {
     if (xp.kd == 0 && epi == EPI_STORE) return 0;
@@ -241,6 +271,26 @@ dgf_status run_gemm(int layout, int nb, int epi, GemmParams p, hipStream_t s, co
   if (layout == DGF_LAYOUT_NT && epi == EPI_STORE && p.K <= 64 && (nb == 1 || p.B[1] == p.B[0]) &&
       (p.M + 63) / 64 <= 65535)
     return hip_check(timed(s, what, [&] { return launch_gemm_short(nb, p, s); }), what);
+  const MmPlan mp = plan_mm(layout, p.M, p.K);
+  if (mp.kd >= 0) {
+    p.ksplit_depth = mp.kd;
+    p.stack_slots = mp.up;
+    const bool joined = mp.kd > 0 || epi != EPI_STORE;  // roots go through the combine kernel
+    p.to_part = joined ? 1 : 0;
+    if (!joined)
+      for (int b = 0; b < nb; ++b)
+        if (!p.C[b]) return fail(DGF_EINVAL, "%s: product %d has no output", what, b);
+    if (joined) {
+      if (!partials) return fail(DGF_EWORKSPACE, "%s: no workspace for the partial roots", what);
+      p.part = partials;
+      p.ldp = round8(p.N);
+      p.part_stride = p.M * p.ldp;
+    }
+    DGF_TRY(hip_check(timed(s, what, [&] { return launch_mm(p, nb, mp.nlh, s); }), what));
+    if (joined)
+      DGF_TRY(hip_check(timed(s, join_what, [&] { return launch_combine_epi(epi, nb, p, s); }), join_what));
+    return DGF_OK;
+  }
   const XsPlan xp = plan_xs(layout, nb, p.M, p.N, p.K);
   if (xp.waves > 0) {
     p.ksplit_depth = xp.kd;

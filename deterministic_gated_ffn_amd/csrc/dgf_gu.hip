@@ -32,44 +32,6 @@ constexpr int kGuRing = 4;   // ring slots of weight units: PR - 1 units in flig
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// Depth D of leaf j in the midpoint tree over n leaves, and the number m of
-// right-child steps that end its root-to-leaf path (the merges it triggers).
-struct LeafPos {
-  int D, m;
-};
-constexpr LeafPos leaf_pos(int n, int j) {
-  int lo = 0, hi = n, D = 0, m = 0;
-  while (hi - lo > 1) {
-    const int mid = lo + (hi - lo) / 2;
-    if (j < mid) {
-      hi = mid;
-      m = 0;
-    } else {
-      lo = mid;
-      ++m;
-    }
-    ++D;
-  }
-  return LeafPos{D, m};
-}
-
-// Feed leaf J of an N-leaf subtree (N <= 8, so depth <= 3): merge it with the
-// pending left siblings its position closes, then park it at its depth; after
-// the last leaf v is the subtree root.
-template <int NP, int N, int J>
-__device__ __forceinline__ void push_leaf(uint32_t (&v)[NP], uint32_t (&st)[3][NP]) {
-  constexpr LeafPos lp = leaf_pos(N, J);
-#pragma unroll
-  for (int t = 0; t < lp.m; ++t)
-#pragma unroll
-    for (int q = 0; q < NP; ++q) v[q] = node2(st[lp.D - 1 - t][q], v[q]);
-  constexpr int d = lp.D - lp.m;
-  if constexpr (d > 0) {
-#pragma unroll
-    for (int q = 0; q < NP; ++q) st[d - 1][q] = v[q];
-  }
-}
-
 template <int MT>
 constexpr int nr_of() {
   return MT == 1 ? kGuMaxNL : 5;  // activation leaves held in registers

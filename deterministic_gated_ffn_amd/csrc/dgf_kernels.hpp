@@ -67,6 +67,14 @@ struct GuParams {
 bool gu_act_applies(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gu_act(const GuParams &p, hipStream_t stream);
 
+// Tiled tree GEMM for many tokens (dgf_mm.hip): NT, 128 x 128 output tiles
+// per workgroup, grid.z = nb << ksplit_depth; stack_slots holds the number of
+// top levels of each K piece's tree (<= 3) above lower subtrees of at most 8
+// leaves (nlh: the larger lower-subtree size, the smaller being nlh - 1).
+size_t mm_lds_bytes();
+int mm_upper_levels(int Lp);
+hipError_t launch_mm(GemmParams p, int nb, int nlh, hipStream_t stream);
+
 // Output row tiles of 16 per wave of the NT / NN tree GEMM kernel variants.
 int gemm_row_tiles(int layout, int nb, int epi);
 hipError_t launch_gemm(int layout, int nb, int epi, GemmParams p, int waves, hipStream_t stream);

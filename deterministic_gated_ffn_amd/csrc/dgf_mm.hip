@@ -1,0 +1,326 @@
+// Tiled tree GEMM for many tokens (gfx950).
+//
+// C_b[m][n] = T_K( A_b[m,:] . B_b[n,:] ): A_b [M, K] and B_b [N, K] both
+// K-contiguous, the canonical tree over K of RL-Kernel PR #325, section
+// "Design" (64-element FP32 leaves rounded to BF16, midpoint nodes adding BF16
+// children in FP32).  This is the compute-bound shape: thousands of tokens, so
+// the weights are reused across many token rows and the kernel is organised
+// around MFMA throughput rather than weight streaming.
+//
+// Work split.  A workgroup of 8 waves owns a 128 x 128 output tile (tokens x
+// outputs) for one K piece (a subtree at depth kd of the tree, as in the other
+// kernels); every wave owns 32 tokens x 64 outputs of it (8 MFMA tiles) and
+// runs every leaf of the piece.  Per leaf the workgroup stages the 128 x 64 A
+// and B tiles in LDS (double buffered, one barrier per leaf; rows swizzled by
+// chunk ^ (row & 7) so that both the row-wise writes and the MFMA-layout reads
+// are conflict-free; two leaves of tiles in flight in registers), and each
+// wave runs two MFMAs per tile from a zero accumulator, the leaf of the other
+// kernels.
+//
+// Tree.  The piece's midpoint tree is cut at depth UP (<= 3): every lower
+// subtree (at most 4 leaves, two compile-time sizes) is reduced in registers
+// with its static post-order as its leaves arrive, the merges of one leaf
+// issued while the next leaf's MFMAs run, and the 2^UP lower roots go through
+// the perfect binary top of the tree, its pending left children parked in
+// the wave's own LDS region (touched once per lower subtree).  The piece root
+// goes to C or, with K split or an epilogue, to the partial buffer that the
+// join kernel finishes.
+//
+// Bound.  Per leaf every wave runs 16 MFMAs but about 150 VALU instructions
+// (rounding, the tree nodes, staging), and the barrier keeps the waves in
+// step, so the LDS reads, the MFMAs and the VALU work of a leaf follow each
+// other instead of overlapping: the kernel reaches about 15% of the MFMA
+// peak at the FFN's 4096-token shapes.
+#include "dgf_device.hpp"
+#include "dgf_kernels.hpp"
+
+namespace dgf {
+namespace {
+
+constexpr int kMmWaves = 8;
+constexpr int kMmBM = 128, kMmBN = 128;  // workgroup tile: tokens x outputs
+constexpr int kMmTM = 2, kMmTN = 4;      // a wave's 16 x 16 tiles: 32 tokens x 64 outputs
+constexpr int kMmNP = kMmTM * kMmTN * 2;  // packed BF16 pairs per lane: index (tn TM + tm) 2 + h
+constexpr size_t kMmStage = (size_t)(kMmBM + kMmBN) * 64 * 2;  // A then B tile of one leaf (bytes)
+// Leaves per lower subtree, at most: past 4 the pending values, the
+// accumulators and the fragments no longer fit a wave's 256 registers.
+constexpr int kMmMaxNL = 4;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+struct MmWg {
+  const GemmParams &p;
+  uint16_t *lds;  // [2 stages][A 128 x 64 | B 128 x 64], then the waves' top-level stacks
+  const uint16_t *A, *B;
+  int64_t lda, ldb;
+  int64_t m0, n0;
+  int tid, wave, lane, r16, g4;
+  int wm, wn;  // this wave's 32-token row block and 64-output column block
+  int plo, phi;
+  uint32_t voa[2], vob[2];  // byte offsets of this thread's chunks within a leaf's A and B tiles
+
+  // Global loads of leaf j's two tiles: thread t covers chunks t and t + 512
+  // of each (8 threads per 128-byte row segment).  A full leaf uses buffer
+  // loads on descriptors rebased at the tile's first byte of the leaf (scalar
+  // arithmetic) with fixed per-thread offsets; rows past M / N fall outside
+  // the descriptor's range and read as zero.  The partial last leaf reads
+  // element by element with zeros past K.
+  __device__ __forceinline__ void fetch(int j, u32x4 (&g)[4]) const {
+    const int64_t kb = (int64_t)j * kLeaf;
+    if (kb + kLeaf <= p.K) {
+      const int64_t ra = (p.M - m0) * lda * 2 - kb * 2, rb = (p.N - n0) * ldb * 2 - kb * 2;
+      const __amdgpu_buffer_rsrc_t sa = __builtin_amdgcn_make_buffer_rsrc(
+          (void *)(A + m0 * lda + kb), (short)0, (int)(ra < 0x7fffffff ? ra : 0x7fffffff), 0x00020000);
+      const __amdgpu_buffer_rsrc_t sb = __builtin_amdgcn_make_buffer_rsrc(
+          (void *)(B + n0 * ldb + kb), (short)0, (int)(rb < 0x7fffffff ? rb : 0x7fffffff), 0x00020000);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        g[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(sa, (int)voa[i], 0, 0));
+        g[2 + i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(sb, (int)vob[i], 0, 0));
+      }
+      return;
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int q = tid + 512 * i, row = q >> 3, kc = q & 7;
+      const int64_t k = kb + 8 * kc;
+      const int64_t m = m0 + row, n = n0 + row;
+      g[i] = m < p.M ? __builtin_bit_cast(u32x4, load_frag_tail(A + m * lda, k, p.K)) : u32x4{0u, 0u, 0u, 0u};
+      g[2 + i] = n < p.N ? __builtin_bit_cast(u32x4, load_frag_tail(B + n * ldb, k, p.K)) : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
+  __device__ __forceinline__ void stage_store(int s, const u32x4 (&g)[4]) const {
+    uint16_t *sa = lds + (size_t)s * (kMmStage / 2), *sb = sa + kMmBM * 64;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int q = tid + 512 * i, row = q >> 3, kc = q & 7;
+      *reinterpret_cast<u32x4 *>(&sa[row * 64 + 8 * (kc ^ (row & 7))]) = g[i];
+      *reinterpret_cast<u32x4 *>(&sb[row * 64 + 8 * (kc ^ (row & 7))]) = g[2 + i];
+    }
+  }
+
+  // The MFMAs of the leaf in stage s: the first K half of every tile (from a
+  // zero accumulator), then the second, each half's fragments read just before
+  // its MFMAs.
+  template <int H>
+  __device__ __forceinline__ void frags(const uint16_t *sa, const uint16_t *sb, bf16x8 (&af)[kMmTM],
+                                        bf16x8 (&bf)[kMmTN]) const {
+#pragma unroll
+    for (int t = 0; t < kMmTM; ++t) {
+      const int row = 32 * wm + 16 * t + r16;
+      af[t] = *reinterpret_cast<const bf16x8 *>(&sa[row * 64 + 8 * ((4 * H + g4) ^ (r16 & 7))]);
+    }
+#pragma unroll
+    for (int t = 0; t < kMmTN; ++t) {
+      const int row = 64 * wn + 16 * t + r16;
+      bf[t] = *reinterpret_cast<const bf16x8 *>(&sb[row * 64 + 8 * ((4 * H + g4) ^ (r16 & 7))]);
+    }
+  }
+
+  __device__ __forceinline__ void leaf_mfma(int s, f32x4 (&acc)[kMmTN][kMmTM]) const {
+    const uint16_t *sa = lds + (size_t)s * (kMmStage / 2), *sb = sa + kMmBM * 64;
+    bf16x8 af[kMmTM], bf[kMmTN];
+    frags<0>(sa, sb, af, bf);
+#pragma unroll
+    for (int tn = 0; tn < kMmTN; ++tn)
+#pragma unroll
+      for (int tm = 0; tm < kMmTM; ++tm) acc[tn][tm] = mfma16(bf[tn], af[tm], f32x4{0.f, 0.f, 0.f, 0.f});
+    frags<1>(sa, sb, af, bf);
+#pragma unroll
+    for (int tn = 0; tn < kMmTN; ++tn)
+#pragma unroll
+      for (int tm = 0; tm < kMmTM; ++tm) acc[tn][tm] = mfma16(bf[tn], af[tm], acc[tn][tm]);
+  }
+
+  __device__ __forceinline__ void pack(const f32x4 (&acc)[kMmTN][kMmTM], uint32_t (&v)[kMmNP]) const {
+#pragma unroll
+    for (int tn = 0; tn < kMmTN; ++tn)
+#pragma unroll
+      for (int tm = 0; tm < kMmTM; ++tm) {
+        v[(tn * kMmTM + tm) * 2 + 0] = pack_rne(acc[tn][tm][0], acc[tn][tm][1]);
+        v[(tn * kMmTM + tm) * 2 + 1] = pack_rne(acc[tn][tm][2], acc[tn][tm][3]);
+      }
+  }
+
+  // One leaf j: its MFMAs from stage (j - plo) & 1; while they run, the
+  // previous leaf of the subtree (rounded, packed) goes into the tree, the
+  // VALU work overlapping the matrix core; then this leaf is packed, leaf
+  // j + 1's tiles (fetched two leaves earlier into register set `nx`) go into
+  // the other stage, leaf j + 3 is fetched into that set, and the barrier
+  // publishes the stage just written and frees the one just read.
+  template <int NL, int J>
+  __device__ __forceinline__ void one_leaf(int j, u32x4 (&nx)[4], uint32_t (&v)[kMmNP],
+                                           uint32_t (&st)[3][kMmNP]) const {
+    const int s = (j - plo) & 1;
+    f32x4 acc[kMmTN][kMmTM];
+    leaf_mfma(s, acc);
+    if constexpr (J > 0) push_leaf<kMmNP, NL, J - 1>(v, st);
+    pack(acc, v);
+    if (j + 1 < phi) stage_store(s ^ 1, nx);
+    if (j + 3 < phi) fetch(j + 3, nx);
+    __syncthreads();
+  }
+
+  // Leaves J.. of a lower subtree of NL leaves, the first being leaf j of the
+  // piece; the two register sets alternate with the leaf's parity in the piece.
+  template <int NL, int J>
+  __device__ __forceinline__ void lower(int j, u32x4 (&r0)[4], u32x4 (&r1)[4], uint32_t (&v)[kMmNP],
+                                        uint32_t (&st)[3][kMmNP]) const {
+    if constexpr (J < NL) {
+      if (((j - plo) & 1) == 0)
+        one_leaf<NL, J>(j, r1, v, st);
+      else
+        one_leaf<NL, J>(j, r0, v, st);
+      lower<NL, J + 1>(j + 1, r0, r1, v, st);
+    } else {
+      push_leaf<kMmNP, NL, NL - 1>(v, st);  // the subtree's last leaf: v becomes its root
+    }
+  }
+
+  template <int NL>
+  __device__ __forceinline__ void lower_tree(int j, u32x4 (&r0)[4], u32x4 (&r1)[4], uint32_t (&v)[kMmNP]) const {
+    uint32_t st[3][kMmNP];
+    lower<NL, 0>(j, r0, r1, v, st);
+  }
+
+  __device__ __forceinline__ void store_root(const uint32_t (&v)[kMmNP], uint16_t *out, int64_t ldo) const {
+#pragma unroll
+    for (int tn = 0; tn < kMmTN; ++tn)
+#pragma unroll
+      for (int tm = 0; tm < kMmTM; ++tm) {
+        const int64_t m = m0 + 32 * wm + 16 * tm + r16, n = n0 + 64 * wn + 16 * tn + 4 * g4;
+        if (m >= p.M || n >= p.N) continue;
+        const uint32_t lo2 = v[(tn * kMmTM + tm) * 2 + 0], hi2 = v[(tn * kMmTM + tm) * 2 + 1];
+        uint16_t *dst = out + m * ldo + n;
+        if (n + 3 < p.N) {
+          *reinterpret_cast<uint2 *>(dst) = make_uint2(lo2, hi2);
+        } else {
+          const uint16_t h4[4] = {(uint16_t)(lo2 & 0xffff), (uint16_t)(lo2 >> 16), (uint16_t)(hi2 & 0xffff),
+                                  (uint16_t)(hi2 >> 16)};
+          for (int e = 0; e < 4; ++e)
+            if (n + e < p.N) dst[e] = h4[e];
+        }
+      }
+  }
+};
+
+// Pending left subtrees of the top levels, in this wave's own LDS region:
+// level t, pair q of lane l at base[(t kMmNP + q) 64 + l] (each lane reads
+// back only what it wrote; consecutive lanes, consecutive dwords).
+__device__ __forceinline__ void park(uint32_t *base, int t, const uint32_t (&v)[kMmNP]) {
+#pragma unroll
+  for (int q = 0; q < kMmNP; ++q) base[(t * kMmNP + q) * 64] = v[q];
+}
+__device__ __forceinline__ void merge(const uint32_t *base, int t, uint32_t (&v)[kMmNP]) {
+#pragma unroll
+  for (int q = 0; q < kMmNP; ++q) v[q] = node2(base[(t * kMmNP + q) * 64], v[q]);
+}
+
+// NLH: the larger of the two lower-subtree sizes (the smaller is NLH - 1).
+template <int NLH>
+__global__ __launch_bounds__(kMmWaves * 64) void k_mm(GemmParams p) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t mm_lds[];
+  const int kd = p.ksplit_depth, up = p.stack_slots;  // K-piece depth; upper levels cut inside the piece
+  const int b = blockIdx.z >> kd, piece = blockIdx.z & ((1 << kd) - 1);
+  // Row-major tile order: the workgroups in flight share the A rows of a few
+  // tile rows (measured a little faster here than grouping tile blocks per
+  // XCD, which shares B rows as well).
+  const int tiles_n = (int)((p.N + kMmBN - 1) / kMmBN);
+  const int tile_m = (int)blockIdx.x / tiles_n, tile_n = (int)blockIdx.x % tiles_n;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  MmWg w{p,
+         mm_lds,
+         p.A[b],
+         p.B[b],
+         p.lda[b],
+         p.ldb[b],
+         (int64_t)tile_m * kMmBM,
+         (int64_t)tile_n * kMmBN,
+         tid,
+         wave,
+         lane,
+         lane & 15,
+         lane >> 4,
+         wave & 3,
+         wave >> 2,
+         0,
+         0,
+         {0u, 0u},
+         {0u, 0u}};
+  subtree_range(p.L, kd, piece, w.plo, w.phi);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int q = tid + 512 * i, row = q >> 3, kc = q & 7;
+    w.voa[i] = (uint32_t)((row * w.lda + 8 * kc) * 2);
+    w.vob[i] = (uint32_t)((row * w.ldb + 8 * kc) * 2);
+  }
+
+  // leaf plo into stage 0; leaves plo + 1 and plo + 2 in flight in the two register sets
+  u32x4 r0[4], r1[4];
+  w.fetch(w.plo, r0);
+  w.stage_store(0, r0);
+  if (w.plo + 1 < w.phi) w.fetch(w.plo + 1, r1);
+  if (w.plo + 2 < w.phi) w.fetch(w.plo + 2, r0);
+  __syncthreads();
+
+  // lower subtrees in order; the top `up` levels over their roots
+  uint32_t v[kMmNP];
+  uint32_t *upl = reinterpret_cast<uint32_t *>(reinterpret_cast<char *>(mm_lds) + 2 * kMmStage) +
+                  (size_t)wave * 3 * kMmNP * 64 + lane;
+  const int nsub = 1 << up;
+  for (int sidx = 0; sidx < nsub; ++sidx) {
+    int lo, hi;
+    subtree_range(w.phi - w.plo, up, sidx, lo, hi);
+    const int j = w.plo + lo;
+    if (hi - lo == NLH)
+      w.template lower_tree<NLH>(j, r0, r1, v);
+    else if constexpr (NLH > 1)
+      w.template lower_tree<NLH - 1>(j, r0, r1, v);
+    // root sidx of the perfect tree over nsub roots: merge with the pending
+    // left subtrees its position closes (trailing ones of sidx), then park it
+    // at its level unless it is the last
+    int t = 0;
+    for (; (sidx >> t) & 1; ++t) merge(upl, t, v);
+    if (sidx + 1 < nsub) park(upl, t, v);
+  }
+  if (p.to_part)
+    w.store_root(v, p.part + ((int64_t)b * (1 << kd) + piece) * p.part_stride, p.ldp);
+  else
+    w.store_root(v, p.C[b], p.ldc[b]);
+}
+
+}  // namespace
+
+size_t mm_lds_bytes() { return 2 * kMmStage + (size_t)kMmWaves * 3 * kMmNP * 64 * 4; }
+
+// Upper levels (<= 3) of a piece with Lp leaves such that every lower subtree
+// holds at most kMmMaxNL leaves; -1 if the piece is too large.
+int mm_upper_levels(int Lp) {
+  for (int up = 0; up <= 3; ++up)
+    if (((Lp + (1 << up) - 1) >> up) <= kMmMaxNL && (1 << up) <= Lp) return up;
+  return -1;
+}
+
+// nlh: the largest lower-subtree size of the plan (1..8); the others are nlh - 1.
+hipError_t launch_mm(GemmParams p, int nb, int nlh, hipStream_t stream) {
+  const int64_t tiles = ((p.M + kMmBM - 1) / kMmBM) * ((p.N + kMmBN - 1) / kMmBN);
+  const dim3 grid((unsigned)tiles, 1u, (unsigned)(nb << p.ksplit_depth));
+  const dim3 block(kMmWaves * 64);
+  const size_t shm = mm_lds_bytes();
+  switch (nlh) {
+    case 1: hipLaunchKernelGGL(k_mm<1>, grid, block, shm, stream, p); break;
+    case 2: hipLaunchKernelGGL(k_mm<2>, grid, block, shm, stream, p); break;
+    case 3: hipLaunchKernelGGL(k_mm<3>, grid, block, shm, stream, p); break;
+    case 4: hipLaunchKernelGGL(k_mm<4>, grid, block, shm, stream, p); break;
+    case 5: hipLaunchKernelGGL(k_mm<5>, grid, block, shm, stream, p); break;
+    case 6: hipLaunchKernelGGL(k_mm<6>, grid, block, shm, stream, p); break;
+    case 7: hipLaunchKernelGGL(k_mm<7>, grid, block, shm, stream, p); break;
+    case 8: hipLaunchKernelGGL(k_mm<8>, grid, block, shm, stream, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dgf

@@ -93,6 +93,22 @@ def test_gemm_tree_matches_oracle(layout, M, N, K):
     assert_bitwise(got, expect, f"{layout} {M}x{N}x{K}")
 
 
+# many tokens: the tiled kernel (128 x 128 output tiles, K pieces of lower
+# subtrees of at most 4 leaves under an LDS-parked top of up to 3 levels)
+MM_SHAPES = [(128, 128, 64), (130, 200, 100), (256, 64, 4096), (300, 257, 1000), (256, 256, 12288), (129, 17, 520),
+             (512, 384, 3000), (200, 1000, 8)]
+
+
+@pytest.mark.parametrize("M,N,K", MM_SHAPES)
+def test_tiled_gemm_matches_oracle(M, N, K):
+    rng = np.random.default_rng(M * 7 + N * 3 + K)
+    A, B = rnd(rng, (M, K)), rnd(rng, (N, K), 0.05)
+    expect = oracle.gemm_tree(A, B, "NT")
+    got = dgf.gemm_tree("NT", padded(A), padded(B))
+    torch.cuda.synchronize()
+    assert_bitwise(got, expect, f"NT {M}x{N}x{K}")
+
+
 @pytest.mark.parametrize("dist", ["wide", "wide60", "cancel", "tiny", "ties"])
 @pytest.mark.parametrize("K", [8, 32, 64, 128, 200])
 def test_leaf_block_rule_adversarial(dist, K):
