@@ -371,11 +371,18 @@ bool dx_fused(int64_t M, int64_t H, int64_t I) { return plan_xs(DGF_LAYOUT_NN, 2
 // the NT tree GEMM.
 bool dw_direct(int64_t M) { return M <= 64; }
 
+// Many tokens: dA and the dX lanes run as NT tree GEMMs on the tiled kernel
+// over transposed copies of the weights (the streaming kernel would re-read
+// every weight once per 32-token tile).
+bool nn_tiled(int64_t M) { return M >= kMmMinM; }
+
 size_t bwd_partials(int64_t M, int64_t H, int64_t I) {
+  const bool t = nn_tiled(M);
   const size_t sizes[4] = {
-      partial_bytes(DGF_LAYOUT_NN, 1, EPI_DSILU, M, I, H),                                       // dA
-      dx_fused(M, H, I) ? partial_bytes(DGF_LAYOUT_NN, 2, EPI_DX, M, H, I)
-                        : partial_bytes(DGF_LAYOUT_NN, 1, EPI_STORE, M, H, I),                   // dX lanes
+      partial_bytes(t ? DGF_LAYOUT_NT : DGF_LAYOUT_NN, 1, EPI_DSILU, M, I, H),                   // dA
+      t                 ? partial_bytes(DGF_LAYOUT_NT, 2, EPI_DX, M, H, I)
+      : dx_fused(M, H, I) ? partial_bytes(DGF_LAYOUT_NN, 2, EPI_DX, M, H, I)
+                          : partial_bytes(DGF_LAYOUT_NN, 1, EPI_STORE, M, H, I),                 // dX lanes
       dw_direct(M) ? 0 : partial_bytes(DGF_LAYOUT_NT, 2, EPI_STORE, I, H, M),                    // dW_gate, dW_up
       dw_direct(M) ? 0 : partial_bytes(DGF_LAYOUT_NT, 1, EPI_STORE, H, I, M)};                   // dW_down
   size_t m = 0;
@@ -390,6 +397,9 @@ size_t bwd_ws_bytes(int64_t M, int64_t H, int64_t I) {
                          : round256((size_t)I * Mp * 2) * 3         // dG^T, dU^T, a^T [I, Mp]
                                + round256((size_t)H * Mp * 2) * 2)  // x^T, dY^T [H, Mp]
          + round256((size_t)M * round8(H) * 2) * 2                  // the dX lanes G, U [M, H]
+         + (nn_tiled(M) ? round256((size_t)I * round8(H) * 2)        // W_down^T [I, H]
+                              + round256((size_t)H * round8(I) * 2) * 2  // W_gate^T, W_up^T [H, I]
+                        : 0)
          + bwd_partials(M, H, I);                                   // K-split partial roots
 }
 
@@ -558,7 +568,24 @@ dgf_status dgf_ffn_bwd(const void *dy, int64_t lddy, const void *x, int64_t ldx,
   }
   const int64_t ld_lane = round8(H);
   uint16_t *Gw = cv.take((size_t)M * ld_lane), *Uw = cv.take((size_t)M * ld_lane);
+  const bool tiled = nn_tiled(M);
+  uint16_t *wdT = nullptr, *wgT = nullptr, *wuT = nullptr;
+  const int64_t ld_wdT = round8(H), ld_wgT = round8(I);
+  if (tiled) {
+    wdT = cv.take((size_t)I * ld_wdT);
+    wgT = cv.take((size_t)H * ld_wgT);
+    wuT = cv.take((size_t)H * ld_wgT);
+  }
   uint16_t *partials = (uint16_t *)((char *)ws + cv.used);
+
+  if (tiled) {  // K-contiguous copies of the weights for the NT form of dA and the dX lanes
+    DGF_TRY(hip_check(timed(s, "transpose W_down", [&] { return launch_transpose((const uint16_t *)w_down, ld_wd, H, I, wdT, ld_wdT, s); }),
+                      "transpose W_down"));
+    DGF_TRY(hip_check(timed(s, "transpose W_gate", [&] { return launch_transpose((const uint16_t *)w_gate, ld_wg, I, H, wgT, ld_wgT, s); }),
+                      "transpose W_gate"));
+    DGF_TRY(hip_check(timed(s, "transpose W_up", [&] { return launch_transpose((const uint16_t *)w_up, ld_wu, I, H, wuT, ld_wgT, s); }),
+                      "transpose W_up"));
+  }
 
   if (!direct) {
     DGF_TRY(hip_check(timed(s, "transpose x", [&] { return launch_transpose((const uint16_t *)x, ldx, M, H, xT, Mp, s); }),
@@ -571,14 +598,14 @@ dgf_status dgf_ffn_bwd(const void *dy, int64_t lddy, const void *x, int64_t ldx,
   GemmParams p = blank();
   p.A[0] = (const uint16_t *)dy;
   p.lda[0] = lddy;
-  p.B[0] = (const uint16_t *)w_down;
-  p.ldb[0] = ld_wd;
+  p.B[0] = tiled ? wdT : (const uint16_t *)w_down;
+  p.ldb[0] = tiled ? ld_wdT : ld_wd;
   p.M = M; p.N = I; p.K = H;
   p.sg = (const uint16_t *)g;
   p.su = (const uint16_t *)u;
   p.ld_gu = ld_gu;
   p.dG = dG; p.dU = dU; p.a_rm = a_rm; p.ld_d = ld_d;
-  DGF_TRY(run_gemm(DGF_LAYOUT_NN, 1, EPI_DSILU, p, s, "dA tree GEMM", partials, "dA join + dsilu"));
+  DGF_TRY(run_gemm(tiled ? DGF_LAYOUT_NT : DGF_LAYOUT_NN, 1, EPI_DSILU, p, s, "dA tree GEMM", partials, "dA join + dsilu"));
   if (!direct) {  // token-major copies for the weight-gradient GEMMs
     DGF_TRY(hip_check(timed(s, "transpose dG", [&] { return launch_transpose(dG, ld_d, M, I, dGT, Mp, s); }), "transpose dG"));
     DGF_TRY(hip_check(timed(s, "transpose dU", [&] { return launch_transpose(dU, ld_d, M, I, dUT, Mp, s); }), "transpose dU"));
@@ -588,17 +615,18 @@ dgf_status dgf_ffn_bwd(const void *dy, int64_t lddy, const void *x, int64_t ldx,
   // dX lanes G = T_I(dG W_gate), U = T_I(dU W_up) and dX = bf16(G + U), the
   // gate lane first: one two-product GEMM whose join does the ordered add
   // (lanes kept when the caller asks for them), or two GEMMs and an add
-  if (dx_fused(M, H, I)) {
+  if (tiled || dx_fused(M, H, I)) {
     GemmParams q = blank();
     q.A[0] = dG; q.A[1] = dU;
     q.lda[0] = q.lda[1] = ld_d;
-    q.B[0] = (const uint16_t *)w_gate; q.ldb[0] = ld_wg;
-    q.B[1] = (const uint16_t *)w_up; q.ldb[1] = ld_wu;
+    q.B[0] = tiled ? wgT : (const uint16_t *)w_gate; q.ldb[0] = tiled ? ld_wgT : ld_wg;
+    q.B[1] = tiled ? wuT : (const uint16_t *)w_up; q.ldb[1] = tiled ? ld_wgT : ld_wu;
     q.C[0] = (uint16_t *)dx_gate_lane; q.C[1] = (uint16_t *)dx_up_lane;
     q.ldc[0] = q.ldc[1] = lddx;
     q.dx = (uint16_t *)dx; q.lddx = lddx;
     q.M = M; q.N = H; q.K = I;
-    DGF_TRY(run_gemm(DGF_LAYOUT_NN, 2, EPI_DX, q, s, "dX lanes tree GEMM", partials, "dX join + lane add"));
+    DGF_TRY(run_gemm(tiled ? DGF_LAYOUT_NT : DGF_LAYOUT_NN, 2, EPI_DX, q, s, "dX lanes tree GEMM", partials,
+                     "dX join + lane add"));
   } else {
     uint16_t *G = dx_gate_lane ? (uint16_t *)dx_gate_lane : Gw;
     uint16_t *U = dx_up_lane ? (uint16_t *)dx_up_lane : Uw;
