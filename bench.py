@@ -50,6 +50,7 @@ def kernel_bytes(name: str, M: int) -> int | None:
         "gate/up + act": 2 * W + act_mh + 3 * act_mi,            # W_gate, W_up, x -> g, u, a
         "gate/up tree GEMM": 2 * W + act_mh + 2 * act_mi,        # W_gate, W_up, x -> g, u
         "down tree GEMM": W + act_mi + act_mh,                    # W_down, a -> y
+        "down all-K tree GEMM": W + act_mi + act_mh,              # W_down, a -> y (M <= 16)
         "dA tree GEMM": W + act_mh + act_mi,                      # W_down, dY -> dA
         "dX lanes tree GEMM": 2 * W + 2 * act_mi + 2 * act_mh,    # W_gate, W_up, dG, dU -> G, U
         "dW_gate/dW_up tree GEMM": 2 * W + 2 * act_mi + act_mh,   # dG, dU, x -> dW_gate, dW_up
@@ -67,6 +68,7 @@ KERNEL_SOURCE = {
     "gate/up + act": "dgf_gu.hip",
     "gate/up tree GEMM": "dgf_xs.hip",
     "down tree GEMM": "dgf_xs.hip",
+    "down all-K tree GEMM": "dgf_dn.hip",
     "dA tree GEMM": "dgf_xs.hip",
     "dX lanes tree GEMM": "dgf_xs.hip",
     "dW_gate/dW_up tree GEMM": "dgf_gemm.hip",

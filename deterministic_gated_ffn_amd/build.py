@@ -15,7 +15,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libdgf.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["dgf_gemm.hip", "dgf_xs.hip", "dgf_gu.hip", "dgf_mm.hip", "dgf_elementwise.hip", "dgf_api.hip"]
+SOURCES = ["dgf_gemm.hip", "dgf_xs.hip", "dgf_gu.hip", "dgf_mm.hip", "dgf_dn.hip", "dgf_elementwise.hip", "dgf_api.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

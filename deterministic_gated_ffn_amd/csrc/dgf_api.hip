@@ -405,7 +405,7 @@ size_t bwd_ws_bytes(int64_t M, int64_t H, int64_t I) {
 
 size_t fwd_ws_bytes(int64_t M, int64_t H, int64_t I) {
   const size_t gu = gu_act_applies(M, I, H) ? 0 : partial_bytes(DGF_LAYOUT_NT, 2, EPI_ACT, M, I, H);  // gate/up partial roots
-  const size_t dn = partial_bytes(DGF_LAYOUT_NT, 1, EPI_STORE, M, H, I);  // down-projection partial roots
+  const size_t dn = allk_applies(M, H, I) ? 0 : partial_bytes(DGF_LAYOUT_NT, 1, EPI_STORE, M, H, I);  // down-projection partial roots
   return round256((size_t)M * round8(I) * 2)  // a [M, I]
          + (gu > dn ? gu : dn);               // the gate/up roots are joined before the down GEMM starts
 }
@@ -511,6 +511,17 @@ dgf_status dgf_ffn_fwd(const void *x, int64_t ldx, const void *w_gate, int64_t l
     DGF_TRY(run_gemm(DGF_LAYOUT_NT, 2, EPI_ACT, p, s, "gate/up tree GEMM", partials, "gate/up join + act"));
   }
 
+  if (allk_applies(M, H, I)) {
+    // every workgroup reduces all of K for its 16 output columns: no partial roots, no join
+    AllkParams d;
+    memset(&d, 0, sizeof d);
+    d.A = a; d.lda = lda_;
+    d.B = (const uint16_t *)w_down; d.ldb = ld_wd;
+    d.C = (uint16_t *)y; d.ldc = ldy;
+    d.M = M; d.N = H; d.K = I; d.L = leaves(I);
+    DGF_TRY(hip_check(timed(s, "down all-K tree GEMM", [&] { return launch_allk(d, s); }), "down all-K tree GEMM"));
+    return ok();
+  }
   GemmParams q = blank();
   q.A[0] = a;
   q.lda[0] = lda_;

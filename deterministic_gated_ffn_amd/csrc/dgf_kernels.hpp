@@ -67,6 +67,23 @@ struct GuParams {
 bool gu_act_applies(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gu_act(const GuParams &p, hipStream_t stream);
 
+// All-K tree GEMM for few tokens (dgf_dn.hip): C [M, N] = A [M, K] B [N, K]^T,
+// both K-contiguous, one workgroup per 16 output columns reducing all of K
+// (no partial roots, no join).  Applies to M <= 16, K a multiple of 64 and
+// L / 8 leaves per wave in {1, 2, 3, 4, 6, 8, 12, 16, 24, 32}.
+struct AllkParams {
+  const uint16_t *A;
+  int64_t lda;
+  const uint16_t *B;
+  int64_t ldb;
+  uint16_t *C;
+  int64_t ldc;
+  int64_t M, N, K;
+  int L;
+};
+bool allk_applies(int64_t M, int64_t N, int64_t K);
+hipError_t launch_allk(const AllkParams &p, hipStream_t stream);
+
 // Tiled tree GEMM for many tokens (dgf_mm.hip): NT, 128 x 128 output tiles
 // per workgroup, grid.z = nb << ksplit_depth; stack_slots holds the number of
 // top levels of each K piece's tree (<= 3) above lower subtrees of at most 8
