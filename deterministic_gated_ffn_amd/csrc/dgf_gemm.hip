@@ -620,12 +620,34 @@ __global__ __launch_bounds__(256) void k_gemm_short(GemmParams p) {
 // from row-major [k][features] operands: the weight gradients, k = tokens.
 // A workgroup of 4 waves owns 64 rows r and CT consecutive tiles of 128
 // columns c.  It copies the K x 64 A tile into LDS feature-major once, and
-// each K x 128 B tile in turn, with zeros past K (up to the next multiple of
-// 32: an all-zero block leaves the sum unchanged), past M and past N.  Every
+// each K x 128 B tile in turn into one of two LDS buffers, with zeros past K
+// (up to the next multiple of 32: an all-zero block leaves the sum
+// unchanged), past M and past N.  The next B tile's loads are issued into
+// registers before the current tile's MFMAs and committed to the other
+// buffer after its stores, so their latency hides behind the stores.  Every
 // wave computes 16 rows x 128 columns per tile and stores them through its
-// own LDS stage as whole 256-byte row segments; the next B tile's loads are
-// issued before those stores.
+// own LDS stage as whole 256-byte row segments.
 constexpr int kTnTile = 128;
+constexpr int kTnMaxQ = 4;  // B-tile items per thread: 64 x 16 chunks of 8 features over 256 threads
+
+// 8 consecutive features f0 .. f0+7 of operand row k, packed (zeros outside)
+__device__ __forceinline__ uint4 tn_load8(const uint16_t *src, int64_t ld, int k, int K, int64_t f0, int64_t F) {
+  if (k < K && f0 + 8 <= F) return *reinterpret_cast<const uint4 *>(src + (int64_t)k * ld + f0);
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+  for (int e = 0; e < 8; ++e)
+    if (k < K && f0 + e < F) w[e >> 1] |= (uint32_t)src[(int64_t)k * ld + f0 + e] << (16 * (e & 1));
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// Feature f = 8 cc + e of row k lands at LDS row f, position k ^ (8 (cc & km)):
+// 16-byte K chunks permuted per feature group, which spreads the transposing
+// writes over the banks and keeps each MFMA operand read one aligned 16-byte chunk.
+__device__ __forceinline__ void tn_put8(uint16_t *dst, int ks, int km, int k, int cc, uint4 q) {
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+  const int kk = k ^ (8 * (cc & km));
+#pragma unroll
+  for (int e = 0; e < 8; ++e) dst[(8 * cc + e) * ks + kk] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+}
 
 template <int NB>
 __global__ __launch_bounds__(256) void k_gemm_tn1(GemmParams p, int ct) {
@@ -637,53 +659,46 @@ __global__ __launch_bounds__(256) void k_gemm_tn1(GemmParams p, int ct) {
   const int KP = 32 * KH;
   const int ks = KP + 8;         // padded K stride of the feature-major tiles
   const int km = KP / 8 - 1;     // K-chunk swizzle mask: chunks stay inside the row's KP elements
+  const int nq = KP * (kTnTile / 8) / 256;  // B-tile items per thread: 2 or 4
   uint16_t *sA = tn_lds;                            // [NB][64][ks]
-  uint16_t *sB = sA + NB * 64 * ks;                 // [128][ks]
-  uint16_t *stage = sB + kTnTile * ks + wave * 16 * kShortStride;  // this wave's [16][kShortStride]
+  uint16_t *sB0 = sA + NB * 64 * ks;                // [2][128][ks]
+  uint16_t *stage = sB0 + 2 * kTnTile * ks + wave * 16 * kShortStride;  // this wave's [16][kShortStride]
   const int64_t r0 = (int64_t)blockIdx.y * 64;
   const int64_t cbase = (int64_t)xcd_tile(blockIdx.x, gridDim.x) * kTnTile * ct;
 
-  // 8 consecutive features f0 .. f0+7 of operand row k (zeros outside)
-  auto load8 = [&](const uint16_t *src, int64_t ld, int k, int64_t f0, int64_t F, uint16_t (&v)[8]) {
-    if (k < K && f0 + 8 <= F) {
-      const uint4 q = *reinterpret_cast<const uint4 *>(src + (int64_t)k * ld + f0);
-      const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+  // item j of this thread: operand row k = q / 16, chunk cc = q % 16 (eight threads per 128-byte row)
+  uint4 nx[kTnMaxQ];
+  auto load_b = [&](int64_t c0) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = (k < K && f0 + e < F) ? src[(int64_t)k * ld + f0 + e] : (uint16_t)0;
-    }
+    for (int j = 0; j < kTnMaxQ; ++j)
+      if (j < nq) {
+        const int q = tid + 256 * j;
+        nx[j] = tn_load8(p.B[0], p.ldb[0], q / (kTnTile / 8), K, c0 + 8 * (q % (kTnTile / 8)), p.N);
+      }
   };
-  // Eight consecutive threads read one 128-byte operand row; feature f = 8 cc + e
-  // of row k lands at LDS row f, position k ^ (8 (cc & km)): 16-byte K chunks
-  // permuted per feature group, which spreads the transposing writes over the
-  // banks and keeps each MFMA operand read one aligned 16-byte chunk.
-  auto fill_b = [&](int64_t c0) {
-    for (int q = tid; q < KP * (kTnTile / 8); q += 256) {
-      const int k = q / (kTnTile / 8), cc = q % (kTnTile / 8);
-      uint16_t v[8];
-      load8(p.B[0], p.ldb[0], k, c0 + 8 * cc, p.N, v);
-      const int kk = k ^ (8 * (cc & km));
+  auto put_b = [&](uint16_t *sB) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sB[(8 * cc + e) * ks + kk] = v[e];
-    }
+    for (int j = 0; j < kTnMaxQ; ++j)
+      if (j < nq) {
+        const int q = tid + 256 * j;
+        tn_put8(sB, ks, km, q / (kTnTile / 8), q % (kTnTile / 8), nx[j]);
+      }
   };
+  load_b(cbase);
   for (int q = tid; q < NB * KP * 8; q += 256) {
     const int b = q / (KP * 8), rem = q % (KP * 8), k = rem / 8, cc = rem % 8;
-    uint16_t v[8];
-    load8(p.A[b], p.lda[b], k, r0 + 8 * cc, p.M, v);
-    const int kk = k ^ (8 * (cc & km));
-#pragma unroll
-    for (int e = 0; e < 8; ++e) sA[(b * 64 + 8 * cc + e) * ks + kk] = v[e];
+    tn_put8(sA + b * 64 * ks, ks, km, k, cc, tn_load8(p.A[b], p.lda[b], k, K, r0 + 8 * cc, p.M));
   }
-  fill_b(cbase);
+  put_b(sB0);
   __syncthreads();
 
   const int64_t m0 = r0 + 16 * wave;
   for (int c = 0; c < ct; ++c) {
     const int64_t c0 = cbase + (int64_t)c * kTnTile;
     if (c0 >= p.N) break;  // the same for every wave of the workgroup
+    const bool more = c + 1 < ct && c0 + kTnTile < p.N;
+    if (more) load_b(c0 + kTnTile);  // in flight during this tile's MFMAs and stores
+    const uint16_t *sB = sB0 + (c & 1) * kTnTile * ks;
     f32x4 acc[NB][8];
 #pragma unroll
     for (int b = 0; b < NB; ++b)
@@ -703,8 +718,6 @@ __global__ __launch_bounds__(256) void k_gemm_tn1(GemmParams p, int ct) {
         for (int b = 0; b < NB; ++b) acc[b][t] = mfma16(w, xa[b], acc[b][t]);
       }
     }
-    __syncthreads();  // every wave is done with this B tile
-    if (c + 1 < ct && c0 + kTnTile < p.N) fill_b(c0 + kTnTile);  // loads in flight during the stores below
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       // lane holds C[m0 + r16][c0 + 16t + 4 g4 + (0..3)]
@@ -733,16 +746,19 @@ __global__ __launch_bounds__(256) void k_gemm_tn1(GemmParams p, int ct) {
       }
       wave_lds_sync();  // the stage is reused by the next product
     }
+    // the other buffer was last read in the previous tile, before the barrier that ended it
+    if (more) put_b(sB0 + ((c + 1) & 1) * kTnTile * ks);
     __syncthreads();  // the next B tile is in LDS
   }
 }
 
 size_t tn1_lds_bytes(int nb, int64_t K) {
   const int64_t ks = 32 * ((K + 31) / 32) + 8;
-  return (size_t)(nb * 64 + kTnTile) * ks * 2 + (size_t)4 * 16 * kShortStride * 2;
+  return (size_t)(nb * 64 + 2 * kTnTile) * ks * 2 + (size_t)4 * 16 * kShortStride * 2;
 }
 
 hipError_t launch_gemm_tn1(int nb, GemmParams p, hipStream_t stream) {
+  if (p.K < 0 || p.K > 64) return hipErrorInvalidValue;
   // column tiles per workgroup: as many as keep at least 4 workgroups per CU busy
   const int64_t tiles_c = (p.N + kTnTile - 1) / kTnTile, tiles_r = (p.M + 63) / 64;
   int ct = 1;

@@ -268,7 +268,8 @@ def test_tiny_ffn_forward_backward_bitwise():
                                    # down projection over all K per workgroup (M <= 16): 1..32 leaves per wave,
                                    # ragged H
                                    (3, 198, 512), (11, 64, 1024), (16, 136, 1536), (16, 96, 2048), (5, 40, 3072),
-                                   (8, 72, 4096), (15, 48, 6144), (12, 16, 12288), (2, 32, 8192), (16, 24, 16384)])
+                                   (8, 72, 4096), (15, 48, 6144), (12, 16, 12288), (2, 32, 8192), (16, 24, 16384),
+                                   (4, 8, 512), (2, 1, 1024)])
 def test_ffn_other_shapes_bitwise(M, H, I):
     rng = np.random.default_rng(M + H + I)
     x, dy = rnd(rng, (M, H)), rnd(rng, (M, H))
