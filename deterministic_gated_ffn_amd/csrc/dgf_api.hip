@@ -70,19 +70,23 @@ hipError_t timed(hipStream_t s, const char *name, F &&launch) {
 bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
 
 // A row-major BF16 matrix operand: non-null, 16-byte aligned, ld >= cols, ld % 8 == 0.
+constexpr int64_t kMaxLd = (int64_t)1 << 23;
+
 dgf_status check_mat(const char *name, const void *p, int64_t ld, int64_t rows, int64_t cols) {
   if (rows == 0 || cols == 0) return DGF_OK;
   if (!p) return fail(DGF_EINVAL, "%s is NULL", name);
   if (!aligned16(p)) return fail(DGF_EINVAL, "%s is not 16-byte aligned", name);
   if (ld < cols) return fail(DGF_EINVAL, "%s: leading dimension %lld < row width %lld", name, (long long)ld, (long long)cols);
   if (ld % 8 != 0) return fail(DGF_EINVAL, "%s: leading dimension %lld is not a multiple of 8", name, (long long)ld);
+  // a 128-row tile's byte offsets from its first row stay below 2^31
+  if (ld >= kMaxLd) return fail(DGF_EUNSUPPORTED, "%s: leading dimension %lld beyond this build's limit (< 2^23)", name, (long long)ld);
   return DGF_OK;
 }
 
 dgf_status check_dims(int64_t M, int64_t N, int64_t K) {
   if (M < 0 || N < 0 || K < 0) return fail(DGF_EINVAL, "negative dimension (M=%lld N=%lld K=%lld)", (long long)M, (long long)N, (long long)K);
-  if (M > ((int64_t)1 << 21) || N > ((int64_t)1 << 30) || K > ((int64_t)1 << 24))
-    return fail(DGF_EUNSUPPORTED, "dimensions beyond this build's limits (M<=2^21, N<=2^30, K<=2^24)");
+  if (M > ((int64_t)1 << 21) || N > ((int64_t)1 << 30) || K > ((int64_t)1 << 23))
+    return fail(DGF_EUNSUPPORTED, "dimensions beyond this build's limits (M<=2^21, N<=2^30, K<=2^23)");
   return DGF_OK;
 }
 

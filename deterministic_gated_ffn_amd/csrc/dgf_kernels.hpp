@@ -86,7 +86,7 @@ hipError_t launch_allk(const AllkParams &p, hipStream_t stream);
 
 // Tiled tree GEMM for many tokens (dgf_mm.hip): NT, 128 x 128 output tiles
 // per workgroup, grid.z = nb << ksplit_depth; stack_slots holds the number of
-// top levels of each K piece's tree (<= 3) above lower subtrees of at most 8
+// top levels of each K piece's tree (<= 3) above lower subtrees of at most 4
 // leaves (nlh: the larger lower-subtree size, the smaller being nlh - 1).
 size_t mm_lds_bytes();
 int mm_upper_levels(int Lp);

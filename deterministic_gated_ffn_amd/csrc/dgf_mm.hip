@@ -303,7 +303,7 @@ int mm_upper_levels(int Lp) {
   return -1;
 }
 
-// nlh: the largest lower-subtree size of the plan (1..8); the others are nlh - 1.
+// nlh: the largest lower-subtree size of the plan (1..kMmMaxNL); the others are nlh - 1.
 hipError_t launch_mm(GemmParams p, int nb, int nlh, hipStream_t stream) {
   const int64_t tiles = ((p.M + kMmBM - 1) / kMmBM) * ((p.N + kMmBN - 1) / kMmBN);
   const dim3 grid((unsigned)tiles, 1u, (unsigned)(nb << p.ksplit_depth));
@@ -314,11 +314,7 @@ hipError_t launch_mm(GemmParams p, int nb, int nlh, hipStream_t stream) {
     case 2: hipLaunchKernelGGL(k_mm<2>, grid, block, shm, stream, p); break;
     case 3: hipLaunchKernelGGL(k_mm<3>, grid, block, shm, stream, p); break;
     case 4: hipLaunchKernelGGL(k_mm<4>, grid, block, shm, stream, p); break;
-    case 5: hipLaunchKernelGGL(k_mm<5>, grid, block, shm, stream, p); break;
-    case 6: hipLaunchKernelGGL(k_mm<6>, grid, block, shm, stream, p); break;
-    case 7: hipLaunchKernelGGL(k_mm<7>, grid, block, shm, stream, p); break;
-    case 8: hipLaunchKernelGGL(k_mm<8>, grid, block, shm, stream, p); break;
-    default: return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;  // lower subtrees hold at most kMmMaxNL leaves
   }
   return hipGetLastError();
 }

@@ -23,7 +23,10 @@
  *  - Tensors are BF16 bit patterns, row-major, device pointers on the current
  *    HIP device, each with a leading dimension in elements (>= the row width).
  *    Matrix operands must have 16-byte aligned base pointers and leading
- *    dimensions that are multiples of 8; otherwise DGF_EINVAL.
+ *    dimensions that are multiples of 8; otherwise DGF_EINVAL.  Leading
+ *    dimensions are below 2^23 elements and K is at most 2^23 (the kernels
+ *    address a tile's rows with 32-bit byte offsets); otherwise
+ *    DGF_EUNSUPPORTED.
  *  - `stream` is a hipStream_t (NULL = the default stream).  Every call only
  *    enqueues work on it and returns; errors raised by a kernel while it runs
  *    surface at the caller's next synchronisation.  Calls are stream-ordered,

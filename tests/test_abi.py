@@ -125,5 +125,10 @@ def test_gemm_validation(lib):
     # TN past one leaf needs transposed copies in the workspace
     assert lib.dgf_gemm_tree(binding.DGF_TN, FAKE, 8, FAKE, 8, FAKE, 8, 4, 4, 100, None, 0, None) == 3
     assert lib.dgf_gemm_tree(binding.DGF_NN, FAKE, 4, FAKE, 8, FAKE, 8, 4, 4, 8, None, 0, None) == 1
+    # a 128-row tile's byte offsets must stay below 2^31: leading dimensions below 2^23, K at most 2^23
+    assert lib.dgf_gemm_tree(binding.DGF_NT, FAKE, 1 << 23, FAKE, 8, FAKE, 8, 4, 4, 4, None, 0, None) == 2
+    assert b"leading dimension" in lib.dgf_last_error()
+    assert lib.dgf_gemm_tree(binding.DGF_NT, FAKE, (1 << 23) + 8, FAKE, (1 << 23) + 8, FAKE, 8,
+                             4, 4, (1 << 23) + 8, None, 0, None) == 2
     assert lib.dgf_act_fwd(None, FAKE, FAKE, 10, None) == 1
     assert lib.dgf_act_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == 0
