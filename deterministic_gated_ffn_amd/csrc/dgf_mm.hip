@@ -20,7 +20,7 @@
 // Tree.  The piece's midpoint tree is cut at depth UP (<= 3): every lower
 // subtree (at most 4 leaves, two compile-time sizes) is reduced in registers
 // with its static post-order as its leaves arrive, the merges of one leaf
-// issued while the next leaf's MFMAs run, and the 2^UP lower roots go through
+// issued while the next leaf's fragment reads drain, and the 2^UP lower roots go through
 // the perfect binary top of the tree, its pending left children parked in
 // the wave's own LDS region (touched once per lower subtree).  The piece root
 // goes to C or, with K split or an epilogue, to the partial buffer that the
@@ -100,9 +100,8 @@ struct MmWg {
     }
   }
 
-  // The MFMAs of the leaf in stage s: the first K half of every tile (from a
-  // zero accumulator), then the second, each half's fragments read just before
-  // its MFMAs.
+  // The MFMA fragments of K half H of the leaf in stage s: this wave's 2 A
+  // and 4 B tiles.
   template <int H>
   __device__ __forceinline__ void frags(const uint16_t *sa, const uint16_t *sb, bf16x8 (&af)[kMmTM],
                                         bf16x8 (&bf)[kMmTN]) const {
@@ -118,21 +117,6 @@ struct MmWg {
     }
   }
 
-  __device__ __forceinline__ void leaf_mfma(int s, f32x4 (&acc)[kMmTN][kMmTM]) const {
-    const uint16_t *sa = lds + (size_t)s * (kMmStage / 2), *sb = sa + kMmBM * 64;
-    bf16x8 af[kMmTM], bf[kMmTN];
-    frags<0>(sa, sb, af, bf);
-#pragma unroll
-    for (int tn = 0; tn < kMmTN; ++tn)
-#pragma unroll
-      for (int tm = 0; tm < kMmTM; ++tm) acc[tn][tm] = mfma16(bf[tn], af[tm], f32x4{0.f, 0.f, 0.f, 0.f});
-    frags<1>(sa, sb, af, bf);
-#pragma unroll
-    for (int tn = 0; tn < kMmTN; ++tn)
-#pragma unroll
-      for (int tm = 0; tm < kMmTM; ++tm) acc[tn][tm] = mfma16(bf[tn], af[tm], acc[tn][tm]);
-  }
-
   __device__ __forceinline__ void pack(const f32x4 (&acc)[kMmTN][kMmTM], uint32_t (&v)[kMmNP]) const {
 #pragma unroll
     for (int tn = 0; tn < kMmTN; ++tn)
@@ -143,9 +127,9 @@ struct MmWg {
       }
   }
 
-  // One leaf j: its MFMAs from stage (j - plo) & 1; while they run, the
-  // previous leaf of the subtree (rounded, packed) goes into the tree, the
-  // VALU work overlapping the matrix core; then this leaf is packed, leaf
+  // One leaf j: its fragment reads from stage (j - plo) & 1; while they
+  // drain, the previous leaf of the subtree (rounded, packed) goes into the
+  // tree; then its MFMAs, and this leaf is packed, leaf
   // j + 1's tiles (fetched two leaves earlier into register set `nx`) go into
   // the other stage, leaf j + 3 is fetched into that set, and the barrier
   // publishes the stage just written and frees the one just read.
@@ -153,9 +137,25 @@ struct MmWg {
   __device__ __forceinline__ void one_leaf(int j, u32x4 (&nx)[4], uint32_t (&v)[kMmNP],
                                            uint32_t (&st)[3][kMmNP]) const {
     const int s = (j - plo) & 1;
+    const uint16_t *sa = lds + (size_t)s * (kMmStage / 2), *sb = sa + kMmBM * 64;
     f32x4 acc[kMmTN][kMmTM];
-    leaf_mfma(s, acc);
+    bf16x8 af0[kMmTM], bf0[kMmTN], af1[kMmTM], bf1[kMmTN];
+    // every fragment read of the leaf goes out first, and the previous
+    // leaf's tree merges (VALU) run while the workgroup's reads drain
+    // through the LDS; then the two K halves' MFMAs
+    frags<0>(sa, sb, af0, bf0);
+    frags<1>(sa, sb, af1, bf1);
+    __builtin_amdgcn_sched_barrier(0);
     if constexpr (J > 0) push_leaf<kMmNP, NL, J - 1>(v, st);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int tn = 0; tn < kMmTN; ++tn)
+#pragma unroll
+      for (int tm = 0; tm < kMmTM; ++tm) acc[tn][tm] = mfma16(bf0[tn], af0[tm], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+    for (int tn = 0; tn < kMmTN; ++tn)
+#pragma unroll
+      for (int tm = 0; tm < kMmTM; ++tm) acc[tn][tm] = mfma16(bf1[tn], af1[tm], acc[tn][tm]);
     pack(acc, v);
     if (j + 1 < phi) stage_store(s ^ 1, nx);
     if (j + 3 < phi) fetch(j + 3, nx);
