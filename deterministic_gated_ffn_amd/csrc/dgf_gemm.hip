@@ -622,13 +622,14 @@ __global__ __launch_bounds__(256) void k_gemm_short(GemmParams p) {
 // columns c.  It copies the K x 64 A tile into LDS feature-major once, and
 // each K x 128 B tile in turn into one of two LDS buffers, with zeros past K
 // (up to the next multiple of 32: an all-zero block leaves the sum
-// unchanged), past M and past N.  The next B tile's loads are issued into
-// registers before the current tile's MFMAs and committed to the other
-// buffer after its stores, so their latency hides behind the stores.  Every
-// wave computes 16 rows x 128 columns per tile and stores them through its
-// own LDS stage as whole 256-byte row segments.
+// unchanged), past M and past N.  A B tile is transposed four operand rows
+// at a time: a thread loads 8 features of rows 4i .. 4i+3 and writes, per
+// feature, the 4 consecutive K values as one 8-byte store.  The next B
+// tile's loads are issued into registers before the current tile's MFMAs and
+// committed to the other buffer after its stores, so their latency hides
+// behind the stores.  Every wave computes 16 rows x 128 columns per tile and
+// stores them through its own LDS stage as whole 256-byte row segments.
 constexpr int kTnTile = 128;
-constexpr int kTnMaxQ = 4;  // B-tile items per thread: 64 x 16 chunks of 8 features over 256 threads
 
 // 8 consecutive features f0 .. f0+7 of operand row k, packed (zeros outside)
 __device__ __forceinline__ uint4 tn_load8(const uint16_t *src, int64_t ld, int k, int K, int64_t f0, int64_t F) {
@@ -639,14 +640,23 @@ __device__ __forceinline__ uint4 tn_load8(const uint16_t *src, int64_t ld, int k
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-// Feature f = 8 cc + e of row k lands at LDS row f, position k ^ (8 (cc & km)):
-// 16-byte K chunks permuted per feature group, which spreads the transposing
-// writes over the banks and keeps each MFMA operand read one aligned 16-byte chunk.
-__device__ __forceinline__ void tn_put8(uint16_t *dst, int ks, int km, int k, int cc, uint4 q) {
-  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-  const int kk = k ^ (8 * (cc & km));
+// Features f = 8 cc + e of operand rows 4 k4 .. 4 k4 + 3 land at LDS row f,
+// positions (4 k4) ^ (8 (cc & km)) .. + 3, one 8-byte store per feature: the
+// K chunks are permuted per feature group (the XOR moves whole 8-element
+// chunks), which spreads the transposing writes over the banks and keeps
+// each MFMA operand read one aligned 16-byte chunk.
+__device__ __forceinline__ void tn_put4x8(uint16_t *dst, int ks, int km, int k4, int cc, const uint4 (&rows)[4]) {
+  const int kk = (4 * k4) ^ (8 * (cc & km));
 #pragma unroll
-  for (int e = 0; e < 8; ++e) dst[(8 * cc + e) * ks + kk] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+  for (int e = 0; e < 8; ++e) {
+    uint32_t h[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint32_t w4[4] = {rows[r].x, rows[r].y, rows[r].z, rows[r].w};
+      h[r] = (e & 1) ? (w4[e >> 1] >> 16) : (w4[e >> 1] & 0xffffu);
+    }
+    *reinterpret_cast<uint2 *>(&dst[(8 * cc + e) * ks + kk]) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+  }
 }
 
 template <int NB>
@@ -659,35 +669,34 @@ __global__ __launch_bounds__(256) void k_gemm_tn1(GemmParams p, int ct) {
   const int KP = 32 * KH;
   const int ks = KP + 8;         // padded K stride of the feature-major tiles
   const int km = KP / 8 - 1;     // K-chunk swizzle mask: chunks stay inside the row's KP elements
-  const int nq = KP * (kTnTile / 8) / 256;  // B-tile items per thread: 2 or 4
+  // B-tile items: (4-row group k4, 8-feature chunk cc), one per thread for the first KP * 4 threads
+  const bool bq = tid < KP * (kTnTile / 8) / 4;
+  const int k4 = tid / (kTnTile / 8), bcc = tid % (kTnTile / 8);
   uint16_t *sA = tn_lds;                            // [NB][64][ks]
   uint16_t *sB0 = sA + NB * 64 * ks;                // [2][128][ks]
   uint16_t *stage = sB0 + 2 * kTnTile * ks + wave * 16 * kShortStride;  // this wave's [16][kShortStride]
   const int64_t r0 = (int64_t)blockIdx.y * 64;
   const int64_t cbase = (int64_t)xcd_tile(blockIdx.x, gridDim.x) * kTnTile * ct;
 
-  // item j of this thread: operand row k = q / 16, chunk cc = q % 16 (eight threads per 128-byte row)
-  uint4 nx[kTnMaxQ];
+  // rows 4 k4 .. 4 k4 + 3, features c0 + 8 bcc .. + 8 (sixteen threads per 128-byte row segment)
+  uint4 nx[4];
   auto load_b = [&](int64_t c0) {
+    if (bq) {
 #pragma unroll
-    for (int j = 0; j < kTnMaxQ; ++j)
-      if (j < nq) {
-        const int q = tid + 256 * j;
-        nx[j] = tn_load8(p.B[0], p.ldb[0], q / (kTnTile / 8), K, c0 + 8 * (q % (kTnTile / 8)), p.N);
-      }
+      for (int r = 0; r < 4; ++r) nx[r] = tn_load8(p.B[0], p.ldb[0], 4 * k4 + r, K, c0 + 8 * bcc, p.N);
+    }
   };
   auto put_b = [&](uint16_t *sB) {
-#pragma unroll
-    for (int j = 0; j < kTnMaxQ; ++j)
-      if (j < nq) {
-        const int q = tid + 256 * j;
-        tn_put8(sB, ks, km, q / (kTnTile / 8), q % (kTnTile / 8), nx[j]);
-      }
+    if (bq) tn_put4x8(sB, ks, km, k4, bcc, nx);
   };
   load_b(cbase);
-  for (int q = tid; q < NB * KP * 8; q += 256) {
-    const int b = q / (KP * 8), rem = q % (KP * 8), k = rem / 8, cc = rem % 8;
-    tn_put8(sA + b * 64 * ks, ks, km, k, cc, tn_load8(p.A[b], p.lda[b], k, K, r0 + 8 * cc, p.M));
+  // the A tiles: items (product b, 4-row group, 8-feature chunk of the 64 rows)
+  for (int q = tid; q < NB * (KP / 4) * 8; q += 256) {
+    const int b = q / (KP * 2), rem = q % (KP * 2), a4 = rem / 8, cc = rem % 8;
+    uint4 rows[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) rows[r] = tn_load8(p.A[b], p.lda[b], 4 * a4 + r, K, r0 + 8 * cc, p.M);
+    tn_put4x8(sA + b * 64 * ks, ks, km, a4, cc, rows);
   }
   put_b(sB0);
   __syncthreads();
