@@ -108,11 +108,26 @@ __global__ __launch_bounds__(kThreads) void k_combine_epi(GemmParams p) {
     } else if constexpr (EPI == EPI_DSILU) {
       // dA with the saved g, u: dU = bf16(dA s), dG = bf16((dA u) s'), a = bf16(s u), row-major [M, N]
       uint32_t dg[4] = {0, 0, 0, 0}, du[4] = {0, 0, 0, 0}, av[4] = {0, 0, 0, 0};
-      const int n_here = c + 8 <= p.N ? 8 : (int)(p.N - c);
-      for (int e = 0; e < n_here; ++e) {
+      uint32_t gq[4], uq[4];
+      const uint16_t *gs = p.sg + m * p.ld_gu + c, *us = p.su + m * p.ld_gu + c;
+      if (c + 8 <= p.N) {  // g and u rows are 16-byte aligned (ld a multiple of 8)
+        const uint4 gv = *reinterpret_cast<const uint4 *>(gs), uv = *reinterpret_cast<const uint4 *>(us);
+        gq[0] = gv.x; gq[1] = gv.y; gq[2] = gv.z; gq[3] = gv.w;
+        uq[0] = uv.x; uq[1] = uv.y; uq[2] = uv.z; uq[3] = uv.w;
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t e = c + 2 * q;
+          gq[q] = (e < p.N ? gs[2 * q] : 0u) | (e + 1 < p.N ? (uint32_t)gs[2 * q + 1] << 16 : 0u);
+          uq[q] = (e < p.N ? us[2 * q] : 0u) | (e + 1 < p.N ? (uint32_t)us[2 * q + 1] << 16 : 0u);
+        }
+      }
+      // all 8 lanes of the chunk are computed (columns past N are never stored)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
         const float da = bf2f(half_of(r0, e));
-        const float g = bf2f(p.sg[m * p.ld_gu + c + e]);
-        const float u = bf2f(p.su[m * p.ld_gu + c + e]);
+        const float g = bf2f(half_of(gq, e));
+        const float u = bf2f(half_of(uq, e));
         const float sg = sigma_f(g);
         const float s = g * sg;
         const float one_m = 1.0f - sg;
