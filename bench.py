@@ -246,6 +246,33 @@ def main():
             print(f"[bench] forward M={Mf}: {us:.1f} us, {gbps:.0f} GB/s", file=sys.stderr, flush=True)
         result["forward"] = fwd
         result["fwd_bwd_us"] = round(ms_step * 1e3, 2)
+        # the training step (forward with g/u saved, then backward) at 1 and 8 tokens as well
+        fb = {}
+        for Mf in (1, 8):
+            xf, dyf = x[:Mf], dy[:Mf]
+
+            def step_m(k):
+                wg, wu, wd = W[k % len(W)]
+                y, g, u = dgf.ffn_fwd(xf, wg, wu, wd, training=True)
+                return dgf.ffn_bwd(dyf, xf, g, u, wg, wu, wd)
+
+            for k in range(args.warmup):
+                step_m(k)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for k in range(args.steps):
+                step_m(k)
+            e1.record()
+            torch.cuda.synchronize()
+            us = 1e3 * e0.elapsed_time(e1) / args.steps
+            gbps = step_bytes(Mf) / (us * 1e-6) / 1e9
+            fb[str(Mf)] = {"us": round(us, 2), "GBps": round(gbps, 1), "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
+                           "algorithmic_bytes": step_bytes(Mf)}
+            print(f"[bench] fwd+bwd M={Mf}: {us:.1f} us, {gbps:.0f} GB/s", file=sys.stderr, flush=True)
+        fb["32"] = {"us": round(ms_step * 1e3, 2), "GBps": round(value, 1),
+                    "frac_hbm_peak": round(value / HBM_PEAK_GBPS, 4), "algorithmic_bytes": step_bytes(M)}
+        result["fwd_bwd"] = fb
 
     if not args.quick:
         result["long_sequence"] = long_sequence(W[0])

@@ -631,13 +631,24 @@ __global__ __launch_bounds__(256) void k_gemm_short(GemmParams p) {
 // stores them through its own LDS stage as whole 256-byte row segments.
 constexpr int kTnTile = 128;
 
-// 8 consecutive features f0 .. f0+7 of operand row k, packed (zeros outside)
+// 8 consecutive features f0 .. f0+7 of operand row k, packed.  A row past K
+// (the zero padding of the MFMA's K) loads row 0 (K >= 1) instead, and the
+// caller zeroes it when it writes the tile (tn_zero_rows), so that no value
+// is needed until then; features past F read as zero.
 __device__ __forceinline__ uint4 tn_load8(const uint16_t *src, int64_t ld, int k, int K, int64_t f0, int64_t F) {
-  if (k < K && f0 + 8 <= F) return *reinterpret_cast<const uint4 *>(src + (int64_t)k * ld + f0);
+  const int64_t row = k < K ? k : 0;
+  if (f0 + 8 <= F) return *reinterpret_cast<const uint4 *>(src + row * ld + f0);
   uint32_t w[4] = {0u, 0u, 0u, 0u};
   for (int e = 0; e < 8; ++e)
-    if (k < K && f0 + e < F) w[e >> 1] |= (uint32_t)src[(int64_t)k * ld + f0 + e] << (16 * (e & 1));
+    if (f0 + e < F) w[e >> 1] |= (uint32_t)src[row * ld + f0 + e] << (16 * (e & 1));
   return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// Zeroes the rows 4 k4 + r past K of a four-row group.
+__device__ __forceinline__ void tn_zero_rows(uint4 (&rows)[4], int k4, int K) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    if (4 * k4 + r >= K) rows[r] = make_uint4(0u, 0u, 0u, 0u);
 }
 
 // Features f = 8 cc + e of operand rows 4 k4 .. 4 k4 + 3 land at LDS row f,
@@ -687,7 +698,10 @@ __global__ __launch_bounds__(256) void k_gemm_tn1(GemmParams p, int ct) {
     }
   };
   auto put_b = [&](uint16_t *sB) {
-    if (bq) tn_put4x8(sB, ks, km, k4, bcc, nx);
+    if (bq) {
+      tn_zero_rows(nx, k4, K);
+      tn_put4x8(sB, ks, km, k4, bcc, nx);
+    }
   };
   load_b(cbase);
   // the A tiles: items (product b, 4-row group, 8-feature chunk of the 64 rows)
@@ -696,6 +710,7 @@ __global__ __launch_bounds__(256) void k_gemm_tn1(GemmParams p, int ct) {
     uint4 rows[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) rows[r] = tn_load8(p.A[b], p.lda[b], 4 * a4 + r, K, r0 + 8 * cc, p.M);
+    tn_zero_rows(rows, a4, K);
     tn_put4x8(sA + b * 64 * ks, ks, km, a4, cc, rows);
   }
   put_b(sB0);
