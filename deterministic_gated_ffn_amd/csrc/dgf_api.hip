@@ -35,7 +35,14 @@ dgf_status hip_check(hipError_t e, const char *what) {
   return DGF_OK;
 }
 
-// Kernel timing hook: caller-created events recorded around each launch.
+}  // namespace
+
+thread_local hipEvent_t dgf::g_launch_events[2] = {nullptr, nullptr};
+
+namespace {
+
+// Kernel timing hook: caller-created events, one pair per launch, recorded
+// as each kernel's own start and end.
 struct Prof {
   hipEvent_t *ev = nullptr;
   int pairs = 0;
@@ -48,12 +55,16 @@ template <class F>
 hipError_t timed(hipStream_t s, const char *name, F &&launch) {
   const int k = g_prof.used;
   const bool rec = g_prof.ev && k < g_prof.pairs;
-  if (rec) {
-    hipError_t e = hipEventRecord(g_prof.ev[2 * k], s);
-    if (e != hipSuccess) return e;
+  if (rec) {  // the launch records them as its kernel's start and end
+    g_launch_events[0] = g_prof.ev[2 * k];
+    g_launch_events[1] = g_prof.ev[2 * k + 1];
   }
   hipError_t e = launch();
-  if (rec && e == hipSuccess) e = hipEventRecord(g_prof.ev[2 * k + 1], s);
+  if (rec && g_launch_events[0]) {  // no kernel took them: an empty interval
+    g_launch_events[0] = g_launch_events[1] = nullptr;
+    if (e == hipSuccess) e = hipEventRecord(g_prof.ev[2 * k], s);
+    if (e == hipSuccess) e = hipEventRecord(g_prof.ev[2 * k + 1], s);
+  }
   if (g_prof.ev) {
     if (k < 4096) g_prof.names[k] = name;
     g_prof.used = k + 1;
@@ -350,7 +361,7 @@ dgf_status zero_mat(uint16_t *C, int64_t ldc, int64_t M, int64_t N, hipStream_t 
   int64_t blocks = (M * N + 255) / 256;
   if (blocks > 65536) blocks = 65536;
   return hip_check(timed(s, "zero fill", [&] {
-                     hipLaunchKernelGGL(k_zero2d, dim3((unsigned)blocks), dim3(256), 0, s, C, ldc, M, N);
+                     dgf_launch(k_zero2d, dim3((unsigned)blocks), dim3(256), 0, s, C, ldc, M, N);
                      return hipGetLastError();
                    }),
                    "zero fill");

@@ -205,16 +205,16 @@ hipError_t launch_allk_mt(const AllkParams &p, int nw, hipStream_t s) {
   const dim3 grid((unsigned)((p.N + kAkCols - 1) / kAkCols)), block(kAkWaves * 64);
   const size_t shm = AkLds<MT>::total;
   switch (nw) {
-    case 1: hipLaunchKernelGGL((k_allk<MT, 1>), grid, block, shm, s, p); break;
-    case 2: hipLaunchKernelGGL((k_allk<MT, 2>), grid, block, shm, s, p); break;
-    case 3: hipLaunchKernelGGL((k_allk<MT, 3>), grid, block, shm, s, p); break;
-    case 4: hipLaunchKernelGGL((k_allk<MT, 4>), grid, block, shm, s, p); break;
-    case 6: hipLaunchKernelGGL((k_allk<MT, 6>), grid, block, shm, s, p); break;
-    case 8: hipLaunchKernelGGL((k_allk<MT, 8>), grid, block, shm, s, p); break;
-    case 12: hipLaunchKernelGGL((k_allk<MT, 12>), grid, block, shm, s, p); break;
-    case 16: hipLaunchKernelGGL((k_allk<MT, 16>), grid, block, shm, s, p); break;
-    case 24: hipLaunchKernelGGL((k_allk<MT, 24>), grid, block, shm, s, p); break;
-    case 32: hipLaunchKernelGGL((k_allk<MT, 32>), grid, block, shm, s, p); break;
+    case 1: dgf_launch((k_allk<MT, 1>), grid, block, shm, s, p); break;
+    case 2: dgf_launch((k_allk<MT, 2>), grid, block, shm, s, p); break;
+    case 3: dgf_launch((k_allk<MT, 3>), grid, block, shm, s, p); break;
+    case 4: dgf_launch((k_allk<MT, 4>), grid, block, shm, s, p); break;
+    case 6: dgf_launch((k_allk<MT, 6>), grid, block, shm, s, p); break;
+    case 8: dgf_launch((k_allk<MT, 8>), grid, block, shm, s, p); break;
+    case 12: dgf_launch((k_allk<MT, 12>), grid, block, shm, s, p); break;
+    case 16: dgf_launch((k_allk<MT, 16>), grid, block, shm, s, p); break;
+    case 24: dgf_launch((k_allk<MT, 24>), grid, block, shm, s, p); break;
+    case 32: dgf_launch((k_allk<MT, 32>), grid, block, shm, s, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

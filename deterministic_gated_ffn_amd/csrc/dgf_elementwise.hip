@@ -371,13 +371,13 @@ __global__ __launch_bounds__(kThreads) void k_transpose(const uint16_t *src, int
 }  // namespace
 
 hipError_t launch_act_fwd(const uint16_t *g, const uint16_t *u, uint16_t *a, int64_t n, hipStream_t s) {
-  hipLaunchKernelGGL(k_act_fwd, dim3(grid_for(n, 1)), dim3(kThreads), 0, s, g, u, a, n);
+  dgf_launch(k_act_fwd, dim3(grid_for(n, 1)), dim3(kThreads), 0, s, g, u, a, n);
   return hipGetLastError();
 }
 
 hipError_t launch_act_bwd(const uint16_t *da, const uint16_t *g, const uint16_t *u, uint16_t *dg, uint16_t *du,
                           uint16_t *a, int64_t n, hipStream_t s) {
-  hipLaunchKernelGGL(k_act_bwd, dim3(grid_for(n, 1)), dim3(kThreads), 0, s, da, g, u, dg, du, a, n);
+  dgf_launch(k_act_bwd, dim3(grid_for(n, 1)), dim3(kThreads), 0, s, da, g, u, dg, du, a, n);
   return hipGetLastError();
 }
 
@@ -392,20 +392,20 @@ hipError_t launch_combine(const uint16_t *const *parts, int S, uint16_t *out, in
   if (nvec > 0) {
     const dim3 g(grid_for(nvec, 1));
     switch (S) {
-      case 1: hipLaunchKernelGGL(k_combine_vec<1>, g, dim3(kThreads), 0, s, P, out, nvec); break;
-      case 2: hipLaunchKernelGGL(k_combine_vec<2>, g, dim3(kThreads), 0, s, P, out, nvec); break;
-      case 4: hipLaunchKernelGGL(k_combine_vec<4>, g, dim3(kThreads), 0, s, P, out, nvec); break;
-      default: hipLaunchKernelGGL(k_combine_vec<8>, g, dim3(kThreads), 0, s, P, out, nvec); break;
+      case 1: dgf_launch(k_combine_vec<1>, g, dim3(kThreads), 0, s, P, out, nvec); break;
+      case 2: dgf_launch(k_combine_vec<2>, g, dim3(kThreads), 0, s, P, out, nvec); break;
+      case 4: dgf_launch(k_combine_vec<4>, g, dim3(kThreads), 0, s, P, out, nvec); break;
+      default: dgf_launch(k_combine_vec<8>, g, dim3(kThreads), 0, s, P, out, nvec); break;
     }
   }
   const int64_t begin = nvec * 8;
   if (begin < n) {
     const dim3 g(grid_for(n - begin, 1));
     switch (S) {
-      case 1: hipLaunchKernelGGL(k_combine_scalar<1>, g, dim3(kThreads), 0, s, P, out, begin, n); break;
-      case 2: hipLaunchKernelGGL(k_combine_scalar<2>, g, dim3(kThreads), 0, s, P, out, begin, n); break;
-      case 4: hipLaunchKernelGGL(k_combine_scalar<4>, g, dim3(kThreads), 0, s, P, out, begin, n); break;
-      default: hipLaunchKernelGGL(k_combine_scalar<8>, g, dim3(kThreads), 0, s, P, out, begin, n); break;
+      case 1: dgf_launch(k_combine_scalar<1>, g, dim3(kThreads), 0, s, P, out, begin, n); break;
+      case 2: dgf_launch(k_combine_scalar<2>, g, dim3(kThreads), 0, s, P, out, begin, n); break;
+      case 4: dgf_launch(k_combine_scalar<4>, g, dim3(kThreads), 0, s, P, out, begin, n); break;
+      default: dgf_launch(k_combine_scalar<8>, g, dim3(kThreads), 0, s, P, out, begin, n); break;
     }
   }
   return hipGetLastError();
@@ -424,20 +424,20 @@ hipError_t launch_combine_t(const void *const *parts, int S, void *out, int64_t 
   if (nvec > 0) {
     const dim3 g(grid_for(nvec, 1));
     switch (S) {
-      case 1: hipLaunchKernelGGL((k_combine_vec_t<1, DT>), g, dim3(kThreads), 0, s, pv, out, nvec); break;
-      case 2: hipLaunchKernelGGL((k_combine_vec_t<2, DT>), g, dim3(kThreads), 0, s, pv, out, nvec); break;
-      case 4: hipLaunchKernelGGL((k_combine_vec_t<4, DT>), g, dim3(kThreads), 0, s, pv, out, nvec); break;
-      default: hipLaunchKernelGGL((k_combine_vec_t<8, DT>), g, dim3(kThreads), 0, s, pv, out, nvec); break;
+      case 1: dgf_launch((k_combine_vec_t<1, DT>), g, dim3(kThreads), 0, s, pv, out, nvec); break;
+      case 2: dgf_launch((k_combine_vec_t<2, DT>), g, dim3(kThreads), 0, s, pv, out, nvec); break;
+      case 4: dgf_launch((k_combine_vec_t<4, DT>), g, dim3(kThreads), 0, s, pv, out, nvec); break;
+      default: dgf_launch((k_combine_vec_t<8, DT>), g, dim3(kThreads), 0, s, pv, out, nvec); break;
     }
   }
   const int64_t begin = nvec * P;
   if (begin < n) {
     const dim3 g(grid_for(n - begin, 1));
     switch (S) {
-      case 1: hipLaunchKernelGGL((k_combine_scalar_t<1, DT>), g, dim3(kThreads), 0, s, pv, out, begin, n); break;
-      case 2: hipLaunchKernelGGL((k_combine_scalar_t<2, DT>), g, dim3(kThreads), 0, s, pv, out, begin, n); break;
-      case 4: hipLaunchKernelGGL((k_combine_scalar_t<4, DT>), g, dim3(kThreads), 0, s, pv, out, begin, n); break;
-      default: hipLaunchKernelGGL((k_combine_scalar_t<8, DT>), g, dim3(kThreads), 0, s, pv, out, begin, n); break;
+      case 1: dgf_launch((k_combine_scalar_t<1, DT>), g, dim3(kThreads), 0, s, pv, out, begin, n); break;
+      case 2: dgf_launch((k_combine_scalar_t<2, DT>), g, dim3(kThreads), 0, s, pv, out, begin, n); break;
+      case 4: dgf_launch((k_combine_scalar_t<4, DT>), g, dim3(kThreads), 0, s, pv, out, begin, n); break;
+      default: dgf_launch((k_combine_scalar_t<8, DT>), g, dim3(kThreads), 0, s, pv, out, begin, n); break;
     }
   }
   return hipGetLastError();
@@ -456,11 +456,11 @@ hipError_t launch_combine_2d(const uint16_t *part, int64_t part_stride, int64_t 
                              int64_t M, int64_t N, hipStream_t s) {
   const dim3 g(grid_for(M * ((N + 7) / 8), 1));
   switch (S) {
-    case 1: hipLaunchKernelGGL(k_combine_2d<1>, g, dim3(kThreads), 0, s, part, part_stride, ldp, out, ldo, M, N); break;
-    case 2: hipLaunchKernelGGL(k_combine_2d<2>, g, dim3(kThreads), 0, s, part, part_stride, ldp, out, ldo, M, N); break;
-    case 4: hipLaunchKernelGGL(k_combine_2d<4>, g, dim3(kThreads), 0, s, part, part_stride, ldp, out, ldo, M, N); break;
-    case 8: hipLaunchKernelGGL(k_combine_2d<8>, g, dim3(kThreads), 0, s, part, part_stride, ldp, out, ldo, M, N); break;
-    case 16: hipLaunchKernelGGL(k_combine_2d<16>, g, dim3(kThreads), 0, s, part, part_stride, ldp, out, ldo, M, N); break;
+    case 1: dgf_launch(k_combine_2d<1>, g, dim3(kThreads), 0, s, part, part_stride, ldp, out, ldo, M, N); break;
+    case 2: dgf_launch(k_combine_2d<2>, g, dim3(kThreads), 0, s, part, part_stride, ldp, out, ldo, M, N); break;
+    case 4: dgf_launch(k_combine_2d<4>, g, dim3(kThreads), 0, s, part, part_stride, ldp, out, ldo, M, N); break;
+    case 8: dgf_launch(k_combine_2d<8>, g, dim3(kThreads), 0, s, part, part_stride, ldp, out, ldo, M, N); break;
+    case 16: dgf_launch(k_combine_2d<16>, g, dim3(kThreads), 0, s, part, part_stride, ldp, out, ldo, M, N); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -468,14 +468,14 @@ hipError_t launch_combine_2d(const uint16_t *part, int64_t part_stride, int64_t 
 
 hipError_t launch_add_lanes(const uint16_t *G, int64_t ldg, const uint16_t *U, int64_t ldu, uint16_t *dx,
                             int64_t lddx, int64_t M, int64_t N, hipStream_t s) {
-  hipLaunchKernelGGL(k_add_lanes, dim3(grid_for(M * ((N + 7) / 8), 1)), dim3(kThreads), 0, s, G, ldg, U, ldu, dx, lddx, M, N);
+  dgf_launch(k_add_lanes, dim3(grid_for(M * ((N + 7) / 8), 1)), dim3(kThreads), 0, s, G, ldg, U, ldu, dx, lddx, M, N);
   return hipGetLastError();
 }
 
 hipError_t launch_transpose(const uint16_t *src, int64_t lds_, int64_t R, int64_t C, uint16_t *dst, int64_t ldd,
                             hipStream_t s) {
   const dim3 g((unsigned)((C + 63) / 64), (unsigned)((R + 63) / 64));
-  hipLaunchKernelGGL(k_transpose, g, dim3(kThreads), 0, s, src, lds_, R, C, dst, ldd);
+  dgf_launch(k_transpose, g, dim3(kThreads), 0, s, src, lds_, R, C, dst, ldd);
   return hipGetLastError();
 }
 
@@ -484,12 +484,12 @@ template <int EPI>
 hipError_t launch_combine_epi_s(int S, int nb, GemmParams p, hipStream_t s) {
   const dim3 g(grid_for(p.M * ((p.N + 7) / 8), 1), EPI == EPI_STORE ? nb : 1);
   switch (S) {
-    case 1: hipLaunchKernelGGL((k_combine_epi<1, EPI>), g, dim3(kThreads), 0, s, p); break;
-    case 2: hipLaunchKernelGGL((k_combine_epi<2, EPI>), g, dim3(kThreads), 0, s, p); break;
-    case 4: hipLaunchKernelGGL((k_combine_epi<4, EPI>), g, dim3(kThreads), 0, s, p); break;
-    case 8: hipLaunchKernelGGL((k_combine_epi<8, EPI>), g, dim3(kThreads), 0, s, p); break;
-    case 16: hipLaunchKernelGGL((k_combine_epi<16, EPI>), g, dim3(kThreads), 0, s, p); break;
-    case 32: hipLaunchKernelGGL((k_combine_epi<32, EPI>), g, dim3(kThreads), 0, s, p); break;
+    case 1: dgf_launch((k_combine_epi<1, EPI>), g, dim3(kThreads), 0, s, p); break;
+    case 2: dgf_launch((k_combine_epi<2, EPI>), g, dim3(kThreads), 0, s, p); break;
+    case 4: dgf_launch((k_combine_epi<4, EPI>), g, dim3(kThreads), 0, s, p); break;
+    case 8: dgf_launch((k_combine_epi<8, EPI>), g, dim3(kThreads), 0, s, p); break;
+    case 16: dgf_launch((k_combine_epi<16, EPI>), g, dim3(kThreads), 0, s, p); break;
+    case 32: dgf_launch((k_combine_epi<32, EPI>), g, dim3(kThreads), 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -790,18 +790,18 @@ hipError_t launch_gemm_tn1(int nb, GemmParams p, hipStream_t stream) {
   dim3 grid((unsigned)((tiles_c + ct - 1) / ct), (unsigned)tiles_r);
   const size_t shm = tn1_lds_bytes(nb, p.K);
   if (nb == 1)
-    hipLaunchKernelGGL((k_gemm_tn1<1>), grid, dim3(256), shm, stream, p, ct);
+    dgf_launch((k_gemm_tn1<1>), grid, dim3(256), shm, stream, p, ct);
   else
-    hipLaunchKernelGGL((k_gemm_tn1<2>), grid, dim3(256), shm, stream, p, ct);
+    dgf_launch((k_gemm_tn1<2>), grid, dim3(256), shm, stream, p, ct);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_short(int nb, GemmParams p, hipStream_t stream) {
   dim3 grid((unsigned)((p.N + kShortN - 1) / kShortN), (unsigned)((p.M + 63) / 64));
   if (nb == 1)
-    hipLaunchKernelGGL((k_gemm_short<1>), grid, dim3(256), 0, stream, p);
+    dgf_launch((k_gemm_short<1>), grid, dim3(256), 0, stream, p);
   else
-    hipLaunchKernelGGL((k_gemm_short<2>), grid, dim3(256), 0, stream, p);
+    dgf_launch((k_gemm_short<2>), grid, dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -811,9 +811,9 @@ hipError_t launch_gemm_short(int nb, GemmParams p, hipStream_t stream) {
   {                                                                                                         \
     const size_t shm = (size_t)waves * p.stack_slots * (NB * RT * MT * 2) * 64 * 4;                         \
     switch (waves) {                                                                                        \
-      case 1: hipLaunchKernelGGL((KERNEL<NB, RT, MT, 1, EPI>), grid, dim3(64), shm, stream, p); break;      \
-      case 2: hipLaunchKernelGGL((KERNEL<NB, RT, MT, 2, EPI>), grid, dim3(128), shm, stream, p); break;     \
-      default: hipLaunchKernelGGL((KERNEL<NB, RT, MT, 4, EPI>), grid, dim3(256), shm, stream, p); break;    \
+      case 1: dgf_launch((KERNEL<NB, RT, MT, 1, EPI>), grid, dim3(64), shm, stream, p); break;      \
+      case 2: dgf_launch((KERNEL<NB, RT, MT, 2, EPI>), grid, dim3(128), shm, stream, p); break;     \
+      default: dgf_launch((KERNEL<NB, RT, MT, 4, EPI>), grid, dim3(256), shm, stream, p); break;    \
     }                                                                                                       \
   }
 

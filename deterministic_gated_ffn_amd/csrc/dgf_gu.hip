@@ -289,9 +289,9 @@ hipError_t launch_gu_act(const GuParams &p, hipStream_t stream) {
   const int64_t groups = (tiles_n + per - 1) / per;
   const dim3 grid((unsigned)groups, 1u), block(kGuWaves * 64);
   if (mt == 1)
-    hipLaunchKernelGGL(k_gate_up_act<1>, grid, block, GuLds<1>::total, stream, p);
+    dgf_launch(k_gate_up_act<1>, grid, block, GuLds<1>::total, stream, p);
   else
-    hipLaunchKernelGGL(k_gate_up_act<2>, grid, block, GuLds<2>::total, stream, p);
+    dgf_launch(k_gate_up_act<2>, grid, block, GuLds<2>::total, stream, p);
   return hipGetLastError();
 }
 

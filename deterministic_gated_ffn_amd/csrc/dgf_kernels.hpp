@@ -1,10 +1,28 @@
 // Host-visible kernel interfaces of libdgf (internal; the public ABI is include/dgf.h).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace dgf {
+
+// Start/stop events for the next kernel launch, set by the library's timing
+// hook: the launch then records them as the kernel's own start and end
+// timestamps (hipExtLaunchKernelGGL), so a timed launch measures the kernel
+// alone, without the gaps of separate event packets around it.
+extern thread_local hipEvent_t g_launch_events[2];
+
+template <typename F, typename... Args>
+inline void dgf_launch(F kernel, dim3 grid, dim3 block, size_t shm, hipStream_t s, Args... args) {
+  if (g_launch_events[0]) {
+    hipEvent_t start = g_launch_events[0], stop = g_launch_events[1];
+    g_launch_events[0] = g_launch_events[1] = nullptr;
+    hipExtLaunchKernelGGL(kernel, grid, block, (std::uint32_t)shm, s, start, stop, 0u, args...);
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, shm, s, args...);
+  }
+}
 
 enum { DGF_LAYOUT_NT = 0, DGF_LAYOUT_NN = 1, DGF_LAYOUT_TN = 2 };
 enum { EPI_STORE = 0, EPI_ACT = 1, EPI_DSILU = 2, EPI_DX = 3 };

@@ -310,10 +310,10 @@ hipError_t launch_mm(GemmParams p, int nb, int nlh, hipStream_t stream) {
   const dim3 block(kMmWaves * 64);
   const size_t shm = mm_lds_bytes();
   switch (nlh) {
-    case 1: hipLaunchKernelGGL(k_mm<1>, grid, block, shm, stream, p); break;
-    case 2: hipLaunchKernelGGL(k_mm<2>, grid, block, shm, stream, p); break;
-    case 3: hipLaunchKernelGGL(k_mm<3>, grid, block, shm, stream, p); break;
-    case 4: hipLaunchKernelGGL(k_mm<4>, grid, block, shm, stream, p); break;
+    case 1: dgf_launch(k_mm<1>, grid, block, shm, stream, p); break;
+    case 2: dgf_launch(k_mm<2>, grid, block, shm, stream, p); break;
+    case 3: dgf_launch(k_mm<3>, grid, block, shm, stream, p); break;
+    case 4: dgf_launch(k_mm<4>, grid, block, shm, stream, p); break;
     default: return hipErrorInvalidValue;  // lower subtrees hold at most kMmMaxNL leaves
   }
   return hipGetLastError();

@@ -484,14 +484,14 @@ hipError_t launch_xs(int layout, GemmParams p, int nb, int waves, int groups, hi
   const size_t shm = xs_lds_bytes(layout, mt, waves);
   if (layout == DGF_LAYOUT_NT) {
     if (mt == 1)
-      hipLaunchKernelGGL((k_xs<DGF_LAYOUT_NT, 1>), grid, block, shm, stream, p);
+      dgf_launch((k_xs<DGF_LAYOUT_NT, 1>), grid, block, shm, stream, p);
     else
-      hipLaunchKernelGGL((k_xs<DGF_LAYOUT_NT, 2>), grid, block, shm, stream, p);
+      dgf_launch((k_xs<DGF_LAYOUT_NT, 2>), grid, block, shm, stream, p);
   } else {
     if (mt == 1)
-      hipLaunchKernelGGL((k_xs<DGF_LAYOUT_NN, 1>), grid, block, shm, stream, p);
+      dgf_launch((k_xs<DGF_LAYOUT_NN, 1>), grid, block, shm, stream, p);
     else
-      hipLaunchKernelGGL((k_xs<DGF_LAYOUT_NN, 2>), grid, block, shm, stream, p);
+      dgf_launch((k_xs<DGF_LAYOUT_NN, 2>), grid, block, shm, stream, p);
   }
   return hipGetLastError();
 }
