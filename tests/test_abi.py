@@ -132,3 +132,18 @@ def test_gemm_validation(lib):
                              4, 4, (1 << 23) + 8, None, 0, None) == 2
     assert lib.dgf_act_fwd(None, FAKE, FAKE, 10, None) == 1
     assert lib.dgf_act_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == 0
+
+
+def test_profile_hook_validation(lib):
+    assert lib.dgf_profile_begin(None, 1) == 1
+    assert lib.dgf_profile_begin(None, -1) == 1
+    arr = (ctypes.c_void_p * 2)(FAKE, None)
+    assert lib.dgf_profile_begin(arr, 1) == 1
+    assert b"NULL" in lib.dgf_last_error()
+    # no events: nothing is recorded, and a call that launches nothing counts nothing
+    assert lib.dgf_profile_begin(None, 0) == 0
+    arr4 = (ctypes.c_void_p * 4)(*([FAKE] * 4))
+    assert lib.dgf_tree_combine_typed(arr4, 4, FAKE, 0, binding.DGF_BF16, None) == 0
+    assert lib.dgf_profile_end() == 0
+    assert lib.dgf_profile_name(0) == b""
+    assert lib.dgf_profile_name(-1) == b""

@@ -474,3 +474,28 @@ def test_sub_leaf_token_shards_need_the_gather():
     got = dgf.gemm_tree("TN", dev(dg), dev(x))  # the gathered tokens: one leaf over all 32
     torch.cuda.synchronize()
     assert_bitwise(got, full, "gathered dW")
+
+
+def test_kernel_timing_hook_keeps_results_and_times_each_launch():
+    """The timing hook hands its events to the launches themselves: the timed
+    call gives the same bits, every launch gets a positive duration, and the
+    durations fit inside the call's own wall time."""
+    rng = np.random.default_rng(11)
+    M, H, I = 32, 512, 1024
+    x = dev(rnd(rng, (M, H)))
+    wg, wu, wd = (dev(rnd(rng, s, 0.02)) for s in ((I, H), (I, H), (H, I)))
+    y0 = inputs.bits(dgf.ffn_fwd(x, wg, wu, wd))
+    timer = dgf.KernelTimer(max_kernels=16)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    timer.start()
+    y1 = dgf.ffn_fwd(x, wg, wu, wd)
+    timer.stop()
+    e1.record()
+    torch.cuda.synchronize()
+    assert (inputs.bits(y1) == y0).all(), "a timed call changed the result"
+    d = timer.durations_ms()
+    assert timer.count == len(d) >= 2
+    assert d[0][0] == "gate/up + act"
+    assert all(ms > 0 for _, ms in d), d
+    assert sum(ms for _, ms in d) <= e0.elapsed_time(e1) * 1.05, (d, e0.elapsed_time(e1))
