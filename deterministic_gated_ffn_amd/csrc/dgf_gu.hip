@@ -205,26 +205,42 @@ struct GuWave {
 #pragma unroll
     for (int g = 0; g < PR - 1; ++g) load_unit(g / (2 * NL), (g % (2 * NL)) / NL, g % NL, ring[g], voff);
     // activation fragments of this wave's leaves: the first NR in registers,
-    // the rest in LDS (rows past M clamped to a valid row; never stored)
+    // the rest in LDS.  They are loaded as whole 128-byte row segments (lane:
+    // row 8 s + lane / 8 of token block t, 16-byte chunk lane % 8 of the leaf;
+    // rows past M clamped to a valid row, never stored), every row segment
+    // by one instruction, and rearranged into the MFMA layout through the
+    // wave's slab, as the weight units are.  Fragment-layout loads would
+    // split every line over two instructions.
     bf16x8 xr[NR][MT][2];
-    const uint16_t *arow[MT];
+    u32x4 raw[NL][MT][2];
 #pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      const int64_t m = m0 + 16 * t + r16 < p.M ? m0 + 16 * t + r16 : p.M - 1;
-      arow[t] = p.x + m * p.ldx;
-    }
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int64_t r = m0 + 16 * t + 8 * s + (lane >> 3);
+        const uint16_t *row = p.x + (r < p.M ? r : p.M - 1) * p.ldx + 8 * (lane & 7);
+#pragma unroll
+        for (int j = 0; j < NL; ++j)
+          raw[j][t][s] = __builtin_bit_cast(u32x4, load_frag(row, (int64_t)(lo + j) * kLeaf));
+      }
+    const int wr = lane >> 3, wc = lane & 7;
 #pragma unroll
     for (int j = 0; j < NL; ++j)
 #pragma unroll
-      for (int t = 0; t < MT; ++t)
+      for (int t = 0; t < MT; ++t) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s) *reinterpret_cast<u32x4 *>(&slab[(8 * s + wr) * 64 + 8 * (wc ^ wr)]) = raw[j][t][s];
+        wave_lds_sync();
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-          const bf16x8 f = load_frag(arow[t], (int64_t)(lo + j) * kLeaf + 32 * s + 8 * g4);
+          const bf16x8 f = *reinterpret_cast<const bf16x8 *>(&slab[r16 * 64 + 8 * ((4 * s + g4) ^ (r16 & 7))]);
           if (j < NR)
             xr[j < NR ? j : 0][t][s] = f;
           else
             xl[((j - NR) * MT + t) * 2 * 64 + s * 64 + lane] = __builtin_bit_cast(u32x4, f);
         }
+        wave_lds_sync();  // the slab's reads are done before it is rewritten
+      }
     wave_lds_sync();
     for (int i = 0; i < T; ++i) {
       uint32_t v[NP], st[3][NP], rg[NP];
