@@ -374,23 +374,41 @@ struct XsWave {
   __device__ __forceinline__ void run() const {
     constexpr int NF = NL - (TAIL ? 1 : 0);
     if (T <= 0) return;  // no tile for this workgroup (the same for all its waves)
-    // stationary activation fragments of this wave's leaves (rows past M clamped)
+    // stationary activation fragments of this wave's leaves, loaded as whole
+    // 128-byte row segments (lane: row 8 s + lane / 8 of token block t,
+    // 16-byte chunk lane % 8 of the leaf; rows past M clamped, never stored;
+    // zeros past K) and rearranged into the MFMA layout through this wave's
+    // slab: fragment-layout loads would split every line over two instructions
     XFrag<MT> xs;
-    const uint16_t *arow[MT];
-#pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      const int64_t m = m0 + 16 * t + r16 < p.M ? m0 + 16 * t + r16 : p.M - 1;
-      arow[t] = p.A[b] + m * p.lda[b];
-    }
-#pragma unroll
-    for (int j = 0; j < NL; ++j)
+    {
+      u32x4 raw[NL][MT][2];
 #pragma unroll
       for (int t = 0; t < MT; ++t)
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-          const int64_t k = (int64_t)(lo + j) * kLeaf + 32 * s + 8 * g4;
-          xs.v[j][t][s] = (TAIL && j == NF) ? load_frag_tail(arow[t], k, p.K) : load_frag(arow[t], k);
+          const int64_t r = m0 + 16 * t + 8 * s + (lane >> 3);
+          const uint16_t *row = p.A[b] + (r < p.M ? r : p.M - 1) * p.lda[b];
+#pragma unroll
+          for (int j = 0; j < NL; ++j) {
+            const int64_t k = (int64_t)(lo + j) * kLeaf + 8 * (lane & 7);
+            raw[j][t][s] = __builtin_bit_cast(u32x4, (TAIL && j == NF) ? load_frag_tail(row, k, p.K) : load_frag(row, k));
+          }
         }
+      const int wr = lane >> 3, wc = lane & 7;
+#pragma unroll
+      for (int j = 0; j < NL; ++j)
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+#pragma unroll
+          for (int s = 0; s < 2; ++s)
+            *reinterpret_cast<u32x4 *>(&slab[(8 * s + wr) * 64 + 8 * (wc ^ wr)]) = raw[j][t][s];
+          wave_lds_sync();
+#pragma unroll
+          for (int s = 0; s < 2; ++s)
+            xs.v[j][t][s] = *reinterpret_cast<const bf16x8 *>(&slab[r16 * 64 + 8 * ((4 * s + g4) ^ (r16 & 7))]);
+          wave_lds_sync();  // the slab's reads are done before it is rewritten
+        }
+    }
     WF ring[PR];
     uint32_t voff[2 * RT];
     unit_offsets(voff);
