@@ -1,6 +1,6 @@
 // All-K tree GEMM for few tokens (gfx950): the down projection.
 //
-// C[m][n] = T_K( A[m,:] . B[n,:] ) for M <= 16 tokens, A [M, K] and B [N, K]
+// C[m][n] = T_K( A[m,:] . B[n,:] ) for M <= 24 tokens, A [M, K] and B [N, K]
 // both K-contiguous, with the canonical tree of RL-Kernel PR #325, section
 // "Design".  The activation operand of the down projection (a, M x I) is a
 // few hundred KB, small enough to be read from L2 by every workgroup, so
@@ -17,9 +17,9 @@
 // Every workgroup reads all of A: 16 M_pad x 128 bytes of activation per
 // 2 KB weight leaf.  A compute unit keeps only so many cache-line misses in
 // flight, so activation lines compete with weight lines for them; measured on
-// the Qwen3-8B down projection, one 16-token tile (activation at most equal
-// to weight traffic) beats the split-K kernel with its join, two tiles (17 to
-// 32 tokens, twice the weight traffic) do not, so only one is built.
+// the Qwen3-8B down projection, the all-K kernel beats the split-K kernel
+// with its join up to 24 tokens (two token tiles from 17), and loses past
+// that, when the activation lines outgrow what the join costs.
 #include "dgf_device.hpp"
 #include "dgf_kernels.hpp"
 
@@ -223,7 +223,7 @@ hipError_t launch_allk_mt(const AllkParams &p, int nw, hipStream_t s) {
 }  // namespace
 
 bool allk_applies(int64_t M, int64_t N, int64_t K) {
-  if (M < 1 || M > 16 || N < 1 || K % kLeaf != 0) return false;
+  if (M < 1 || M > 24 || N < 1 || K % kLeaf != 0) return false;
   const int64_t L = K / kLeaf;
   if (L % kAkWaves != 0) return false;
   const int64_t nw = L / kAkWaves;
@@ -232,7 +232,8 @@ bool allk_applies(int64_t M, int64_t N, int64_t K) {
 }
 
 hipError_t launch_allk(const AllkParams &p, hipStream_t stream) {
-  if (p.M > 16) return hipErrorInvalidValue;
+  if (p.M > 24) return hipErrorInvalidValue;
+  if (p.M > 16) return launch_allk_mt<2>(p, p.L / kAkWaves, stream);
   return launch_allk_mt<1>(p, p.L / kAkWaves, stream);
 }
 

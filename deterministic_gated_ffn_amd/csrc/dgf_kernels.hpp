@@ -87,7 +87,7 @@ hipError_t launch_gu_act(const GuParams &p, hipStream_t stream);
 
 // All-K tree GEMM for few tokens (dgf_dn.hip): C [M, N] = A [M, K] B [N, K]^T,
 // both K-contiguous, one workgroup per 16 output columns reducing all of K
-// (no partial roots, no join).  Applies to M <= 16, K a multiple of 64 and
+// (no partial roots, no join).  Applies to M <= 24, K a multiple of 64 and
 // L / 8 leaves per wave in {1, 2, 3, 4, 6, 8, 12, 16, 24, 32}.
 struct AllkParams {
   const uint16_t *A;
