@@ -54,6 +54,7 @@ def kernel_bytes(name: str, M: int) -> int | None:
         "dA tree GEMM": W + act_mh + act_mi,                      # W_down, dY -> dA
         "dX lanes tree GEMM": 2 * W + 2 * act_mi + 2 * act_mh,    # W_gate, W_up, dG, dU -> G, U
         "dW_gate/dW_up tree GEMM": 2 * W + 2 * act_mi + act_mh,   # dG, dU, x -> dW_gate, dW_up
+        "dW_gate/dW_up + dX join": 2 * W + 2 * act_mi + 2 * act_mh,  # the same, and dX from the lanes' roots
         "dW_down tree GEMM": W + act_mh + act_mi,                 # dY, a -> dW_down
     }
     return table.get(name)
@@ -72,9 +73,10 @@ KERNEL_SOURCE = {
     "dA tree GEMM": "dgf_xs.hip",
     "dX lanes tree GEMM": "dgf_xs.hip",
     "dW_gate/dW_up tree GEMM": "dgf_gemm.hip",
+    "dW_gate/dW_up + dX join": "dgf_gemm.hip",
     "dW_down tree GEMM": "dgf_gemm.hip",
 }
-SHARED_HEADERS = ("dgf_device.hpp", "dgf_kernels.hpp")
+SHARED_HEADERS = ("dgf_device.hpp", "dgf_kernels.hpp", "dgf_join.hpp")
 
 
 def source_digest(name: str) -> str:

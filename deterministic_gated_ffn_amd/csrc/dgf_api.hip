@@ -272,8 +272,12 @@ size_t partial_bytes(int layout, int nb, int epi, int64_t M, int64_t N, int64_t 
 
 // One tree GEMM: the MFMA kernel, then (K split) the combine of the partials.
 // `partials` must hold partial_bytes() of workspace.
+// defer_join (EPI_DX on the streaming kernel, at most 8 K pieces): the join
+// is not launched; its arguments go to *defer_join and deferred is set, for
+// the weight-gradient launch to run.  dx_join (TN): that deferred join.
 dgf_status run_gemm(int layout, int nb, int epi, GemmParams p, hipStream_t s, const char *what,
-                    uint16_t *partials = nullptr, const char *join_what = "K-piece join") {
+                    uint16_t *partials = nullptr, const char *join_what = "K-piece join",
+                    GemmParams *defer_join = nullptr, bool *deferred = nullptr, const GemmParams *dx_join = nullptr) {
   if (p.M == 0 || p.N == 0) return DGF_OK;
   if ((p.M + 31) / 32 > 65535 || (p.N + 15) / 16 > 0x7fffffff)
     return fail(DGF_EUNSUPPORTED, "%s: %lld x %lld output exceeds the launch grid", what, (long long)p.M, (long long)p.N);
@@ -281,7 +285,7 @@ dgf_status run_gemm(int layout, int nb, int epi, GemmParams p, hipStream_t s, co
   if (layout == DGF_LAYOUT_TN) {
     if (epi != EPI_STORE || p.K > 64 || (nb == 2 && p.B[1] != p.B[0]) || (p.M + 63) / 64 > 65535)
       return fail(DGF_EUNSUPPORTED, "%s: the TN kernel takes one leaf (K <= 64) and a shared B", what);
-    return hip_check(timed(s, what, [&] { return launch_gemm_tn1(nb, p, s); }), what);
+    return hip_check(timed(s, what, [&] { return launch_gemm_tn1(nb, p, s, dx_join); }), what);
   }
   if (layout == DGF_LAYOUT_NT && epi == EPI_STORE && p.K <= 64 && (nb == 1 || p.B[1] == p.B[0]) &&
       (p.M + 63) / 64 <= 65535)
@@ -321,6 +325,11 @@ dgf_status run_gemm(int layout, int nb, int epi, GemmParams p, hipStream_t s, co
       p.part_stride = p.M * p.ldp;
     }
     DGF_TRY(hip_check(timed(s, what, [&] { return launch_xs(layout, p, nb, xp.waves, xp.groups, s); }), what));
+    if (joined && defer_join && epi == EPI_DX && xp.kd <= 3) {
+      *defer_join = p;
+      *deferred = true;
+      return DGF_OK;
+    }
     if (joined)
       DGF_TRY(hip_check(timed(s, join_what, [&] { return launch_combine_epi(epi, nb, p, s); }), join_what));
     return DGF_OK;
@@ -641,6 +650,8 @@ dgf_status dgf_ffn_bwd(const void *dy, int64_t lddy, const void *x, int64_t ldx,
   // dX lanes G = T_I(dG W_gate), U = T_I(dU W_up) and dX = bf16(G + U), the
   // gate lane first: one two-product GEMM whose join does the ordered add
   // (lanes kept when the caller asks for them), or two GEMMs and an add
+  GemmParams dx_join = blank();
+  bool dx_deferred = false;
   if (tiled || dx_fused(M, H, I)) {
     GemmParams q = blank();
     q.A[0] = dG; q.A[1] = dU;
@@ -651,8 +662,10 @@ dgf_status dgf_ffn_bwd(const void *dy, int64_t lddy, const void *x, int64_t ldx,
     q.ldc[0] = q.ldc[1] = lddx;
     q.dx = (uint16_t *)dx; q.lddx = lddx;
     q.M = M; q.N = H; q.K = I;
+    // with the one-leaf weight gradients the join runs on extra workgroups
+    // of the dW_gate/dW_up launch (it reads only the lanes' partial roots)
     DGF_TRY(run_gemm(tiled ? DGF_LAYOUT_NT : DGF_LAYOUT_NN, 2, EPI_DX, q, s, "dX lanes tree GEMM", partials,
-                     "dX join + lane add"));
+                     "dX join + lane add", direct ? &dx_join : nullptr, &dx_deferred));
   } else {
     uint16_t *G = dx_gate_lane ? (uint16_t *)dx_gate_lane : Gw;
     uint16_t *U = dx_up_lane ? (uint16_t *)dx_up_lane : Uw;
@@ -688,7 +701,11 @@ dgf_status dgf_ffn_bwd(const void *dy, int64_t lddy, const void *x, int64_t ldx,
     w.lda[0] = w.lda[1] = ld_d;
     w.B[0] = w.B[1] = (const uint16_t *)x;
     w.ldb[0] = w.ldb[1] = ldx;
-    DGF_TRY(run_gemm(DGF_LAYOUT_TN, 2, EPI_STORE, w, s, "dW_gate/dW_up tree GEMM"));
+    if (dx_deferred)
+      DGF_TRY(run_gemm(DGF_LAYOUT_TN, 2, EPI_STORE, w, s, "dW_gate/dW_up + dX join", nullptr, nullptr, nullptr,
+                       nullptr, &dx_join));
+    else
+      DGF_TRY(run_gemm(DGF_LAYOUT_TN, 2, EPI_STORE, w, s, "dW_gate/dW_up tree GEMM"));
     v.A[0] = (const uint16_t *)dy; v.lda[0] = lddy;
     v.B[0] = a_rm; v.ldb[0] = ld_d;
     DGF_TRY(run_gemm(DGF_LAYOUT_TN, 1, EPI_STORE, v, s, "dW_down tree GEMM"));

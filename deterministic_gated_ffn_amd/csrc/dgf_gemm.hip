@@ -13,8 +13,11 @@
 // MFMA roles: A operand = 16 weight rows x 32 K, B operand = 32 K x 16 tokens,
 // so lane l ends with D[4(l/16)+r][l%16]: four consecutive output columns of
 // one token, which the epilogues store as 8 contiguous bytes.
+#include <string.h>
+
 #include "dgf_device.hpp"
 #include "dgf_kernels.hpp"
+#include "dgf_join.hpp"
 
 namespace dgf {
 
@@ -670,9 +673,32 @@ __device__ __forceinline__ void tn_put4x8(uint16_t *dst, int ks, int km, int k4,
   }
 }
 
+// The dX lanes' join (EPI_DX over 2^kd <= 8 K pieces) on the workgroups past
+// the weight-gradient tiles (grid rows gridDim.y - jrows ..): independent
+// work that fills the kernel's tail instead of a launch of its own.
+template <int S>
+__device__ void tn_dx_join(const GemmParams &j, int jrow, int jrows) {
+  const int64_t chunks = (j.N + 7) / 8;
+  const int64_t nthreads = (int64_t)jrows * gridDim.x * 256;
+  for (int64_t i = ((int64_t)jrow * gridDim.x + blockIdx.x) * 256 + threadIdx.x; i < j.M * chunks; i += nthreads) {
+    const int64_t m = i / chunks, c = (i % chunks) * 8;
+    join_epi_chunk<S, EPI_DX>(j, 0, m, c);
+  }
+}
+
 template <int NB>
-__global__ __launch_bounds__(256) void k_gemm_tn1(GemmParams p, int ct) {
+__global__ __launch_bounds__(256) void k_gemm_tn1(GemmParams p, int ct, GemmParams jn, int jrows) {
   extern __shared__ __attribute__((aligned(16))) uint16_t tn_lds[];
+  if (jrows > 0 && (int)blockIdx.y >= (int)gridDim.y - jrows) {
+    const int jrow = (int)blockIdx.y - ((int)gridDim.y - jrows);
+    switch (jn.ksplit_depth) {
+      case 0: tn_dx_join<1>(jn, jrow, jrows); break;
+      case 1: tn_dx_join<2>(jn, jrow, jrows); break;
+      case 2: tn_dx_join<4>(jn, jrow, jrows); break;
+      default: tn_dx_join<8>(jn, jrow, jrows); break;
+    }
+    return;
+  }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, g4 = lane >> 4;
   const int K = (int)p.K;
@@ -781,18 +807,32 @@ size_t tn1_lds_bytes(int nb, int64_t K) {
   return (size_t)(nb * 64 + 2 * kTnTile) * ks * 2 + (size_t)4 * 16 * kShortStride * 2;
 }
 
-hipError_t launch_gemm_tn1(int nb, GemmParams p, hipStream_t stream) {
+hipError_t launch_gemm_tn1(int nb, GemmParams p, hipStream_t stream, const GemmParams *dx_join) {
   if (p.K < 0 || p.K > 64) return hipErrorInvalidValue;
+  if (dx_join && dx_join->ksplit_depth > 3) return hipErrorInvalidValue;
   // column tiles per workgroup: as many as keep at least 4 workgroups per CU busy
   const int64_t tiles_c = (p.N + kTnTile - 1) / kTnTile, tiles_r = (p.M + 63) / 64;
   int ct = 1;
   while (ct < 8 && tiles_c % (2 * ct) == 0 && (tiles_c / (2 * ct)) * tiles_r >= 4 * 256) ct *= 2;
-  dim3 grid((unsigned)((tiles_c + ct - 1) / ct), (unsigned)tiles_r);
+  const int64_t gx = (tiles_c + ct - 1) / ct;
+  // the dX join's rows of workgroups: about 64 workgroups of one chunk per thread
+  int jrows = 0;
+  GemmParams jn;
+  memset(&jn, 0, sizeof jn);
+  if (dx_join) {
+    jn = *dx_join;
+    const int64_t items = jn.M * ((jn.N + 7) / 8);
+    const int64_t wgs = (items + 255) / 256 < 64 ? (items + 255) / 256 : 64;
+    jrows = (int)((wgs + gx - 1) / gx);
+    if (jrows < 1) jrows = 1;
+  }
+  if (tiles_r + jrows > 65535) return hipErrorInvalidValue;
+  dim3 grid((unsigned)gx, (unsigned)(tiles_r + jrows));
   const size_t shm = tn1_lds_bytes(nb, p.K);
   if (nb == 1)
-    dgf_launch((k_gemm_tn1<1>), grid, dim3(256), shm, stream, p, ct);
+    dgf_launch((k_gemm_tn1<1>), grid, dim3(256), shm, stream, p, ct, jn, jrows);
   else
-    dgf_launch((k_gemm_tn1<2>), grid, dim3(256), shm, stream, p, ct);
+    dgf_launch((k_gemm_tn1<2>), grid, dim3(256), shm, stream, p, ct, jn, jrows);
   return hipGetLastError();
 }
 

@@ -115,8 +115,10 @@ int gemm_row_tiles(int layout, int nb, int epi);
 hipError_t launch_gemm(int layout, int nb, int epi, GemmParams p, int waves, hipStream_t stream);
 // NT, EPI_STORE, K <= 64 (one leaf), B shared by the NB products
 hipError_t launch_gemm_short(int nb, GemmParams p, hipStream_t stream);
-// TN, EPI_STORE, K <= 64 (one leaf): A_b [K][M] and B [K][N] row-major, B shared by the NB products
-hipError_t launch_gemm_tn1(int nb, GemmParams p, hipStream_t stream);
+// TN, EPI_STORE, K <= 64 (one leaf): A_b [K][M] and B [K][N] row-major, B shared by the NB products.
+// dx_join (optional): the dX lanes' join (EPI_DX, at most 8 K pieces) run by extra workgroups of the
+// same launch; it shares no memory with the weight gradients.
+hipError_t launch_gemm_tn1(int nb, GemmParams p, hipStream_t stream, const GemmParams *dx_join = nullptr);
 
 hipError_t launch_act_fwd(const uint16_t *g, const uint16_t *u, uint16_t *a, int64_t n, hipStream_t s);
 hipError_t launch_act_bwd(const uint16_t *da, const uint16_t *g, const uint16_t *u, uint16_t *dg, uint16_t *du,
