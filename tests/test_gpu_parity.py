@@ -73,7 +73,9 @@ def padded(bits, ld_extra=8):
 
 # ---------------------------------------------------------------- tree GEMMs
 SHAPES = [(1, 16, 64), (4, 48, 256), (5, 33, 100), (16, 20, 24), (17, 100, 1000), (32, 64, 4096),
-          (33, 40, 768), (64, 16, 192), (3, 7, 8), (40, 130, 520), (2, 1, 12288)]
+          (33, 40, 768), (64, 16, 192), (3, 7, 8), (40, 130, 520), (2, 1, 12288),
+          # past the streaming kernel's 1024 leaves: the generic tree GEMM with its LDS stack and K split
+          (3, 24, 65600)]
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES)
