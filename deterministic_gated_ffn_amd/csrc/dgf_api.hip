@@ -55,15 +55,16 @@ template <class F>
 hipError_t timed(hipStream_t s, const char *name, F &&launch) {
   const int k = g_prof.used;
   const bool rec = g_prof.ev && k < g_prof.pairs;
-  if (rec) {  // the launch records them as its kernel's start and end
+  if (rec) {  // the launches record them as their kernels' start and end
     g_launch_events[0] = g_prof.ev[2 * k];
     g_launch_events[1] = g_prof.ev[2 * k + 1];
   }
   hipError_t e = launch();
-  if (rec && g_launch_events[0]) {  // no kernel took them: an empty interval
+  if (rec) {
+    const bool none = g_launch_events[0] != nullptr;  // no kernel took them: an empty interval
     g_launch_events[0] = g_launch_events[1] = nullptr;
-    if (e == hipSuccess) e = hipEventRecord(g_prof.ev[2 * k], s);
-    if (e == hipSuccess) e = hipEventRecord(g_prof.ev[2 * k + 1], s);
+    if (none && e == hipSuccess) e = hipEventRecord(g_prof.ev[2 * k], s);
+    if (none && e == hipSuccess) e = hipEventRecord(g_prof.ev[2 * k + 1], s);
   }
   if (g_prof.ev) {
     if (k < 4096) g_prof.names[k] = name;

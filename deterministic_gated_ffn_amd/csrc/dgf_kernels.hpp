@@ -7,18 +7,19 @@
 
 namespace dgf {
 
-// Start/stop events for the next kernel launch, set by the library's timing
-// hook: the launch then records them as the kernel's own start and end
-// timestamps (hipExtLaunchKernelGGL), so a timed launch measures the kernel
-// alone, without the gaps of separate event packets around it.
+// Start/stop events of the timed step in progress, set by the library's
+// timing hook: the step's first kernel records the start event as its own
+// start timestamp and every kernel of the step records the stop event as its
+// own end (hipExtLaunchKernelGGL; the last one's stands), so a timed step
+// measures its kernels, without the gaps of separate event packets.
 extern thread_local hipEvent_t g_launch_events[2];
 
 template <typename F, typename... Args>
 inline void dgf_launch(F kernel, dim3 grid, dim3 block, size_t shm, hipStream_t s, Args... args) {
-  if (g_launch_events[0]) {
-    hipEvent_t start = g_launch_events[0], stop = g_launch_events[1];
-    g_launch_events[0] = g_launch_events[1] = nullptr;
-    hipExtLaunchKernelGGL(kernel, grid, block, (std::uint32_t)shm, s, start, stop, 0u, args...);
+  if (g_launch_events[1]) {
+    hipEvent_t start = g_launch_events[0];
+    g_launch_events[0] = nullptr;
+    hipExtLaunchKernelGGL(kernel, grid, block, (std::uint32_t)shm, s, start, g_launch_events[1], 0u, args...);
   } else {
     hipLaunchKernelGGL(kernel, grid, block, shm, s, args...);
   }

@@ -186,9 +186,10 @@ dgf_status dgf_act_bwd(const void *da, const void *g, const void *u,
  * Kernel timing (for benchmarks and profilers).  events: 2*n_pairs hipEvent_t
  * handles created by the caller.  Until dgf_profile_end(), the calling
  * thread's entry points record events[2k] and events[2k+1] as the start and
- * end of the k-th kernel they launch (k < n_pairs; the kernel's own dispatch
- * timestamps, so hipEventElapsedTime gives its execution time), on the call's
- * stream, in launch order.  dgf_profile_end() stops recording and returns the number of launches
+ * end of their k-th launch step (k < n_pairs; a step is one kernel, or the
+ * two of a vector body and its scalar tail), taken from the kernels' own
+ * dispatch timestamps, so hipEventElapsedTime gives the step's execution time,
+ * on the call's stream, in launch order.  dgf_profile_end() stops recording and returns the number of launches
  * made since dgf_profile_begin (only the first n_pairs were timed);
  * dgf_profile_name(k) names launch k (the string is static; "" when k is out
  * of range) until the next dgf_profile_begin.  The state is thread-local.

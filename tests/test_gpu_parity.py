@@ -503,3 +503,20 @@ def test_kernel_timing_hook_keeps_results_and_times_each_launch():
     assert d[0][0] == "gate/up + act"
     assert all(ms > 0 for _, ms in d), d
     assert sum(ms for _, ms in d) <= e0.elapsed_time(e1) * 1.05, (d, e0.elapsed_time(e1))
+
+
+def test_kernel_timing_hook_spans_a_two_kernel_step():
+    """tree_combine over a length that is not a multiple of 8 runs a vector body
+    and a scalar tail: one timed step whose interval covers both kernels."""
+    rng = np.random.default_rng(12)
+    n = 1 << 20
+    parts = [dev(rnd(rng, (n + 3,))) for _ in range(4)]
+    ref = dgf.tree_combine(parts)
+    timer = dgf.KernelTimer(max_kernels=4)
+    timer.start()
+    got = dgf.tree_combine(parts)
+    timer.stop()
+    torch.cuda.synchronize()
+    assert (inputs.bits(got) == inputs.bits(ref)).all()
+    d = timer.durations_ms()
+    assert timer.count == 1 and len(d) == 1 and d[0][0] == "tree_combine" and d[0][1] > 0, d
