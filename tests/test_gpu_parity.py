@@ -307,9 +307,21 @@ def test_repeat_and_batch_invariance(qwen_weights):
     assert (inputs.bits(y) == ys[0]).all(), "training forward differs from inference"
     for k in b1:
         assert (inputs.bits(b1[k]) == inputs.bits(b2[k])).all(), f"{k} not bitwise repeatable"
-    for M in (1, 8):
+    # every forward path (one or two token tiles, all-K or split-K down projection) gives the same rows
+    for M in (1, 8, 16, 17, 24, 25):
         yM = inputs.bits(dgf.ffn_fwd(x32[:M], wg, wu, wd))
         assert (yM == ys[0][:M]).all(), f"M={M} rows differ from the M=32 rows"
+    # other buffers for the same weights, another stream: the same bits
+    wg2, wu2, wd2 = wg.clone(), wu.clone(), wd.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        y3, g3, u3 = dgf.ffn_fwd(x32, wg2, wu2, wd2, training=True)
+        b3 = dgf.ffn_bwd(dy32, x32, g3, u3, wg2, wu2, wd2)
+    side.synchronize()
+    assert (inputs.bits(y3) == ys[0]).all(), "forward differs on other buffers / another stream"
+    for k in b1:
+        assert (inputs.bits(b3[k]) == inputs.bits(b1[k])).all(), f"{k} differs on other buffers / another stream"
 
 
 def test_full_size_forward_backward_vs_oracle(qwen_weights):
