@@ -261,7 +261,9 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_gate_up_act(GuParams p) {
   subtree_range(p.L, 3, wave, lo, hi);
   const int tiles_n = (int)((p.N + kGuCols - 1) / kGuCols);
   const int per = (tiles_n + (int)gridDim.x - 1) / (int)gridDim.x;
-  const int t0 = (int)blockIdx.x * per;
+  // consecutive tile ranges on one XCD: the workgroups that share an output
+  // line (16-column tiles, 64-column lines) write it into the same L2
+  const int t0 = xcd_tile((int)blockIdx.x, (int)gridDim.x) * per;
   const int T = t0 < tiles_n ? min(per, tiles_n - t0) : 0;
   char *base = reinterpret_cast<char *>(gu_lds) + Lay::roots_bytes + (size_t)wave * (Lay::x_bytes + Lay::slab_bytes);
   Wv w{p,
