@@ -709,7 +709,19 @@ dgf_status dgf_ffn_bwd(const void *dy, int64_t lddy, const void *x, int64_t ldx,
       DGF_TRY(run_gemm(DGF_LAYOUT_TN, 2, EPI_STORE, w, s, "dW_gate/dW_up tree GEMM"));
     v.A[0] = (const uint16_t *)dy; v.lda[0] = lddy;
     v.B[0] = a_rm; v.ldb[0] = ld_d;
-    DGF_TRY(run_gemm(DGF_LAYOUT_TN, 1, EPI_STORE, v, s, "dW_down tree GEMM"));
+    if (H % 16 == 0) {
+      // the two row halves of dW_down as the kernel's two products over the
+      // shared B = a: every staged B tile serves twice the rows, and the
+      // launch fits one round of workgroups (each element is still its own
+      // one-leaf sum)
+      v.M = H / 2;
+      v.A[1] = (const uint16_t *)dy + H / 2; v.lda[1] = lddy;
+      v.B[1] = a_rm; v.ldb[1] = ld_d;
+      v.C[1] = (uint16_t *)dw_down + (H / 2) * ld_dwd; v.ldc[1] = ld_dwd;
+      DGF_TRY(run_gemm(DGF_LAYOUT_TN, 2, EPI_STORE, v, s, "dW_down tree GEMM"));
+    } else {
+      DGF_TRY(run_gemm(DGF_LAYOUT_TN, 1, EPI_STORE, v, s, "dW_down tree GEMM"));
+    }
   } else {
     w.A[0] = dGT; w.A[1] = dUT;
     w.lda[0] = w.lda[1] = Mp;

@@ -810,10 +810,11 @@ size_t tn1_lds_bytes(int nb, int64_t K) {
 hipError_t launch_gemm_tn1(int nb, GemmParams p, hipStream_t stream, const GemmParams *dx_join) {
   if (p.K < 0 || p.K > 64) return hipErrorInvalidValue;
   if (dx_join && dx_join->ksplit_depth > 3) return hipErrorInvalidValue;
-  // column tiles per workgroup: as many as keep at least 4 workgroups per CU busy
+  // column tiles per workgroup: as many as keep at least 3 workgroups per CU busy (the LDS of the
+  // one-leaf tiles holds 3 per CU, so the weight gradients of the FFN shapes run as one round)
   const int64_t tiles_c = (p.N + kTnTile - 1) / kTnTile, tiles_r = (p.M + 63) / 64;
   int ct = 1;
-  while (ct < 8 && tiles_c % (2 * ct) == 0 && (tiles_c / (2 * ct)) * tiles_r >= 4 * 256) ct *= 2;
+  while (ct < 8 && tiles_c % (2 * ct) == 0 && (tiles_c / (2 * ct)) * tiles_r >= 3 * 256) ct *= 2;
   const int64_t gx = (tiles_c + ct - 1) / ct;
   // the dX join's rows of workgroups: about 64 workgroups of one chunk per thread
   int jrows = 0;
