@@ -41,8 +41,9 @@ thread_local hipEvent_t dgf::g_launch_events[2] = {nullptr, nullptr};
 
 namespace {
 
-// Kernel timing hook: caller-created events, one pair per launch, recorded
-// as each kernel's own start and end.
+// Kernel timing hook: caller-created events, one pair per launch step (one
+// kernel, or a vector body and its scalar tail), recorded as the kernels' own
+// start and end timestamps.
 struct Prof {
   hipEvent_t *ev = nullptr;
   int pairs = 0;

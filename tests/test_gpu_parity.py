@@ -532,3 +532,29 @@ def test_kernel_timing_hook_spans_a_two_kernel_step():
     assert (inputs.bits(got) == inputs.bits(ref)).all()
     d = timer.durations_ms()
     assert timer.count == 1 and len(d) == 1 and d[0][0] == "tree_combine" and d[0][1] > 0, d
+
+
+def test_concurrent_calls_on_two_streams():
+    """The library keeps no device state: two training steps enqueued on two
+    streams at once, each with its own buffers, give the bits of one step alone."""
+    rng = np.random.default_rng(13)
+    M, H, I = 32, 512, 1536
+    x, dy = dev(rnd(rng, (M, H))), dev(rnd(rng, (M, H)))
+    wg, wu, wd = (dev(rnd(rng, s, 0.02)) for s in ((I, H), (I, H), (H, I)))
+    y0, g0, u0 = dgf.ffn_fwd(x, wg, wu, wd, training=True)
+    r0 = dgf.ffn_bwd(dy, x, g0, u0, wg, wu, wd)
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = []
+    for st in streams:
+        st.wait_stream(torch.cuda.current_stream())
+    for _ in range(3):
+        for st in streams:
+            with torch.cuda.stream(st):
+                y, g, u = dgf.ffn_fwd(x, wg, wu, wd, training=True)
+                outs.append((y, dgf.ffn_bwd(dy, x, g, u, wg, wu, wd)))
+    torch.cuda.synchronize()
+    for y, r in outs:
+        assert (inputs.bits(y) == inputs.bits(y0)).all()
+        for k in r0:
+            assert (inputs.bits(r[k]) == inputs.bits(r0[k])).all(), k
