@@ -280,7 +280,13 @@ def main():
         result["long_sequence"] = long_sequence(W[0])
 
     if not args.no_cpu_baseline and not args.quick:
-        result["cpu_baseline"] = cpu_baseline(M)
+        # the outputs of one step, kept as BF16 bits for the comparison with the oracle's sample
+        wg, wu, wd = W[0]
+        y, g, u = dgf.ffn_fwd(x, wg, wu, wd, training=True)
+        r = dgf.ffn_bwd(dy, x, g, u, wg, wu, wd)
+        torch.cuda.synchronize()
+        gpu = {k: inputs.bits(t) for k, t in {"y": y, "g": g, "u": u, **r}.items()}
+        result["cpu_baseline"], result["oracle_parity"] = cpu_baseline(M, gpu)
 
     print(json.dumps(result), flush=True)
 
@@ -318,9 +324,19 @@ def long_sequence(weights, M: int = 4096, steps: int = 5, warmup: int = 2) -> di
             "steps": steps}
 
 
-def cpu_baseline(M: int) -> dict:
+def ordinal(b):
+    """BF16 bit patterns as integers in value order (+0 and -0 both 0), so that
+    the difference of two is their distance in ulps."""
+    import numpy as np
+    b = np.asarray(b, np.uint16).astype(np.int32)
+    return np.where(b & 0x8000, -(b & 0x7FFF), b & 0x7FFF)
+
+
+def cpu_baseline(M: int, gpu: dict) -> tuple[dict, dict]:
     """The CPU oracle on a bounded sample of the same step: the full M=32
-    forward, the full dA and dX, and 1/16 of the dW rows (scaled by 16)."""
+    forward, the full dA and dX, and 1/16 of the dW rows (scaled by 16).
+    Also compares that sample with the same elements of the step's outputs on
+    the GPU (`gpu`: BF16 bits of y, g, u, dX, dW_gate, dW_up, dW_down)."""
     import numpy as np
 
     import oracle
@@ -339,21 +355,39 @@ def cpu_baseline(M: int) -> dict:
     dg, du, a = oracle.act_bwd(da, o["g"], o["u"])
     G = oracle.gemm_tree(dg, wg, "NN")
     U = oracle.gemm_tree(du, wu, "NN")
-    oracle.tree_combine([G, U])
+    dx = oracle.tree_combine([G, U]).reshape(M, H)
     t_dx = time.perf_counter() - t0
     frac = 16
     t0 = time.perf_counter()
-    oracle.gemm_tree(np.ascontiguousarray(dg[:, :I // frac]), x, "TN")
-    oracle.gemm_tree(np.ascontiguousarray(du[:, :I // frac]), x, "TN")
-    oracle.gemm_tree(np.ascontiguousarray(dy[:, :H // frac]), a, "TN")
+    dwg = oracle.gemm_tree(np.ascontiguousarray(dg[:, :I // frac]), x, "TN")
+    dwu = oracle.gemm_tree(np.ascontiguousarray(du[:, :I // frac]), x, "TN")
+    dwd = oracle.gemm_tree(np.ascontiguousarray(dy[:, :H // frac]), a, "TN")
     t_dw = (time.perf_counter() - t0) * frac
     total = t_fwd + t_dx + t_dw
-    return {"value": round(step_bytes(M) / total / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "sample": f"C oracle (OpenMP, {os.environ.get('OMP_NUM_THREADS')} threads) on the M=32 training step: "
-                      f"full forward ({t_fwd:.1f} s), full dA/dsilu/dX ({t_dx:.1f} s), dW on 1/{frac} of the rows "
-                      f"scaled x{frac} ({t_dw:.1f} s)",
-            "seconds_per_step": round(total, 2), "cpu": platform.processor() or platform.machine(),
-            "os_cpu_count": os.cpu_count()}
+    baseline = {"value": round(step_bytes(M) / total / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+                "sample": f"C oracle (OpenMP, {os.environ.get('OMP_NUM_THREADS')} threads) on the M=32 training step: "
+                          f"full forward ({t_fwd:.1f} s), full dA/dsilu/dX ({t_dx:.1f} s), dW on 1/{frac} of the rows "
+                          f"scaled x{frac} ({t_dw:.1f} s)",
+                "seconds_per_step": round(total, 2), "cpu": platform.processor() or platform.machine(),
+                "os_cpu_count": os.cpu_count()}
+
+    # the GPU step's outputs against the oracle on the same elements: exact BF16 matches and ulp distances
+    pairs = {"y": (gpu["y"], o["y"]), "g": (gpu["g"], o["g"]), "u": (gpu["u"], o["u"]), "dX": (gpu["dX"], dx),
+             "dW_gate": (gpu["dW_gate"][:I // frac], dwg), "dW_up": (gpu["dW_up"][:I // frac], dwu),
+             "dW_down": (gpu["dW_down"][:H // frac], dwd)}
+    per, n_all, bad_all, ulp_all = {}, 0, 0, 0
+    for k, (got, ref) in pairs.items():
+        got, ref = np.asarray(got, np.uint16), np.asarray(ref, np.uint16).reshape(np.shape(got))
+        bad = int((got != ref).sum())
+        ulp = int(np.abs(ordinal(got) - ordinal(ref)).max()) if got.size else 0
+        per[k] = {"elements": int(got.size), "mismatches": bad, "max_ulp": ulp}
+        n_all, bad_all, ulp_all = n_all + got.size, bad_all + bad, max(ulp_all, ulp)
+    parity = {"vs": "oracle", "elements": int(n_all), "mismatches": bad_all,
+              "exact_match_fraction": round(1 - bad_all / n_all, 9) if n_all else None, "max_ulp": ulp_all,
+              "outputs": per,
+              "sample": f"the M=32 training step on weight copy 0: y, g, u and dX in full, the first 1/{frac} "
+                        "of the rows of dW_gate, dW_up and dW_down"}
+    return baseline, parity
 
 
 if __name__ == "__main__":
