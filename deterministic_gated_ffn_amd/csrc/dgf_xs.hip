@@ -374,6 +374,20 @@ struct XsWave {
   __device__ __forceinline__ void run() const {
     constexpr int NF = NL - (TAIL ? 1 : 0);
     if (T <= 0) return;  // no tile for this workgroup (the same for all its waves)
+    // the first weight units are issued before the activation loads, so that
+    // their HBM latency overlaps the activation's (registers only: the slab
+    // is free for the rearrangement below)
+    WF ring[PR];
+    uint32_t voff[2 * RT];
+    unit_offsets(voff);
+    if constexpr (NF > 0) {
+      constexpr int UN = NN ? 2 * NF : NF;
+#pragma unroll
+      for (int g = 0; g < PR - 1; ++g) {
+        const int u = g % UN;
+        load_unit(g / UN, NN ? u / 2 : u, NN ? u % 2 : 0, ring[g], voff);
+      }
+    }
     // stationary activation fragments of this wave's leaves, loaded as whole
     // 128-byte row segments (lane: row 8 s + lane / 8 of token block t,
     // 16-byte chunk lane % 8 of the leaf; rows past M clamped, never stored;
@@ -408,17 +422,6 @@ struct XsWave {
             xs.v[j][t][s] = *reinterpret_cast<const bf16x8 *>(&slab[r16 * 64 + 8 * ((4 * s + g4) ^ (r16 & 7))]);
           wave_lds_sync();  // the slab's reads are done before it is rewritten
         }
-    }
-    WF ring[PR];
-    uint32_t voff[2 * RT];
-    unit_offsets(voff);
-    if constexpr (NF > 0) {
-      constexpr int UN = NN ? 2 * NF : NF;
-#pragma unroll
-      for (int g = 0; g < PR - 1; ++g) {
-        const int u = g % UN;
-        load_unit(g / UN, NN ? u / 2 : u, NN ? u % 2 : 0, ring[g], voff);
-      }
     }
     for (int i = 0; i < T; i += PR) {
       tile<NL, TAIL, 0>(i, ring, xs, voff);
