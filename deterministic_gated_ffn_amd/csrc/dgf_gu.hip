@@ -62,10 +62,10 @@ struct GuWave {
   int wave, lane, r16, g4;
   int lo;
   int64_t m0;
-  int t0, T;
+  int t0, ts, T;  // tiles t0 + i ts, i < T
   int64_t wbytes[2];
 
-  __device__ __forceinline__ int64_t col0(int i) const { return (int64_t)(t0 + (i < T ? i : T - 1)) * kGuCols; }
+  __device__ __forceinline__ int64_t col0(int i) const { return (int64_t)(t0 + (i < T ? i : T - 1) * ts) * kGuCols; }
 
   // Weight unit (tile i, product b, leaf lo + j): 16 rows x 128 bytes.  Rows
   // past N read as zero (range check of the rebased descriptor), and so does
@@ -260,11 +260,12 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_gate_up_act(GuParams p) {
   int lo, hi;
   subtree_range(p.L, 3, wave, lo, hi);
   const int tiles_n = (int)((p.N + kGuCols - 1) / kGuCols);
-  const int per = (tiles_n + (int)gridDim.x - 1) / (int)gridDim.x;
-  // consecutive tile ranges on one XCD: the workgroups that share an output
-  // line (16-column tiles, 64-column lines) write it into the same L2
-  const int t0 = xcd_tile((int)blockIdx.x, (int)gridDim.x) * per;
-  const int T = t0 < tiles_n ? min(per, tiles_n - t0) : 0;
+  // tiles t0, t0 + G, t0 + 2G, ... with t0 consecutive on one XCD: at each
+  // step the workgroups of an XCD write neighbouring 16-column tiles, so the
+  // four pieces of a 64-column output line reach one L2 at about one time
+  const int G = (int)gridDim.x;
+  const int t0 = xcd_tile((int)blockIdx.x, G);
+  const int T = t0 < tiles_n ? (tiles_n - t0 + G - 1) / G : 0;
   char *base = reinterpret_cast<char *>(gu_lds) + Lay::roots_bytes + (size_t)wave * (Lay::x_bytes + Lay::slab_bytes);
   Wv w{p,
        gu_lds,
@@ -277,6 +278,7 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_gate_up_act(GuParams p) {
        lo,
        (int64_t)blockIdx.y * 16 * MT,
        t0,
+       G,
        T,
        {p.N * p.ldw[0] * 2, p.N * p.ldw[1] * 2}};
   switch (hi - lo) {  // 1..8 by the launch conditions (8 <= L <= 64)
@@ -302,7 +304,7 @@ hipError_t launch_gu_act(const GuParams &p, hipStream_t stream) {
   const int mt = p.M <= 16 ? 1 : 2;
   const int64_t tiles_n = (p.N + kGuCols - 1) / kGuCols;
   // one wave of workgroups over the 256 CUs (one workgroup per CU by LDS);
-  // each takes a contiguous run of ceil(tiles / groups) tiles
+  // each takes ceil(tiles / groups) tiles, `groups` apart
   int64_t per = (tiles_n + 255) / 256;
   const int64_t groups = (tiles_n + per - 1) / per;
   const dim3 grid((unsigned)groups, 1u), block(kGuWaves * 64);
