@@ -273,7 +273,10 @@ def test_tiny_ffn_forward_backward_bitwise():
                                    (8, 72, 4096), (15, 48, 6144), (12, 16, 12288), (2, 32, 8192), (16, 24, 16384),
                                    (4, 8, 512), (2, 1, 1024),
                                    # ... and with two token tiles (17 to 24 tokens)
-                                   (17, 64, 1024), (20, 200, 1536), (24, 136, 3072), (23, 16, 12288)])
+                                   (17, 64, 1024), (20, 200, 1536), (24, 136, 3072), (23, 16, 12288),
+                                   # fused gate/up with more 16-column tiles than workgroups, unevenly
+                                   # spread (301 and 514 tiles, the last one ragged)
+                                   (8, 512, 4810), (32, 576, 8220)])
 def test_ffn_other_shapes_bitwise(M, H, I):
     rng = np.random.default_rng(M + H + I)
     x, dy = rnd(rng, (M, H)), rnd(rng, (M, H))
