@@ -664,6 +664,9 @@ dgf_status dgf_ffn_bwd(const void *dy, int64_t lddy, const void *x, int64_t ldx,
     q.ldc[0] = q.ldc[1] = lddx;
     q.dx = (uint16_t *)dx; q.lddx = lddx;
     q.M = M; q.N = H; q.K = I;
+    // with two token tiles the 2 x 2^kd activation slices are the largest of the
+    // streaming launches: each is read by the workgroups of one XCD
+    q.xcd_slices = M > 16 ? 1 : 0;
     // with the one-leaf weight gradients the join runs on extra workgroups
     // of the dW_gate/dW_up launch (it reads only the lanes' partial roots)
     DGF_TRY(run_gemm(tiled ? DGF_LAYOUT_NT : DGF_LAYOUT_NN, 2, EPI_DX, q, s, "dX lanes tree GEMM", partials,

@@ -55,6 +55,9 @@ struct GemmParams {
   // EPI_DX (combine only): dx = bf16(G + U) of the two lanes; C[0], C[1] keep the lanes when set
   uint16_t *dx;
   int64_t lddx;
+  // weight-streaming kernel: when set (and each XCD can take whole (product, K piece) slices),
+  // run each slice's workgroups on one XCD so that its activation slice is fetched by one L2
+  int xcd_slices;
 };
 
 // Weight-streaming tree GEMM with stationary activations (dgf_xs.hip):

@@ -441,13 +441,26 @@ __global__ __launch_bounds__(kXsWaves * 64) void k_xs(GemmParams p) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int kd = p.ksplit_depth;
-  const int b = blockIdx.z >> kd, piece = blockIdx.z & ((1 << kd) - 1);
+  // Workgroups are dealt to the 8 XCDs round robin in launch order; with
+  // xcd_slices they are renumbered so that each XCD runs whole (product,
+  // K piece) slices, whose workgroups then read the slice's activation
+  // through one L2.
+  int vx = (int)blockIdx.x, vy = (int)blockIdx.y, vz = (int)blockIdx.z;
+  const unsigned gxy = gridDim.x * gridDim.y, nwg = gxy * gridDim.z;
+  if (p.xcd_slices && (nwg & 7u) == 0 && ((nwg >> 3) % gxy) == 0) {
+    unsigned lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+    lin = (lin & 7u) * (nwg >> 3) + (lin >> 3);
+    vx = (int)(lin % gridDim.x);
+    vy = (int)((lin / gridDim.x) % gridDim.y);
+    vz = (int)(lin / gxy);
+  }
+  const int b = vz >> kd, piece = vz & ((1 << kd) - 1);
   int lo, hi;
   subtree_range(p.L, kd + dw, (piece << dw) | wave, lo, hi);
   const int tiles_n = (int)((p.N + Wv::COLS - 1) / Wv::COLS);
   // contiguous tile ranges: workgroup g takes tiles g*per .. g*per + per - 1
   const int per = (tiles_n + (int)gridDim.x - 1) / (int)gridDim.x;
-  const int t0 = (int)blockIdx.x * per;
+  const int t0 = vx * per;
   const int T = t0 < tiles_n ? min(per, tiles_n - t0) : 0;
   Wv w{p,
        xs_lds,
@@ -461,7 +474,7 @@ __global__ __launch_bounds__(kXsWaves * 64) void k_xs(GemmParams p) {
        lo,
        hi - lo,
        (int64_t)hi * kLeaf > p.K,
-       (int64_t)blockIdx.y * 16 * MT,
+       (int64_t)vy * 16 * MT,
        tiles_n,
        t0,
        T,
