@@ -26,11 +26,16 @@ def parse_value(tok: str) -> Fraction:
 
 
 def bf16_bits_exact(v: Fraction) -> int:
-    """Exact BF16 encoding of a value that must be representable (normal range)."""
+    """Exact BF16 encoding of a value that must be representable: normal
+    (1.m * 2^e, e >= -126) or subnormal (m * 2^-133, exponent field 0)."""
     if v == 0:
         return 0
     s = 0x8000 if v < 0 else 0
     v = abs(v)
+    sub = v / Fraction(2) ** -133
+    if v < Fraction(2) ** -126:
+        assert sub.denominator == 1 and 0 < sub < 128, f"not representable in BF16: {v}"
+        return s | int(sub)
     e = 0
     while v >= 2:
         v /= 2; e += 1
@@ -38,6 +43,7 @@ def bf16_bits_exact(v: Fraction) -> int:
         v *= 2; e -= 1
     m = (v - 1) * 128
     assert m.denominator == 1, f"not representable in BF16: {v}"
+    assert e + 127 < 255, f"past the BF16 range: {v}"
     return s | ((e + 127) << 7) | int(m)
 
 
@@ -76,4 +82,30 @@ def block_cases():
         b = np.array([bf16_bits_exact(parse_value(t)) for t in bv.split()], np.uint16)
         accf = np.array([int(acc, 16)], np.uint32).view(np.float32)[0]
         out.append((name, accf, a, b, int(exp, 16), why))
+    return out
+
+
+def _vector(n: int, spec: str) -> np.ndarray:
+    v = np.zeros(n, np.uint16)
+    if spec == "ones":
+        v[:] = 0x3F80
+    else:
+        for it in spec.split():
+            i, val = it.split(":"); v[int(i)] = bf16_bits_exact(parse_value(val))
+    return v
+
+
+def leaf_cases():
+    out = []
+    for name, n, av, bv, exp, why in load_table("leaf_cases.txt"):
+        n = int(n)
+        out.append((name, _vector(n, av), _vector(n, bv), int(exp, 16), why))
+    return out
+
+
+def act_cases():
+    out = []
+    for name, g, u, da, output, exp, other, why in load_table("act_cases.txt"):
+        vals = [bf16_bits_exact(parse_value(t)) for t in (g, u, da)]
+        out.append((name, *vals, output, int(exp, 16), int(other, 16), why))
     return out

@@ -15,7 +15,7 @@ import torch
 
 import oracle
 from oracle import fp64
-from tests.goldens import block_cases, tree_cases
+from tests.goldens import act_cases, block_cases, leaf_cases, tree_cases
 from deterministic_gated_ffn_amd import inputs
 
 F2B = oracle.f32_to_bf16_bits
@@ -41,6 +41,61 @@ def test_tree_hand_worked(case):
 def test_block_rule_hand_worked(case):
     name, acc, a, b, expected, why = case
     assert f32_bits(oracle.block_step(float(acc), a, b)) == expected, why
+
+
+@pytest.mark.parametrize("case", leaf_cases(), ids=lambda c: c[0])
+def test_leaf_block_width_and_order_hand_worked(case):
+    # 8-wide blocks in ascending K order, separated from 4- and 16-wide blocks
+    # and from the descending order by hand-worked values
+    name, a, b, expected, why = case
+    assert f32_bits(oracle.leaf_f32(a, b)) == expected, why
+
+
+def _derive_act_intermediates(g: float):
+    """The FP32 chain at g from exact arithmetic: a 50-digit decimal exp and
+    Fraction arithmetic, each step rounded to FP32 (nearest even)."""
+    getcontext().prec = 50
+    e = _rn_f32(Fraction(Decimal(-g).exp()))
+    den = _rn_f32(1 + Fraction(e))
+    sig = _rn_f32(1 / Fraction(den))
+    silu = _rn_f32(Fraction(g) * Fraction(sig))
+    om = _rn_f32(1 - Fraction(sig))
+    t = _rn_f32(Fraction(g) * Fraction(om))
+    ds = _rn_f32(Fraction(sig) * Fraction(_rn_f32(1 + Fraction(t))))
+    return sig, silu, ds
+
+
+def test_activation_intermediates_at_one():
+    # the FP32 values the hand-worked activation cases are derived from
+    sig, silu, ds = _derive_act_intermediates(1.0)
+    assert (f32_bits(sig), f32_bits(silu), f32_bits(ds)) == (0x3F3B26A8, 0x3F3B26A8, 0x3F6D7BD1)
+    assert f32_bits(oracle.sigma(1.0)) == 0x3F3B26A8
+    assert f32_bits(oracle.silu(1.0)) == 0x3F3B26A8
+    assert f32_bits(oracle.dsilu(1.0)) == 0x3F6D7BD1
+
+
+@pytest.mark.parametrize("case", act_cases(), ids=lambda c: c[0])
+def test_activation_rounds_each_stage_once(case):
+    # a, dU and dG are each one BF16 rounding of an FP32 value: the
+    # hand-worked value differs from the reading that rounds silu(g), dA*u or
+    # silu'(g) to BF16 first
+    name, g, u, da, output, expected, other, why = case
+    assert expected != other
+    G, U, DA = (np.array([v], np.uint16) for v in (g, u, da))
+    if output == "a":
+        got = int(oracle.act_fwd(G, U)[0])
+    else:
+        dg, du, _ = oracle.act_bwd(DA, G, U)
+        got = int((dg if output == "dG" else du)[0])
+    assert got == expected, why
+    # the same element inside a longer vector (no dependence on position)
+    n = 37
+    Gv, Uv, DAv = (np.full(n, v, np.uint16) for v in (g, u, da))
+    if output == "a":
+        assert (oracle.act_fwd(Gv, Uv) == expected).all()
+    else:
+        dg, du, _ = oracle.act_bwd(DAv, Gv, Uv)
+        assert ((dg if output == "dG" else du) == expected).all()
 
 
 def test_leaf_is_block_chain():
