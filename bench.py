@@ -110,11 +110,46 @@ def measured_traffic(kernel: str) -> int | None:
     return figures[kernel]
 
 
+def sample_us(run, steps: int, samples: int) -> dict:
+    """Times `samples` independent regions of `steps` calls of run(k) (k counts
+    calls), each bracketed by device synchronisations and HIP events on the
+    current stream; returns the per-call microseconds of every region and their
+    median, min and max."""
+    import statistics
+
+    import torch
+    per, k = [], 0
+    for _ in range(samples):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            run(k)
+            k += 1
+        e1.record()
+        torch.cuda.synchronize()
+        per.append(1e3 * e0.elapsed_time(e1) / steps)
+    return {"median": statistics.median(per), "min": min(per), "max": max(per), "samples": [round(v, 3) for v in per]}
+
+
+def stats_entry(st: dict, nbytes: int | None = None, flops: int | None = None) -> dict:
+    out = {"us": round(st["median"], 2), "us_min": round(st["min"], 2), "us_max": round(st["max"], 2),
+           "samples_us": st["samples"]}
+    if nbytes:
+        gbps = nbytes / (st["median"] * 1e-6) / 1e9
+        out.update({"GBps": round(gbps, 1), "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4), "algorithmic_bytes": nbytes})
+    if flops:
+        tf = flops / (st["median"] * 1e-6) / 1e12
+        out.update({"TFLOPs": round(tf, 2), "frac_mfma_peak": round(tf / BF16_MFMA_PEAK_TFLOPS, 4), "flops": flops})
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--samples", type=int, default=5, help="independent timed regions of --steps calls each")
     ap.add_argument("--copies", type=int, default=3, help="resident weight copies rotated per step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quick", action="store_true", help="skip the forward-only and CPU legs (profiling runs)")
@@ -156,19 +191,15 @@ def main():
     torch.cuda.synchronize()
     print("[bench] warmup done", file=sys.stderr, flush=True)
 
-    # the timed region: K steps between two events, nothing else recorded
-    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
+    # the timed regions: `samples` regions of exactly K steps, each between two
+    # synchronisations, nothing else recorded; the step time is their median
     wall0 = time.perf_counter()
-    t_start.record()
-    for k in range(args.steps):
-        step(k)
-    t_end.record()
-    torch.cuda.synchronize()
+    st = sample_us(step, args.steps, args.samples)
     wall = time.perf_counter() - wall0
-    ms_step = t_start.elapsed_time(t_end) / args.steps
+    ms_step = st["median"] * 1e-3
     value = step_bytes(M) / (ms_step * 1e-3) / 1e9
-    print(f"[bench] fwd+bwd M=32: {ms_step * 1e3:.1f} us/step, {value:.0f} GB/s", file=sys.stderr, flush=True)
+    print(f"[bench] fwd+bwd M=32: {ms_step * 1e3:.1f} us/step (median of {args.samples}; "
+          f"{st['min']:.1f}..{st['max']:.1f}), {value:.0f} GB/s", file=sys.stderr, flush=True)
 
     # a second, profiled region of K steps: HIP events around every launch, on
     # the launch stream (they add their own gaps, so the step time comes from
@@ -188,7 +219,8 @@ def main():
     per = {}
     for name, ms in timer.durations_ms():
         per.setdefault(name, []).append(ms)
-    kernels = {n: {"launches": len(v), "avg_us": 1e3 * sum(v) / len(v)} for n, v in per.items()}
+    kernels = {n: {"launches": len(v), "avg_us": 1e3 * sum(v) / len(v), "median_us": round(1e3 * sorted(v)[len(v) // 2], 2),
+                   "min_us": round(1e3 * min(v), 2), "max_us": round(1e3 * max(v), 2)} for n, v in per.items()}
     dom = max(per, key=lambda n: sum(per[n]))
     dom_us = kernels[dom]["avg_us"]
     dom_bytes = kernel_bytes(dom, M)
@@ -205,7 +237,11 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "samples": args.samples,
         "ms_per_step": round(ms_step, 4),
+        "us_per_step_min": round(st["min"], 2),
+        "us_per_step_max": round(st["max"], 2),
+        "us_per_step_samples": st["samples"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -230,22 +266,16 @@ def main():
         fwd = {}
         for Mf in (1, 8, 32):
             xf = x[:Mf]
+
+            def fwd_m(k, xf=xf):
+                wg, wu, wd = W[k % len(W)]
+                dgf.ffn_fwd(xf, wg, wu, wd)
+
             for k in range(args.warmup):
-                wg, wu, wd = W[k % len(W)]
-                dgf.ffn_fwd(xf, wg, wu, wd)
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for k in range(args.steps):
-                wg, wu, wd = W[k % len(W)]
-                dgf.ffn_fwd(xf, wg, wu, wd)
-            e1.record()
-            torch.cuda.synchronize()
-            us = 1e3 * e0.elapsed_time(e1) / args.steps
-            gbps = fwd_bytes(Mf) / (us * 1e-6) / 1e9
-            fwd[str(Mf)] = {"us": round(us, 2), "GBps": round(gbps, 1), "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
-                            "algorithmic_bytes": fwd_bytes(Mf)}
-            print(f"[bench] forward M={Mf}: {us:.1f} us, {gbps:.0f} GB/s", file=sys.stderr, flush=True)
+                fwd_m(k)
+            fwd[str(Mf)] = stats_entry(sample_us(fwd_m, args.steps, args.samples), fwd_bytes(Mf))
+            print(f"[bench] forward M={Mf}: {fwd[str(Mf)]['us']:.1f} us, {fwd[str(Mf)]['GBps']:.0f} GB/s",
+                  file=sys.stderr, flush=True)
         result["forward"] = fwd
         result["fwd_bwd_us"] = round(ms_step * 1e3, 2)
         # the training step (forward with g/u saved, then backward) at 1 and 8 tokens as well
@@ -253,31 +283,22 @@ def main():
         for Mf in (1, 8):
             xf, dyf = x[:Mf], dy[:Mf]
 
-            def step_m(k):
+            def step_m(k, xf=xf, dyf=dyf):
                 wg, wu, wd = W[k % len(W)]
                 y, g, u = dgf.ffn_fwd(xf, wg, wu, wd, training=True)
                 return dgf.ffn_bwd(dyf, xf, g, u, wg, wu, wd)
 
             for k in range(args.warmup):
                 step_m(k)
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for k in range(args.steps):
-                step_m(k)
-            e1.record()
-            torch.cuda.synchronize()
-            us = 1e3 * e0.elapsed_time(e1) / args.steps
-            gbps = step_bytes(Mf) / (us * 1e-6) / 1e9
-            fb[str(Mf)] = {"us": round(us, 2), "GBps": round(gbps, 1), "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
-                           "algorithmic_bytes": step_bytes(Mf)}
-            print(f"[bench] fwd+bwd M={Mf}: {us:.1f} us, {gbps:.0f} GB/s", file=sys.stderr, flush=True)
-        fb["32"] = {"us": round(ms_step * 1e3, 2), "GBps": round(value, 1),
-                    "frac_hbm_peak": round(value / HBM_PEAK_GBPS, 4), "algorithmic_bytes": step_bytes(M)}
+            fb[str(Mf)] = stats_entry(sample_us(step_m, args.steps, args.samples), step_bytes(Mf))
+            print(f"[bench] fwd+bwd M={Mf}: {fb[str(Mf)]['us']:.1f} us, {fb[str(Mf)]['GBps']:.0f} GB/s",
+                  file=sys.stderr, flush=True)
+        fb["32"] = stats_entry(st, step_bytes(M))
         result["fwd_bwd"] = fb
+        result["two_stream_lanes"] = two_stream_lanes(W, x, dy, args, kernels)
 
     if not args.quick:
-        result["long_sequence"] = long_sequence(W[0])
+        result["long_sequence"] = long_sequence(W[0], samples=args.samples)
 
     if not args.no_cpu_baseline and not args.quick:
         # the outputs of one step, kept as BF16 bits for the comparison with the oracle's sample
@@ -291,9 +312,9 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def long_sequence(weights, M: int = 4096, steps: int = 5, warmup: int = 2) -> dict:
+def long_sequence(weights, M: int = 4096, steps: int = 5, warmup: int = 2, samples: int = 5) -> dict:
     """The compute-bound shape: fwd+bwd at M=4096 tokens (8 sequences x 512),
-    timed over `steps` steps; 18 M H I flops per step (nine products)."""
+    `samples` regions of `steps` steps; 18 M H I flops per step (nine products)."""
     import torch
     from deterministic_gated_ffn_amd import binding as dgf
     from deterministic_gated_ffn_amd import inputs
@@ -302,26 +323,62 @@ def long_sequence(weights, M: int = 4096, steps: int = 5, warmup: int = 2) -> di
     x_c, dy_c = inputs.activations(M)
     x, dy = x_c.cuda(), dy_c.cuda()
 
-    def step():
+    def step(k):
         y, g, u = dgf.ffn_fwd(x, wg, wu, wd, training=True)
         return dgf.ffn_bwd(dy, x, g, u, wg, wu, wd)
 
-    for _ in range(warmup):
-        step()
+    for k in range(warmup):
+        step(k)
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+    st = sample_us(step, steps, samples)
     flops = 18 * M * H * I
-    tflops = flops / (ms * 1e-3) / 1e12
-    print(f"[bench] fwd+bwd M={M}: {ms:.3f} ms, {tflops:.1f} TFLOP/s", file=sys.stderr, flush=True)
-    return {"M": M, "ms_per_step": round(ms, 4), "flops_per_step": flops, "TFLOPs": round(tflops, 2),
-            "peak_TFLOPs": BF16_MFMA_PEAK_TFLOPS, "frac_mfma_peak": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
-            "steps": steps}
+    out = {"M": M, "ms_per_step": round(st["median"] * 1e-3, 4), "ms_min": round(st["min"] * 1e-3, 4),
+           "ms_max": round(st["max"] * 1e-3, 4), "flops_per_step": flops,
+           "TFLOPs": round(flops / (st["median"] * 1e-6) / 1e12, 2), "peak_TFLOPs": BF16_MFMA_PEAK_TFLOPS,
+           "steps": steps, "samples": samples, "samples_ms": [round(v * 1e-3, 4) for v in st["samples"]]}
+    out["frac_mfma_peak"] = round(out["TFLOPs"] / BF16_MFMA_PEAK_TFLOPS, 4)
+    # the forward alone at the same shape (inference mode)
+    for k in range(warmup):
+        dgf.ffn_fwd(x, wg, wu, wd)
+    fs = sample_us(lambda k: dgf.ffn_fwd(x, wg, wu, wd), steps, samples)
+    out["forward"] = stats_entry(fs, flops=6 * M * H * I)
+    print(f"[bench] fwd+bwd M={M}: {out['ms_per_step']:.3f} ms, {out['TFLOPs']:.1f} TFLOP/s; "
+          f"forward {fs['median'] * 1e-3:.3f} ms", file=sys.stderr, flush=True)
+    return out
+
+
+def two_stream_lanes(W, x, dy, args, kernels) -> dict:
+    """The dX lanes at M=32 three ways, from the same dG and dU: the two lane
+    GEMMs on two streams joined by events, then the ordered add (the pages'
+    next step for the backward); the same calls on one stream; and the
+    library's own one-launch lanes (its kernel time, from the profiled region,
+    plus the join that runs inside the weight-gradient launch)."""
+    import torch
+    from deterministic_gated_ffn_amd import binding as dgf
+    from deterministic_gated_ffn_amd import schedules
+
+    wg, wu, wd = W[0]
+    y, g, u = dgf.ffn_fwd(x, wg, wu, wd, training=True)
+    dA = dgf.gemm_tree("NN", dy, wd)
+    dG, dU, _ = dgf.act_bwd(dA, g, u)
+    torch.cuda.synchronize()
+    two = schedules.TwoStreamLanes()
+    copies = [(W[k][0], W[k][1]) for k in range(len(W))]
+    run_two = lambda k: two(dG, dU, *copies[k % len(copies)])
+    run_serial = lambda k: schedules.serial_lanes(dG, dU, *copies[k % len(copies)])
+    for k in range(args.warmup):
+        run_two(k)
+        run_serial(k)
+    out = {"two_streams": stats_entry(sample_us(run_two, args.steps, args.samples)),
+           "one_stream": stats_entry(sample_us(run_serial, args.steps, args.samples)),
+           "fused_lanes_kernel_us": kernels.get("dX lanes tree GEMM", {}).get("avg_us"),
+           "note": "two NN tree GEMMs (gate lane, up lane) and the two-part rank tree for the ordered add; "
+                   "the fused figure is the library's one-launch lanes kernel, whose join runs on extra "
+                   "workgroups of the dW_gate/dW_up launch"}
+    print(f"[bench] dX lanes: two streams {out['two_streams']['us']:.1f} us, one stream "
+          f"{out['one_stream']['us']:.1f} us, fused launch {out['fused_lanes_kernel_us']} us",
+          file=sys.stderr, flush=True)
+    return out
 
 
 def ordinal(b):
@@ -382,7 +439,19 @@ def cpu_baseline(M: int, gpu: dict) -> tuple[dict, dict]:
         ulp = int(np.abs(ordinal(got) - ordinal(ref)).max()) if got.size else 0
         per[k] = {"elements": int(got.size), "mismatches": bad, "max_ulp": ulp}
         n_all, bad_all, ulp_all = n_all + got.size, bad_all + bad, max(ulp_all, ulp)
+    # the same GPU outputs against the float64 brute-force FFN (no intermediate rounding)
+    from oracle import fp64
+    f = fp64.ffn_fwd(x, wg, wu, wd)
+    fb = fp64.ffn_bwd(dy, x, wg, wu, wd)
+    rel = {"y": fp64.rel_l2(gpu["y"], f["y"]), "g": fp64.rel_l2(gpu["g"], f["g"]), "u": fp64.rel_l2(gpu["u"], f["u"]),
+           "dX": fp64.rel_l2(gpu["dX"], fb["dX"]),
+           "dW_gate": fp64.rel_l2(gpu["dW_gate"][:I // frac], fb["dW_gate"][:I // frac]),
+           "dW_up": fp64.rel_l2(gpu["dW_up"][:I // frac], fb["dW_up"][:I // frac]),
+           "dW_down": fp64.rel_l2(gpu["dW_down"][:H // frac], fb["dW_down"][:H // frac])}
+    del f, fb
     parity = {"vs": "oracle", "elements": int(n_all), "mismatches": bad_all,
+              "rel_l2_vs_fp64": {k: float(f"{v:.3e}") for k, v in rel.items()},
+              "rel_l2_vs_fp64_max": float(f"{max(rel.values()):.3e}"), "rel_l2_bar": 1e-2,
               "exact_match_fraction": round(1 - bad_all / n_all, 9) if n_all else None, "max_ulp": ulp_all,
               "outputs": per,
               "sample": f"the M=32 training step on weight copy 0: y, g, u and dX in full, the first 1/{frac} "

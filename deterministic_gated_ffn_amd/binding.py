@@ -8,6 +8,7 @@ GPU) every call raises.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
@@ -82,6 +83,13 @@ def _stream(stream=None) -> int:
     return stream.cuda_stream
 
 
+def _on(stream):
+    """Allocate on the launch stream: outputs and the workspace come from that
+    stream's pool, so the caching allocator cannot hand a block to another
+    stream while the launched kernels still use it."""
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+
+
 def _mat(t: torch.Tensor, name: str):
     """(pointer, leading dimension) of a row-major BF16 matrix view on the GPU."""
     if t.dtype != torch.bfloat16:
@@ -116,6 +124,11 @@ def leaf_size() -> int:
 def ffn_fwd(x, w_gate, w_up, w_down, training: bool = False, out=None, stream=None):
     """y = W_down (silu(W_gate x) * (W_up x)) through the canonical tree.
     Returns y, or (y, g, u) when training."""
+    with _on(stream):
+        return _ffn_fwd(x, w_gate, w_up, w_down, training, out, stream)
+
+
+def _ffn_fwd(x, w_gate, w_up, w_down, training, out, stream):
     L = load()
     M, H = x.shape
     I = w_gate.shape[0]
@@ -136,6 +149,11 @@ def ffn_fwd(x, w_gate, w_up, w_down, training: bool = False, out=None, stream=No
 
 def ffn_bwd(dy, x, g, u, w_gate, w_up, w_down, lanes: bool = False, stream=None):
     """Returns dict dX, dW_gate, dW_up, dW_down (and G, U lanes if lanes=True)."""
+    with _on(stream):
+        return _ffn_bwd(dy, x, g, u, w_gate, w_up, w_down, lanes, stream)
+
+
+def _ffn_bwd(dy, x, g, u, w_gate, w_up, w_down, lanes, stream):
     L = load()
     M, H = x.shape
     I = w_gate.shape[0]
@@ -166,6 +184,11 @@ _COMBINE_DTYPES = {torch.bfloat16: DGF_BF16, torch.float16: DGF_FP16, torch.floa
 def tree_combine(parts, out=None, stream=None):
     """Balanced combine of S in {1,2,4,8} equally sized tensors (rank order);
     BF16, FP16 or FP32, all parts of one dtype."""
+    with _on(stream):
+        return _tree_combine(parts, out, stream)
+
+
+def _tree_combine(parts, out, stream):
     L = load()
     parts = list(parts)
     n = parts[0].numel()
@@ -194,6 +217,11 @@ def tree_combine_ptrs(ptrs, S: int, out_ptr: int, n: int, stream=None, dtype: in
 
 def gemm_tree(layout: str, A, B, out=None, stream=None):
     """NT: A [M,K], B [N,K]; NN: A [M,K], B [K,N]; TN: A [K,M], B [K,N] -> C [M,N]."""
+    with _on(stream):
+        return _gemm_tree(layout, A, B, out, stream)
+
+
+def _gemm_tree(layout, A, B, out, stream):
     L = load()
     lay = _LAYOUTS[layout]
     if layout == "NT":
@@ -212,14 +240,16 @@ def gemm_tree(layout: str, A, B, out=None, stream=None):
 
 def act_fwd(g, u, stream=None):
     L = load()
-    a = torch.empty_like(g)
+    with _on(stream):
+        a = torch.empty_like(g)
     _check(L.dgf_act_fwd(g.data_ptr(), u.data_ptr(), a.data_ptr(), g.numel(), _stream(stream)), "dgf_act_fwd")
     return a
 
 
 def act_bwd(da, g, u, stream=None):
     L = load()
-    dg, du, a = torch.empty_like(g), torch.empty_like(g), torch.empty_like(g)
+    with _on(stream):
+        dg, du, a = torch.empty_like(g), torch.empty_like(g), torch.empty_like(g)
     _check(L.dgf_act_bwd(da.data_ptr(), g.data_ptr(), u.data_ptr(), dg.data_ptr(), du.data_ptr(), a.data_ptr(),
                          g.numel(), _stream(stream)), "dgf_act_bwd")
     return dg, du, a

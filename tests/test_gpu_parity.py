@@ -111,7 +111,16 @@ def test_tiled_gemm_matches_oracle(M, N, K):
     assert_bitwise(got, expect, f"NT {M}x{N}x{K}")
 
 
-@pytest.mark.parametrize("dist", ["wide", "wide60", "cancel", "tiny", "ties"])
+def subnormal_mix(rng, shape):
+    """Half BF16 subnormals (exponent field 0, any nonzero fraction), half
+    normals just above them (exponents -126..-110), random signs."""
+    sub = rng.integers(1, 128, size=shape)
+    nrm = wide(rng, shape, -126, -110)
+    s = rng.integers(0, 2, size=shape) << 15
+    return np.where(rng.random(shape) < 0.5, s | sub, nrm).astype(np.uint16)
+
+
+@pytest.mark.parametrize("dist", ["wide", "wide60", "cancel", "tiny", "ties", "subnormal", "subnormal_tiny"])
 @pytest.mark.parametrize("K", [8, 32, 64, 128, 200])
 def test_leaf_block_rule_adversarial(dist, K):
     # The FP32 leaf's accumulation rule on inputs that separate it from other
@@ -129,6 +138,13 @@ def test_leaf_block_rule_adversarial(dist, K):
         B = np.where(rng.random((N, K)) < 0.2, wide(rng, (N, K), -2, 2), B).astype(np.uint16)
     elif dist == "tiny":
         A, B = wide(rng, (M, K), -70, -55), wide(rng, (N, K), -70, -55)
+    elif dist == "subnormal":
+        # BF16-subnormal operands against large ones: products in the normal FP32 range,
+        # where the subnormal's exponent (-126 for the block grid) decides what is cut
+        A, B = subnormal_mix(rng, (M, K)), wide(rng, (N, K), 90, 126)
+    elif dist == "subnormal_tiny":
+        # ... and against small ones: products and sums in the FP32 subnormal range
+        A, B = subnormal_mix(rng, (M, K)), wide(rng, (N, K), -30, 10)
     else:
         A = F2B((np.where(rng.random((M, K)) < 0.3, 2.0 ** -rng.integers(22, 27, (M, K)), 0)
                  * np.where(rng.random((M, K)) < 0.7, 1, -1)).astype(np.float32))
@@ -291,6 +307,26 @@ def test_ffn_other_shapes_bitwise(M, H, I):
         assert_bitwise(r[k], ob[k], k)
 
 
+@pytest.mark.parametrize("M,H,I", [(48, 1024, 3072), (200, 512, 1536), (130, 256, 4096)])
+def test_inference_forward_many_tokens(M, H, I):
+    # The inference forward (no g/u saved) past 32 tokens: the streaming
+    # gate/up GEMM (33..127 tokens) or the tiled one (128 and more) with the
+    # activation in the join, then the down projection.  Against the oracle,
+    # and the same y bits as the training forward (PR #325, "Correctness
+    # results": training and inference forward agree).
+    rng = np.random.default_rng(M * 3 + H + I)
+    x = rnd(rng, (M, H))
+    wg, wu, wd = rnd(rng, (I, H), 0.02), rnd(rng, (I, H), 0.02), rnd(rng, (H, I), 0.02)
+    o = oracle.ffn_fwd(x, wg, wu, wd)
+    xd, wgd, wud, wdd = padded(x), padded(wg), padded(wu), padded(wd)
+    y_inf = dgf.ffn_fwd(xd, wgd, wud, wdd)
+    y_tr, g, u = dgf.ffn_fwd(xd, wgd, wud, wdd, training=True)
+    torch.cuda.synchronize()
+    assert_bitwise(y_inf, o["y"], f"y (inference) M={M}")
+    assert_bitwise(y_tr, o["y"], f"y (training) M={M}")
+    assert_bitwise(g, o["g"], "g"); assert_bitwise(u, o["u"], "u")
+
+
 # ---------------------------------------------------------------- Qwen3-8B shapes
 @pytest.fixture(scope="module")
 def qwen_weights():
@@ -343,6 +379,8 @@ def test_full_size_forward_backward_vs_oracle(qwen_weights):
     dg, du, a = oracle.act_bwd(da, o["g"], o["u"])
     G = oracle.gemm_tree(dg, B["wg"], "NN"); U = oracle.gemm_tree(du, B["wu"], "NN")
     assert_bitwise(r["G"], G, "G lane"); assert_bitwise(r["U"], U, "U lane")
+    # the standalone dA tree GEMM (K = H along the rows of W_down) at the full shape
+    assert_bitwise(dgf.gemm_tree("NN", dy, wd), da, "dA")
     assert_bitwise(r["dX"], oracle.tree_combine([G, U]).reshape(G.shape), "dX")
     rows = np.random.default_rng(0).choice(12288, 48, replace=False)
     rows_h = np.random.default_rng(1).choice(4096, 48, replace=False)
@@ -360,8 +398,21 @@ def test_full_size_forward_backward_vs_oracle(qwen_weights):
     assert fp64.rel_l2(inputs.bits(r["dW_gate"])[rows], fb["dW_gate"][rows]) <= 1e-2
 
 
+@pytest.fixture(scope="module")
+def qwen_oracle_m32(qwen_weights):
+    """The oracle's M=32 forward and the dX part of the backward at the full shape."""
+    (wg_c, wu_c, wd_c), _ = qwen_weights
+    x_c, dy_c = inputs.activations(32)
+    B = {k: inputs.bits(v) for k, v in (("x", x_c), ("dy", dy_c), ("wg", wg_c), ("wu", wu_c), ("wd", wd_c))}
+    o = oracle.ffn_fwd(B["x"], B["wg"], B["wu"], B["wd"])
+    da = oracle.gemm_tree(B["dy"], B["wd"], "NN")
+    dg, du, _ = oracle.act_bwd(da, o["g"], o["u"])
+    G = oracle.gemm_tree(dg, B["wg"], "NN"); U = oracle.gemm_tree(du, B["wu"], "NN")
+    return {"y": o["y"], "g": o["g"], "dA": da, "G": G, "U": U, "dX": oracle.tree_combine([G, U]).reshape(G.shape)}
+
+
 @pytest.mark.parametrize("S", [2, 4, 8])
-def test_shard_invariance(qwen_weights, S):
+def test_shard_invariance(qwen_weights, qwen_oracle_m32, S):
     # Contiguous K shards computed as separate partial GEMMs and combined with the
     # balanced tree equal the unsharded result bit for bit (PR #325 "Design").
     _, (wg, wu, wd) = qwen_weights
@@ -394,6 +445,8 @@ def test_shard_invariance(qwen_weights, S):
                            (g_c, g, "g"), (da_c, da_full, "dA")):
         gb, rb = inputs.bits(got), inputs.bits(ref.contiguous())
         assert int((gb != rb).sum()) == 0, f"S={S} {name}: {(gb != rb).sum()} mismatches vs unsharded"
+        # and the combined shards against the oracle's unsharded result directly
+        assert_bitwise(got, qwen_oracle_m32[name], f"S={S} combined {name} vs oracle")
 
 
 def test_bad_arguments_raise():
@@ -455,9 +508,10 @@ def test_token_shard_weight_gradients(qwen_weights):
     # the token axis, so 512-token shards of the M=4096 case are 8-leaf
     # subtrees of that tree: per-shard backward passes combined with the
     # balanced tree reproduce the unsharded weight gradients bit for bit.
-    _, (wg, wu, wd) = qwen_weights
+    (wg_c, wu_c, wd_c), (wg, wu, wd) = qwen_weights
     M, S = 4096, 8
-    x, dy = (t.cuda() for t in inputs.activations(M))
+    x_c, dy_c = inputs.activations(M)
+    x, dy = x_c.cuda(), dy_c.cuda()
     y, g, u = dgf.ffn_fwd(x, wg, wu, wd, training=True)
     full = dgf.ffn_bwd(dy, x, g, u, wg, wu, wd)
     Ms = M // S
@@ -469,11 +523,24 @@ def test_token_shard_weight_gradients(qwen_weights):
         assert (inputs.bits(br["dX"]) == inputs.bits(full["dX"][sl])).all()
         for k in parts:
             parts[k].append(br[k].contiguous())
+    combined = {}
     for k, ps in parts.items():
         got = dgf.tree_combine(ps)
         torch.cuda.synchronize()
         gb, rb = inputs.bits(got), inputs.bits(full[k].contiguous())
         assert int((gb != rb).sum()) == 0, f"{k}: {(gb != rb).sum()} mismatches vs unsharded"
+        combined[k] = gb.reshape(full[k].shape)
+    # the combined shards against the oracle directly, on sampled I-slices (every
+    # dW_gate/dW_up row and dW_down column depends on its own slice of I only)
+    B = {k: inputs.bits(v) for k, v in (("x", x_c), ("dy", dy_c), ("wg", wg_c), ("wu", wu_c), ("wd", wd_c))}
+    cols = np.unique(np.concatenate([[0, 12287], np.random.default_rng(512).choice(12288, 2, replace=False)]))
+    wg_s, wu_s = np.ascontiguousarray(B["wg"][cols]), np.ascontiguousarray(B["wu"][cols])
+    wd_s = np.ascontiguousarray(B["wd"][:, cols])
+    os_ = oracle.ffn_fwd(B["x"], wg_s, wu_s, wd_s)
+    obs = oracle.ffn_bwd(B["dy"], B["x"], os_["g"], os_["u"], wg_s, wu_s, wd_s)
+    assert_bitwise(combined["dW_gate"][cols], obs["dW_gate"], "combined dW_gate rows vs oracle")
+    assert_bitwise(combined["dW_up"][cols], obs["dW_up"], "combined dW_up rows vs oracle")
+    assert_bitwise(combined["dW_down"][:, cols], obs["dW_down"], "combined dW_down columns vs oracle")
 
 
 def test_sub_leaf_token_shards_need_the_gather():
