@@ -31,6 +31,8 @@ SIGNATURES = {
     "dgf_ffn_fwd_workspace": (_SZ, [_I64, _I64, _I64]),
     "dgf_ffn_fwd": (_I, [_P, _I64, _P, _I64, _P, _I64, _P, _I64, _P, _I64, _P, _P, _I64,
                          _I64, _I64, _I64, _P, _SZ, _P]),
+    "dgf_ffn_fwd_static": (_I, [_P, _I64, _P, _I64, _P, _I64, _P, _I64, _P, _I64, _P, _P, _I64,
+                                _I64, _I64, _I64, _P]),
     "dgf_ffn_bwd_workspace": (_SZ, [_I64, _I64, _I64]),
     "dgf_ffn_bwd": (_I, [_P, _I64, _P, _I64, _P, _P, _I64, _P, _I64, _P, _I64, _P, _I64,
                          _P, _P, _P, _I64, _P, _I64, _P, _I64, _P, _I64,
@@ -145,6 +147,28 @@ def _ffn_fwd(x, w_gate, w_up, w_down, training, out, stream):
     _check(L.dgf_ffn_fwd(xp, ldx, wg, ldwg, wu, ldwu, wd, ldwd, yp, ldy, gp, up, ld_gu,
                          M, H, I, ws.data_ptr(), ws.numel(), _stream(stream)), "dgf_ffn_fwd")
     return (y, g, u) if training else y
+
+
+STATIC_SCRATCH_BYTES = 16 << 20  # DGF_STATIC_SCRATCH_BYTES
+
+
+def ffn_fwd_static(x, w_gate, w_up, w_down, y, g=None, u=None, stream=None):
+    """dgf_ffn_fwd_static: the forward into caller-given y (and g, u when
+    training) with the library's own scratch; allocates nothing."""
+    L = load()
+    M, H = x.shape
+    I = w_gate.shape[0]
+    xp, ldx = _mat(x, "x"); wg, ldwg = _mat(w_gate, "w_gate"); wu, ldwu = _mat(w_up, "w_up")
+    wd, ldwd = _mat(w_down, "w_down"); yp, ldy = _mat(y, "y")
+    gp = up = None
+    ld_gu = 0
+    if g is not None or u is not None:
+        (gp, ld_gu), (up, ldu) = _mat(g, "g"), _mat(u, "u")
+        if ldu != ld_gu:
+            raise ValueError("g and u must share a leading dimension")
+    _check(L.dgf_ffn_fwd_static(xp, ldx, wg, ldwg, wu, ldwu, wd, ldwd, yp, ldy, gp, up, ld_gu, M, H, I,
+                                _stream(stream)), "dgf_ffn_fwd_static")
+    return y
 
 
 def ffn_bwd(dy, x, g, u, w_gate, w_up, w_down, lanes: bool = False, stream=None):

@@ -4,6 +4,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 #include "dgf.h"
@@ -445,6 +446,34 @@ size_t gemm_ws_bytes(int layout, int64_t M, int64_t N, int64_t K) {
   return round256((size_t)M * Kp * 2) + round256((size_t)N * Kp * 2) + b;
 }
 
+// Library-owned scratch for dgf_ffn_fwd_static: one copy of this array per
+// GPU the library runs on, held until the process ends.  Host code never uses
+// the array's name as an address: its device address on each GPU comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+constexpr size_t kStaticScratchBytes = (size_t)DGF_STATIC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch` (resolved on the first call on
+// that device, then cached).
+dgf_status static_scratch(void **out) {
+  int dev = -1;
+  DGF_TRY(hip_check(hipGetDevice(&dev), "hipGetDevice"));
+  if (dev < 0 || dev >= kMaxDevices) return fail(DGF_EUNSUPPORTED, "device %d beyond this build's %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    DGF_TRY(hip_check(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)"));
+    if (!ptr || ((uintptr_t)ptr & 255) != 0) return fail(DGF_EHIP, "scratch: bad device address %p", ptr);
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return DGF_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -558,6 +587,24 @@ dgf_status dgf_ffn_fwd(const void *x, int64_t ldx, const void *w_gate, int64_t l
   q.M = M; q.N = H; q.K = I;
   DGF_TRY(run_gemm(DGF_LAYOUT_NT, 1, EPI_STORE, q, s, "down tree GEMM", partials, "down join"));
   return ok();
+}
+
+dgf_status dgf_ffn_fwd_static(const void *x, int64_t ldx, const void *w_gate, int64_t ld_wg, const void *w_up,
+                              int64_t ld_wu, const void *w_down, int64_t ld_wd, void *y, int64_t ldy, void *g_save,
+                              void *u_save, int64_t ld_gu, int64_t M, int64_t H, int64_t I, void *stream) {
+  DGF_TRY(check_dims(M, I, H));
+  DGF_TRY(check_dims(M, H, I));
+  if (H == 0 || I == 0) return fail(DGF_EINVAL, "H and I must be positive (H=%lld I=%lld)", (long long)H, (long long)I);
+  if (M == 0) return ok();
+  const size_t need = fwd_ws_bytes(M, H, I);
+  if (need > kStaticScratchBytes)
+    return fail(DGF_EUNSUPPORTED, "forward without allocation: needs %zu bytes of scratch, past the library's %zu "
+                "(M=%lld, H=%lld, I=%lld); use dgf_ffn_fwd with a workspace", need, kStaticScratchBytes,
+                (long long)M, (long long)H, (long long)I);
+  void *ws = nullptr;
+  DGF_TRY(static_scratch(&ws));
+  return dgf_ffn_fwd(x, ldx, w_gate, ld_wg, w_up, ld_wu, w_down, ld_wd, y, ldy, g_save, u_save, ld_gu, M, H, I, ws,
+                     kStaticScratchBytes, stream);
 }
 
 size_t dgf_ffn_bwd_workspace(int64_t M, int64_t H, int64_t I) {

@@ -34,8 +34,10 @@
  *    fusion claimed (PR #357, section "Compute/communication fusion").
  *  - Ownership: the caller allocates every buffer, the workspace included.  The
  *    library allocates and frees nothing and keeps no device state; the only
- *    globals are the thread-local error message and timing-hook state.  Calls on different streams may
- *    run concurrently as long as their output and workspace buffers differ.
+ *    globals are the thread-local error message and timing-hook state, and the
+ *    static scratch array of dgf_ffn_fwd_static (the one entry point without a
+ *    workspace argument).  Calls on different streams may run concurrently as
+ *    long as their output and workspace buffers differ.
  *  - Errors are status codes; nothing aborts or throws across the ABI.
  *    dgf_last_error() describes the last non-OK status of the calling thread.
  *    Arguments are validated before any HIP call is made.
@@ -96,6 +98,30 @@ dgf_status dgf_ffn_fwd(const void *x, int64_t ldx,
                        void *g_save, void *u_save, int64_t ld_gu,
                        int64_t M, int64_t H, int64_t I,
                        void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * The forward without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Arguments, results and errors as dgf_ffn_fwd (the same
+ * kernels, the same bits); the workspace is the library's own static device
+ * array of DGF_STATIC_SCRATCH_BYTES, one per GPU, kept until the process
+ * ends.  A problem whose dgf_ffn_fwd_workspace(M,H,I) exceeds that size
+ * returns DGF_EUNSUPPORTED before anything is enqueued (H=4096, I=12288: up
+ * to 128 tokens).  The call allocates nothing and calls no allocating
+ * library routine; its first call on a device resolves the array's address
+ * there (hipGetSymbolAddress).  Every call on a GPU shares that GPU's array:
+ * calls that may overlap on one GPU (other streams, other threads) race and
+ * must be serialised by the caller.  Nothing in the array needs clearing
+ * between calls: each call writes every scratch byte it reads.
+ */
+#define DGF_STATIC_SCRATCH_BYTES (16u << 20)
+dgf_status dgf_ffn_fwd_static(const void *x, int64_t ldx,
+                              const void *w_gate, int64_t ld_wg,
+                              const void *w_up, int64_t ld_wu,
+                              const void *w_down, int64_t ld_wd,
+                              void *y, int64_t ldy,
+                              void *g_save, void *u_save, int64_t ld_gu,
+                              int64_t M, int64_t H, int64_t I, void *stream);
 
 /*
  * Backward from dY [M,H] (lddy), the input x [M,H] (ldx) and the saved g, u
