@@ -40,14 +40,55 @@ namespace {
 constexpr int kMmWaves = 8;
 constexpr int kMmBM = 128, kMmBN = 128;  // workgroup tile: tokens x outputs
 constexpr int kMmTM = 2, kMmTN = 4;      // a wave's 16 x 16 tiles: 32 tokens x 64 outputs
-constexpr int kMmNP = kMmTM * kMmTN * 2;  // packed BF16 pairs per lane: index (tn TM + tm) 2 + h
+constexpr int kMmNV = kMmTM * kMmTN * 4;  // tree values per lane: index (tn TM + tm) 4 + e
+constexpr int kMmNP = kMmNV / 2;          // the same as packed BF16 pairs (parked levels)
 constexpr size_t kMmStage = (size_t)(kMmBM + kMmBN) * 64 * 2;  // A then B tile of one leaf (bytes)
-// Leaves per lower subtree, at most: past 4 the pending values, the
-// accumulators and the fragments no longer fit a wave's 256 registers.
+// Leaves per lower subtree, at most: their pending values stay in registers.
 constexpr int kMmMaxNL = 4;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// BF16 rounding (nearest even) of x, kept in FP32 format: the BF16 value in
+// the high half and zeros below, one v_cvt_pk_bf16_f32 with a zero partner.
+// Tree values stay in this form, so a node is one FP32 add and one rounding.
+__device__ __forceinline__ float rbf(float x) {
+  const f32x2 v = {0.f, x};
+  return __builtin_bit_cast(float, __builtin_convertvector(v, bf16x2));
+}
+
+// The high halves of two FP32-form BF16 values as one packed pair (lo, hi).
+__device__ __forceinline__ uint32_t pack_hi(float lo, float hi) {
+  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
+
+// An empty instruction that "defines" each value, ordered with the
+// surrounding scheduling barriers: the values are computed before it.
+__device__ __forceinline__ void pin(float (&v)[kMmNV]) {
+#pragma unroll
+  for (int q = 0; q < kMmNV; ++q) asm volatile("" : "+v"(v[q]));
+}
+
+// Feed leaf J (values v, FP32 form) of an N-leaf lower subtree (N <= 4):
+// merge it with the pending left siblings its position closes, then park it
+// at its depth; after the last leaf v is the subtree root.
+template <int N, int J>
+__device__ __forceinline__ void push_f(float (&v)[kMmNV], float (&st)[2][kMmNV]) {
+  constexpr LeafPos lp = leaf_pos(N, J);
+#pragma unroll
+  for (int t = 0; t < lp.m; ++t)
+#pragma unroll
+    for (int q = 0; q < kMmNV; ++q) v[q] = rbf(st[lp.D - 1 - t][q] + v[q]);
+  constexpr int d = lp.D - lp.m;
+  if constexpr (d > 0) {
+#pragma unroll
+    for (int q = 0; q < kMmNV; ++q) st[d - 1][q] = v[q];
+  }
+}
+
+// TAIL: K is not a whole number of leaves (the last leaf is partial and
+// loads element by element); otherwise every leaf takes the buffer path and
+// the leaf sequence has no branches.
+template <bool TAIL>
 struct MmWg {
   const GemmParams &p;
   uint16_t *lds;  // [2 stages][A 128 x 64 | B 128 x 64], then the waves' top-level stacks
@@ -58,6 +99,9 @@ struct MmWg {
   int wm, wn;  // this wave's 32-token row block and 64-output column block
   int plo, phi;
   uint32_t voa[2], vob[2];  // byte offsets of this thread's chunks within a leaf's A and B tiles
+  // whole-leaf path: descriptors at the tile's first row (k = 0), over the
+  // rows from there on (rows past M / N fall outside and read as zero)
+  __amdgpu_buffer_rsrc_t sa_tile, sb_tile;
 
   // Global loads of leaf j's two tiles: thread t covers chunks t and t + 512
   // of each (8 threads per 128-byte row segment).  A full leaf uses buffer
@@ -65,18 +109,16 @@ struct MmWg {
   // arithmetic) with fixed per-thread offsets; rows past M / N fall outside
   // the descriptor's range and read as zero.  The partial last leaf reads
   // element by element with zeros past K.
+  // A leaf past the piece (j >= phi) is pushed out of the descriptors'
+  // range: no memory request (the register set it fills is never used).
   __device__ __forceinline__ void fetch(int j, u32x4 (&g)[4]) const {
     const int64_t kb = (int64_t)j * kLeaf;
-    if (kb + kLeaf <= p.K) {
-      const int64_t ra = (p.M - m0) * lda * 2 - kb * 2, rb = (p.N - n0) * ldb * 2 - kb * 2;
-      const __amdgpu_buffer_rsrc_t sa = __builtin_amdgcn_make_buffer_rsrc(
-          (void *)(A + m0 * lda + kb), (short)0, (int)(ra < 0x7fffffff ? ra : 0x7fffffff), 0x00020000);
-      const __amdgpu_buffer_rsrc_t sb = __builtin_amdgcn_make_buffer_rsrc(
-          (void *)(B + n0 * ldb + kb), (short)0, (int)(rb < 0x7fffffff ? rb : 0x7fffffff), 0x00020000);
+    if (!TAIL || kb + kLeaf <= p.K) {
+      const uint32_t add = j < phi ? (uint32_t)(kb * 2) : 0x80000000u;
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        g[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(sa, (int)voa[i], 0, 0));
-        g[2 + i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(sb, (int)vob[i], 0, 0));
+        g[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(sa_tile, (int)(voa[i] + add), 0, 0));
+        g[2 + i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(sb_tile, (int)(vob[i] + add), 0, 0));
       }
       return;
     }
@@ -117,37 +159,13 @@ struct MmWg {
     }
   }
 
-  __device__ __forceinline__ void pack(const f32x4 (&acc)[kMmTN][kMmTM], uint32_t (&v)[kMmNP]) const {
-#pragma unroll
-    for (int tn = 0; tn < kMmTN; ++tn)
-#pragma unroll
-      for (int tm = 0; tm < kMmTM; ++tm) {
-        v[(tn * kMmTM + tm) * 2 + 0] = pack_rne(acc[tn][tm][0], acc[tn][tm][1]);
-        v[(tn * kMmTM + tm) * 2 + 1] = pack_rne(acc[tn][tm][2], acc[tn][tm][3]);
-      }
-  }
-
-  // One leaf j: its fragment reads from stage (j - plo) & 1; while they
-  // drain, the previous leaf of the subtree (rounded, packed) goes into the
-  // tree; then its MFMAs, and this leaf is packed, leaf
-  // j + 1's tiles (fetched two leaves earlier into register set `nx`) go into
-  // the other stage, leaf j + 3 is fetched into that set, and the barrier
-  // publishes the stage just written and frees the one just read.
-  template <int NL, int J>
-  __device__ __forceinline__ void one_leaf(int j, u32x4 (&nx)[4], uint32_t (&v)[kMmNP],
-                                           uint32_t (&st)[3][kMmNP]) const {
-    const int s = (j - plo) & 1;
+  // The canonical leaf of the wave's 8 tiles: two MFMAs per tile from a zero
+  // accumulator (K 0..31, then 32..63).
+  __device__ __forceinline__ void leaf_mfma(int s, f32x4 (&acc)[kMmTN][kMmTM]) const {
     const uint16_t *sa = lds + (size_t)s * (kMmStage / 2), *sb = sa + kMmBM * 64;
-    f32x4 acc[kMmTN][kMmTM];
     bf16x8 af0[kMmTM], bf0[kMmTN], af1[kMmTM], bf1[kMmTN];
-    // every fragment read of the leaf goes out first, and the previous
-    // leaf's tree merges (VALU) run while the workgroup's reads drain
-    // through the LDS; then the two K halves' MFMAs
     frags<0>(sa, sb, af0, bf0);
     frags<1>(sa, sb, af1, bf1);
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (J > 0) push_leaf<kMmNP, NL, J - 1>(v, st);
-    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int tn = 0; tn < kMmTN; ++tn)
 #pragma unroll
@@ -156,42 +174,91 @@ struct MmWg {
     for (int tn = 0; tn < kMmTN; ++tn)
 #pragma unroll
       for (int tm = 0; tm < kMmTM; ++tm) acc[tn][tm] = mfma16(bf1[tn], af1[tm], acc[tn][tm]);
-    pack(acc, v);
-    if (j + 1 < phi) stage_store(s ^ 1, nx);
-    if (j + 3 < phi) fetch(j + 3, nx);
+  }
+
+  // A leaf's accumulators rounded to BF16, FP32 form.
+  __device__ __forceinline__ void round_leaf(const f32x4 (&acc)[kMmTN][kMmTM], float (&v)[kMmNV]) const {
+#pragma unroll
+    for (int tn = 0; tn < kMmTN; ++tn)
+#pragma unroll
+      for (int tm = 0; tm < kMmTM; ++tm)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[(tn * kMmTM + tm) * 4 + e] = rbf(acc[tn][tm][e]);
+  }
+
+  // Leaf j (leaf J of a lower subtree of NL leaves) from stage s into acc, in
+  // one scheduling region: the fragment reads, then the MFMAs interleaved
+  // with the tree step of leaf J - 1 (rounding and merges of prev:
+  // independent VALU work, about seven instructions per MFMA), then leaf
+  // j + 1's tiles (fetched two leaves earlier into register set `nx`) into
+  // the other stage and the fetch of leaf j + 3 into that set; the barrier
+  // publishes the stage just written and frees the one just read.
+  template <int NL, int J>
+  __device__ __forceinline__ void one_leaf(int j, int s, u32x4 (&nx)[4], const f32x4 (&prev)[kMmTN][kMmTM],
+                                           f32x4 (&acc)[kMmTN][kMmTM], float (&v)[kMmNV],
+                                           float (&st)[2][kMmNV]) const {
+    __builtin_amdgcn_sched_barrier(0);
+    leaf_mfma(s, acc);
+    if constexpr (J > 0) {
+      round_leaf(prev, v);
+      push_f<NL, J - 1>(v, st);
+    }
+    // past the piece's last leaf the stage store writes a stage nobody reads
+    // and the fetch requests nothing, so the leaf sequence needs no branch
+    if (!TAIL || j + 1 < phi) stage_store(s ^ 1, nx);
+    if (!TAIL || j + 3 < phi) fetch(j + 3, nx);
+    if constexpr (!TAIL) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);  // fragment reads
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);  // a share of the tree step
+      }
+      __builtin_amdgcn_sched_group_barrier(0x200, 4, 0);  // stage store
+      __builtin_amdgcn_sched_group_barrier(0x020, 4, 0);  // next fetch
+    }
+    __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
   }
 
   // Leaves J.. of a lower subtree of NL leaves, the first being leaf j of the
-  // piece; the two register sets alternate with the leaf's parity in the piece.
-  template <int NL, int J>
-  __device__ __forceinline__ void lower(int j, u32x4 (&r0)[4], u32x4 (&r1)[4], uint32_t (&v)[kMmNP],
-                                        uint32_t (&st)[3][kMmNP]) const {
+  // piece, whose parity in the piece is P0: the stage and register set of
+  // every leaf are compile-time, and the two accumulator sets alternate with J.
+  template <int NL, int J, int P0>
+  __device__ __forceinline__ void leaves(int j, u32x4 (&r0)[4], u32x4 (&r1)[4], f32x4 (&prev)[kMmTN][kMmTM],
+                                         f32x4 (&acc)[kMmTN][kMmTM], float (&v)[kMmNV], float (&st)[2][kMmNV]) const {
     if constexpr (J < NL) {
-      if (((j - plo) & 1) == 0)
-        one_leaf<NL, J>(j, r1, v, st);
+      constexpr int S = (P0 ^ J) & 1;
+      if constexpr (S == 0)
+        one_leaf<NL, J>(j, 0, r1, prev, acc, v, st);
       else
-        one_leaf<NL, J>(j, r0, v, st);
-      lower<NL, J + 1>(j + 1, r0, r1, v, st);
+        one_leaf<NL, J>(j, 1, r0, prev, acc, v, st);
+      leaves<NL, J + 1, P0>(j + 1, r0, r1, acc, prev, v, st);
     } else {
-      push_leaf<kMmNP, NL, NL - 1>(v, st);  // the subtree's last leaf: v becomes its root
+      round_leaf(prev, v);
+      push_f<NL, NL - 1>(v, st);  // the subtree's last leaf: v becomes its root
     }
   }
 
   template <int NL>
-  __device__ __forceinline__ void lower_tree(int j, u32x4 (&r0)[4], u32x4 (&r1)[4], uint32_t (&v)[kMmNP]) const {
-    uint32_t st[3][kMmNP];
-    lower<NL, 0>(j, r0, r1, v, st);
+  __device__ __forceinline__ void lower_tree(int j, u32x4 (&r0)[4], u32x4 (&r1)[4], float (&v)[kMmNV]) const {
+    float st[2][kMmNV];
+    f32x4 a0[kMmTN][kMmTM], a1[kMmTN][kMmTM];
+    if (((j - plo) & 1) == 0)
+      leaves<NL, 0, 0>(j, r0, r1, a0, a1, v, st);
+    else
+      leaves<NL, 0, 1>(j, r0, r1, a0, a1, v, st);
   }
 
-  __device__ __forceinline__ void store_root(const uint32_t (&v)[kMmNP], uint16_t *out, int64_t ldo) const {
+  __device__ __forceinline__ void store_root(const float (&v)[kMmNV], uint16_t *out, int64_t ldo) const {
 #pragma unroll
     for (int tn = 0; tn < kMmTN; ++tn)
 #pragma unroll
       for (int tm = 0; tm < kMmTM; ++tm) {
         const int64_t m = m0 + 32 * wm + 16 * tm + r16, n = n0 + 64 * wn + 16 * tn + 4 * g4;
         if (m >= p.M || n >= p.N) continue;
-        const uint32_t lo2 = v[(tn * kMmTM + tm) * 2 + 0], hi2 = v[(tn * kMmTM + tm) * 2 + 1];
+        const int i = (tn * kMmTM + tm) * 4;
+        const uint32_t lo2 = pack_hi(v[i], v[i + 1]), hi2 = pack_hi(v[i + 2], v[i + 3]);
         uint16_t *dst = out + m * ldo + n;
         if (n + 3 < p.N) {
           *reinterpret_cast<uint2 *>(dst) = make_uint2(lo2, hi2);
@@ -205,32 +272,44 @@ struct MmWg {
   }
 };
 
-// Pending left subtrees of the top levels, in this wave's own LDS region:
-// level t, pair q of lane l at base[(t kMmNP + q) 64 + l] (each lane reads
-// back only what it wrote; consecutive lanes, consecutive dwords).
-__device__ __forceinline__ void park(uint32_t *base, int t, const uint32_t (&v)[kMmNP]) {
+// Pending left subtrees of the top levels, in this wave's own LDS region as
+// packed BF16 pairs: level t, pair q of lane l at base[(t kMmNP + q) 64 + l]
+// (each lane reads back only what it wrote; consecutive lanes, consecutive
+// dwords).
+__device__ __forceinline__ void park(uint32_t *base, int t, const float (&v)[kMmNV]) {
 #pragma unroll
-  for (int q = 0; q < kMmNP; ++q) base[(t * kMmNP + q) * 64] = v[q];
+  for (int q = 0; q < kMmNP; ++q) base[(t * kMmNP + q) * 64] = pack_hi(v[2 * q], v[2 * q + 1]);
 }
-__device__ __forceinline__ void merge(const uint32_t *base, int t, uint32_t (&v)[kMmNP]) {
+__device__ __forceinline__ void merge(const uint32_t *base, int t, float (&v)[kMmNV]) {
 #pragma unroll
-  for (int q = 0; q < kMmNP; ++q) v[q] = node2(base[(t * kMmNP + q) * 64], v[q]);
+  for (int q = 0; q < kMmNP; ++q) {
+    const uint32_t l = base[(t * kMmNP + q) * 64];
+    v[2 * q] = rbf(bf_lo(l) + v[2 * q]);
+    v[2 * q + 1] = rbf(bf_hi(l) + v[2 * q + 1]);
+  }
 }
 
 // NLH: the larger of the two lower-subtree sizes (the smaller is NLH - 1).
-template <int NLH>
+template <int NLH, bool TAIL>
 __global__ __launch_bounds__(kMmWaves * 64) void k_mm(GemmParams p) {
   extern __shared__ __attribute__((aligned(16))) uint16_t mm_lds[];
   const int kd = p.ksplit_depth, up = p.stack_slots;  // K-piece depth; upper levels cut inside the piece
   const int b = blockIdx.z >> kd, piece = blockIdx.z & ((1 << kd) - 1);
   // Row-major tile order: the workgroups in flight share the A rows of a few
-  // tile rows (measured a little faster here than grouping tile blocks per
-  // XCD, which shares B rows as well).
+  // tile rows (a banded per-XCD order measured the same).
   const int tiles_n = (int)((p.N + kMmBN - 1) / kMmBN);
   const int tile_m = (int)blockIdx.x / tiles_n, tile_n = (int)blockIdx.x % tiles_n;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  MmWg w{p,
+  const int64_t m0 = (int64_t)tile_m * kMmBM, n0 = (int64_t)tile_n * kMmBN;
+  // descriptors at the tile's first row (k = 0) over the rows from there on;
+  // a tile's rows times the leading dimension stay below 2^31 bytes (ld < 2^23)
+  const int64_t ra = (p.M - m0) * p.lda[b] * 2, rb = (p.N - n0) * p.ldb[b] * 2;
+  const __amdgpu_buffer_rsrc_t sa_tile = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(p.A[b] + m0 * p.lda[b]), (short)0, (int)(ra < 0x7fffffff ? ra : 0x7fffffff), 0x00020000);
+  const __amdgpu_buffer_rsrc_t sb_tile = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(p.B[b] + n0 * p.ldb[b]), (short)0, (int)(rb < 0x7fffffff ? rb : 0x7fffffff), 0x00020000);
+  MmWg<TAIL> w{p,
          mm_lds,
          p.A[b],
          p.B[b],
@@ -248,7 +327,9 @@ __global__ __launch_bounds__(kMmWaves * 64) void k_mm(GemmParams p) {
          0,
          0,
          {0u, 0u},
-         {0u, 0u}};
+         {0u, 0u},
+         sa_tile,
+         sb_tile};
   subtree_range(p.L, kd, piece, w.plo, w.phi);
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -261,12 +342,12 @@ __global__ __launch_bounds__(kMmWaves * 64) void k_mm(GemmParams p) {
   u32x4 r0[4], r1[4];
   w.fetch(w.plo, r0);
   w.stage_store(0, r0);
-  if (w.plo + 1 < w.phi) w.fetch(w.plo + 1, r1);
-  if (w.plo + 2 < w.phi) w.fetch(w.plo + 2, r0);
+  w.fetch(w.plo + 1, r1);  // empty past the piece
+  w.fetch(w.plo + 2, r0);
   __syncthreads();
 
   // lower subtrees in order; the top `up` levels over their roots
-  uint32_t v[kMmNP];
+  float v[kMmNV];
   uint32_t *upl = reinterpret_cast<uint32_t *>(reinterpret_cast<char *>(mm_lds) + 2 * kMmStage) +
                   (size_t)wave * 3 * kMmNP * 64 + lane;
   const int nsub = 1 << up;
@@ -309,11 +390,16 @@ hipError_t launch_mm(GemmParams p, int nb, int nlh, hipStream_t stream) {
   const dim3 grid((unsigned)tiles, 1u, (unsigned)(nb << p.ksplit_depth));
   const dim3 block(kMmWaves * 64);
   const size_t shm = mm_lds_bytes();
-  switch (nlh) {
-    case 1: dgf_launch(k_mm<1>, grid, block, shm, stream, p); break;
-    case 2: dgf_launch(k_mm<2>, grid, block, shm, stream, p); break;
-    case 3: dgf_launch(k_mm<3>, grid, block, shm, stream, p); break;
-    case 4: dgf_launch(k_mm<4>, grid, block, shm, stream, p); break;
+  const bool tail = p.K % kLeaf != 0;
+  switch (nlh * 2 + (tail ? 1 : 0)) {
+    case 2: dgf_launch(k_mm<1, false>, grid, block, shm, stream, p); break;
+    case 3: dgf_launch(k_mm<1, true>, grid, block, shm, stream, p); break;
+    case 4: dgf_launch(k_mm<2, false>, grid, block, shm, stream, p); break;
+    case 5: dgf_launch(k_mm<2, true>, grid, block, shm, stream, p); break;
+    case 6: dgf_launch(k_mm<3, false>, grid, block, shm, stream, p); break;
+    case 7: dgf_launch(k_mm<3, true>, grid, block, shm, stream, p); break;
+    case 8: dgf_launch(k_mm<4, false>, grid, block, shm, stream, p); break;
+    case 9: dgf_launch(k_mm<4, true>, grid, block, shm, stream, p); break;
     default: return hipErrorInvalidValue;  // lower subtrees hold at most kMmMaxNL leaves
   }
   return hipGetLastError();
