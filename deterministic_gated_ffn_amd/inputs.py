@@ -13,6 +13,9 @@ Recipe (the pages load no model or dataset: RL-Kernel PR #325, section "Note"):
     tokens uses rows [0, M), so M = 1/8/32/4096 share their first rows.  The
     M=4096 case is read as 8 sequences x 512 tokens, sequence-major.
 Weights use the [out, in] layout (PR #325, section "Operator test matrix").
+The FP16 cases draw the same FP32 values and round them to FP16 instead
+(nearest even); every value of these distributions is in FP16's normal range
+or a subnormal, none overflows.
 """
 from __future__ import annotations
 
@@ -27,65 +30,69 @@ QWEN3_8B_I = 12288
 FULL_ROWS = 4096
 
 
-def _randn(gen: torch.Generator, shape, scale: float | None = None) -> torch.Tensor:
+STORED = (torch.bfloat16, torch.float16)
+
+
+def _randn(gen: torch.Generator, shape, scale: float | None = None, dtype=torch.bfloat16) -> torch.Tensor:
     t = torch.randn(*shape, generator=gen, dtype=torch.float32)
     if scale is not None:
         t = t * scale
-    return t.to(torch.bfloat16)
+    return t.to(dtype)
 
 
-def tiny_case(M: int = 4, H: int = 256, I: int = 768, seed: int = 0) -> dict:
-    """The tiny fwd+bwd case; CPU BF16 tensors."""
+def tiny_case(M: int = 4, H: int = 256, I: int = 768, seed: int = 0, dtype=torch.bfloat16) -> dict:
+    """The tiny fwd+bwd case; CPU tensors of the stored type."""
     gen = torch.Generator("cpu").manual_seed(seed)
-    x = _randn(gen, (M, H))
-    w_gate = _randn(gen, (I, H), 0.02)
-    w_up = _randn(gen, (I, H), 0.02)
-    w_down = _randn(gen, (H, I), 0.02)
-    dy = _randn(gen, (M, H))
+    x = _randn(gen, (M, H), dtype=dtype)
+    w_gate = _randn(gen, (I, H), 0.02, dtype)
+    w_up = _randn(gen, (I, H), 0.02, dtype)
+    w_down = _randn(gen, (H, I), 0.02, dtype)
+    dy = _randn(gen, (M, H), dtype=dtype)
     return {"x": x, "w_gate": w_gate, "w_up": w_up, "w_down": w_down, "dy": dy}
 
 
 @functools.lru_cache(maxsize=4)
-def ffn_weights(H: int = QWEN3_8B_H, I: int = QWEN3_8B_I, seed: int = 0):
+def ffn_weights(H: int = QWEN3_8B_H, I: int = QWEN3_8B_I, seed: int = 0, dtype=torch.bfloat16):
     gen = torch.Generator("cpu").manual_seed(seed)
-    w_gate = _randn(gen, (I, H), 0.02)
-    w_up = _randn(gen, (I, H), 0.02)
-    w_down = _randn(gen, (H, I), 0.02)
+    w_gate = _randn(gen, (I, H), 0.02, dtype)
+    w_up = _randn(gen, (I, H), 0.02, dtype)
+    w_down = _randn(gen, (H, I), 0.02, dtype)
     return w_gate, w_up, w_down
 
 
 @functools.lru_cache(maxsize=2)
-def _activations_full(H: int, rows: int, seed: int):
+def _activations_full(H: int, rows: int, seed: int, dtype=torch.bfloat16):
     gen = torch.Generator("cpu").manual_seed(seed)
-    x_full = _randn(gen, (rows, H))
-    dy_full = _randn(gen, (rows, H))
+    x_full = _randn(gen, (rows, H), dtype=dtype)
+    dy_full = _randn(gen, (rows, H), dtype=dtype)
     return x_full, dy_full
 
 
-def activations(M: int, H: int = QWEN3_8B_H, seed: int = 1, rows: int = FULL_ROWS):
-    """x[:M], dY[:M] of the shared 4096-row draws (CPU BF16)."""
+def activations(M: int, H: int = QWEN3_8B_H, seed: int = 1, rows: int = FULL_ROWS, dtype=torch.bfloat16):
+    """x[:M], dY[:M] of the shared 4096-row draws (CPU, stored type)."""
     if M > rows:
         raise ValueError(f"M={M} exceeds the {rows} generated rows")
-    x_full, dy_full = _activations_full(H, rows, seed)
+    x_full, dy_full = _activations_full(H, rows, seed, dtype)
     return x_full[:M], dy_full[:M]
 
 
-def qwen3_case(M: int, H: int = QWEN3_8B_H, I: int = QWEN3_8B_I, wseed: int = 0, aseed: int = 1) -> dict:
-    w_gate, w_up, w_down = ffn_weights(H, I, wseed)
-    x, dy = activations(M, H, aseed)
+def qwen3_case(M: int, H: int = QWEN3_8B_H, I: int = QWEN3_8B_I, wseed: int = 0, aseed: int = 1,
+               dtype=torch.bfloat16) -> dict:
+    w_gate, w_up, w_down = ffn_weights(H, I, wseed, dtype)
+    x, dy = activations(M, H, aseed, dtype=dtype)
     return {"x": x, "w_gate": w_gate, "w_up": w_up, "w_down": w_down, "dy": dy}
 
 
 def bits(t: torch.Tensor) -> np.ndarray:
-    """BF16 tensor -> numpy uint16 bit patterns (host copy)."""
-    assert t.dtype == torch.bfloat16
+    """BF16 or FP16 tensor -> numpy uint16 bit patterns (host copy)."""
+    assert t.dtype in STORED, t.dtype
     return t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
 
 
-def from_bits(a: np.ndarray) -> torch.Tensor:
-    """numpy uint16 bit patterns -> CPU BF16 tensor."""
+def from_bits(a: np.ndarray, dtype=torch.bfloat16) -> torch.Tensor:
+    """numpy uint16 bit patterns -> CPU tensor of the stored type."""
     a = np.ascontiguousarray(np.asarray(a, dtype=np.uint16))
-    return torch.from_numpy(a.view(np.int16).copy()).view(torch.bfloat16)
+    return torch.from_numpy(a.view(np.int16).copy()).view(dtype)
 
 
 def sha256(t: torch.Tensor) -> str:

@@ -3,7 +3,8 @@
 Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``bench.py`` may import this package.  The product path (the HIP library and
 its Python binding) never imports, links or falls back to it, and the two share
-no code.  BF16 tensors cross this interface as ``numpy.uint16`` bit patterns.
+no code.  BF16 and FP16 tensors cross this interface as ``numpy.uint16`` bit
+patterns; functions with a ``dtype`` argument take "bf16" (default) or "fp16".
 
 ``dgf_oracle.c`` is the tree oracle (canonical leaf/tree of RL-Kernel PR #325,
 section "Design"); ``fp64.py`` is the float64 brute-force FFN used as an
@@ -72,8 +73,37 @@ def lib():
         L.oracle_ffn_fwd.argtypes = [P] * 8 + [I64] * 3
         L.oracle_ffn_bwd.restype = None
         L.oracle_ffn_bwd.argtypes = [P] * 17 + [I64] * 3
+        # the same functions for a stored type (0 BF16, 1 FP16) given first
+        Ci = ctypes.c_int
+        L.oracle_block_step_t.restype = ctypes.c_float
+        L.oracle_block_step_t.argtypes = [Ci, ctypes.c_float, P, I64, P, I64, Ci]
+        L.oracle_leaf_f32_t.restype = ctypes.c_float
+        L.oracle_leaf_f32_t.argtypes = [Ci, P, I64, P, I64, I64]
+        L.oracle_dot_tree_t.restype = ctypes.c_uint16
+        L.oracle_dot_tree_t.argtypes = [Ci, P, I64, P, I64, I64]
+        L.oracle_dot_subtree_t.restype = ctypes.c_uint16
+        L.oracle_dot_subtree_t.argtypes = [Ci, P, I64, P, I64, I64, I64, I64]
+        L.oracle_gemm_tree_t.restype = None
+        L.oracle_gemm_tree_t.argtypes = [Ci, P, I64, I64, P, I64, I64, P, I64, I64, I64, I64]
+        L.oracle_act_fwd_t.restype = None
+        L.oracle_act_fwd_t.argtypes = [Ci, P, P, P, I64]
+        L.oracle_act_bwd_t.restype = None
+        L.oracle_act_bwd_t.argtypes = [Ci, P, P, P, P, P, P, I64]
+        L.oracle_ffn_fwd_t.restype = None
+        L.oracle_ffn_fwd_t.argtypes = [Ci] + [P] * 8 + [I64] * 3
+        L.oracle_ffn_bwd_t.restype = None
+        L.oracle_ffn_bwd_t.argtypes = [Ci] + [P] * 17 + [I64] * 3
         _lib = L
     return _lib
+
+
+_ELEM = {"bf16": 0, "fp16": 1}
+
+
+def _dt(dtype: str) -> int:
+    if dtype not in _ELEM:
+        raise ValueError(f"stored type must be bf16 or fp16, got {dtype!r}")
+    return _ELEM[dtype]
 
 
 def _u16(a) -> np.ndarray:
@@ -100,33 +130,40 @@ def bf16_bits_to_f32(h) -> np.ndarray:
     return (np.asarray(h, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
+def bits_to_f32(h, dtype: str = "bf16") -> np.ndarray:
+    """Stored bits -> float32 (exact for both types)."""
+    if _dt(dtype) == 1:
+        return np.asarray(h, dtype=np.uint16).view(np.float16).astype(np.float32)
+    return bf16_bits_to_f32(h)
+
+
 # ------------------------------------------------------------------ leaf and tree
-def block_step(acc: float, a, b) -> np.float32:
+def block_step(acc: float, a, b, dtype: str = "bf16") -> np.float32:
     a, b = _u16(a), _u16(b)
     assert a.shape == b.shape and a.ndim == 1 and a.size <= 8
-    return np.float32(lib().oracle_block_step(ctypes.c_float(acc), _p(a), 1, _p(b), 1, a.size))
+    return np.float32(lib().oracle_block_step_t(_dt(dtype), ctypes.c_float(acc), _p(a), 1, _p(b), 1, a.size))
 
 
-def leaf_f32(a, b) -> np.float32:
+def leaf_f32(a, b, dtype: str = "bf16") -> np.float32:
     a, b = _u16(a), _u16(b)
     assert a.shape == b.shape and a.ndim == 1 and a.size <= 64
-    return np.float32(lib().oracle_leaf_f32(_p(a), 1, _p(b), 1, a.size))
+    return np.float32(lib().oracle_leaf_f32_t(_dt(dtype), _p(a), 1, _p(b), 1, a.size))
 
 
-def dot_tree(a, b) -> int:
-    """Canonical tree of sum_k a[k]*b[k] -> BF16 bits."""
+def dot_tree(a, b, dtype: str = "bf16") -> int:
+    """Canonical tree of sum_k a[k]*b[k] -> stored bits."""
     a, b = _u16(a), _u16(b)
     assert a.shape == b.shape and a.ndim == 1
-    return int(lib().oracle_dot_tree(_p(a), 1, _p(b), 1, a.size))
+    return int(lib().oracle_dot_tree_t(_dt(dtype), _p(a), 1, _p(b), 1, a.size))
 
 
-def dot_subtree(a, b, leaf_lo: int, leaf_hi: int) -> int:
+def dot_subtree(a, b, leaf_lo: int, leaf_hi: int, dtype: str = "bf16") -> int:
     """Tree over leaves [leaf_lo, leaf_hi) of the full-length reduction a.b."""
     a, b = _u16(a), _u16(b)
-    return int(lib().oracle_dot_subtree(_p(a), 1, _p(b), 1, a.size, leaf_lo, leaf_hi))
+    return int(lib().oracle_dot_subtree_t(_dt(dtype), _p(a), 1, _p(b), 1, a.size, leaf_lo, leaf_hi))
 
 
-def gemm_tree(A, B, layout: str = "NT") -> np.ndarray:
+def gemm_tree(A, B, layout: str = "NT", dtype: str = "bf16") -> np.ndarray:
     """Tree GEMM over K.  NT: A [M,K], B [N,K] -> C [M,N] = A B^T.
     NN: A [M,K], B [K,N] -> A B.  TN: A [K,M], B [K,N] -> A^T B."""
     A, B = _u16(A), _u16(B)
@@ -143,7 +180,7 @@ def gemm_tree(A, B, layout: str = "NT") -> np.ndarray:
         raise ValueError(layout)
     assert K == K2
     C = np.zeros((M, N), np.uint16)
-    lib().oracle_gemm_tree(_p(A), sam, sak, _p(B), sbk, sbn, _p(C), N, M, N, K)
+    lib().oracle_gemm_tree_t(_dt(dtype), _p(A), sam, sak, _p(B), sbk, sbn, _p(C), N, M, N, K)
     return C
 
 
@@ -198,34 +235,34 @@ def dsilu(g: float) -> np.float32:
     return np.float32(lib().oracle_dsilu(ctypes.c_float(g)))
 
 
-def act_fwd(g, u) -> np.ndarray:
+def act_fwd(g, u, dtype: str = "bf16") -> np.ndarray:
     g, u = _u16(g), _u16(u)
     a = np.zeros_like(g)
-    lib().oracle_act_fwd(_p(g), _p(u), _p(a), g.size)
+    lib().oracle_act_fwd_t(_dt(dtype), _p(g), _p(u), _p(a), g.size)
     return a
 
 
-def act_bwd(da, g, u):
+def act_bwd(da, g, u, dtype: str = "bf16"):
     da, g, u = _u16(da), _u16(g), _u16(u)
     dg, du, a = np.zeros_like(g), np.zeros_like(g), np.zeros_like(g)
-    lib().oracle_act_bwd(_p(da), _p(g), _p(u), _p(dg), _p(du), _p(a), g.size)
+    lib().oracle_act_bwd_t(_dt(dtype), _p(da), _p(g), _p(u), _p(dg), _p(du), _p(a), g.size)
     return dg, du, a
 
 
 # ------------------------------------------------------------------ FFN
-def ffn_fwd(x, w_gate, w_up, w_down):
-    """Returns dict with g, u, a, y (BF16 bits)."""
+def ffn_fwd(x, w_gate, w_up, w_down, dtype: str = "bf16"):
+    """Returns dict with g, u, a, y (stored bits)."""
     x, wg, wu, wd = _u16(x), _u16(w_gate), _u16(w_up), _u16(w_down)
     M, H = x.shape
     I = wg.shape[0]
     assert wg.shape == (I, H) and wu.shape == (I, H) and wd.shape == (H, I)
     g = np.zeros((M, I), np.uint16); u = np.zeros_like(g); a = np.zeros_like(g)
     y = np.zeros((M, H), np.uint16)
-    lib().oracle_ffn_fwd(_p(x), _p(wg), _p(wu), _p(wd), _p(g), _p(u), _p(a), _p(y), M, H, I)
+    lib().oracle_ffn_fwd_t(_dt(dtype), _p(x), _p(wg), _p(wu), _p(wd), _p(g), _p(u), _p(a), _p(y), M, H, I)
     return {"g": g, "u": u, "a": a, "y": y}
 
 
-def ffn_bwd(dy, x, g, u, w_gate, w_up, w_down):
+def ffn_bwd(dy, x, g, u, w_gate, w_up, w_down, dtype: str = "bf16"):
     """Returns dict with dA, dG, dU, a, G, U, dX, dW_gate, dW_up, dW_down."""
     dy, x, g, u = _u16(dy), _u16(x), _u16(g), _u16(u)
     wg, wu, wd = _u16(w_gate), _u16(w_up), _u16(w_down)
@@ -236,8 +273,8 @@ def ffn_bwd(dy, x, g, u, w_gate, w_up, w_down):
     da, dg, du, a = z(M, I), z(M, I), z(M, I), z(M, I)
     gl, ul, dx = z(M, H), z(M, H), z(M, H)
     dwg, dwu, dwd = z(I, H), z(I, H), z(H, I)
-    lib().oracle_ffn_bwd(_p(dy), _p(x), _p(g), _p(u), _p(wg), _p(wu), _p(wd),
-                         _p(da), _p(dg), _p(du), _p(a), _p(gl), _p(ul), _p(dx),
-                         _p(dwg), _p(dwu), _p(dwd), M, H, I)
+    lib().oracle_ffn_bwd_t(_dt(dtype), _p(dy), _p(x), _p(g), _p(u), _p(wg), _p(wu), _p(wd),
+                           _p(da), _p(dg), _p(du), _p(a), _p(gl), _p(ul), _p(dx),
+                           _p(dwg), _p(dwu), _p(dwd), M, H, I)
     return {"dA": da, "dG": dg, "dU": du, "a": a, "G": gl, "U": ul, "dX": dx,
             "dW_gate": dwg, "dW_up": dwu, "dW_down": dwd}

@@ -26,6 +26,12 @@
  *    ascending blocks of 8, each block adding its 8 exact products to the FP32
  *    running value with one rounding (parity of this choice is unpinned by the
  *    pages; it is pinned by hand-worked cases in the tests);
+ *  - FP16 (PR #357 "[PERF][distributed]: optimize deterministic ROCm
+ *    collectives with HIP IPC", section "Determinism and correctness": FP32,
+ *    FP16 and BF16 follow one tree): the same leaf, tree and stages with FP16
+ *    storage; every rounding to the stored type is FP16 nearest even with IEEE
+ *    subnormals and overflow to infinity, and the leaf uses the same block
+ *    rule with FP16's exponents (a subnormal counts as exponent -14);
  *  - silu(g) = g * sigma(g), sigma(g) = 1 / (1 + e), e = exp(-g) correctly
  *    rounded to FP32, each FP32 operation rounded separately (no contraction);
  *    the activation is rounded to BF16 once: a = bf16(fl32(silu(g) * u)).
@@ -38,6 +44,7 @@
 #include <math.h>
 
 typedef uint16_t bf16_t;
+typedef uint16_t f16_t;
 
 /* ---------------------------------------------------------------- BF16 <-> FP32 */
 
@@ -66,6 +73,63 @@ static bf16_t node_add(bf16_t l, bf16_t r)
 {
     float s = bf16_to_f32(l) + bf16_to_f32(r);
     return f32_to_bf16(s);
+}
+
+/* ---------------------------------------------------------------- FP16 <-> FP32 */
+
+/* IEEE binary16 -> FP32 (exact): sign, 5-bit exponent (bias 15), 10-bit
+ * fraction; exponent 0 holds subnormals (fraction * 2^-24). */
+static float f16_to_f32(f16_t h)
+{
+    int sign = (h >> 15) & 1, e = (h >> 10) & 0x1F, f = h & 0x3FF;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -24);
+    else if (e == 31)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexp((double)(f | 0x400), e - 25);
+    return (float)(sign ? -v : v);
+}
+
+/* FP32 -> IEEE binary16, round to nearest even.  The magnitude is split into
+ * the FP16 step q at its binade (2^(e-10) for normals, 2^-24 below 2^-14), the
+ * quotient |x| / q (exact in double) is rounded to an integer with ties to
+ * even, and the integer is re-encoded; 65520 and above overflow to infinity. */
+static f16_t f32_to_f16(float x)
+{
+    uint32_t u;
+    memcpy(&u, &x, 4);
+    f16_t sign = (f16_t)((u >> 16) & 0x8000u);
+    if (isnan(x)) return (f16_t)(sign | 0x7E00u);
+    double a = fabs((double)x);
+    if (a >= 65520.0) return (f16_t)(sign | 0x7C00u);
+    int e = a > 0 ? ilogb(a) : -25;          /* binade of |x| */
+    if (e < -14) e = -14;                     /* subnormal range shares the 2^-24 step */
+    double q = ldexp(1.0, e - 10);
+    double m = a / q;                         /* exact: a power-of-two divisor */
+    double r = floor(m), frac = m - r;
+    if (frac > 0.5 || (frac == 0.5 && fmod(r, 2.0) != 0.0)) r += 1.0;
+    /* r in [0, 2048]; 2048 carries into the next binade */
+    if (r >= 2048.0) { r = 1024.0; e += 1; }
+    if (e == -14 && r < 1024.0) return (f16_t)(sign | (f16_t)r);        /* subnormal (or zero) */
+    return (f16_t)(sign | (f16_t)((e + 15) << 10) | (f16_t)((int)r - 1024));
+}
+
+/* ---------------------------------------------------------------- stored types */
+
+/* The stored 16-bit element types (codes as for the typed combine). */
+enum { DT_BF16 = 0, DT_FP16 = 1 };
+
+static float elem_to_f32(int dt, uint16_t h) { return dt == DT_FP16 ? f16_to_f32(h) : bf16_to_f32(h); }
+static uint16_t f32_to_elem(int dt, float f) { return dt == DT_FP16 ? f32_to_f16(f) : f32_to_bf16(f); }
+
+/* One node of the tree in either type: two children added in FP32, the sum
+ * rounded to the stored type. */
+static uint16_t node_add_t(int dt, uint16_t l, uint16_t r)
+{
+    float s = elem_to_f32(dt, l) + elem_to_f32(dt, r);
+    return f32_to_elem(dt, s);
 }
 
 /* ------------------------------------------------------------ exact integer tools */
@@ -132,15 +196,20 @@ static float round_to_f32(i128 v, int e)
 
 /* ------------------------------------------------------------ the FP32 leaf */
 
-/* Split a finite BF16 into signed integer significand and exponent so that
- * value = sig * 2^(ex - 7); zero returns 0.  Denormals use ex = -126. */
-static int bf16_split(bf16_t h, int32_t *sig, int *ex)
+/* Split a finite stored value into a signed integer significand and an
+ * exponent so that value = sig * 2^(ex - F), F the type's fraction width (BF16
+ * 7, FP16 10); zero returns 0.  Subnormals take the smallest normal exponent
+ * (BF16 -126, FP16 -14). */
+static int elem_split(int dt, uint16_t h, int32_t *sig, int *ex)
 {
-    int be = (h >> 7) & 0xFF;
-    int32_t m = h & 0x7F;
+    const int fb = dt == DT_FP16 ? 10 : 7;          /* fraction bits */
+    const int eb = dt == DT_FP16 ? 5 : 8;           /* exponent bits */
+    const int bias = (1 << (eb - 1)) - 1;
+    int be = (h >> fb) & ((1 << eb) - 1);
+    int32_t m = h & ((1 << fb) - 1);
     if (be == 0 && m == 0) return 0;
-    if (be == 0) *ex = -126;
-    else { *ex = be - 127; m |= 0x80; }
+    if (be == 0) *ex = 1 - bias;
+    else { *ex = be - bias; m |= 1 << fb; }
     *sig = (h & 0x8000) ? -m : m;
     return 1;
 }
@@ -170,20 +239,22 @@ static int f32_split(float f, int64_t *sig, int *ex)
  *   4. the exact sum T of the cut terms is cut toward minus infinity to 8 bits
  *      below its own FP32 ulp (never finer than 2^-157);
  *   5. that value is rounded to FP32, nearest even.
+ * The rule is the same for BF16 and FP16 operands; only the split differs.
  */
-float oracle_block_step(float acc, const bf16_t *a, ptrdiff_t sa,
-                        const bf16_t *b, ptrdiff_t sb, int n)
+static float block_step_t(int dt, float acc, const uint16_t *a, ptrdiff_t sa,
+                          const uint16_t *b, ptrdiff_t sb, int n)
 {
+    const int fb = dt == DT_FP16 ? 10 : 7;
     int32_t psig[8];
     int pexp[8], nz[8];
     int emax = -100000, any = 0;
     for (int k = 0; k < n; ++k) {
         int32_t sa_, sb_;
         int ea, eb;
-        nz[k] = bf16_split(a[k * sa], &sa_, &ea) & bf16_split(b[k * sb], &sb_, &eb);
+        nz[k] = elem_split(dt, a[k * sa], &sa_, &ea) & elem_split(dt, b[k * sb], &sb_, &eb);
         if (!nz[k]) continue;
-        psig[k] = sa_ * sb_;                    /* |psig| < 2^16 */
-        pexp[k] = ea + eb;                      /* product = psig * 2^(pexp-14) */
+        psig[k] = sa_ * sb_;                    /* |psig| < 2^(2fb+2) */
+        pexp[k] = ea + eb;                      /* product = psig * 2^(pexp-2fb) */
         if (pexp[k] > emax) emax = pexp[k];
         any = 1;
     }
@@ -193,7 +264,7 @@ float oracle_block_step(float acc, const bf16_t *a, ptrdiff_t sa,
     int64_t sp = 0;                             /* products, in grid units */
     for (int k = 0; k < n; ++k) {
         if (!nz[k]) continue;
-        int sh = (pexp[k] - 14) - grid;         /* = 10 - (emax - pexp) */
+        int sh = (pexp[k] - 2 * fb) - grid;     /* = 24 - 2fb - (emax - pexp) */
         if (sh >= 0) sp += (int64_t)psig[k] << sh;
         else sp += trunc_shift(psig[k], -sh);
     }
@@ -228,70 +299,105 @@ float oracle_block_step(float acc, const bf16_t *a, ptrdiff_t sa,
     return round_to_f32(t, e);
 }
 
+float oracle_block_step_t(int dt, float acc, const uint16_t *a, ptrdiff_t sa,
+                          const uint16_t *b, ptrdiff_t sb, int n)
+{
+    return block_step_t(dt, acc, a, sa, b, sb, n);
+}
+
+float oracle_block_step(float acc, const bf16_t *a, ptrdiff_t sa,
+                        const bf16_t *b, ptrdiff_t sb, int n)
+{
+    return block_step_t(DT_BF16, acc, a, sa, b, sb, n);
+}
+
 /* The FP32 leaf over n <= 64 consecutive K elements: ascending blocks of 8
  * starting from an accumulator of +0. */
-static float leaf_f32(const bf16_t *a, ptrdiff_t sa, const bf16_t *b, ptrdiff_t sb, int64_t n)
+static float leaf_f32(int dt, const uint16_t *a, ptrdiff_t sa, const uint16_t *b, ptrdiff_t sb, int64_t n)
 {
     float acc = 0.0f;
     for (int64_t k = 0; k < n; k += 8) {
         int w = (int)(n - k < 8 ? n - k : 8);
-        acc = oracle_block_step(acc, a + k * sa, sa, b + k * sb, sb, w);
+        acc = block_step_t(dt, acc, a + k * sa, sa, b + k * sb, sb, w);
     }
     return acc;
 }
 
+float oracle_leaf_f32_t(int dt, const uint16_t *a, ptrdiff_t sa, const uint16_t *b, ptrdiff_t sb, int64_t n)
+{
+    return leaf_f32(dt, a, sa, b, sb, n);
+}
+
 float oracle_leaf_f32(const bf16_t *a, ptrdiff_t sa, const bf16_t *b, ptrdiff_t sb, int64_t n)
 {
-    return leaf_f32(a, sa, b, sb, n);
+    return leaf_f32(DT_BF16, a, sa, b, sb, n);
 }
 
 /* ------------------------------------------------------------ the tree */
 
 enum { LEAF = 64 };
 
-/* T(lo, hi) over leaves [lo, hi): a single leaf is the BF16-rounded FP32 leaf;
- * otherwise split at mid = lo + floor((hi - lo) / 2) and add the two BF16
- * children in FP32, rounding to BF16. */
-static bf16_t tree(const bf16_t *a, ptrdiff_t sa, const bf16_t *b, ptrdiff_t sb,
-                   int64_t K, int64_t lo, int64_t hi)
+/* T(lo, hi) over leaves [lo, hi): a single leaf is the FP32 leaf rounded to
+ * the stored type; otherwise split at mid = lo + floor((hi - lo) / 2) and add
+ * the two children in FP32, rounding to the stored type. */
+static uint16_t tree(int dt, const uint16_t *a, ptrdiff_t sa, const uint16_t *b, ptrdiff_t sb,
+                     int64_t K, int64_t lo, int64_t hi)
 {
     if (hi - lo == 1) {
         int64_t k0 = lo * LEAF;
         int64_t n = K - k0 < LEAF ? K - k0 : LEAF;
-        return f32_to_bf16(leaf_f32(a + k0 * sa, sa, b + k0 * sb, sb, n));
+        return f32_to_elem(dt, leaf_f32(dt, a + k0 * sa, sa, b + k0 * sb, sb, n));
     }
     int64_t mid = lo + (hi - lo) / 2;
-    bf16_t l = tree(a, sa, b, sb, K, lo, mid);
-    bf16_t r = tree(a, sa, b, sb, K, mid, hi);
-    return node_add(l, r);
+    uint16_t l = tree(dt, a, sa, b, sb, K, lo, mid);
+    uint16_t r = tree(dt, a, sa, b, sb, K, mid, hi);
+    return node_add_t(dt, l, r);
 }
 
 /* One output element: the canonical tree over K of a[k*sa] * b[k*sb].
  * K = 0 gives +0. */
-bf16_t oracle_dot_tree(const bf16_t *a, ptrdiff_t sa, const bf16_t *b, ptrdiff_t sb, int64_t K)
+uint16_t oracle_dot_tree_t(int dt, const uint16_t *a, ptrdiff_t sa, const uint16_t *b, ptrdiff_t sb, int64_t K)
 {
     if (K <= 0) return 0;
     int64_t L = (K + LEAF - 1) / LEAF;
-    return tree(a, sa, b, sb, K, 0, L);
+    return tree(dt, a, sa, b, sb, K, 0, L);
+}
+
+bf16_t oracle_dot_tree(const bf16_t *a, ptrdiff_t sa, const bf16_t *b, ptrdiff_t sb, int64_t K)
+{
+    return oracle_dot_tree_t(DT_BF16, a, sa, b, sb, K);
 }
 
 /* The tree over the leaves [leaf_lo, leaf_hi) of a length-K reduction: the
  * partial a contiguous K shard contributes (a subtree when the shard is one). */
+uint16_t oracle_dot_subtree_t(int dt, const uint16_t *a, ptrdiff_t sa, const uint16_t *b, ptrdiff_t sb,
+                              int64_t K, int64_t leaf_lo, int64_t leaf_hi)
+{
+    return tree(dt, a, sa, b, sb, K, leaf_lo, leaf_hi);
+}
+
 bf16_t oracle_dot_subtree(const bf16_t *a, ptrdiff_t sa, const bf16_t *b, ptrdiff_t sb,
                           int64_t K, int64_t leaf_lo, int64_t leaf_hi)
 {
-    return tree(a, sa, b, sb, K, leaf_lo, leaf_hi);
+    return tree(DT_BF16, a, sa, b, sb, K, leaf_lo, leaf_hi);
 }
 
 /* C[m*ldc + n] = T_K( sum_k A[m*sam + k*sak] * B[k*sbk + n*sbn] ). */
-void oracle_gemm_tree(const bf16_t *A, int64_t sam, int64_t sak,
-                      const bf16_t *B, int64_t sbk, int64_t sbn,
-                      bf16_t *C, int64_t ldc, int64_t M, int64_t N, int64_t K)
+void oracle_gemm_tree_t(int dt, const uint16_t *A, int64_t sam, int64_t sak,
+                        const uint16_t *B, int64_t sbk, int64_t sbn,
+                        uint16_t *C, int64_t ldc, int64_t M, int64_t N, int64_t K)
 {
 #pragma omp parallel for collapse(2) schedule(dynamic, 64)
     for (int64_t m = 0; m < M; ++m)
         for (int64_t n = 0; n < N; ++n)
-            C[m * ldc + n] = oracle_dot_tree(A + m * sam, sak, B + n * sbn, sbk, K);
+            C[m * ldc + n] = oracle_dot_tree_t(dt, A + m * sam, sak, B + n * sbn, sbk, K);
+}
+
+void oracle_gemm_tree(const bf16_t *A, int64_t sam, int64_t sak,
+                      const bf16_t *B, int64_t sbk, int64_t sbn,
+                      bf16_t *C, int64_t ldc, int64_t M, int64_t N, int64_t K)
+{
+    oracle_gemm_tree_t(DT_BF16, A, sam, sak, B, sbk, sbn, C, ldc, M, N, K);
 }
 
 /* The fixed balanced combine over S in {1,2,4,8} parts, in rank order:
@@ -314,51 +420,11 @@ int oracle_tree_combine(const bf16_t *const *parts, int S, bf16_t *out, int64_t 
 
 /* ------------------------------------------------------------ FP16 and FP32 combine */
 
+
 /* The same fixed rank tree in FP16 and FP32 (PR #357, "Determinism and
  * correctness": FP32, FP16 and BF16 follow one rank tree).  An FP16 node adds
  * its two children in FP32 and rounds the sum to FP16 (nearest even), as the
  * BF16 node does; an FP32 node is one FP32 addition. */
-
-typedef uint16_t f16_t;
-
-/* IEEE binary16 -> FP32 (exact): sign, 5-bit exponent (bias 15), 10-bit
- * fraction; exponent 0 holds subnormals (fraction * 2^-24). */
-static float f16_to_f32(f16_t h)
-{
-    int sign = (h >> 15) & 1, e = (h >> 10) & 0x1F, f = h & 0x3FF;
-    double v;
-    if (e == 0)
-        v = ldexp((double)f, -24);
-    else if (e == 31)
-        v = f ? NAN : INFINITY;
-    else
-        v = ldexp((double)(f | 0x400), e - 25);
-    return (float)(sign ? -v : v);
-}
-
-/* FP32 -> IEEE binary16, round to nearest even.  The magnitude is split into
- * the FP16 step q at its binade (2^(e-10) for normals, 2^-24 below 2^-14), the
- * quotient |x| / q (exact in double) is rounded to an integer with ties to
- * even, and the integer is re-encoded; 65520 and above overflow to infinity. */
-static f16_t f32_to_f16(float x)
-{
-    uint32_t u;
-    memcpy(&u, &x, 4);
-    f16_t sign = (f16_t)((u >> 16) & 0x8000u);
-    if (isnan(x)) return (f16_t)(sign | 0x7E00u);
-    double a = fabs((double)x);
-    if (a >= 65520.0) return (f16_t)(sign | 0x7C00u);
-    int e = a > 0 ? ilogb(a) : -25;          /* binade of |x| */
-    if (e < -14) e = -14;                     /* subnormal range shares the 2^-24 step */
-    double q = ldexp(1.0, e - 10);
-    double m = a / q;                         /* exact: a power-of-two divisor */
-    double r = floor(m), frac = m - r;
-    if (frac > 0.5 || (frac == 0.5 && fmod(r, 2.0) != 0.0)) r += 1.0;
-    /* r in [0, 2048]; 2048 carries into the next binade */
-    if (r >= 2048.0) { r = 1024.0; e += 1; }
-    if (e == -14 && r < 1024.0) return (f16_t)(sign | (f16_t)r);        /* subnormal (or zero) */
-    return (f16_t)(sign | (f16_t)((e + 15) << 10) | (f16_t)((int)r - 1024));
-}
 
 static f16_t node_add_f16(f16_t l, f16_t r)
 {
@@ -432,52 +498,92 @@ float oracle_dsilu(float g)
     return sg * onep;
 }
 
-/* a = bf16(silu(g) * u), one BF16 rounding. */
-void oracle_act_fwd(const bf16_t *g, const bf16_t *u, bf16_t *a, int64_t n)
+/* a = rnd(silu(g) * u), one rounding to the stored type. */
+void oracle_act_fwd_t(int dt, const uint16_t *g, const uint16_t *u, uint16_t *a, int64_t n)
 {
 #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < n; ++i) {
-        float s = oracle_silu(bf16_to_f32(g[i]));
-        a[i] = f32_to_bf16(s * bf16_to_f32(u[i]));
+        float s = oracle_silu(elem_to_f32(dt, g[i]));
+        a[i] = f32_to_elem(dt, s * elem_to_f32(dt, u[i]));
     }
 }
 
-/* dU = bf16(dA * silu(g)), dG = bf16((dA * u) * silu'(g)); a is recomputed. */
-void oracle_act_bwd(const bf16_t *da, const bf16_t *g, const bf16_t *u,
-                    bf16_t *dg, bf16_t *du, bf16_t *a, int64_t n)
+void oracle_act_fwd(const bf16_t *g, const bf16_t *u, bf16_t *a, int64_t n)
+{
+    oracle_act_fwd_t(DT_BF16, g, u, a, n);
+}
+
+/* dU = rnd(dA * silu(g)), dG = rnd((dA * u) * silu'(g)); a is recomputed. */
+void oracle_act_bwd_t(int dt, const uint16_t *da, const uint16_t *g, const uint16_t *u,
+                      uint16_t *dg, uint16_t *du, uint16_t *a, int64_t n)
 {
 #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < n; ++i) {
-        float gv = bf16_to_f32(g[i]), uv = bf16_to_f32(u[i]), dav = bf16_to_f32(da[i]);
+        float gv = elem_to_f32(dt, g[i]), uv = elem_to_f32(dt, u[i]), dav = elem_to_f32(dt, da[i]);
         float s = oracle_silu(gv);
         float ds = oracle_dsilu(gv);
-        du[i] = f32_to_bf16(dav * s);
+        du[i] = f32_to_elem(dt, dav * s);
         float dau = dav * uv;
-        dg[i] = f32_to_bf16(dau * ds);
-        if (a) a[i] = f32_to_bf16(s * uv);
+        dg[i] = f32_to_elem(dt, dau * ds);
+        if (a) a[i] = f32_to_elem(dt, s * uv);
     }
+}
+
+void oracle_act_bwd(const bf16_t *da, const bf16_t *g, const bf16_t *u,
+                    bf16_t *dg, bf16_t *du, bf16_t *a, int64_t n)
+{
+    oracle_act_bwd_t(DT_BF16, da, g, u, dg, du, a, n);
 }
 
 /* ------------------------------------------------------------ the FFN */
 
-/* Forward: g = T_H(x W_gate^T), u = T_H(x W_up^T), a = bf16(silu(g) u),
+/* Forward: g = T_H(x W_gate^T), u = T_H(x W_up^T), a = rnd(silu(g) u),
  * y = T_I(a W_down^T).  Row-major, contiguous: x [M,H], W_gate/W_up [I,H],
  * W_down [H,I]; g, u, a [M,I]; y [M,H]. */
+void oracle_ffn_fwd_t(int dt, const uint16_t *x, const uint16_t *wg, const uint16_t *wu, const uint16_t *wd,
+                      uint16_t *g, uint16_t *u, uint16_t *a, uint16_t *y,
+                      int64_t M, int64_t H, int64_t I)
+{
+    oracle_gemm_tree_t(dt, x, H, 1, wg, 1, H, g, I, M, I, H);
+    oracle_gemm_tree_t(dt, x, H, 1, wu, 1, H, u, I, M, I, H);
+    oracle_act_fwd_t(dt, g, u, a, M * I);
+    oracle_gemm_tree_t(dt, a, I, 1, wd, 1, I, y, H, M, H, I);
+}
+
 void oracle_ffn_fwd(const bf16_t *x, const bf16_t *wg, const bf16_t *wu, const bf16_t *wd,
                     bf16_t *g, bf16_t *u, bf16_t *a, bf16_t *y,
                     int64_t M, int64_t H, int64_t I)
 {
-    oracle_gemm_tree(x, H, 1, wg, 1, H, g, I, M, I, H);
-    oracle_gemm_tree(x, H, 1, wu, 1, H, u, I, M, I, H);
-    oracle_act_fwd(g, u, a, M * I);
-    oracle_gemm_tree(a, I, 1, wd, 1, I, y, H, M, H, I);
+    oracle_ffn_fwd_t(DT_BF16, x, wg, wu, wd, g, u, a, y, M, H, I);
 }
 
 /* Backward from dY [M,H] and the saved g, u:
  *   dA = T_H(dY W_down)                 (K = H, over the rows of W_down)
- *   dU = bf16(dA silu(g)), dG = bf16(dA u silu'(g)), a recomputed
- *   G  = T_I(dG W_gate), U = T_I(dU W_up),  dX = bf16(G + U)  (gate first)
+ *   dU = rnd(dA silu(g)), dG = rnd(dA u silu'(g)), a recomputed
+ *   G  = T_I(dG W_gate), U = T_I(dU W_up),  dX = rnd(G + U)  (gate first)
  *   dW_gate = T_M(dG^T x), dW_up = T_M(dU^T x), dW_down = T_M(dY^T a). */
+void oracle_ffn_bwd_t(int dt, const uint16_t *dy, const uint16_t *x, const uint16_t *g, const uint16_t *u,
+                      const uint16_t *wg, const uint16_t *wu, const uint16_t *wd,
+                      uint16_t *da, uint16_t *dg, uint16_t *du, uint16_t *a,
+                      uint16_t *gl, uint16_t *ul, uint16_t *dx,
+                      uint16_t *dwg, uint16_t *dwu, uint16_t *dwd,
+                      int64_t M, int64_t H, int64_t I)
+{
+    oracle_gemm_tree_t(dt, dy, H, 1, wd, I, 1, da, I, M, I, H);
+    oracle_act_bwd_t(dt, da, g, u, dg, du, a, M * I);
+    oracle_gemm_tree_t(dt, dg, I, 1, wg, H, 1, gl, H, M, H, I);
+    oracle_gemm_tree_t(dt, du, I, 1, wu, H, 1, ul, H, M, H, I);
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < M * H; ++i) {
+        uint16_t acc = gl[i];                /* gate contribution first */
+        acc = node_add_t(dt, acc, ul[i]);    /* then the up contribution */
+        dx[i] = acc;
+    }
+    oracle_gemm_tree_t(dt, dg, 1, I, x, H, 1, dwg, H, I, H, M);
+    oracle_gemm_tree_t(dt, du, 1, I, x, H, 1, dwu, H, I, H, M);
+    oracle_gemm_tree_t(dt, dy, 1, H, a, I, 1, dwd, I, H, I, M);
+}
+
 void oracle_ffn_bwd(const bf16_t *dy, const bf16_t *x, const bf16_t *g, const bf16_t *u,
                     const bf16_t *wg, const bf16_t *wu, const bf16_t *wd,
                     bf16_t *da, bf16_t *dg, bf16_t *du, bf16_t *a,
@@ -485,19 +591,7 @@ void oracle_ffn_bwd(const bf16_t *dy, const bf16_t *x, const bf16_t *g, const bf
                     bf16_t *dwg, bf16_t *dwu, bf16_t *dwd,
                     int64_t M, int64_t H, int64_t I)
 {
-    oracle_gemm_tree(dy, H, 1, wd, I, 1, da, I, M, I, H);
-    oracle_act_bwd(da, g, u, dg, du, a, M * I);
-    oracle_gemm_tree(dg, I, 1, wg, H, 1, gl, H, M, H, I);
-    oracle_gemm_tree(du, I, 1, wu, H, 1, ul, H, M, H, I);
-#pragma omp parallel for schedule(static)
-    for (int64_t i = 0; i < M * H; ++i) {
-        bf16_t acc = gl[i];              /* gate contribution first */
-        acc = node_add(acc, ul[i]);      /* then the up contribution */
-        dx[i] = acc;
-    }
-    oracle_gemm_tree(dg, 1, I, x, H, 1, dwg, H, I, H, M);
-    oracle_gemm_tree(du, 1, I, x, H, 1, dwu, H, I, H, M);
-    oracle_gemm_tree(dy, 1, H, a, I, 1, dwd, I, H, I, M);
+    oracle_ffn_bwd_t(DT_BF16, dy, x, g, u, wg, wu, wd, da, dg, du, a, gl, ul, dx, dwg, dwu, dwd, M, H, I);
 }
 
 int oracle_leaf_size(void) { return LEAF; }

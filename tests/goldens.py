@@ -47,6 +47,31 @@ def bf16_bits_exact(v: Fraction) -> int:
     return s | ((e + 127) << 7) | int(m)
 
 
+def f16_bits_exact(v: Fraction) -> int:
+    """Exact FP16 encoding of a value that must be representable: normal
+    (1.m * 2^e, -14 <= e <= 15, 10 fraction bits) or subnormal (m * 2^-24)."""
+    if v == 0:
+        return 0
+    s = 0x8000 if v < 0 else 0
+    v = abs(v)
+    if v < Fraction(2) ** -14:
+        sub = v / Fraction(2) ** -24
+        assert sub.denominator == 1 and 0 < sub < 1024, f"not representable in FP16: {v}"
+        return s | int(sub)
+    e = 0
+    while v >= 2:
+        v /= 2; e += 1
+    while v < 1:
+        v *= 2; e -= 1
+    m = (v - 1) * 1024
+    assert m.denominator == 1, f"not representable in FP16: {v}"
+    assert e + 15 < 31, f"past the FP16 range: {v}"
+    return s | ((e + 15) << 10) | int(m)
+
+
+_ENC = {"bf16": (bf16_bits_exact, 0x3F80), "fp16": (f16_bits_exact, 0x3C00)}
+
+
 def load_table(name: str):
     rows = []
     with open(os.path.join(GOLDEN, name)) as f:
@@ -58,48 +83,44 @@ def load_table(name: str):
     return rows
 
 
-def tree_cases():
+def _vector(n: int, spec: str, fmt: str = "bf16") -> np.ndarray:
+    enc, one = _ENC[fmt]
+    v = np.zeros(n, np.uint16)
+    if spec == "ones":
+        v[:] = one
+    else:
+        for it in spec.split():
+            i, val = it.split(":"); v[int(i)] = enc(parse_value(val))
+    return v
+
+
+def tree_cases(fmt: str = "bf16"):
+    name_ = {"bf16": "tree_cases.txt", "fp16": "tree_f16_cases.txt"}[fmt]
     out = []
-    for name, K, xs, ws, exp, why in load_table("tree_cases.txt"):
+    for name, K, xs, ws, exp, why in load_table(name_):
         K = int(K)
-        x = np.zeros(K, np.uint16)
-        if xs == "ones":
-            x[:] = 0x3F80
-        else:
-            for it in xs.split():
-                i, v = it.split(":"); x[int(i)] = bf16_bits_exact(parse_value(v))
-        w = np.zeros(K, np.uint16)
-        for it in ws.split():
-            i, v = it.split(":"); w[int(i)] = bf16_bits_exact(parse_value(v))
-        out.append((name, x, w, int(exp, 16), why))
+        out.append((name, _vector(K, xs, fmt), _vector(K, ws, fmt), int(exp, 16), why))
     return out
 
 
-def block_cases():
+def block_cases(fmt: str = "bf16"):
+    enc = _ENC[fmt][0]
+    name_ = {"bf16": "block_rule_cases.txt", "fp16": "block_rule_f16_cases.txt"}[fmt]
     out = []
-    for name, acc, av, bv, exp, why in load_table("block_rule_cases.txt"):
-        a = np.array([bf16_bits_exact(parse_value(t)) for t in av.split()], np.uint16)
-        b = np.array([bf16_bits_exact(parse_value(t)) for t in bv.split()], np.uint16)
+    for name, acc, av, bv, exp, why in load_table(name_):
+        a = np.array([enc(parse_value(t)) for t in av.split()], np.uint16)
+        b = np.array([enc(parse_value(t)) for t in bv.split()], np.uint16)
         accf = np.array([int(acc, 16)], np.uint32).view(np.float32)[0]
         out.append((name, accf, a, b, int(exp, 16), why))
     return out
 
 
-def _vector(n: int, spec: str) -> np.ndarray:
-    v = np.zeros(n, np.uint16)
-    if spec == "ones":
-        v[:] = 0x3F80
-    else:
-        for it in spec.split():
-            i, val = it.split(":"); v[int(i)] = bf16_bits_exact(parse_value(val))
-    return v
-
-
-def leaf_cases():
+def leaf_cases(fmt: str = "bf16"):
+    name_ = {"bf16": "leaf_cases.txt", "fp16": "leaf_f16_cases.txt"}[fmt]
     out = []
-    for name, n, av, bv, exp, why in load_table("leaf_cases.txt"):
+    for name, n, av, bv, exp, why in load_table(name_):
         n = int(n)
-        out.append((name, _vector(n, av), _vector(n, bv), int(exp, 16), why))
+        out.append((name, _vector(n, av, fmt), _vector(n, bv, fmt), int(exp, 16), why))
     return out
 
 

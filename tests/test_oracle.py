@@ -455,3 +455,184 @@ def test_inputs_are_seeded_and_shaped():
         assert torch.equal(a[k].view(torch.int16), b[k].view(torch.int16))
     assert a["x"].shape == (4, 256) and a["w_gate"].shape == (768, 256) and a["w_down"].shape == (256, 768)
     assert a["w_gate"].dtype == torch.bfloat16
+
+
+# ------------------------------------------------------------ FP16 storage
+# The same tree with FP16 storage ("[PERF][distributed]: optimize deterministic
+# ROCm collectives with HIP IPC", section "Determinism and correctness").
+H2F = lambda h: np.asarray(h, np.uint16).view(np.float16).astype(np.float32)
+F2H = lambda x: np.asarray(x, np.float32).astype(np.float16).view(np.uint16)
+
+
+@pytest.mark.parametrize("case", block_cases("fp16"), ids=lambda c: c[0])
+def test_f16_block_rule_hand_worked(case):
+    name, acc, a, b, expected, why = case
+    assert f32_bits(oracle.block_step(float(acc), a, b, "fp16")) == expected, why
+
+
+@pytest.mark.parametrize("case", leaf_cases("fp16"), ids=lambda c: c[0])
+def test_f16_leaf_block_width_and_order_hand_worked(case):
+    name, a, b, expected, why = case
+    assert f32_bits(oracle.leaf_f32(a, b, "fp16")) == expected, why
+
+
+@pytest.mark.parametrize("case", tree_cases("fp16"), ids=lambda c: c[0])
+def test_f16_tree_hand_worked(case):
+    name, x, w, expected, why = case
+    assert oracle.dot_tree(x, w, "fp16") == expected, why
+
+
+def test_f16_single_block_on_grid_is_correct_rounding():
+    # products of FP16 integers times a common power of two lie on the grid:
+    # one block is then one correct rounding of the exact sum (Fractions)
+    rng = np.random.default_rng(12)
+    for _ in range(300):
+        n = int(rng.integers(1, 9))
+        a = F2H(rng.integers(-2000, 2001, n) * 2.0 ** int(rng.integers(-12, 4)))
+        b = F2H(rng.integers(-2000, 2001, n).astype(np.float32))
+        exact = sum(Fraction(float(x)) * Fraction(float(y)) for x, y in zip(H2F(a), H2F(b)))
+        got = float(oracle.block_step(0.0, a, b, "fp16"))
+        assert got == _rn_f32(exact)
+
+
+def test_f16_leaf_is_block_chain_and_differs_from_bf16_reading():
+    rng = np.random.default_rng(13)
+    a = F2H(rng.standard_normal(64) * 0.02); b = F2H(rng.standard_normal(64))
+    acc = np.float32(0.0)
+    for j in range(8):
+        acc = oracle.block_step(float(acc), a[8 * j:8 * j + 8], b[8 * j:8 * j + 8], "fp16")
+    assert f32_bits(acc) == f32_bits(oracle.leaf_f32(a, b, "fp16"))
+    # the FP16 bits are not read as BF16 anywhere: the leaf is close to the FP64 dot
+    ref = float(np.dot(H2F(a).astype(np.float64), H2F(b).astype(np.float64)))
+    assert abs(float(acc) - ref) <= 1e-6 * max(1.0, abs(ref))
+
+
+def test_f16_integer_inputs_are_exact_everywhere():
+    # |partial sums| <= 192 < 2048: no rounding at any leaf, node or block in FP16
+    rng = np.random.default_rng(17)
+    for K in (1, 7, 63, 64, 65, 130, 192):
+        for _ in range(20):
+            x = rng.integers(-1, 2, K); w = rng.integers(-1, 2, K)
+            got = oracle.dot_tree(F2H(x), F2H(w), "fp16")
+            assert H2F(np.uint16(got)) == float(np.dot(x, w))
+    # integers up to 2047 are exact in FP16 (spacing 1 below 2048)
+    x = np.zeros(4096); w = np.zeros(4096)
+    idx = rng.choice(4096, 300, replace=False)
+    x[idx] = rng.integers(1, 4, 300); w[idx] = rng.integers(1, 3, 300)
+    assert np.dot(x, w) < 2048
+    assert H2F(np.uint16(oracle.dot_tree(F2H(x), F2H(w), "fp16"))) == float(np.dot(x, w))
+
+
+def test_f16_integer_gemm_layouts_exact():
+    rng = np.random.default_rng(18)
+    M, N, K = 5, 7, 150
+    A = rng.integers(-3, 4, (M, K)); B = rng.integers(-3, 4, (N, K))
+    a16 = F2H(A); b16 = F2H(B)
+    want = (A @ B.T).astype(np.float32)
+    np.testing.assert_array_equal(H2F(oracle.gemm_tree(a16, b16, "NT", "fp16")), want)
+    np.testing.assert_array_equal(H2F(oracle.gemm_tree(a16, np.ascontiguousarray(b16.T), "NN", "fp16")), want)
+    np.testing.assert_array_equal(H2F(oracle.gemm_tree(np.ascontiguousarray(a16.T), np.ascontiguousarray(b16.T),
+                                                       "TN", "fp16")), want)
+
+
+def test_f16_power_of_two_scaling():
+    rng = np.random.default_rng(19)
+    for K in (40, 64, 200, 1000):
+        x = F2H(rng.standard_normal(K)); w = F2H(rng.standard_normal(K) * 0.02)
+        base = H2F(np.uint16(oracle.dot_tree(x, w, "fp16")))
+        xs = F2H(H2F(x) * np.float32(8.0)); ws = F2H(H2F(w) * np.float32(2.0 ** -3))
+        assert not (H2F(ws) == 0).any() or (H2F(w) == 0).all()
+        scaled = H2F(np.uint16(oracle.dot_tree(xs, ws, "fp16")))
+        assert scaled == base
+
+
+def _rn_f16(fr: Fraction) -> int:
+    """Correct RNE of an exact rational to FP16 bits (subnormals, overflow to inf)."""
+    s = 0x8000 if fr < 0 else 0
+    v = abs(fr)
+    if v == 0:
+        return s
+    e = max(math.floor(math.log2(v)), -14)
+    while e > -14 and Fraction(2) ** e > v:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= v:
+        e += 1
+    ulp = Fraction(2) ** (e - 10)
+    q = v / ulp
+    n = q.numerator // q.denominator
+    r = q - n
+    if r > Fraction(1, 2) or (r == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    val = n * ulp
+    if val >= 65520 or val >= Fraction(65504) + Fraction(16):
+        return s | 0x7C00
+    return s | int(np.array([float(val)], np.float16).view(np.uint16)[0])
+
+
+def _rn_f16_prod(x: float, y: float) -> int:
+    """FP16 rounding of the exact product x*y; a zero product keeps IEEE's sign."""
+    if x == 0 or y == 0:
+        return 0x8000 if math.copysign(1.0, x) * math.copysign(1.0, y) < 0 else 0
+    return _rn_f16(Fraction(x) * Fraction(y))
+
+
+def test_f16_activation_matches_exact_derivation():
+    # a = rnd16(silu(g) u), dU = rnd16(dA silu(g)), dG = rnd16((dA u) silu'(g)),
+    # with the FP32 chain re-derived by exact arithmetic and one FP16 rounding
+    rng = np.random.default_rng(21)
+    n = 120
+    g = F2H(rng.standard_normal(n) * 3.0); u = F2H(rng.standard_normal(n)); da = F2H(rng.standard_normal(n) * 0.1)
+    g[:4] = F2H(np.array([0.0, 1.0, -20.0, 11.0], np.float32))
+    a = oracle.act_fwd(g, u, "fp16")
+    dg, du, a2 = oracle.act_bwd(da, g, u, "fp16")
+    for i in range(n):
+        gv, uv, dv = float(H2F(g[i])), float(H2F(u[i])), float(H2F(da[i]))
+        sig, silu, ds = _derive_act_intermediates(gv)
+        assert int(a[i]) == _rn_f16_prod(silu, uv), i
+        assert int(a2[i]) == int(a[i])
+        assert int(du[i]) == _rn_f16_prod(dv, silu), i
+        dau = float(np.float32(dv) * np.float32(uv))  # one FP32 product (exact-rounded by IEEE)
+        assert int(dg[i]) == _rn_f16_prod(dau, ds), i
+
+
+def test_f16_activation_rounds_once_not_through_bf16():
+    # silu(1) u at u = 1 + 2^-10: FP16 keeps 10 fraction bits where BF16 keeps 7
+    g = F2H(np.array([1.0], np.float32)); u = F2H(np.array([1.0 + 2.0 ** -10], np.float32))
+    sig, silu, ds = _derive_act_intermediates(1.0)
+    want = _rn_f16(Fraction(silu) * Fraction(1.0 + 2.0 ** -10))
+    assert int(oracle.act_fwd(g, u, "fp16")[0]) == want
+    assert want != int(F2H(np.float32(B2F(F2B(np.float32(silu * (1.0 + 2.0 ** -10)))))))
+
+
+def _f16_tiny():
+    case = inputs.tiny_case(dtype=torch.float16)
+    return {k: inputs.bits(v) for k, v in case.items()}
+
+
+def test_f16_tiny_ffn_within_rel_l2_of_fp64():
+    b = _f16_tiny()
+    o = oracle.ffn_fwd(b["x"], b["w_gate"], b["w_up"], b["w_down"], "fp16")
+    f = fp64.ffn_fwd(b["x"], b["w_gate"], b["w_up"], b["w_down"], "fp16")
+    for k in ("g", "u", "a", "y"):
+        assert fp64.rel_l2(o[k], f[k], "fp16") <= 2e-3, k
+    ob = oracle.ffn_bwd(b["dy"], b["x"], o["g"], o["u"], b["w_gate"], b["w_up"], b["w_down"], "fp16")
+    fb = fp64.ffn_bwd(b["dy"], b["x"], b["w_gate"], b["w_up"], b["w_down"], "fp16")
+    for k in ("dA", "dG", "dU", "dX", "dW_gate", "dW_up", "dW_down"):
+        assert fp64.rel_l2(ob[k], fb[k], "fp16") <= 2e-3, k
+    np.testing.assert_array_equal(ob["a"], o["a"])
+
+
+def test_f16_ffn_stages_compose_and_dx_is_gate_then_up():
+    b = _f16_tiny()
+    o = oracle.ffn_fwd(b["x"], b["w_gate"], b["w_up"], b["w_down"], "fp16")
+    np.testing.assert_array_equal(o["g"], oracle.gemm_tree(b["x"], b["w_gate"], "NT", "fp16"))
+    np.testing.assert_array_equal(o["a"], oracle.act_fwd(o["g"], o["u"], "fp16"))
+    np.testing.assert_array_equal(o["y"], oracle.gemm_tree(o["a"], b["w_down"], "NT", "fp16"))
+    ob = oracle.ffn_bwd(b["dy"], b["x"], o["g"], o["u"], b["w_gate"], b["w_up"], b["w_down"], "fp16")
+    np.testing.assert_array_equal(ob["dA"], oracle.gemm_tree(b["dy"], b["w_down"], "NN", "fp16"))
+    np.testing.assert_array_equal(ob["G"], oracle.gemm_tree(ob["dG"], b["w_gate"], "NN", "fp16"))
+    np.testing.assert_array_equal(ob["dX"], oracle.tree_combine_typed([ob["G"], ob["U"]], "fp16").reshape(ob["dX"].shape))
+    np.testing.assert_array_equal(ob["dW_up"], oracle.gemm_tree(ob["dU"], b["x"], "TN", "fp16"))
+    # FP16 and BF16 storage give different bits from the same FP32 draws
+    bb = {k: inputs.bits(v) for k, v in inputs.tiny_case().items()}
+    assert not np.array_equal(oracle.ffn_fwd(bb["x"], bb["w_gate"], bb["w_up"], bb["w_down"])["y"], o["y"])
