@@ -43,6 +43,14 @@ SIGNATURES = {
     "dgf_gemm_tree": (_I, [_I, _P, _I64, _P, _I64, _P, _I64, _I64, _I64, _I64, _P, _SZ, _P]),
     "dgf_act_fwd": (_I, [_P, _P, _P, _I64, _P]),
     "dgf_act_bwd": (_I, [_P, _P, _P, _P, _P, _P, _I64, _P]),
+    "dgf_ffn_fwd_typed": (_I, [_P, _I64, _P, _I64, _P, _I64, _P, _I64, _P, _I64, _P, _P, _I64,
+                               _I64, _I64, _I64, _P, _SZ, _I, _P]),
+    "dgf_ffn_bwd_typed": (_I, [_P, _I64, _P, _I64, _P, _P, _I64, _P, _I64, _P, _I64, _P, _I64,
+                               _P, _P, _P, _I64, _P, _I64, _P, _I64, _P, _I64,
+                               _I64, _I64, _I64, _P, _SZ, _I, _P]),
+    "dgf_gemm_tree_typed": (_I, [_I, _P, _I64, _P, _I64, _P, _I64, _I64, _I64, _I64, _P, _SZ, _I, _P]),
+    "dgf_act_fwd_typed": (_I, [_P, _P, _P, _I64, _I, _P]),
+    "dgf_act_bwd_typed": (_I, [_P, _P, _P, _P, _P, _P, _I64, _I, _P]),
     "dgf_profile_begin": (_I, [ctypes.POINTER(_P), _I]),
     "dgf_profile_end": (_I, []),
     "dgf_profile_name": (ctypes.c_char_p, [_I]),
@@ -92,10 +100,26 @@ def _on(stream):
     return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
 
 
+DGF_BF16, DGF_FP16, DGF_FP32 = 0, 1, 2
+# stored types of the FFN and the tree GEMM: BF16 (the untyped entry points) or FP16
+_STORED = {torch.bfloat16: DGF_BF16, torch.float16: DGF_FP16}
+
+
+def _stored(*ts) -> int:
+    """The dtype code shared by every given tensor (BF16 or FP16)."""
+    dt = ts[0].dtype
+    if dt not in _STORED:
+        raise TypeError(f"expected bfloat16 or float16 tensors, got {dt}")
+    for t in ts:
+        if t.dtype != dt:
+            raise TypeError(f"all tensors must share one dtype ({dt} and {t.dtype} given)")
+    return _STORED[dt]
+
+
 def _mat(t: torch.Tensor, name: str):
-    """(pointer, leading dimension) of a row-major BF16 matrix view on the GPU."""
-    if t.dtype != torch.bfloat16:
-        raise TypeError(f"{name}: expected bfloat16, got {t.dtype}")
+    """(pointer, leading dimension) of a row-major BF16 or FP16 matrix view on the GPU."""
+    if t.dtype not in _STORED:
+        raise TypeError(f"{name}: expected bfloat16 or float16, got {t.dtype}")
     if not t.is_cuda:
         raise ValueError(f"{name}: expected a GPU tensor")
     if t.dim() != 2 or t.stride(1) != 1:
@@ -104,9 +128,9 @@ def _mat(t: torch.Tensor, name: str):
 
 
 def _empty(rows: int, cols: int, like: torch.Tensor, ld: int | None = None) -> torch.Tensor:
-    """Row-major BF16 [rows, cols] whose leading dimension is a multiple of 8."""
+    """Row-major [rows, cols] of like's dtype whose leading dimension is a multiple of 8."""
     ld = ld or ((cols + 7) // 8) * 8
-    buf = torch.empty((rows, ld), dtype=torch.bfloat16, device=like.device)
+    buf = torch.empty((rows, ld), dtype=like.dtype, device=like.device)
     return buf[:, :cols]
 
 
@@ -124,7 +148,8 @@ def leaf_size() -> int:
 
 
 def ffn_fwd(x, w_gate, w_up, w_down, training: bool = False, out=None, stream=None):
-    """y = W_down (silu(W_gate x) * (W_up x)) through the canonical tree.
+    """y = W_down (silu(W_gate x) * (W_up x)) through the canonical tree, in the
+    tensors' stored type (BF16: dgf_ffn_fwd, FP16: dgf_ffn_fwd_typed).
     Returns y, or (y, g, u) when training."""
     with _on(stream):
         return _ffn_fwd(x, w_gate, w_up, w_down, training, out, stream)
@@ -132,6 +157,7 @@ def ffn_fwd(x, w_gate, w_up, w_down, training: bool = False, out=None, stream=No
 
 def _ffn_fwd(x, w_gate, w_up, w_down, training, out, stream):
     L = load()
+    dt = _stored(x, w_gate, w_up, w_down, *([out] if out is not None else []))
     M, H = x.shape
     I = w_gate.shape[0]
     y = out if out is not None else _empty(M, H, x)
@@ -144,8 +170,12 @@ def _ffn_fwd(x, w_gate, w_up, w_down, training, out, stream):
     ws = _workspace(L.dgf_ffn_fwd_workspace(M, H, I), x)
     xp, ldx = _mat(x, "x"); wg, ldwg = _mat(w_gate, "w_gate"); wu, ldwu = _mat(w_up, "w_up")
     wd, ldwd = _mat(w_down, "w_down"); yp, ldy = _mat(y, "y")
-    _check(L.dgf_ffn_fwd(xp, ldx, wg, ldwg, wu, ldwu, wd, ldwd, yp, ldy, gp, up, ld_gu,
-                         M, H, I, ws.data_ptr(), ws.numel(), _stream(stream)), "dgf_ffn_fwd")
+    if dt == DGF_BF16:
+        _check(L.dgf_ffn_fwd(xp, ldx, wg, ldwg, wu, ldwu, wd, ldwd, yp, ldy, gp, up, ld_gu,
+                             M, H, I, ws.data_ptr(), ws.numel(), _stream(stream)), "dgf_ffn_fwd")
+    else:
+        _check(L.dgf_ffn_fwd_typed(xp, ldx, wg, ldwg, wu, ldwu, wd, ldwd, yp, ldy, gp, up, ld_gu,
+                                   M, H, I, ws.data_ptr(), ws.numel(), dt, _stream(stream)), "dgf_ffn_fwd_typed")
     return (y, g, u) if training else y
 
 
@@ -172,13 +202,15 @@ def ffn_fwd_static(x, w_gate, w_up, w_down, y, g=None, u=None, stream=None):
 
 
 def ffn_bwd(dy, x, g, u, w_gate, w_up, w_down, lanes: bool = False, stream=None):
-    """Returns dict dX, dW_gate, dW_up, dW_down (and G, U lanes if lanes=True)."""
+    """Returns dict dX, dW_gate, dW_up, dW_down (and G, U lanes if lanes=True),
+    in the tensors' stored type (BF16: dgf_ffn_bwd, FP16: dgf_ffn_bwd_typed)."""
     with _on(stream):
         return _ffn_bwd(dy, x, g, u, w_gate, w_up, w_down, lanes, stream)
 
 
 def _ffn_bwd(dy, x, g, u, w_gate, w_up, w_down, lanes, stream):
     L = load()
+    dt = _stored(dy, x, g, u, w_gate, w_up, w_down)
     M, H = x.shape
     I = w_gate.shape[0]
     dx = _empty(M, H, x)
@@ -190,18 +222,20 @@ def _ffn_bwd(dy, x, g, u, w_gate, w_up, w_down, lanes, stream):
     if ldg != ldu:
         raise ValueError("g and u must share a leading dimension")
     wg, ldwg = _mat(w_gate, "w_gate"); wu, ldwu = _mat(w_up, "w_up"); wd, ldwd = _mat(w_down, "w_down")
-    _check(L.dgf_ffn_bwd(dyp, lddy, xp, ldx, gp, upp, ldg, wg, ldwg, wu, ldwu, wd, ldwd,
-                         dx.data_ptr(), gl.data_ptr() if lanes else None, ul.data_ptr() if lanes else None,
-                         dx.stride(0), dwg.data_ptr(), dwg.stride(0), dwu.data_ptr(), dwu.stride(0),
-                         dwd.data_ptr(), dwd.stride(0), M, H, I, ws.data_ptr(), ws.numel(), _stream(stream)),
-           "dgf_ffn_bwd")
+    args = (dyp, lddy, xp, ldx, gp, upp, ldg, wg, ldwg, wu, ldwu, wd, ldwd,
+            dx.data_ptr(), gl.data_ptr() if lanes else None, ul.data_ptr() if lanes else None,
+            dx.stride(0), dwg.data_ptr(), dwg.stride(0), dwu.data_ptr(), dwu.stride(0),
+            dwd.data_ptr(), dwd.stride(0), M, H, I, ws.data_ptr(), ws.numel())
+    if dt == DGF_BF16:
+        _check(L.dgf_ffn_bwd(*args, _stream(stream)), "dgf_ffn_bwd")
+    else:
+        _check(L.dgf_ffn_bwd_typed(*args, dt, _stream(stream)), "dgf_ffn_bwd_typed")
     r = {"dX": dx, "dW_gate": dwg, "dW_up": dwu, "dW_down": dwd}
     if lanes:
         r["G"], r["U"] = gl, ul
     return r
 
 
-DGF_BF16, DGF_FP16, DGF_FP32 = 0, 1, 2
 _COMBINE_DTYPES = {torch.bfloat16: DGF_BF16, torch.float16: DGF_FP16, torch.float32: DGF_FP32}
 
 
@@ -240,13 +274,15 @@ def tree_combine_ptrs(ptrs, S: int, out_ptr: int, n: int, stream=None, dtype: in
 
 
 def gemm_tree(layout: str, A, B, out=None, stream=None):
-    """NT: A [M,K], B [N,K]; NN: A [M,K], B [K,N]; TN: A [K,M], B [K,N] -> C [M,N]."""
+    """NT: A [M,K], B [N,K]; NN: A [M,K], B [K,N]; TN: A [K,M], B [K,N] -> C [M,N],
+    in the operands' stored type (BF16: dgf_gemm_tree, FP16: dgf_gemm_tree_typed)."""
     with _on(stream):
         return _gemm_tree(layout, A, B, out, stream)
 
 
 def _gemm_tree(layout, A, B, out, stream):
     L = load()
+    dt = _stored(A, B, *([out] if out is not None else []))
     lay = _LAYOUTS[layout]
     if layout == "NT":
         (M, K), N = A.shape, B.shape[0]
@@ -257,25 +293,50 @@ def _gemm_tree(layout, A, B, out, stream):
     C = out if out is not None else _empty(M, N, A)
     ws = _workspace(L.dgf_gemm_tree_workspace(lay, M, N, K), A)
     ap, lda = _mat(A, "A"); bp, ldb = _mat(B, "B"); cp, ldc = _mat(C, "C")
-    _check(L.dgf_gemm_tree(lay, ap, lda, bp, ldb, cp, ldc, M, N, K, ws.data_ptr(), ws.numel(), _stream(stream)),
-           "dgf_gemm_tree")
+    if dt == DGF_BF16:
+        _check(L.dgf_gemm_tree(lay, ap, lda, bp, ldb, cp, ldc, M, N, K, ws.data_ptr(), ws.numel(), _stream(stream)),
+               "dgf_gemm_tree")
+    else:
+        _check(L.dgf_gemm_tree_typed(lay, ap, lda, bp, ldb, cp, ldc, M, N, K, ws.data_ptr(), ws.numel(), dt,
+                                     _stream(stream)), "dgf_gemm_tree_typed")
     return C
 
 
+def _flat(t: torch.Tensor, name: str) -> int:
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous GPU tensor")
+    return t.data_ptr()
+
+
 def act_fwd(g, u, stream=None):
+    """a = rnd(silu(g) u) elementwise in the stored type of g and u."""
     L = load()
+    dt = _stored(g, u)
+    if u.numel() != g.numel():
+        raise ValueError("g and u must have the same size")
     with _on(stream):
         a = torch.empty_like(g)
-    _check(L.dgf_act_fwd(g.data_ptr(), u.data_ptr(), a.data_ptr(), g.numel(), _stream(stream)), "dgf_act_fwd")
+    gp, up = _flat(g, "g"), _flat(u, "u")
+    if dt == DGF_BF16:
+        _check(L.dgf_act_fwd(gp, up, a.data_ptr(), g.numel(), _stream(stream)), "dgf_act_fwd")
+    else:
+        _check(L.dgf_act_fwd_typed(gp, up, a.data_ptr(), g.numel(), dt, _stream(stream)), "dgf_act_fwd_typed")
     return a
 
 
 def act_bwd(da, g, u, stream=None):
+    """dG, dU and the recomputed a elementwise in the stored type of da, g, u."""
     L = load()
+    dt = _stored(da, g, u)
+    if u.numel() != g.numel() or da.numel() != g.numel():
+        raise ValueError("da, g and u must have the same size")
     with _on(stream):
         dg, du, a = torch.empty_like(g), torch.empty_like(g), torch.empty_like(g)
-    _check(L.dgf_act_bwd(da.data_ptr(), g.data_ptr(), u.data_ptr(), dg.data_ptr(), du.data_ptr(), a.data_ptr(),
-                         g.numel(), _stream(stream)), "dgf_act_bwd")
+    ptrs = (_flat(da, "da"), _flat(g, "g"), _flat(u, "u"), dg.data_ptr(), du.data_ptr(), a.data_ptr(), g.numel())
+    if dt == DGF_BF16:
+        _check(L.dgf_act_bwd(*ptrs, _stream(stream)), "dgf_act_bwd")
+    else:
+        _check(L.dgf_act_bwd_typed(*ptrs, dt, _stream(stream)), "dgf_act_bwd_typed")
     return dg, du, a
 
 

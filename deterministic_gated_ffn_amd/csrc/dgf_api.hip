@@ -116,10 +116,21 @@ int tree_depth(int n) {
   return d;
 }
 
-GemmParams blank() {
+GemmParams blank(int fmt) {
   GemmParams p;
   memset(&p, 0, sizeof p);
+  p.fmt = fmt;
   return p;
+}
+
+// Public dtype code -> stored type of the kernels: BF16 and FP16 share the
+// tree; an FP32 FFN has no declared leaf rule (its MFMA differs), so it is
+// rejected as unsupported.
+dgf_status stored_type(int dtype, int *fmt) {
+  if (dtype == DGF_BF16) { *fmt = FMT_BF16; return DGF_OK; }
+  if (dtype == DGF_FP16) { *fmt = FMT_F16; return DGF_OK; }
+  if (dtype == DGF_FP32) return fail(DGF_EUNSUPPORTED, "dtype FP32: only BF16 and FP16 storage is implemented here");
+  return fail(DGF_EINVAL, "unknown dtype %d", dtype);
 }
 
 // Launch shape of one tree GEMM.  A wave owns 16 RT output columns (RT from
@@ -354,7 +365,7 @@ dgf_status run_gemm(int layout, int nb, int epi, GemmParams p, hipStream_t s, co
     const int S = 1 << pl.kdepth;
     for (int b = 0; b < nb; ++b)
       DGF_TRY(hip_check(timed(s, "K-split combine", [&] {
-                          return launch_combine_2d(p.part + (int64_t)b * S * p.part_stride, p.part_stride, p.ldp, S,
+                          return launch_combine_2d(p.fmt, p.part + (int64_t)b * S * p.part_stride, p.part_stride, p.ldp, S,
                                                    p.C[b], p.ldc[b], p.M, p.N, s);
                         }),
                         "K-split combine"));
@@ -478,7 +489,7 @@ dgf_status static_scratch(void **out) {
 
 extern "C" {
 
-int dgf_abi_version(void) { return 1; }
+int dgf_abi_version(void) { return 2; }
 
 int dgf_leaf_size(void) { return 64; }
 
@@ -511,9 +522,14 @@ size_t dgf_ffn_fwd_workspace(int64_t M, int64_t H, int64_t I) {
   return fwd_ws_bytes(M, H, I);
 }
 
-dgf_status dgf_ffn_fwd(const void *x, int64_t ldx, const void *w_gate, int64_t ld_wg, const void *w_up, int64_t ld_wu,
-                       const void *w_down, int64_t ld_wd, void *y, int64_t ldy, void *g_save, void *u_save,
-                       int64_t ld_gu, int64_t M, int64_t H, int64_t I, void *ws, size_t ws_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+dgf_status ffn_fwd_impl(int fmt, const void *x, int64_t ldx, const void *w_gate, int64_t ld_wg, const void *w_up,
+                        int64_t ld_wu, const void *w_down, int64_t ld_wd, void *y, int64_t ldy, void *g_save,
+                        void *u_save, int64_t ld_gu, int64_t M, int64_t H, int64_t I, void *ws, size_t ws_bytes,
+                        void *stream) {
   DGF_TRY(check_dims(M, I, H));
   DGF_TRY(check_dims(M, H, I));
   if (H == 0 || I == 0) return fail(DGF_EINVAL, "H and I must be positive (H=%lld I=%lld)", (long long)H, (long long)I);
@@ -546,10 +562,10 @@ dgf_status dgf_ffn_fwd(const void *x, int64_t ldx, const void *w_gate, int64_t l
     f.w[1] = (const uint16_t *)w_up; f.ldw[1] = ld_wu;
     f.a = a; f.lda = lda_;
     f.g = (uint16_t *)g_save; f.u = (uint16_t *)u_save; f.ldgu = ld_gu;
-    f.M = M; f.N = I; f.K = H; f.L = leaves(H);
+    f.M = M; f.N = I; f.K = H; f.L = leaves(H); f.fmt = fmt;
     DGF_TRY(hip_check(timed(s, "gate/up + act", [&] { return launch_gu_act(f, s); }), "gate/up + act"));
   } else {
-    GemmParams p = blank();
+    GemmParams p = blank(fmt);
     p.A[0] = p.A[1] = (const uint16_t *)x;
     p.lda[0] = p.lda[1] = ldx;
     p.shared_a = 1;
@@ -573,11 +589,11 @@ dgf_status dgf_ffn_fwd(const void *x, int64_t ldx, const void *w_gate, int64_t l
     d.A = a; d.lda = lda_;
     d.B = (const uint16_t *)w_down; d.ldb = ld_wd;
     d.C = (uint16_t *)y; d.ldc = ldy;
-    d.M = M; d.N = H; d.K = I; d.L = leaves(I);
+    d.M = M; d.N = H; d.K = I; d.L = leaves(I); d.fmt = fmt;
     DGF_TRY(hip_check(timed(s, "down all-K tree GEMM", [&] { return launch_allk(d, s); }), "down all-K tree GEMM"));
     return ok();
   }
-  GemmParams q = blank();
+  GemmParams q = blank(fmt);
   q.A[0] = a;
   q.lda[0] = lda_;
   q.B[0] = (const uint16_t *)w_down;
@@ -587,6 +603,27 @@ dgf_status dgf_ffn_fwd(const void *x, int64_t ldx, const void *w_gate, int64_t l
   q.M = M; q.N = H; q.K = I;
   DGF_TRY(run_gemm(DGF_LAYOUT_NT, 1, EPI_STORE, q, s, "down tree GEMM", partials, "down join"));
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+dgf_status dgf_ffn_fwd(const void *x, int64_t ldx, const void *w_gate, int64_t ld_wg, const void *w_up, int64_t ld_wu,
+                       const void *w_down, int64_t ld_wd, void *y, int64_t ldy, void *g_save, void *u_save,
+                       int64_t ld_gu, int64_t M, int64_t H, int64_t I, void *ws, size_t ws_bytes, void *stream) {
+  return ffn_fwd_impl(FMT_BF16, x, ldx, w_gate, ld_wg, w_up, ld_wu, w_down, ld_wd, y, ldy, g_save, u_save, ld_gu, M, H,
+                      I, ws, ws_bytes, stream);
+}
+
+dgf_status dgf_ffn_fwd_typed(const void *x, int64_t ldx, const void *w_gate, int64_t ld_wg, const void *w_up,
+                             int64_t ld_wu, const void *w_down, int64_t ld_wd, void *y, int64_t ldy, void *g_save,
+                             void *u_save, int64_t ld_gu, int64_t M, int64_t H, int64_t I, void *ws, size_t ws_bytes,
+                             int dtype, void *stream) {
+  int fmt = 0;
+  DGF_TRY(stored_type(dtype, &fmt));
+  return ffn_fwd_impl(fmt, x, ldx, w_gate, ld_wg, w_up, ld_wu, w_down, ld_wd, y, ldy, g_save, u_save, ld_gu, M, H, I,
+                      ws, ws_bytes, stream);
 }
 
 dgf_status dgf_ffn_fwd_static(const void *x, int64_t ldx, const void *w_gate, int64_t ld_wg, const void *w_up,
@@ -612,11 +649,16 @@ size_t dgf_ffn_bwd_workspace(int64_t M, int64_t H, int64_t I) {
   return bwd_ws_bytes(M, H, I);
 }
 
-dgf_status dgf_ffn_bwd(const void *dy, int64_t lddy, const void *x, int64_t ldx, const void *g, const void *u,
-                       int64_t ld_gu, const void *w_gate, int64_t ld_wg, const void *w_up, int64_t ld_wu,
-                       const void *w_down, int64_t ld_wd, void *dx, void *dx_gate_lane, void *dx_up_lane,
-                       int64_t lddx, void *dw_gate, int64_t ld_dwg, void *dw_up, int64_t ld_dwu, void *dw_down,
-                       int64_t ld_dwd, int64_t M, int64_t H, int64_t I, void *ws, size_t ws_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+dgf_status ffn_bwd_impl(int fmt, const void *dy, int64_t lddy, const void *x, int64_t ldx, const void *g,
+                        const void *u, int64_t ld_gu, const void *w_gate, int64_t ld_wg, const void *w_up,
+                        int64_t ld_wu, const void *w_down, int64_t ld_wd, void *dx, void *dx_gate_lane,
+                        void *dx_up_lane, int64_t lddx, void *dw_gate, int64_t ld_dwg, void *dw_up, int64_t ld_dwu,
+                        void *dw_down, int64_t ld_dwd, int64_t M, int64_t H, int64_t I, void *ws, size_t ws_bytes,
+                        void *stream) {
   DGF_TRY(check_dims(M, I, H));
   DGF_TRY(check_dims(M, H, I));
   if (H == 0 || I == 0) return fail(DGF_EINVAL, "H and I must be positive (H=%lld I=%lld)", (long long)H, (long long)I);
@@ -679,7 +721,7 @@ dgf_status dgf_ffn_bwd(const void *dy, int64_t lddy, const void *x, int64_t ldx,
   }
 
   // dA = T_H(dY W_down) with the dsilu epilogue
-  GemmParams p = blank();
+  GemmParams p = blank(fmt);
   p.A[0] = (const uint16_t *)dy;
   p.lda[0] = lddy;
   p.B[0] = tiled ? wdT : (const uint16_t *)w_down;
@@ -699,10 +741,10 @@ dgf_status dgf_ffn_bwd(const void *dy, int64_t lddy, const void *x, int64_t ldx,
   // dX lanes G = T_I(dG W_gate), U = T_I(dU W_up) and dX = bf16(G + U), the
   // gate lane first: one two-product GEMM whose join does the ordered add
   // (lanes kept when the caller asks for them), or two GEMMs and an add
-  GemmParams dx_join = blank();
+  GemmParams dx_join = blank(fmt);
   bool dx_deferred = false;
   if (tiled || dx_fused(M, H, I)) {
-    GemmParams q = blank();
+    GemmParams q = blank(fmt);
     q.A[0] = dG; q.A[1] = dU;
     q.lda[0] = q.lda[1] = ld_d;
     q.B[0] = tiled ? wgT : (const uint16_t *)w_gate; q.ldb[0] = tiled ? ld_wgT : ld_wg;
@@ -723,7 +765,7 @@ dgf_status dgf_ffn_bwd(const void *dy, int64_t lddy, const void *x, int64_t ldx,
     uint16_t *U = dx_up_lane ? (uint16_t *)dx_up_lane : Uw;
     const int64_t ldG = dx_gate_lane ? lddx : ld_lane, ldU = dx_up_lane ? lddx : ld_lane;
     for (int lane_i = 0; lane_i < 2; ++lane_i) {
-      GemmParams q = blank();
+      GemmParams q = blank(fmt);
       q.A[0] = lane_i == 0 ? dG : dU;
       q.lda[0] = ld_d;
       q.B[0] = (const uint16_t *)(lane_i == 0 ? w_gate : w_up);
@@ -735,17 +777,17 @@ dgf_status dgf_ffn_bwd(const void *dy, int64_t lddy, const void *x, int64_t ldx,
                        partials));
     }
     if (dx)
-      DGF_TRY(hip_check(timed(s, "dX ordered add", [&] { return launch_add_lanes(G, ldG, U, ldU, (uint16_t *)dx, lddx, M, H, s); }),
+      DGF_TRY(hip_check(timed(s, "dX ordered add", [&] { return launch_add_lanes(fmt, G, ldG, U, ldU, (uint16_t *)dx, lddx, M, H, s); }),
                         "dX ordered add"));
   }
 
   // dW_gate = T_M(dG^T x), dW_up = T_M(dU^T x); dW_down = T_M(dY^T a): one
   // leaf over the row-major operands, or NT over the transposed copies
-  GemmParams w = blank();
+  GemmParams w = blank(fmt);
   w.C[0] = (uint16_t *)dw_gate; w.ldc[0] = ld_dwg;
   w.C[1] = (uint16_t *)dw_up; w.ldc[1] = ld_dwu;
   w.M = I; w.N = H; w.K = M;
-  GemmParams v = blank();
+  GemmParams v = blank(fmt);
   v.C[0] = (uint16_t *)dw_down; v.ldc[0] = ld_dwd;
   v.M = H; v.N = I; v.K = M;
   if (direct) {
@@ -784,6 +826,32 @@ dgf_status dgf_ffn_bwd(const void *dy, int64_t lddy, const void *x, int64_t ldx,
     DGF_TRY(run_gemm(DGF_LAYOUT_NT, 1, EPI_STORE, v, s, "dW_down tree GEMM", partials));
   }
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+dgf_status dgf_ffn_bwd(const void *dy, int64_t lddy, const void *x, int64_t ldx, const void *g, const void *u,
+                       int64_t ld_gu, const void *w_gate, int64_t ld_wg, const void *w_up, int64_t ld_wu,
+                       const void *w_down, int64_t ld_wd, void *dx, void *dx_gate_lane, void *dx_up_lane,
+                       int64_t lddx, void *dw_gate, int64_t ld_dwg, void *dw_up, int64_t ld_dwu, void *dw_down,
+                       int64_t ld_dwd, int64_t M, int64_t H, int64_t I, void *ws, size_t ws_bytes, void *stream) {
+  return ffn_bwd_impl(FMT_BF16, dy, lddy, x, ldx, g, u, ld_gu, w_gate, ld_wg, w_up, ld_wu, w_down, ld_wd, dx,
+                      dx_gate_lane, dx_up_lane, lddx, dw_gate, ld_dwg, dw_up, ld_dwu, dw_down, ld_dwd, M, H, I, ws,
+                      ws_bytes, stream);
+}
+
+dgf_status dgf_ffn_bwd_typed(const void *dy, int64_t lddy, const void *x, int64_t ldx, const void *g, const void *u,
+                             int64_t ld_gu, const void *w_gate, int64_t ld_wg, const void *w_up, int64_t ld_wu,
+                             const void *w_down, int64_t ld_wd, void *dx, void *dx_gate_lane, void *dx_up_lane,
+                             int64_t lddx, void *dw_gate, int64_t ld_dwg, void *dw_up, int64_t ld_dwu, void *dw_down,
+                             int64_t ld_dwd, int64_t M, int64_t H, int64_t I, void *ws, size_t ws_bytes, int dtype,
+                             void *stream) {
+  int fmt = 0;
+  DGF_TRY(stored_type(dtype, &fmt));
+  return ffn_bwd_impl(fmt, dy, lddy, x, ldx, g, u, ld_gu, w_gate, ld_wg, w_up, ld_wu, w_down, ld_wd, dx, dx_gate_lane,
+                      dx_up_lane, lddx, dw_gate, ld_dwg, dw_up, ld_dwu, dw_down, ld_dwd, M, H, I, ws, ws_bytes, stream);
 }
 
 dgf_status dgf_tree_combine(const void *const *parts, int S, void *out, int64_t n, void *stream) {
@@ -829,8 +897,12 @@ size_t dgf_gemm_tree_workspace(int layout, int64_t M, int64_t N, int64_t K) {
   return gemm_ws_bytes(layout, M, N, K);
 }
 
-dgf_status dgf_gemm_tree(int layout, const void *A, int64_t lda, const void *B, int64_t ldb, void *C, int64_t ldc,
-                         int64_t M, int64_t N, int64_t K, void *ws, size_t ws_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+dgf_status gemm_tree_impl(int fmt, int layout, const void *A, int64_t lda, const void *B, int64_t ldb, void *C,
+                          int64_t ldc, int64_t M, int64_t N, int64_t K, void *ws, size_t ws_bytes, void *stream) {
   if (layout != DGF_NT && layout != DGF_NN && layout != DGF_TN) return fail(DGF_EINVAL, "unknown layout %d", layout);
   DGF_TRY(check_dims(M, N, K));
   if (M == 0 || N == 0) return ok();
@@ -851,7 +923,7 @@ dgf_status dgf_gemm_tree(int layout, const void *A, int64_t lda, const void *B, 
   if (need && (!ws || ws_bytes < need || !aligned16(ws)))
     return fail(DGF_EWORKSPACE, "gemm_tree workspace: need %zu bytes (16-byte aligned), got %zu", need, ws ? ws_bytes : 0);
 
-  GemmParams p = blank();
+  GemmParams p = blank(fmt);
   p.M = M; p.N = N; p.K = K;
   p.C[0] = (uint16_t *)C;
   p.ldc[0] = ldc;
@@ -879,19 +951,19 @@ dgf_status dgf_gemm_tree(int layout, const void *A, int64_t lda, const void *B, 
   return ok();
 }
 
-dgf_status dgf_act_fwd(const void *g, const void *u, void *a, int64_t n, void *stream) {
+dgf_status act_fwd_impl(int fmt, const void *g, const void *u, void *a, int64_t n, void *stream) {
   if (n < 0) return fail(DGF_EINVAL, "negative length");
   if (n == 0) return ok();
   if (!g || !u || !a) return fail(DGF_EINVAL, "NULL pointer");
   if (((uintptr_t)g | (uintptr_t)u | (uintptr_t)a) & 1) return fail(DGF_EINVAL, "pointers must be 2-byte aligned");
   hipStream_t s = (hipStream_t)stream;
-  DGF_TRY(hip_check(timed(s, "act_fwd", [&] { return launch_act_fwd((const uint16_t *)g, (const uint16_t *)u, (uint16_t *)a, n, s); }),
+  DGF_TRY(hip_check(timed(s, "act_fwd", [&] { return launch_act_fwd(fmt, (const uint16_t *)g, (const uint16_t *)u, (uint16_t *)a, n, s); }),
                     "act_fwd"));
   return ok();
 }
 
-dgf_status dgf_act_bwd(const void *da, const void *g, const void *u, void *dg, void *du, void *a, int64_t n,
-                       void *stream) {
+dgf_status act_bwd_impl(int fmt, const void *da, const void *g, const void *u, void *dg, void *du, void *a, int64_t n,
+                        void *stream) {
   if (n < 0) return fail(DGF_EINVAL, "negative length");
   if (n == 0) return ok();
   if (!da || !g || !u || !dg || !du) return fail(DGF_EINVAL, "NULL pointer");
@@ -899,11 +971,50 @@ dgf_status dgf_act_bwd(const void *da, const void *g, const void *u, void *dg, v
     return fail(DGF_EINVAL, "pointers must be 2-byte aligned");
   hipStream_t s = (hipStream_t)stream;
   DGF_TRY(hip_check(timed(s, "act_bwd", [&] {
-                      return launch_act_bwd((const uint16_t *)da, (const uint16_t *)g, (const uint16_t *)u, (uint16_t *)dg,
-                                            (uint16_t *)du, (uint16_t *)a, n, s);
+                      return launch_act_bwd(fmt, (const uint16_t *)da, (const uint16_t *)g, (const uint16_t *)u,
+                                            (uint16_t *)dg, (uint16_t *)du, (uint16_t *)a, n, s);
                     }),
                     "act_bwd"));
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+dgf_status dgf_gemm_tree(int layout, const void *A, int64_t lda, const void *B, int64_t ldb, void *C, int64_t ldc,
+                         int64_t M, int64_t N, int64_t K, void *ws, size_t ws_bytes, void *stream) {
+  return gemm_tree_impl(FMT_BF16, layout, A, lda, B, ldb, C, ldc, M, N, K, ws, ws_bytes, stream);
+}
+
+dgf_status dgf_gemm_tree_typed(int layout, const void *A, int64_t lda, const void *B, int64_t ldb, void *C,
+                               int64_t ldc, int64_t M, int64_t N, int64_t K, void *ws, size_t ws_bytes, int dtype,
+                               void *stream) {
+  int fmt = 0;
+  DGF_TRY(stored_type(dtype, &fmt));
+  return gemm_tree_impl(fmt, layout, A, lda, B, ldb, C, ldc, M, N, K, ws, ws_bytes, stream);
+}
+
+dgf_status dgf_act_fwd(const void *g, const void *u, void *a, int64_t n, void *stream) {
+  return act_fwd_impl(FMT_BF16, g, u, a, n, stream);
+}
+
+dgf_status dgf_act_fwd_typed(const void *g, const void *u, void *a, int64_t n, int dtype, void *stream) {
+  int fmt = 0;
+  DGF_TRY(stored_type(dtype, &fmt));
+  return act_fwd_impl(fmt, g, u, a, n, stream);
+}
+
+dgf_status dgf_act_bwd(const void *da, const void *g, const void *u, void *dg, void *du, void *a, int64_t n,
+                       void *stream) {
+  return act_bwd_impl(FMT_BF16, da, g, u, dg, du, a, n, stream);
+}
+
+dgf_status dgf_act_bwd_typed(const void *da, const void *g, const void *u, void *dg, void *du, void *a, int64_t n,
+                             int dtype, void *stream) {
+  int fmt = 0;
+  DGF_TRY(stored_type(dtype, &fmt));
+  return act_bwd_impl(fmt, da, g, u, dg, du, a, n, stream);
 }
 
 }  // extern "C"

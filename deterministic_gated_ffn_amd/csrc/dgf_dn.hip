@@ -35,14 +35,14 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // Feed leaf J of an N-leaf subtree (N <= 32): merge it with the pending left
 // siblings its position closes, then park it at its depth.
-template <int NP, int N, int J>
+template <class T, int NP, int N, int J>
 __device__ __forceinline__ void push_leaf_deep(uint32_t (&v)[NP], uint32_t (&st)[kAkMaxD][NP]) {
   constexpr LeafPos lp = leaf_pos(N, J);
   static_assert(lp.D <= kAkMaxD, "subtree too deep");
 #pragma unroll
   for (int t = 0; t < lp.m; ++t)
 #pragma unroll
-    for (int q = 0; q < NP; ++q) v[q] = node2(st[lp.D - 1 - t][q], v[q]);
+    for (int q = 0; q < NP; ++q) v[q] = node2t<T>(st[lp.D - 1 - t][q], v[q]);
   constexpr int d = lp.D - lp.m;
   if constexpr (d > 0) {
 #pragma unroll
@@ -58,9 +58,9 @@ struct AkLds {
   static constexpr size_t total = roots + kAkWaves * (slab_w + slab_a);
 };
 
-template <int MT, int NW>
+template <class T, int MT, int NW>
 struct AkWave {
-  static constexpr int NP = MT * 2;  // packed BF16 pairs per lane: index 2 t + h
+  static constexpr int NP = MT * 2;  // packed pairs of stored values per lane: index 2 t + h
   static constexpr int PR = kAkRing;
   struct Unit {
     u32x4 w[2];       // weight rows 8 i + lane / 8 of the tile, 16-byte K chunk lane % 8
@@ -95,7 +95,7 @@ struct AkWave {
 
   // One leaf: both operands through the slabs (row r's chunk c at
   // r*64 + 8 (c ^ (r & 7))), two MFMAs per token tile from a zero
-  // accumulator, packed to BF16.
+  // accumulator, rounded and packed.
   __device__ __forceinline__ void leaf(const Unit &u, uint32_t (&v)[NP]) const {
     const int wr = lane >> 3, wc = lane & 7;
 #pragma unroll
@@ -103,25 +103,25 @@ struct AkWave {
 #pragma unroll
     for (int i = 0; i < 2 * MT; ++i) *reinterpret_cast<u32x4 *>(&sa[(8 * i + wr) * 64 + 8 * (wc ^ wr)]) = u.a[i];
     wave_lds_sync();
-    const bf16x8 w0 = *reinterpret_cast<const bf16x8 *>(&sw[r16 * 64 + 8 * ((0 + g4) ^ (r16 & 7))]);
-    const bf16x8 w1 = *reinterpret_cast<const bf16x8 *>(&sw[r16 * 64 + 8 * ((4 + g4) ^ (r16 & 7))]);
-    bf16x8 x[MT][2];
+    const typename T::frag w0 = *reinterpret_cast<const typename T::frag *>(&sw[r16 * 64 + 8 * ((0 + g4) ^ (r16 & 7))]);
+    const typename T::frag w1 = *reinterpret_cast<const typename T::frag *>(&sw[r16 * 64 + 8 * ((4 + g4) ^ (r16 & 7))]);
+    typename T::frag x[MT][2];
 #pragma unroll
     for (int t = 0; t < MT; ++t)
 #pragma unroll
       for (int h = 0; h < 2; ++h)
-        x[t][h] = *reinterpret_cast<const bf16x8 *>(&sa[(16 * t + r16) * 64 + 8 * ((4 * h + g4) ^ (r16 & 7))]);
+        x[t][h] = *reinterpret_cast<const typename T::frag *>(&sa[(16 * t + r16) * 64 + 8 * ((4 * h + g4) ^ (r16 & 7))]);
     f32x4 acc[MT];
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
-      acc[t] = mfma16(w0, x[t][0], f32x4{0.f, 0.f, 0.f, 0.f});
-      acc[t] = mfma16(w1, x[t][1], acc[t]);
+      acc[t] = T::mfma(w0, x[t][0], f32x4{0.f, 0.f, 0.f, 0.f});
+      acc[t] = T::mfma(w1, x[t][1], acc[t]);
     }
     wave_lds_sync();  // slab reads done before the next leaf overwrites them
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
-      v[2 * t + 0] = pack_rne(acc[t][0], acc[t][1]);
-      v[2 * t + 1] = pack_rne(acc[t][2], acc[t][3]);
+      v[2 * t + 0] = T::pack(acc[t][0], acc[t][1]);
+      v[2 * t + 1] = T::pack(acc[t][2], acc[t][3]);
     }
   }
 
@@ -134,7 +134,7 @@ struct AkWave {
       if constexpr (J + PR - 1 < NW) load(J + PR - 1, ring[(J + PR - 1) % PR]);
       __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of this leaf's MFMAs
       leaf(ring[J % PR], v);
-      push_leaf_deep<NP, NW, J>(v, st);
+      push_leaf_deep<T, NP, NW, J>(v, st);
       leaves<J + 1>(ring, v, st);
     }
   }
@@ -158,7 +158,7 @@ struct AkWave {
       uint32_t r[kAkWaves];
 #pragma unroll
       for (int w2 = 0; w2 < kAkWaves; ++w2) r[w2] = roots[(w2 * NP + 2 * t + h) * 64 + lane];
-      o[h] = node2(node2(node2(r[0], r[1]), node2(r[2], r[3])), node2(node2(r[4], r[5]), node2(r[6], r[7])));
+      o[h] = node2t<T>(node2t<T>(node2t<T>(r[0], r[1]), node2t<T>(r[2], r[3])), node2t<T>(node2t<T>(r[4], r[5]), node2t<T>(r[6], r[7])));
     }
     const int64_t m = 16 * t + r16, n = n0 + 4 * g4;
     if (m >= p.M || n >= p.N) return;
@@ -174,14 +174,14 @@ struct AkWave {
   }
 };
 
-template <int MT, int NW>
+template <class T, int MT, int NW>
 __global__ __launch_bounds__(kAkWaves * 64) void k_allk(AllkParams p) {
   extern __shared__ __attribute__((aligned(16))) uint32_t ak_lds[];
   using Lay = AkLds<MT>;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   char *base = reinterpret_cast<char *>(ak_lds) + Lay::roots + (size_t)wave * (Lay::slab_w + Lay::slab_a);
-  AkWave<MT, NW> w{p,
+  AkWave<T, MT, NW> w{p,
                    reinterpret_cast<uint16_t *>(base),
                    reinterpret_cast<uint16_t *>(base + Lay::slab_w),
                    ak_lds,
@@ -200,21 +200,21 @@ __global__ __launch_bounds__(kAkWaves * 64) void k_allk(AllkParams p) {
   w.run();
 }
 
-template <int MT>
+template <class T, int MT>
 hipError_t launch_allk_mt(const AllkParams &p, int nw, hipStream_t s) {
   const dim3 grid((unsigned)((p.N + kAkCols - 1) / kAkCols)), block(kAkWaves * 64);
   const size_t shm = AkLds<MT>::total;
   switch (nw) {
-    case 1: dgf_launch((k_allk<MT, 1>), grid, block, shm, s, p); break;
-    case 2: dgf_launch((k_allk<MT, 2>), grid, block, shm, s, p); break;
-    case 3: dgf_launch((k_allk<MT, 3>), grid, block, shm, s, p); break;
-    case 4: dgf_launch((k_allk<MT, 4>), grid, block, shm, s, p); break;
-    case 6: dgf_launch((k_allk<MT, 6>), grid, block, shm, s, p); break;
-    case 8: dgf_launch((k_allk<MT, 8>), grid, block, shm, s, p); break;
-    case 12: dgf_launch((k_allk<MT, 12>), grid, block, shm, s, p); break;
-    case 16: dgf_launch((k_allk<MT, 16>), grid, block, shm, s, p); break;
-    case 24: dgf_launch((k_allk<MT, 24>), grid, block, shm, s, p); break;
-    case 32: dgf_launch((k_allk<MT, 32>), grid, block, shm, s, p); break;
+    case 1: dgf_launch((k_allk<T, MT, 1>), grid, block, shm, s, p); break;
+    case 2: dgf_launch((k_allk<T, MT, 2>), grid, block, shm, s, p); break;
+    case 3: dgf_launch((k_allk<T, MT, 3>), grid, block, shm, s, p); break;
+    case 4: dgf_launch((k_allk<T, MT, 4>), grid, block, shm, s, p); break;
+    case 6: dgf_launch((k_allk<T, MT, 6>), grid, block, shm, s, p); break;
+    case 8: dgf_launch((k_allk<T, MT, 8>), grid, block, shm, s, p); break;
+    case 12: dgf_launch((k_allk<T, MT, 12>), grid, block, shm, s, p); break;
+    case 16: dgf_launch((k_allk<T, MT, 16>), grid, block, shm, s, p); break;
+    case 24: dgf_launch((k_allk<T, MT, 24>), grid, block, shm, s, p); break;
+    case 32: dgf_launch((k_allk<T, MT, 32>), grid, block, shm, s, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -233,8 +233,12 @@ bool allk_applies(int64_t M, int64_t N, int64_t K) {
 
 hipError_t launch_allk(const AllkParams &p, hipStream_t stream) {
   if (p.M > 24) return hipErrorInvalidValue;
-  if (p.M > 16) return launch_allk_mt<2>(p, p.L / kAkWaves, stream);
-  return launch_allk_mt<1>(p, p.L / kAkWaves, stream);
+  if (p.fmt == FMT_F16) {
+    if (p.M > 16) return launch_allk_mt<F16, 2>(p, p.L / kAkWaves, stream);
+    return launch_allk_mt<F16, 1>(p, p.L / kAkWaves, stream);
+  }
+  if (p.M > 16) return launch_allk_mt<Bf16, 2>(p, p.L / kAkWaves, stream);
+  return launch_allk_mt<Bf16, 1>(p, p.L / kAkWaves, stream);
 }
 
 }  // namespace dgf

@@ -1,5 +1,7 @@
 // Elementwise kernels: the activation and its derivative, the fixed balanced
-// combine of S partial results, and a BF16 transpose.
+// combine of S partial results, and a 16-bit transpose.  T is the stored type
+// (BF16 or FP16): values are widened to FP32 exactly and each result is rounded
+// to T once (nearest even).
 #include "dgf_device.hpp"
 #include "dgf_kernels.hpp"
 #include "dgf_join.hpp"
@@ -17,40 +19,42 @@ unsigned grid_for(int64_t work, int per_thread) {
   return (unsigned)blocks;
 }
 
-// a = bf16(silu(g) u), silu(g) = g * sigma(g)
+// a = rnd(silu(g) u), silu(g) = g * sigma(g)
+template <class T>
 __global__ __launch_bounds__(kThreads) void k_act_fwd(const uint16_t *g, const uint16_t *u, uint16_t *a, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += (int64_t)gridDim.x * kThreads) {
-    const float gv = bf2f(g[i]);
+    const float gv = T::f(g[i]);
     const float s = gv * sigma_f(gv);
-    a[i] = f2bf(s * bf2f(u[i]));
+    a[i] = T::r(s * T::f(u[i]));
   }
 }
 
-// dU = bf16(dA silu(g)), dG = bf16((dA u) silu'(g)), silu' = sigma (1 + g (1 - sigma))
+// dU = rnd(dA silu(g)), dG = rnd((dA u) silu'(g)), silu' = sigma (1 + g (1 - sigma))
+template <class T>
 __global__ __launch_bounds__(kThreads) void k_act_bwd(const uint16_t *da, const uint16_t *g, const uint16_t *u,
                                                       uint16_t *dg, uint16_t *du, uint16_t *a, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += (int64_t)gridDim.x * kThreads) {
-    const float gv = bf2f(g[i]), uv = bf2f(u[i]), dav = bf2f(da[i]);
+    const float gv = T::f(g[i]), uv = T::f(u[i]), dav = T::f(da[i]);
     const float sg = sigma_f(gv);
     const float s = gv * sg;
     const float one_m = 1.0f - sg;
     const float t = gv * one_m;
     const float onep = 1.0f + t;
     const float ds = sg * onep;
-    du[i] = f2bf(dav * s);
+    du[i] = T::r(dav * s);
     const float dau = dav * uv;
-    dg[i] = f2bf(dau * ds);
-    if (a) a[i] = f2bf(s * uv);
+    dg[i] = T::r(dau * ds);
+    if (a) a[i] = T::r(s * uv);
   }
 }
 
-template <int S, int EPI>
+template <class T, int S, int EPI>
 __global__ __launch_bounds__(kThreads) void k_combine_epi(GemmParams p) {
   const int64_t chunks = (p.N + 7) / 8;
   const int b = blockIdx.y;
   for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < p.M * chunks; i += (int64_t)gridDim.x * kThreads) {
     const int64_t m = i / chunks, c = (i % chunks) * 8;
-    join_epi_chunk<S, EPI>(p, b, m, c);
+    join_epi_chunk<T, S, EPI>(p, b, m, c);
   }
 }
 
@@ -168,7 +172,7 @@ __global__ __launch_bounds__(kThreads) void k_combine_scalar_t(PartsV parts, voi
 
 // out[m][n] = balanced combine over S partial roots (the top levels of the
 // tree above the workgroups' K pieces); 8 elements per thread.
-template <int S>
+template <class T, int S>
 __global__ __launch_bounds__(kThreads) void k_combine_2d(const uint16_t *part, int64_t part_stride, int64_t ldp,
                                                          uint16_t *out, int64_t ldo, int64_t M, int64_t N) {
   const int64_t per_row = (N + 7) / 8;
@@ -187,25 +191,27 @@ __global__ __launch_bounds__(kThreads) void k_combine_2d(const uint16_t *part, i
 #pragma unroll
         for (int j = 0; j < width / 2; ++j)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) r[j][q] = node2(r[2 * j][q], r[2 * j + 1][q]);
+          for (int q = 0; q < 4; ++q) r[j][q] = node2t<T>(r[2 * j][q], r[2 * j + 1][q]);
       *reinterpret_cast<uint4 *>(o) = make_uint4(r[0][0], r[0][1], r[0][2], r[0][3]);
     } else {
       for (int64_t e = 0; c + e < N; ++e) {
         float r[S];
 #pragma unroll
-        for (int s = 0; s < S; ++s) r[s] = bf2f(part[s * part_stride + m * ldp + c + e]);
+        for (int s = 0; s < S; ++s) r[s] = T::f(part[s * part_stride + m * ldp + c + e]);
 #pragma unroll
         for (int width = S; width > 1; width >>= 1)
 #pragma unroll
-          for (int j = 0; j < width / 2; ++j) r[j] = bf2f(f2bf(r[2 * j] + r[2 * j + 1]));
-        o[e] = f2bf(r[0]);
+          for (int j = 0; j < width / 2; ++j) r[j] = T::f(T::r(r[2 * j] + r[2 * j + 1]));
+        o[e] = T::r(r[0]);
       }
     }
   }
 }
 
-// dx = bf16(G + U), the gate contribution first (an FP32 add of two BF16 lanes,
-// rounded to BF16); 8 elements per thread, rows of N (a multiple of 8 leading dims).
+// dx = rnd(G + U), the gate contribution first (an FP32 add of two stored
+// lanes, rounded to the stored type); 8 elements per thread, rows of N (a
+// multiple of 8 leading dims).
+template <class T>
 __global__ __launch_bounds__(kThreads) void k_add_lanes(const uint16_t *G, int64_t ldg, const uint16_t *U, int64_t ldu,
                                                         uint16_t *dx, int64_t lddx, int64_t M, int64_t N) {
   const int64_t per_row = (N + 7) / 8;
@@ -215,9 +221,10 @@ __global__ __launch_bounds__(kThreads) void k_add_lanes(const uint16_t *G, int64
     uint16_t *o = dx + m * lddx + c;
     if (c + 8 <= N) {
       const uint4 gv = *reinterpret_cast<const uint4 *>(g), uv = *reinterpret_cast<const uint4 *>(u);
-      *reinterpret_cast<uint4 *>(o) = make_uint4(node2(gv.x, uv.x), node2(gv.y, uv.y), node2(gv.z, uv.z), node2(gv.w, uv.w));
+      *reinterpret_cast<uint4 *>(o) =
+          make_uint4(node2t<T>(gv.x, uv.x), node2t<T>(gv.y, uv.y), node2t<T>(gv.z, uv.z), node2t<T>(gv.w, uv.w));
     } else {
-      for (int64_t j = 0; c + j < N; ++j) o[j] = f2bf(bf2f(g[j]) + bf2f(u[j]));
+      for (int64_t j = 0; c + j < N; ++j) o[j] = T::r(T::f(g[j]) + T::f(u[j]));
     }
   }
 }
@@ -266,14 +273,20 @@ __global__ __launch_bounds__(kThreads) void k_transpose(const uint16_t *src, int
 
 }  // namespace
 
-hipError_t launch_act_fwd(const uint16_t *g, const uint16_t *u, uint16_t *a, int64_t n, hipStream_t s) {
-  dgf_launch(k_act_fwd, dim3(grid_for(n, 1)), dim3(kThreads), 0, s, g, u, a, n);
+hipError_t launch_act_fwd(int fmt, const uint16_t *g, const uint16_t *u, uint16_t *a, int64_t n, hipStream_t s) {
+  if (fmt == FMT_F16)
+    dgf_launch(k_act_fwd<F16>, dim3(grid_for(n, 1)), dim3(kThreads), 0, s, g, u, a, n);
+  else
+    dgf_launch(k_act_fwd<Bf16>, dim3(grid_for(n, 1)), dim3(kThreads), 0, s, g, u, a, n);
   return hipGetLastError();
 }
 
-hipError_t launch_act_bwd(const uint16_t *da, const uint16_t *g, const uint16_t *u, uint16_t *dg, uint16_t *du,
-                          uint16_t *a, int64_t n, hipStream_t s) {
-  dgf_launch(k_act_bwd, dim3(grid_for(n, 1)), dim3(kThreads), 0, s, da, g, u, dg, du, a, n);
+hipError_t launch_act_bwd(int fmt, const uint16_t *da, const uint16_t *g, const uint16_t *u, uint16_t *dg,
+                          uint16_t *du, uint16_t *a, int64_t n, hipStream_t s) {
+  if (fmt == FMT_F16)
+    dgf_launch(k_act_bwd<F16>, dim3(grid_for(n, 1)), dim3(kThreads), 0, s, da, g, u, dg, du, a, n);
+  else
+    dgf_launch(k_act_bwd<Bf16>, dim3(grid_for(n, 1)), dim3(kThreads), 0, s, da, g, u, dg, du, a, n);
   return hipGetLastError();
 }
 
@@ -348,23 +361,34 @@ hipError_t launch_combine_typed(const void *const *parts, int S, void *out, int6
   }
 }
 
-hipError_t launch_combine_2d(const uint16_t *part, int64_t part_stride, int64_t ldp, int S, uint16_t *out, int64_t ldo,
-                             int64_t M, int64_t N, hipStream_t s) {
+template <class T>
+hipError_t launch_combine_2d_t(const uint16_t *part, int64_t part_stride, int64_t ldp, int S, uint16_t *out,
+                               int64_t ldo, int64_t M, int64_t N, hipStream_t s) {
   const dim3 g(grid_for(M * ((N + 7) / 8), 1));
   switch (S) {
-    case 1: dgf_launch(k_combine_2d<1>, g, dim3(kThreads), 0, s, part, part_stride, ldp, out, ldo, M, N); break;
-    case 2: dgf_launch(k_combine_2d<2>, g, dim3(kThreads), 0, s, part, part_stride, ldp, out, ldo, M, N); break;
-    case 4: dgf_launch(k_combine_2d<4>, g, dim3(kThreads), 0, s, part, part_stride, ldp, out, ldo, M, N); break;
-    case 8: dgf_launch(k_combine_2d<8>, g, dim3(kThreads), 0, s, part, part_stride, ldp, out, ldo, M, N); break;
-    case 16: dgf_launch(k_combine_2d<16>, g, dim3(kThreads), 0, s, part, part_stride, ldp, out, ldo, M, N); break;
+    case 1: dgf_launch((k_combine_2d<T, 1>), g, dim3(kThreads), 0, s, part, part_stride, ldp, out, ldo, M, N); break;
+    case 2: dgf_launch((k_combine_2d<T, 2>), g, dim3(kThreads), 0, s, part, part_stride, ldp, out, ldo, M, N); break;
+    case 4: dgf_launch((k_combine_2d<T, 4>), g, dim3(kThreads), 0, s, part, part_stride, ldp, out, ldo, M, N); break;
+    case 8: dgf_launch((k_combine_2d<T, 8>), g, dim3(kThreads), 0, s, part, part_stride, ldp, out, ldo, M, N); break;
+    case 16: dgf_launch((k_combine_2d<T, 16>), g, dim3(kThreads), 0, s, part, part_stride, ldp, out, ldo, M, N); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_add_lanes(const uint16_t *G, int64_t ldg, const uint16_t *U, int64_t ldu, uint16_t *dx,
+hipError_t launch_combine_2d(int fmt, const uint16_t *part, int64_t part_stride, int64_t ldp, int S, uint16_t *out,
+                             int64_t ldo, int64_t M, int64_t N, hipStream_t s) {
+  if (fmt == FMT_F16) return launch_combine_2d_t<F16>(part, part_stride, ldp, S, out, ldo, M, N, s);
+  return launch_combine_2d_t<Bf16>(part, part_stride, ldp, S, out, ldo, M, N, s);
+}
+
+hipError_t launch_add_lanes(int fmt, const uint16_t *G, int64_t ldg, const uint16_t *U, int64_t ldu, uint16_t *dx,
                             int64_t lddx, int64_t M, int64_t N, hipStream_t s) {
-  dgf_launch(k_add_lanes, dim3(grid_for(M * ((N + 7) / 8), 1)), dim3(kThreads), 0, s, G, ldg, U, ldu, dx, lddx, M, N);
+  const dim3 g(grid_for(M * ((N + 7) / 8), 1));
+  if (fmt == FMT_F16)
+    dgf_launch(k_add_lanes<F16>, g, dim3(kThreads), 0, s, G, ldg, U, ldu, dx, lddx, M, N);
+  else
+    dgf_launch(k_add_lanes<Bf16>, g, dim3(kThreads), 0, s, G, ldg, U, ldu, dx, lddx, M, N);
   return hipGetLastError();
 }
 
@@ -376,30 +400,36 @@ hipError_t launch_transpose(const uint16_t *src, int64_t lds_, int64_t R, int64_
 }
 
 
-template <int EPI>
+template <class T, int EPI>
 hipError_t launch_combine_epi_s(int S, int nb, GemmParams p, hipStream_t s) {
   const dim3 g(grid_for(p.M * ((p.N + 7) / 8), 1), EPI == EPI_STORE ? nb : 1);
   switch (S) {
-    case 1: dgf_launch((k_combine_epi<1, EPI>), g, dim3(kThreads), 0, s, p); break;
-    case 2: dgf_launch((k_combine_epi<2, EPI>), g, dim3(kThreads), 0, s, p); break;
-    case 4: dgf_launch((k_combine_epi<4, EPI>), g, dim3(kThreads), 0, s, p); break;
-    case 8: dgf_launch((k_combine_epi<8, EPI>), g, dim3(kThreads), 0, s, p); break;
-    case 16: dgf_launch((k_combine_epi<16, EPI>), g, dim3(kThreads), 0, s, p); break;
-    case 32: dgf_launch((k_combine_epi<32, EPI>), g, dim3(kThreads), 0, s, p); break;
+    case 1: dgf_launch((k_combine_epi<T, 1, EPI>), g, dim3(kThreads), 0, s, p); break;
+    case 2: dgf_launch((k_combine_epi<T, 2, EPI>), g, dim3(kThreads), 0, s, p); break;
+    case 4: dgf_launch((k_combine_epi<T, 4, EPI>), g, dim3(kThreads), 0, s, p); break;
+    case 8: dgf_launch((k_combine_epi<T, 8, EPI>), g, dim3(kThreads), 0, s, p); break;
+    case 16: dgf_launch((k_combine_epi<T, 16, EPI>), g, dim3(kThreads), 0, s, p); break;
+    case 32: dgf_launch((k_combine_epi<T, 32, EPI>), g, dim3(kThreads), 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_combine_epi(int epi, int nb, GemmParams p, hipStream_t s) {
+template <class T>
+hipError_t launch_combine_epi_t(int epi, int nb, GemmParams p, hipStream_t s) {
   const int S = 1 << p.ksplit_depth;
   switch (epi) {
-    case EPI_STORE: return launch_combine_epi_s<EPI_STORE>(S, nb, p, s);
-    case EPI_ACT: return launch_combine_epi_s<EPI_ACT>(S, nb, p, s);
-    case EPI_DSILU: return launch_combine_epi_s<EPI_DSILU>(S, nb, p, s);
-    case EPI_DX: return launch_combine_epi_s<EPI_DX>(S, nb, p, s);
+    case EPI_STORE: return launch_combine_epi_s<T, EPI_STORE>(S, nb, p, s);
+    case EPI_ACT: return launch_combine_epi_s<T, EPI_ACT>(S, nb, p, s);
+    case EPI_DSILU: return launch_combine_epi_s<T, EPI_DSILU>(S, nb, p, s);
+    case EPI_DX: return launch_combine_epi_s<T, EPI_DX>(S, nb, p, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_combine_epi(int epi, int nb, GemmParams p, hipStream_t s) {
+  if (p.fmt == FMT_F16) return launch_combine_epi_t<F16>(epi, nb, p, s);
+  return launch_combine_epi_t<Bf16>(epi, nb, p, s);
 }
 
 }  // namespace dgf

@@ -25,7 +25,7 @@ namespace dgf {
 
 // Every wave parks its subtree root in slot 0 of its own stack region; wave 0
 // then combines the WAVES roots with the balanced top of the tree.
-template <int NP, int WAVES>
+template <class T, int NP, int WAVES>
 __device__ __forceinline__ bool wg_combine(uint32_t (&root)[NP], uint32_t *stack_lds, int stack_words, int wave,
                                            int lane) {
   if constexpr (WAVES == 1) {
@@ -40,14 +40,14 @@ __device__ __forceinline__ bool wg_combine(uint32_t (&root)[NP], uint32_t *stack
     for (int w = 0; w < WAVES; ++w)
 #pragma unroll
       for (int p = 0; p < NP; ++p) r[w][p] = stack_lds[w * stack_words + p * 64 + lane];
-    combine_roots<NP, WAVES>(r);
+    combine_roots<T, NP, WAVES>(r);
 #pragma unroll
     for (int p = 0; p < NP; ++p) root[p] = r[0][p];
     return true;
   }
 }
 
-// Store 4 consecutive BF16 (two packed pairs) at C[m][n..n+3], bounds-checked.
+// Store 4 consecutive stored values (two packed pairs) at C[m][n..n+3], bounds-checked.
 __device__ __forceinline__ void store4(uint16_t *C, int64_t ldc, int64_t m, int64_t n, int64_t M, int64_t N,
                                        uint32_t p0, uint32_t p1) {
   if (m >= M) return;
@@ -68,8 +68,9 @@ constexpr int log2i() {
 }
 
 // Streamed-once weight fragment: a non-temporal 16-byte load.
-__device__ __forceinline__ bf16x8 load_frag_nt(const uint16_t *row, int64_t k) {
-  return __builtin_nontemporal_load(reinterpret_cast<const bf16x8 *>(row + k));
+template <class T>
+__device__ __forceinline__ typename T::frag load_frag_nt(const uint16_t *row, int64_t k) {
+  return __builtin_nontemporal_load(reinterpret_cast<const typename T::frag *>(row + k));
 }
 
 // ------------------------------------------------------------------ NT
@@ -81,7 +82,7 @@ __device__ __forceinline__ bf16x8 load_frag_nt(const uint16_t *row, int64_t k) {
 // ahead of the MFMAs that use them, both at the same distance: loads complete
 // in issue order, so an activation load issued after a weight load would
 // otherwise make the wait for it also wait for that younger weight load.
-template <int NB, int RT, int MT, int WAVES, int EPI>
+template <class T, int NB, int RT, int MT, int WAVES, int EPI>
 __global__ __launch_bounds__(WAVES * 64) void k_gemm_nt(GemmParams p) {
   constexpr bool SHARED_A = (EPI == EPI_ACT);  // gate and up share the activation operand
   constexpr int NA = SHARED_A ? 1 : NB;
@@ -122,8 +123,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_nt(GemmParams p) {
     for (int a = 0; a < NA; ++a) arow[a][t] = p.A[a] + m * p.lda[a] + 8 * g4;
   }
 
-  struct WF { bf16x8 v[NB][RT][2]; };
-  struct XF { bf16x8 v[NA][MT][2]; };
+  struct WF { typename T::frag v[NB][RT][2]; };
+  struct XF { typename T::frag v[NA][MT][2]; };
   auto load_w = [&](int leaf, WF &w) {
     const int64_t k = (int64_t)leaf * kLeaf;
 #pragma unroll
@@ -131,7 +132,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_nt(GemmParams p) {
 #pragma unroll
       for (int b = 0; b < NB; ++b)
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) w.v[b][rt][s] = load_frag_nt(brow[b][rt], k + 32 * s);
+        for (int rt = 0; rt < RT; ++rt) w.v[b][rt][s] = load_frag_nt<T>(brow[b][rt], k + 32 * s);
   };
   auto load_x = [&](int leaf, XF &x) {
     const int64_t k = (int64_t)leaf * kLeaf;
@@ -140,7 +141,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_nt(GemmParams p) {
 #pragma unroll
       for (int t = 0; t < MT; ++t)
 #pragma unroll
-        for (int s = 0; s < 2; ++s) x.v[a][t][s] = load_frag(arow[a][t], k + 32 * s);
+        for (int s = 0; s < 2; ++s) x.v[a][t][s] = load_frag<T>(arow[a][t], k + 32 * s);
   };
 
   TreeStack<NP> st{dyn_lds + wave * stack_words + lane};
@@ -158,10 +159,10 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_nt(GemmParams p) {
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
           const int q = ((b * RT + rt) * MT + t) * 2;
-          v[q + 0] = pack_rne(acc[b][rt][t][0], acc[b][rt][t][1]);
-          v[q + 1] = pack_rne(acc[b][rt][t][2], acc[b][rt][t][3]);
+          v[q + 0] = T::pack(acc[b][rt][t][0], acc[b][rt][t][1]);
+          v[q + 1] = T::pack(acc[b][rt][t][2], acc[b][rt][t][3]);
         }
-    tree_push<NP>(st, v, root, nl, j);
+    tree_push<T, NP>(st, v, root, nl, j);
   };
   auto leaf_mfma = [&](const WF &w, const XF &x, int j) {
     f32x4 acc[NB][RT][MT];
@@ -171,8 +172,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_nt(GemmParams p) {
       for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
-          acc[b][rt][t] = mfma16(w.v[b][rt][0], x.v[SHARED_A ? 0 : b][t][0], f32x4{0.f, 0.f, 0.f, 0.f});
-          acc[b][rt][t] = mfma16(w.v[b][rt][1], x.v[SHARED_A ? 0 : b][t][1], acc[b][rt][t]);
+          acc[b][rt][t] = T::mfma(w.v[b][rt][0], x.v[SHARED_A ? 0 : b][t][0], f32x4{0.f, 0.f, 0.f, 0.f});
+          acc[b][rt][t] = T::mfma(w.v[b][rt][1], x.v[SHARED_A ? 0 : b][t][1], acc[b][rt][t]);
         }
     finish_leaf(acc, j);
   };
@@ -222,24 +223,24 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_nt(GemmParams p) {
     for (int s = 0; s < 2; ++s) {
       if (kb + 32 * s >= p.K) break;
       const int64_t k = kb + 32 * s;
-      bf16x8 xf[NA][MT];
+      typename T::frag xf[NA][MT];
 #pragma unroll
       for (int a = 0; a < NA; ++a)
 #pragma unroll
-        for (int t = 0; t < MT; ++t) xf[a][t] = load_frag_tail(arow[a][t], k, p.K - 8 * g4);
+        for (int t = 0; t < MT; ++t) xf[a][t] = load_frag_tail<T>(arow[a][t], k, p.K - 8 * g4);
 #pragma unroll
       for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-          const bf16x8 wf = load_frag_tail(brow[b][rt], k, p.K - 8 * g4);
+          const typename T::frag wf = load_frag_tail<T>(brow[b][rt], k, p.K - 8 * g4);
 #pragma unroll
-          for (int t = 0; t < MT; ++t) acc[b][rt][t] = mfma16(wf, xf[SHARED_A ? 0 : b][t], acc[b][rt][t]);
+          for (int t = 0; t < MT; ++t) acc[b][rt][t] = T::mfma(wf, xf[SHARED_A ? 0 : b][t], acc[b][rt][t]);
         }
     }
     finish_leaf(acc, nl - 1);
   }
 
-  if (!wg_combine<NP, WAVES>(root, dyn_lds, stack_words, wave, lane)) return;
+  if (!wg_combine<T, NP, WAVES>(root, dyn_lds, stack_words, wave, lane)) return;
 
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
@@ -258,7 +259,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_nt(GemmParams p) {
             store4(p.C[b], p.ldc[b], m, n, p.M, p.N, root[q], root[q + 1]);
         }
       } else if constexpr (EPI == EPI_ACT) {
-        // gate (b = 0) and up (b = 1) of the same (m, n): a = bf16(silu(g) u)
+        // gate (b = 0) and up (b = 1) of the same (m, n): a = rnd(silu(g) u)
         const int qg = ((0 * RT + rt) * MT + t) * 2, qu = ((1 * RT + rt) * MT + t) * 2;
         uint32_t ap[2];
 #pragma unroll
@@ -267,12 +268,12 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_nt(GemmParams p) {
           float a2[2];
 #pragma unroll
           for (int e = 0; e < 2; ++e) {
-            const float g = e ? bf_hi(gp) : bf_lo(gp);
-            const float u = e ? bf_hi(up) : bf_lo(up);
+            const float g = e ? T::hi(gp) : T::lo(gp);
+            const float u = e ? T::hi(up) : T::lo(up);
             const float s = g * sigma_f(g);
             a2[e] = s * u;
           }
-          ap[h] = pack_rne(a2[0], a2[1]);
+          ap[h] = T::pack(a2[0], a2[1]);
         }
         store4(p.act_out, p.ld_act, m, n, p.M, p.N, ap[0], ap[1]);
         if (p.C[0]) store4(p.C[0], p.ldc[0], m, n, p.M, p.N, root[qg], root[qg + 1]);
@@ -294,7 +295,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_nt(GemmParams p) {
 // banks.
 __device__ __forceinline__ int slab_swz(int n) { return (n ^ (n >> 3)) & 7; }
 
-template <int NB, int RT, int MT, int WAVES, int EPI>
+template <class T, int NB, int RT, int MT, int WAVES, int EPI>
 __global__ __launch_bounds__(WAVES * 64) void k_gemm_nn(GemmParams p) {
   constexpr int NP = NB * RT * MT * 2;
   constexpr int DW = log2i<WAVES>();
@@ -368,7 +369,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_nn(GemmParams p) {
   for (int q = 0; q < NP; ++q) root[q] = 0;
 
   // activation fragments of one leaf (both K halves)
-  struct XF { bf16x8 v[NB][MT][2]; };
+  struct XF { typename T::frag v[NB][MT][2]; };
   auto load_x = [&](int leaf, XF &x) {
     const int64_t kb = (int64_t)leaf * kLeaf;
 #pragma unroll
@@ -376,7 +377,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_nn(GemmParams p) {
 #pragma unroll
       for (int t = 0; t < MT; ++t)
 #pragma unroll
-        for (int s = 0; s < 2; ++s) x.v[b][t][s] = load_frag(arow[b][t], kb + 32 * s + 8 * g4);
+        for (int s = 0; s < 2; ++s) x.v[b][t][s] = load_frag<T>(arow[b][t], kb + 32 * s + 8 * g4);
   };
   auto load_x_tail = [&](int leaf, XF &x) {
     const int64_t kb = (int64_t)leaf * kLeaf;
@@ -385,7 +386,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_nn(GemmParams p) {
 #pragma unroll
       for (int t = 0; t < MT; ++t)
 #pragma unroll
-        for (int s = 0; s < 2; ++s) x.v[b][t][s] = load_frag_tail(arow[b][t], kb + 32 * s + 8 * g4, p.K);
+        for (int s = 0; s < 2; ++s) x.v[b][t][s] = load_frag_tail<T>(arow[b][t], kb + 32 * s + 8 * g4, p.K);
   };
 
   // stage the slab transposed, two MFMA halves per column tile, then the tree
@@ -419,10 +420,10 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_nn(GemmParams p) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
           const int n = 16 * rt + r16;
-          const bf16x8 wf =
-              *reinterpret_cast<const bf16x8 *>(&slab[wave][b][n * 64 + 8 * ((4 * s + g4) ^ slab_swz(n))]);
+          const typename T::frag wf =
+              *reinterpret_cast<const typename T::frag *>(&slab[wave][b][n * 64 + 8 * ((4 * s + g4) ^ slab_swz(n))]);
 #pragma unroll
-          for (int t = 0; t < MT; ++t) acc[b][rt][t] = mfma16(wf, x.v[b][t][s], acc[b][rt][t]);
+          for (int t = 0; t < MT; ++t) acc[b][rt][t] = T::mfma(wf, x.v[b][t][s], acc[b][rt][t]);
         }
     }
     wave_lds_sync();  // slab reads done before the next leaf overwrites it
@@ -434,10 +435,10 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_nn(GemmParams p) {
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
           const int qi = ((b * RT + rt) * MT + t) * 2;
-          v[qi + 0] = pack_rne(acc[b][rt][t][0], acc[b][rt][t][1]);
-          v[qi + 1] = pack_rne(acc[b][rt][t][2], acc[b][rt][t][3]);
+          v[qi + 0] = T::pack(acc[b][rt][t][0], acc[b][rt][t][1]);
+          v[qi + 1] = T::pack(acc[b][rt][t][2], acc[b][rt][t][3]);
         }
-    tree_push<NP>(st, v, root, nl, j);
+    tree_push<T, NP>(st, v, root, nl, j);
   };
 
   if (full_n) {
@@ -486,7 +487,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_nn(GemmParams p) {
     leaf_body(nl - 1, q, x, true);
   }
 
-  if (!wg_combine<NP, WAVES>(root, dyn_lds, stack_words, wave, lane)) return;
+  if (!wg_combine<T, NP, WAVES>(root, dyn_lds, stack_words, wave, lane)) return;
 
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
@@ -505,8 +506,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_nn(GemmParams p) {
             store4(p.C[b], p.ldc[b], m, n, p.M, p.N, root[q], root[q + 1]);
         }
       } else if constexpr (EPI == EPI_DSILU) {
-        // dA at (m, n = i) with the saved g, u: dU = bf16(dA s), dG = bf16((dA u) s'),
-        // a = bf16(s u); written row-major [M, I].
+        // dA at (m, n = i) with the saved g, u: dU = rnd(dA s), dG = rnd((dA u) s'),
+        // a = rnd(s u); written row-major [M, I].
         if (m < p.M) {
           const int q = (rt * MT + t) * 2;
 #pragma unroll
@@ -514,19 +515,19 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_nn(GemmParams p) {
             const int64_t i = n + r;
             if (i >= p.N) break;
             const uint32_t pr = root[q + (r >> 1)];
-            const float da = (r & 1) ? bf_hi(pr) : bf_lo(pr);
-            const float g = bf2f(p.sg[m * p.ld_gu + i]);
-            const float u = bf2f(p.su[m * p.ld_gu + i]);
+            const float da = (r & 1) ? T::hi(pr) : T::lo(pr);
+            const float g = T::f(p.sg[m * p.ld_gu + i]);
+            const float u = T::f(p.su[m * p.ld_gu + i]);
             const float sg = sigma_f(g);
             const float s = g * sg;
             const float one_m = 1.0f - sg;
             const float tt = g * one_m;
             const float onep = 1.0f + tt;
             const float ds = sg * onep;
-            const uint16_t du = f2bf(da * s);
+            const uint16_t du = T::r(da * s);
             const float dau = da * u;
-            const uint16_t dg = f2bf(dau * ds);
-            const uint16_t a = f2bf(s * u);
+            const uint16_t dg = T::r(dau * ds);
+            const uint16_t a = T::r(s * u);
             if (p.dG) p.dG[m * p.ld_d + i] = dg;
             if (p.dU) p.dU[m * p.ld_d + i] = du;
             if (p.a_rm) p.a_rm[m * p.ld_d + i] = a;
@@ -539,15 +540,15 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_nn(GemmParams p) {
 
 // ------------------------------------------------------------------ one leaf
 
-// C_b[m][n] = bf16( leaf(A_b[m,:] . B[n,:]) ) for K <= 64: a single leaf, so
+// C_b[m][n] = rnd( leaf(A_b[m,:] . B[n,:]) ) for K <= 64: a single leaf, so
 // no tree node; this is the weight-gradient shape (K = tokens) and is bound by
 // its output writes.  A workgroup of 4 waves owns 64 m-rows x 128 n-columns;
 // wave w computes m-rows 16w..16w+15 against all 128 columns (the B fragments
-// are shared by the NB products), stages each 16 x 128 BF16 result in LDS and
+// are shared by the NB products), stages each 16 x 128 result in LDS and
 // stores it as whole 256-byte row segments.
 constexpr int kShortN = 128, kShortStride = kShortN + 8;
 
-template <int NB>
+template <class T, int NB>
 __global__ __launch_bounds__(256) void k_gemm_short(GemmParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t stage[4][16 * kShortStride];
   const int lane = threadIdx.x & 63;
@@ -575,14 +576,14 @@ __global__ __launch_bounds__(256) void k_gemm_short(GemmParams p) {
   for (int s = 0; s < 2; ++s) {
     if (32 * s >= p.K) break;  // all-zero block: the accumulator is unchanged
     const int64_t k = 32 * s + 8 * g4;
-    bf16x8 xa[NB];
+    typename T::frag xa[NB];
 #pragma unroll
-    for (int b = 0; b < NB; ++b) xa[b] = load_frag_tail(arow[b], k, p.K);
+    for (int b = 0; b < NB; ++b) xa[b] = load_frag_tail<T>(arow[b], k, p.K);
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      const bf16x8 w = load_frag_tail(brow[c], k, p.K);
+      const typename T::frag w = load_frag_tail<T>(brow[c], k, p.K);
 #pragma unroll
-      for (int b = 0; b < NB; ++b) acc[b][c] = mfma16(w, xa[b], acc[b][c]);
+      for (int b = 0; b < NB; ++b) acc[b][c] = T::mfma(w, xa[b], acc[b][c]);
     }
   }
 
@@ -592,7 +593,7 @@ __global__ __launch_bounds__(256) void k_gemm_short(GemmParams p) {
     // lane holds C[m0 + r16][n0 + 16c + 4 g4 + (0..3)]
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      const uint2 v = make_uint2(pack_rne(acc[b][c][0], acc[b][c][1]), pack_rne(acc[b][c][2], acc[b][c][3]));
+      const uint2 v = make_uint2(T::pack(acc[b][c][0], acc[b][c][1]), T::pack(acc[b][c][2], acc[b][c][3]));
       *reinterpret_cast<uint2 *>(&st[r16 * kShortStride + 16 * c + 4 * g4]) = v;
     }
     wave_lds_sync();
@@ -619,7 +620,7 @@ __global__ __launch_bounds__(256) void k_gemm_short(GemmParams p) {
 
 // ------------------------------------------------------------------ one leaf, TN
 
-// C_b[r][c] = bf16( leaf( sum_k A_b[k][r] B[k][c] ) ) for K <= 64, straight
+// C_b[r][c] = rnd( leaf( sum_k A_b[k][r] B[k][c] ) ) for K <= 64, straight
 // from row-major [k][features] operands: the weight gradients, k = tokens.
 // A workgroup of 4 waves owns 64 rows r and CT consecutive tiles of 128
 // columns c.  It copies the K x 64 A tile into LDS feature-major once, and
@@ -676,26 +677,26 @@ __device__ __forceinline__ void tn_put4x8(uint16_t *dst, int ks, int km, int k4,
 // The dX lanes' join (EPI_DX over 2^kd <= 8 K pieces) on the workgroups past
 // the weight-gradient tiles (grid rows gridDim.y - jrows ..): independent
 // work that fills the kernel's tail instead of a launch of its own.
-template <int S>
+template <class T, int S>
 __device__ void tn_dx_join(const GemmParams &j, int jrow, int jrows) {
   const int64_t chunks = (j.N + 7) / 8;
   const int64_t nthreads = (int64_t)jrows * gridDim.x * 256;
   for (int64_t i = ((int64_t)jrow * gridDim.x + blockIdx.x) * 256 + threadIdx.x; i < j.M * chunks; i += nthreads) {
     const int64_t m = i / chunks, c = (i % chunks) * 8;
-    join_epi_chunk<S, EPI_DX>(j, 0, m, c);
+    join_epi_chunk<T, S, EPI_DX>(j, 0, m, c);
   }
 }
 
-template <int NB>
+template <class T, int NB>
 __global__ __launch_bounds__(256) void k_gemm_tn1(GemmParams p, int ct, GemmParams jn, int jrows) {
   extern __shared__ __attribute__((aligned(16))) uint16_t tn_lds[];
   if (jrows > 0 && (int)blockIdx.y >= (int)gridDim.y - jrows) {
     const int jrow = (int)blockIdx.y - ((int)gridDim.y - jrows);
     switch (jn.ksplit_depth) {
-      case 0: tn_dx_join<1>(jn, jrow, jrows); break;
-      case 1: tn_dx_join<2>(jn, jrow, jrows); break;
-      case 2: tn_dx_join<4>(jn, jrow, jrows); break;
-      default: tn_dx_join<8>(jn, jrow, jrows); break;
+      case 0: tn_dx_join<T, 1>(jn, jrow, jrows); break;
+      case 1: tn_dx_join<T, 2>(jn, jrow, jrows); break;
+      case 2: tn_dx_join<T, 4>(jn, jrow, jrows); break;
+      default: tn_dx_join<T, 8>(jn, jrow, jrows); break;
     }
     return;
   }
@@ -755,17 +756,17 @@ __global__ __launch_bounds__(256) void k_gemm_tn1(GemmParams p, int ct, GemmPara
 #pragma unroll
       for (int t = 0; t < 8; ++t) acc[b][t] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int s = 0; s < KH; ++s) {
-      bf16x8 xa[NB];
+      typename T::frag xa[NB];
       const int ra = 16 * wave + r16;
 #pragma unroll
       for (int b = 0; b < NB; ++b)
-        xa[b] = *reinterpret_cast<const bf16x8 *>(&sA[(b * 64 + ra) * ks + 8 * ((4 * s + g4) ^ ((ra >> 3) & km))]);
+        xa[b] = *reinterpret_cast<const typename T::frag *>(&sA[(b * 64 + ra) * ks + 8 * ((4 * s + g4) ^ ((ra >> 3) & km))]);
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
         const int rb = 16 * t + r16;
-        const bf16x8 w = *reinterpret_cast<const bf16x8 *>(&sB[rb * ks + 8 * ((4 * s + g4) ^ ((rb >> 3) & km))]);
+        const typename T::frag w = *reinterpret_cast<const typename T::frag *>(&sB[rb * ks + 8 * ((4 * s + g4) ^ ((rb >> 3) & km))]);
 #pragma unroll
-        for (int b = 0; b < NB; ++b) acc[b][t] = mfma16(w, xa[b], acc[b][t]);
+        for (int b = 0; b < NB; ++b) acc[b][t] = T::mfma(w, xa[b], acc[b][t]);
       }
     }
 #pragma unroll
@@ -773,7 +774,7 @@ __global__ __launch_bounds__(256) void k_gemm_tn1(GemmParams p, int ct, GemmPara
       // lane holds C[m0 + r16][c0 + 16t + 4 g4 + (0..3)]
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        const uint2 v = make_uint2(pack_rne(acc[b][t][0], acc[b][t][1]), pack_rne(acc[b][t][2], acc[b][t][3]));
+        const uint2 v = make_uint2(T::pack(acc[b][t][0], acc[b][t][1]), T::pack(acc[b][t][2], acc[b][t][3]));
         *reinterpret_cast<uint2 *>(&stage[r16 * kShortStride + 16 * t + 4 * g4]) = v;
       }
       wave_lds_sync();
@@ -807,7 +808,8 @@ size_t tn1_lds_bytes(int nb, int64_t K) {
   return (size_t)(nb * 64 + 2 * kTnTile) * ks * 2 + (size_t)4 * 16 * kShortStride * 2;
 }
 
-hipError_t launch_gemm_tn1(int nb, GemmParams p, hipStream_t stream, const GemmParams *dx_join) {
+template <class T>
+hipError_t launch_gemm_tn1_t(int nb, GemmParams p, hipStream_t stream, const GemmParams *dx_join) {
   if (p.K < 0 || p.K > 64) return hipErrorInvalidValue;
   if (dx_join && dx_join->ksplit_depth > 3) return hipErrorInvalidValue;
   // column tiles per workgroup: as many as keep at least 3 workgroups per CU busy (the LDS of the
@@ -831,19 +833,31 @@ hipError_t launch_gemm_tn1(int nb, GemmParams p, hipStream_t stream, const GemmP
   dim3 grid((unsigned)gx, (unsigned)(tiles_r + jrows));
   const size_t shm = tn1_lds_bytes(nb, p.K);
   if (nb == 1)
-    dgf_launch((k_gemm_tn1<1>), grid, dim3(256), shm, stream, p, ct, jn, jrows);
+    dgf_launch((k_gemm_tn1<T, 1>), grid, dim3(256), shm, stream, p, ct, jn, jrows);
   else
-    dgf_launch((k_gemm_tn1<2>), grid, dim3(256), shm, stream, p, ct, jn, jrows);
+    dgf_launch((k_gemm_tn1<T, 2>), grid, dim3(256), shm, stream, p, ct, jn, jrows);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_tn1(int nb, GemmParams p, hipStream_t stream, const GemmParams *dx_join) {
+  if (dx_join && dx_join->fmt != p.fmt) return hipErrorInvalidValue;
+  if (p.fmt == FMT_F16) return launch_gemm_tn1_t<F16>(nb, p, stream, dx_join);
+  return launch_gemm_tn1_t<Bf16>(nb, p, stream, dx_join);
+}
+
+template <class T>
+hipError_t launch_gemm_short_t(int nb, GemmParams p, hipStream_t stream) {
+  dim3 grid((unsigned)((p.N + kShortN - 1) / kShortN), (unsigned)((p.M + 63) / 64));
+  if (nb == 1)
+    dgf_launch((k_gemm_short<T, 1>), grid, dim3(256), 0, stream, p);
+  else
+    dgf_launch((k_gemm_short<T, 2>), grid, dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_short(int nb, GemmParams p, hipStream_t stream) {
-  dim3 grid((unsigned)((p.N + kShortN - 1) / kShortN), (unsigned)((p.M + 63) / 64));
-  if (nb == 1)
-    dgf_launch((k_gemm_short<1>), grid, dim3(256), 0, stream, p);
-  else
-    dgf_launch((k_gemm_short<2>), grid, dim3(256), 0, stream, p);
-  return hipGetLastError();
+  if (p.fmt == FMT_F16) return launch_gemm_short_t<F16>(nb, p, stream);
+  return launch_gemm_short_t<Bf16>(nb, p, stream);
 }
 
 // ------------------------------------------------------------------ launch
@@ -852,9 +866,9 @@ hipError_t launch_gemm_short(int nb, GemmParams p, hipStream_t stream) {
   {                                                                                                         \
     const size_t shm = (size_t)waves * p.stack_slots * (NB * RT * MT * 2) * 64 * 4;                         \
     switch (waves) {                                                                                        \
-      case 1: dgf_launch((KERNEL<NB, RT, MT, 1, EPI>), grid, dim3(64), shm, stream, p); break;      \
-      case 2: dgf_launch((KERNEL<NB, RT, MT, 2, EPI>), grid, dim3(128), shm, stream, p); break;     \
-      default: dgf_launch((KERNEL<NB, RT, MT, 4, EPI>), grid, dim3(256), shm, stream, p); break;    \
+      case 1: dgf_launch((KERNEL<T, NB, RT, MT, 1, EPI>), grid, dim3(64), shm, stream, p); break;   \
+      case 2: dgf_launch((KERNEL<T, NB, RT, MT, 2, EPI>), grid, dim3(128), shm, stream, p); break;  \
+      default: dgf_launch((KERNEL<T, NB, RT, MT, 4, EPI>), grid, dim3(256), shm, stream, p); break; \
     }                                                                                                       \
   }
 
@@ -869,7 +883,8 @@ int gemm_row_tiles(int layout, int nb, int epi) {
   return epi == EPI_DSILU ? 2 : 4;
 }
 
-hipError_t launch_gemm(int layout, int nb, int epi, GemmParams p, int waves, hipStream_t stream) {
+template <class T>
+hipError_t launch_gemm_t(int layout, int nb, int epi, GemmParams p, int waves, hipStream_t stream) {
   const int mt = p.M <= 16 ? 1 : 2;
   const int rt = gemm_row_tiles(layout, nb, epi);
   const int64_t tiles_n = (p.N + 16 * rt - 1) / (16 * rt);
@@ -886,6 +901,11 @@ hipError_t launch_gemm(int layout, int nb, int epi, GemmParams p, int waves, hip
     else return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_gemm(int layout, int nb, int epi, GemmParams p, int waves, hipStream_t stream) {
+  if (p.fmt == FMT_F16) return launch_gemm_t<F16>(layout, nb, epi, p, waves, stream);
+  return launch_gemm_t<Bf16>(layout, nb, epi, p, waves, stream);
 }
 
 }  // namespace dgf

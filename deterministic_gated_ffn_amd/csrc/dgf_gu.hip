@@ -1,7 +1,7 @@
 // Fused gate/up projection and activation for few tokens (gfx950).
 //
-// a[m][n] = bf16( silu(g) u ) with g = T_K(x[m,:] . W_gate[n,:]) and
-// u = T_K(x[m,:] . W_up[n,:]), both rounded to BF16 (the stage boundaries of
+// a[m][n] = rnd( silu(g) u ) with g = T_K(x[m,:] . W_gate[n,:]) and
+// u = T_K(x[m,:] . W_up[n,:]), both rounded to the stored type (the stage boundaries of
 // RL-Kernel PR #325, sections "Design" and "Operator test matrix").
 //
 // One workgroup of 8 waves owns whole output tiles of 16 columns and all K:
@@ -47,9 +47,9 @@ struct GuLds {
   static constexpr size_t total = roots_bytes + kGuWaves * (x_bytes + slab_bytes);
 };
 
-template <int MT>
+template <class T, int MT>
 struct GuWave {
-  static constexpr int NP = MT * 2;  // packed BF16 pairs per lane: index 2 t + h
+  static constexpr int NP = MT * 2;  // packed pairs of stored values per lane: index 2 t + h
   static constexpr int NR = nr_of<MT>();
   struct WF {
     u32x4 v[2];  // rows 8 i2 + lane / 8 of the tile, 16-byte K chunk lane % 8 of the leaf
@@ -62,10 +62,10 @@ struct GuWave {
   int wave, lane, r16, g4;
   int lo;
   int64_t m0;
-  int t0, ts, T;  // tiles t0 + i ts, i < T
+  int t0, ts, ntl;  // tiles t0 + i ts, i < ntl
   int64_t wbytes[2];
 
-  __device__ __forceinline__ int64_t col0(int i) const { return (int64_t)(t0 + (i < T ? i : T - 1) * ts) * kGuCols; }
+  __device__ __forceinline__ int64_t col0(int i) const { return (int64_t)(t0 + (i < ntl ? i : ntl - 1) * ts) * kGuCols; }
 
   // Weight unit (tile i, product b, leaf lo + j): 16 rows x 128 bytes.  Rows
   // past N read as zero (range check of the rebased descriptor), and so does
@@ -73,7 +73,7 @@ struct GuWave {
   // no memory request at all).
   __device__ __forceinline__ void load_unit(int i, int b, int j, WF &w, const uint32_t (&voff)[2][2]) const {
     const int64_t base = (col0(i) * p.ldw[b] + (int64_t)(lo + j) * kLeaf) * 2;
-    const int64_t left = i < T ? wbytes[b] - base : 0;
+    const int64_t left = i < ntl ? wbytes[b] - base : 0;
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         (void *)((const char *)p.w[b] + base), (short)0,
         (int)(left > 0 ? (left < 0x7fffffff ? left : 0x7fffffff) : 0), 0x00020000);
@@ -84,16 +84,16 @@ struct GuWave {
 
   // Leaf J of product b: the 16 weight rows through the slab (row r's chunk c
   // at r*64 + 8 (c ^ (r & 7)): conflict-free row writes and MFMA-layout
-  // reads), two MFMAs per token tile from a zero accumulator, packed to BF16.
+  // reads), two MFMAs per token tile from a zero accumulator, rounded and packed.
   template <int J>
-  __device__ __forceinline__ void leaf(const WF &w, const bf16x8 (&xr)[NR][MT][2], uint32_t (&v)[NP]) const {
+  __device__ __forceinline__ void leaf(const WF &w, const typename T::frag (&xr)[NR][MT][2], uint32_t (&v)[NP]) const {
     const int wr = lane >> 3, wc = lane & 7;
 #pragma unroll
     for (int i2 = 0; i2 < 2; ++i2) *reinterpret_cast<u32x4 *>(&slab[(8 * i2 + wr) * 64 + 8 * (wc ^ wr)]) = w.v[i2];
     wave_lds_sync();
-    const bf16x8 w0 = *reinterpret_cast<const bf16x8 *>(&slab[r16 * 64 + 8 * ((0 + g4) ^ (r16 & 7))]);
-    const bf16x8 w1 = *reinterpret_cast<const bf16x8 *>(&slab[r16 * 64 + 8 * ((4 + g4) ^ (r16 & 7))]);
-    bf16x8 xf[MT][2];
+    const typename T::frag w0 = *reinterpret_cast<const typename T::frag *>(&slab[r16 * 64 + 8 * ((0 + g4) ^ (r16 & 7))]);
+    const typename T::frag w1 = *reinterpret_cast<const typename T::frag *>(&slab[r16 * 64 + 8 * ((4 + g4) ^ (r16 & 7))]);
+    typename T::frag xf[MT][2];
 #pragma unroll
     for (int t = 0; t < MT; ++t)
 #pragma unroll
@@ -101,19 +101,19 @@ struct GuWave {
         if constexpr (J < NR)
           xf[t][s] = xr[J][t][s];
         else
-          xf[t][s] = __builtin_bit_cast(bf16x8, xl[((J - NR) * MT + t) * 2 * 64 + s * 64 + lane]);
+          xf[t][s] = __builtin_bit_cast(typename T::frag, xl[((J - NR) * MT + t) * 2 * 64 + s * 64 + lane]);
       }
     f32x4 acc[MT];
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
-      acc[t] = mfma16(w0, xf[t][0], f32x4{0.f, 0.f, 0.f, 0.f});
-      acc[t] = mfma16(w1, xf[t][1], acc[t]);
+      acc[t] = T::mfma(w0, xf[t][0], f32x4{0.f, 0.f, 0.f, 0.f});
+      acc[t] = T::mfma(w1, xf[t][1], acc[t]);
     }
     wave_lds_sync();  // slab reads done before the next unit overwrites it
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
-      v[2 * t + 0] = pack_rne(acc[t][0], acc[t][1]);
-      v[2 * t + 1] = pack_rne(acc[t][2], acc[t][3]);
+      v[2 * t + 0] = T::pack(acc[t][0], acc[t][1]);
+      v[2 * t + 1] = T::pack(acc[t][2], acc[t][3]);
     }
   }
 
@@ -122,7 +122,7 @@ struct GuWave {
   // slot 0); each unit first issues the loads of the unit PR - 1 ahead
   // (possibly of the next tile) into the slot the previous unit freed.
   template <int NL, int PR, int U>
-  __device__ __forceinline__ void units(int i, WF (&ring)[PR], const bf16x8 (&xr)[NR][MT][2], uint32_t (&v)[NP],
+  __device__ __forceinline__ void units(int i, WF (&ring)[PR], const typename T::frag (&xr)[NR][MT][2], uint32_t (&v)[NP],
                                         uint32_t (&st)[3][NP], uint32_t (&rg)[NP], const uint32_t (&voff)[2][2]) const {
     constexpr int UN = 2 * NL;
     if constexpr (U < UN) {
@@ -131,7 +131,7 @@ struct GuWave {
       load_unit(i + nx / UN, nu / NL, nu % NL, ring[nx % PR], voff);
       __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of this unit's MFMAs
       leaf<J>(ring[U % PR], xr, v);
-      push_leaf<NP, NL, J>(v, st);
+      push_leaf<T, NP, NL, J>(v, st);
       if constexpr (J == NL - 1 && b == 0) {
 #pragma unroll
         for (int q = 0; q < NP; ++q) rg[q] = v[q];
@@ -161,15 +161,15 @@ struct GuWave {
         uint32_t r[kGuWaves];
 #pragma unroll
         for (int w2 = 0; w2 < kGuWaves; ++w2) r[w2] = buf[((b * kGuWaves + w2) * NP + 2 * t + h) * 64 + lane];
-        o[b][h] = node2(node2(node2(r[0], r[1]), node2(r[2], r[3])), node2(node2(r[4], r[5]), node2(r[6], r[7])));
+        o[b][h] = node2t<T>(node2t<T>(node2t<T>(r[0], r[1]), node2t<T>(r[2], r[3])), node2t<T>(node2t<T>(r[4], r[5]), node2t<T>(r[6], r[7])));
       }
     uint32_t av[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const float ga = bf_lo(o[0][h]), gb = bf_hi(o[0][h]);
-      const float ua = bf_lo(o[1][h]), ub = bf_hi(o[1][h]);
+      const float ga = T::lo(o[0][h]), gb = T::hi(o[0][h]);
+      const float ua = T::lo(o[1][h]), ub = T::hi(o[1][h]);
       const float sa = ga * sigma_f(ga), sb = gb * sigma_f(gb);
-      av[h] = pack_rne(sa * ua, sb * ub);
+      av[h] = T::pack(sa * ua, sb * ub);
     }
     const int64_t m = m0 + 16 * t + r16, n = col0(i) + 4 * g4;
     if (m >= p.M || n >= p.N) return;
@@ -191,7 +191,7 @@ struct GuWave {
 
   template <int NL>
   __device__ __forceinline__ void run() const {
-    if (T <= 0) return;
+    if (ntl <= 0) return;
     // the first weight units go out before the activation loads: the stream
     // starts while the activations arrive
     uint32_t voff[2][2];
@@ -211,7 +211,7 @@ struct GuWave {
     // by one instruction, and rearranged into the MFMA layout through the
     // wave's slab, as the weight units are.  Fragment-layout loads would
     // split every line over two instructions.
-    bf16x8 xr[NR][MT][2];
+    typename T::frag xr[NR][MT][2];
     u32x4 raw[NL][MT][2];
 #pragma unroll
     for (int t = 0; t < MT; ++t)
@@ -221,7 +221,7 @@ struct GuWave {
         const uint16_t *row = p.x + (r < p.M ? r : p.M - 1) * p.ldx + 8 * (lane & 7);
 #pragma unroll
         for (int j = 0; j < NL; ++j)
-          raw[j][t][s] = __builtin_bit_cast(u32x4, load_frag(row, (int64_t)(lo + j) * kLeaf));
+          raw[j][t][s] = __builtin_bit_cast(u32x4, load_frag<T>(row, (int64_t)(lo + j) * kLeaf));
       }
     const int wr = lane >> 3, wc = lane & 7;
 #pragma unroll
@@ -233,7 +233,7 @@ struct GuWave {
         wave_lds_sync();
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-          const bf16x8 f = *reinterpret_cast<const bf16x8 *>(&slab[r16 * 64 + 8 * ((4 * s + g4) ^ (r16 & 7))]);
+          const typename T::frag f = *reinterpret_cast<const typename T::frag *>(&slab[r16 * 64 + 8 * ((4 * s + g4) ^ (r16 & 7))]);
           if (j < NR)
             xr[j < NR ? j : 0][t][s] = f;
           else
@@ -242,7 +242,7 @@ struct GuWave {
         wave_lds_sync();  // the slab's reads are done before it is rewritten
       }
     wave_lds_sync();
-    for (int i = 0; i < T; ++i) {
+    for (int i = 0; i < ntl; ++i) {
       uint32_t v[NP], st[3][NP], rg[NP];
       units<NL, PR, 0>(i, ring, xr, v, st, rg, voff);
       finish_tile(i, rg, v);
@@ -250,10 +250,10 @@ struct GuWave {
   }
 };
 
-template <int MT>
+template <class T, int MT>
 __global__ __launch_bounds__(kGuWaves * 64) void k_gate_up_act(GuParams p) {
   extern __shared__ __attribute__((aligned(16))) uint32_t gu_lds[];
-  using Wv = GuWave<MT>;
+  using Wv = GuWave<T, MT>;
   using Lay = GuLds<MT>;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -265,7 +265,7 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_gate_up_act(GuParams p) {
   // four pieces of a 64-column output line reach one L2 at about one time
   const int G = (int)gridDim.x;
   const int t0 = xcd_tile((int)blockIdx.x, G);
-  const int T = t0 < tiles_n ? (tiles_n - t0 + G - 1) / G : 0;
+  const int ntl = t0 < tiles_n ? (tiles_n - t0 + G - 1) / G : 0;
   char *base = reinterpret_cast<char *>(gu_lds) + Lay::roots_bytes + (size_t)wave * (Lay::x_bytes + Lay::slab_bytes);
   Wv w{p,
        gu_lds,
@@ -279,7 +279,7 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_gate_up_act(GuParams p) {
        (int64_t)blockIdx.y * 16 * MT,
        t0,
        G,
-       T,
+       ntl,
        {p.N * p.ldw[0] * 2, p.N * p.ldw[1] * 2}};
   switch (hi - lo) {  // 1..8 by the launch conditions (8 <= L <= 64)
     case 1: w.template run<1>(); break;
@@ -300,7 +300,8 @@ bool gu_act_applies(int64_t M, int64_t N, int64_t K) {
   return M >= 1 && M <= 32 && N >= 1 && K % kLeaf == 0 && L >= kGuWaves && L <= kGuWaves * kGuMaxNL;
 }
 
-hipError_t launch_gu_act(const GuParams &p, hipStream_t stream) {
+template <class T>
+hipError_t launch_gu_act_t(const GuParams &p, hipStream_t stream) {
   const int mt = p.M <= 16 ? 1 : 2;
   const int64_t tiles_n = (p.N + kGuCols - 1) / kGuCols;
   // one wave of workgroups over the 256 CUs (one workgroup per CU by LDS);
@@ -309,10 +310,15 @@ hipError_t launch_gu_act(const GuParams &p, hipStream_t stream) {
   const int64_t groups = (tiles_n + per - 1) / per;
   const dim3 grid((unsigned)groups, 1u), block(kGuWaves * 64);
   if (mt == 1)
-    dgf_launch(k_gate_up_act<1>, grid, block, GuLds<1>::total, stream, p);
+    dgf_launch(k_gate_up_act<T, 1>, grid, block, GuLds<1>::total, stream, p);
   else
-    dgf_launch(k_gate_up_act<2>, grid, block, GuLds<2>::total, stream, p);
+    dgf_launch(k_gate_up_act<T, 2>, grid, block, GuLds<2>::total, stream, p);
   return hipGetLastError();
+}
+
+hipError_t launch_gu_act(const GuParams &p, hipStream_t stream) {
+  if (p.fmt == FMT_F16) return launch_gu_act_t<F16>(p, stream);
+  return launch_gu_act_t<Bf16>(p, stream);
 }
 
 }  // namespace dgf

@@ -26,6 +26,8 @@ inline void dgf_launch(F kernel, dim3 grid, dim3 block, size_t shm, hipStream_t 
 }
 
 enum { DGF_LAYOUT_NT = 0, DGF_LAYOUT_NN = 1, DGF_LAYOUT_TN = 2 };
+// stored type of every 16-bit tensor of a launch (the public dtype codes)
+enum { FMT_BF16 = 0, FMT_F16 = 1 };
 enum { EPI_STORE = 0, EPI_ACT = 1, EPI_DSILU = 2, EPI_DX = 3 };
 
 // Arguments of one tree-GEMM launch (two products when NB = 2).
@@ -37,6 +39,7 @@ struct GemmParams {
   uint16_t *C[2];        // [M, N] outputs (EPI_STORE; optional g/u or lanes otherwise)
   int64_t ldc[2];
   int64_t M, N, K;
+  int fmt;               // stored type: FMT_BF16 or FMT_F16
   int L;                 // leaves = ceil(K / 64)
   int stack_slots;       // LDS tree-stack slots per wave (>= 1, >= a wave subtree's depth)
   int ksplit_depth;      // the K leaves are split over 2^ksplit_depth workgroups (grid.z)
@@ -84,6 +87,7 @@ struct GuParams {
   uint16_t *g, *u;
   int64_t ldgu;
   int64_t M, N, K;
+  int fmt;
   int L;
 };
 bool gu_act_applies(int64_t M, int64_t N, int64_t K);
@@ -101,6 +105,7 @@ struct AllkParams {
   uint16_t *C;
   int64_t ldc;
   int64_t M, N, K;
+  int fmt;
   int L;
 };
 bool allk_applies(int64_t M, int64_t N, int64_t K);
@@ -124,19 +129,20 @@ hipError_t launch_gemm_short(int nb, GemmParams p, hipStream_t stream);
 // same launch; it shares no memory with the weight gradients.
 hipError_t launch_gemm_tn1(int nb, GemmParams p, hipStream_t stream, const GemmParams *dx_join = nullptr);
 
-hipError_t launch_act_fwd(const uint16_t *g, const uint16_t *u, uint16_t *a, int64_t n, hipStream_t s);
-hipError_t launch_act_bwd(const uint16_t *da, const uint16_t *g, const uint16_t *u, uint16_t *dg, uint16_t *du,
-                          uint16_t *a, int64_t n, hipStream_t s);
+// elementwise launches take the stored type first (FMT_BF16 or FMT_F16)
+hipError_t launch_act_fwd(int fmt, const uint16_t *g, const uint16_t *u, uint16_t *a, int64_t n, hipStream_t s);
+hipError_t launch_act_bwd(int fmt, const uint16_t *da, const uint16_t *g, const uint16_t *u, uint16_t *dg,
+                          uint16_t *du, uint16_t *a, int64_t n, hipStream_t s);
 hipError_t launch_combine(const uint16_t *const *parts, int S, uint16_t *out, int64_t n, hipStream_t s);
 // the same rank tree for BF16, FP16 or FP32 parts (dtype one of DGF_COMBINE_*)
 enum { DGF_COMBINE_BF16 = 0, DGF_COMBINE_FP16 = 1, DGF_COMBINE_FP32 = 2 };
 hipError_t launch_combine_typed(const void *const *parts, int S, void *out, int64_t n, int dtype, hipStream_t s);
 // out [M, N] (ldo) = balanced combine over S partials part[s] [M, N] (ldp),
 // part[s] = part + s * part_stride
-hipError_t launch_combine_2d(const uint16_t *part, int64_t part_stride, int64_t ldp, int S, uint16_t *out, int64_t ldo,
-                             int64_t M, int64_t N, hipStream_t s);
-// dx [M, N] = bf16(G + U) per element (the gate lane first), row-major with leading dims
-hipError_t launch_add_lanes(const uint16_t *G, int64_t ldg, const uint16_t *U, int64_t ldu, uint16_t *dx,
+hipError_t launch_combine_2d(int fmt, const uint16_t *part, int64_t part_stride, int64_t ldp, int S, uint16_t *out,
+                             int64_t ldo, int64_t M, int64_t N, hipStream_t s);
+// dx [M, N] = rnd(G + U) per element (the gate lane first), row-major with leading dims
+hipError_t launch_add_lanes(int fmt, const uint16_t *G, int64_t ldg, const uint16_t *U, int64_t ldu, uint16_t *dx,
                             int64_t lddx, int64_t M, int64_t N, hipStream_t s);
 // dst [C, R] (ldd) = transpose of src [R, C] (lds)
 hipError_t launch_transpose(const uint16_t *src, int64_t lds, int64_t R, int64_t C, uint16_t *dst, int64_t ldd,

@@ -2,8 +2,8 @@
 //
 // C_b[m][n] = T_K( A_b[m,:] . B_b[n,:] ): A_b [M, K] and B_b [N, K] both
 // K-contiguous, the canonical tree over K of RL-Kernel PR #325, section
-// "Design" (64-element FP32 leaves rounded to BF16, midpoint nodes adding BF16
-// children in FP32).  This is the compute-bound shape: thousands of tokens, so
+// "Design" (64-element FP32 leaves rounded to the stored type, BF16 or FP16,
+// midpoint nodes adding two stored children in FP32).  This is the compute-bound shape: thousands of tokens, so
 // the weights are reused across many token rows and the kernel is organised
 // around MFMA throughput rather than weight streaming.
 //
@@ -41,43 +41,27 @@ constexpr int kMmWaves = 8;
 constexpr int kMmBM = 128, kMmBN = 128;  // workgroup tile: tokens x outputs
 constexpr int kMmTM = 2, kMmTN = 4;      // a wave's 16 x 16 tiles: 32 tokens x 64 outputs
 constexpr int kMmNV = kMmTM * kMmTN * 4;  // tree values per lane: index (tn TM + tm) 4 + e
-constexpr int kMmNP = kMmNV / 2;          // the same as packed BF16 pairs (parked levels)
+constexpr int kMmNP = kMmNV / 2;          // the same as packed pairs (parked levels)
 constexpr size_t kMmStage = (size_t)(kMmBM + kMmBN) * 64 * 2;  // A then B tile of one leaf (bytes)
 // Leaves per lower subtree, at most: their pending values stay in registers.
 constexpr int kMmMaxNL = 4;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// BF16 rounding (nearest even) of x, kept in FP32 format: the BF16 value in
-// the high half and zeros below, one v_cvt_pk_bf16_f32 with a zero partner.
-// Tree values stay in this form, so a node is one FP32 add and one rounding.
-__device__ __forceinline__ float rbf(float x) {
-  const f32x2 v = {0.f, x};
-  return __builtin_bit_cast(float, __builtin_convertvector(v, bf16x2));
-}
-
-// The high halves of two FP32-form BF16 values as one packed pair (lo, hi).
-__device__ __forceinline__ uint32_t pack_hi(float lo, float hi) {
-  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
-}
-
-// An empty instruction that "defines" each value, ordered with the
-// surrounding scheduling barriers: the values are computed before it.
-__device__ __forceinline__ void pin(float (&v)[kMmNV]) {
-#pragma unroll
-  for (int q = 0; q < kMmNV; ++q) asm volatile("" : "+v"(v[q]));
-}
+// Tree values stay in FP32 form: the stored type's rounding kept as an FP32
+// value (T::rf; for BF16 one v_cvt_pk_bf16_f32 with a zero partner), so a node
+// is one FP32 add and one rounding; T::pack_x packs two such values.
 
 // Feed leaf J (values v, FP32 form) of an N-leaf lower subtree (N <= 4):
 // merge it with the pending left siblings its position closes, then park it
 // at its depth; after the last leaf v is the subtree root.
-template <int N, int J>
+template <class T, int N, int J>
 __device__ __forceinline__ void push_f(float (&v)[kMmNV], float (&st)[2][kMmNV]) {
   constexpr LeafPos lp = leaf_pos(N, J);
 #pragma unroll
   for (int t = 0; t < lp.m; ++t)
 #pragma unroll
-    for (int q = 0; q < kMmNV; ++q) v[q] = rbf(st[lp.D - 1 - t][q] + v[q]);
+    for (int q = 0; q < kMmNV; ++q) v[q] = T::rf(st[lp.D - 1 - t][q] + v[q]);
   constexpr int d = lp.D - lp.m;
   if constexpr (d > 0) {
 #pragma unroll
@@ -88,7 +72,7 @@ __device__ __forceinline__ void push_f(float (&v)[kMmNV], float (&st)[2][kMmNV])
 // TAIL: K is not a whole number of leaves (the last leaf is partial and
 // loads element by element); otherwise every leaf takes the buffer path and
 // the leaf sequence has no branches.
-template <bool TAIL>
+template <class T, bool TAIL>
 struct MmWg {
   const GemmParams &p;
   uint16_t *lds;  // [2 stages][A 128 x 64 | B 128 x 64], then the waves' top-level stacks
@@ -127,8 +111,8 @@ struct MmWg {
       const int q = tid + 512 * i, row = q >> 3, kc = q & 7;
       const int64_t k = kb + 8 * kc;
       const int64_t m = m0 + row, n = n0 + row;
-      g[i] = m < p.M ? __builtin_bit_cast(u32x4, load_frag_tail(A + m * lda, k, p.K)) : u32x4{0u, 0u, 0u, 0u};
-      g[2 + i] = n < p.N ? __builtin_bit_cast(u32x4, load_frag_tail(B + n * ldb, k, p.K)) : u32x4{0u, 0u, 0u, 0u};
+      g[i] = m < p.M ? __builtin_bit_cast(u32x4, load_frag_tail<T>(A + m * lda, k, p.K)) : u32x4{0u, 0u, 0u, 0u};
+      g[2 + i] = n < p.N ? __builtin_bit_cast(u32x4, load_frag_tail<T>(B + n * ldb, k, p.K)) : u32x4{0u, 0u, 0u, 0u};
     }
   }
 
@@ -145,17 +129,17 @@ struct MmWg {
   // The MFMA fragments of K half H of the leaf in stage s: this wave's 2 A
   // and 4 B tiles.
   template <int H>
-  __device__ __forceinline__ void frags(const uint16_t *sa, const uint16_t *sb, bf16x8 (&af)[kMmTM],
-                                        bf16x8 (&bf)[kMmTN]) const {
+  __device__ __forceinline__ void frags(const uint16_t *sa, const uint16_t *sb, typename T::frag (&af)[kMmTM],
+                                        typename T::frag (&bf)[kMmTN]) const {
 #pragma unroll
     for (int t = 0; t < kMmTM; ++t) {
       const int row = 32 * wm + 16 * t + r16;
-      af[t] = *reinterpret_cast<const bf16x8 *>(&sa[row * 64 + 8 * ((4 * H + g4) ^ (r16 & 7))]);
+      af[t] = *reinterpret_cast<const typename T::frag *>(&sa[row * 64 + 8 * ((4 * H + g4) ^ (r16 & 7))]);
     }
 #pragma unroll
     for (int t = 0; t < kMmTN; ++t) {
       const int row = 64 * wn + 16 * t + r16;
-      bf[t] = *reinterpret_cast<const bf16x8 *>(&sb[row * 64 + 8 * ((4 * H + g4) ^ (r16 & 7))]);
+      bf[t] = *reinterpret_cast<const typename T::frag *>(&sb[row * 64 + 8 * ((4 * H + g4) ^ (r16 & 7))]);
     }
   }
 
@@ -163,27 +147,27 @@ struct MmWg {
   // accumulator (K 0..31, then 32..63).
   __device__ __forceinline__ void leaf_mfma(int s, f32x4 (&acc)[kMmTN][kMmTM]) const {
     const uint16_t *sa = lds + (size_t)s * (kMmStage / 2), *sb = sa + kMmBM * 64;
-    bf16x8 af0[kMmTM], bf0[kMmTN], af1[kMmTM], bf1[kMmTN];
+    typename T::frag af0[kMmTM], bf0[kMmTN], af1[kMmTM], bf1[kMmTN];
     frags<0>(sa, sb, af0, bf0);
     frags<1>(sa, sb, af1, bf1);
 #pragma unroll
     for (int tn = 0; tn < kMmTN; ++tn)
 #pragma unroll
-      for (int tm = 0; tm < kMmTM; ++tm) acc[tn][tm] = mfma16(bf0[tn], af0[tm], f32x4{0.f, 0.f, 0.f, 0.f});
+      for (int tm = 0; tm < kMmTM; ++tm) acc[tn][tm] = T::mfma(bf0[tn], af0[tm], f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
     for (int tn = 0; tn < kMmTN; ++tn)
 #pragma unroll
-      for (int tm = 0; tm < kMmTM; ++tm) acc[tn][tm] = mfma16(bf1[tn], af1[tm], acc[tn][tm]);
+      for (int tm = 0; tm < kMmTM; ++tm) acc[tn][tm] = T::mfma(bf1[tn], af1[tm], acc[tn][tm]);
   }
 
-  // A leaf's accumulators rounded to BF16, FP32 form.
+  // A leaf's accumulators rounded to the stored type, FP32 form.
   __device__ __forceinline__ void round_leaf(const f32x4 (&acc)[kMmTN][kMmTM], float (&v)[kMmNV]) const {
 #pragma unroll
     for (int tn = 0; tn < kMmTN; ++tn)
 #pragma unroll
       for (int tm = 0; tm < kMmTM; ++tm)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[(tn * kMmTM + tm) * 4 + e] = rbf(acc[tn][tm][e]);
+        for (int e = 0; e < 4; ++e) v[(tn * kMmTM + tm) * 4 + e] = T::rf(acc[tn][tm][e]);
   }
 
   // Leaf j (leaf J of a lower subtree of NL leaves) from stage s into acc, in
@@ -201,7 +185,7 @@ struct MmWg {
     leaf_mfma(s, acc);
     if constexpr (J > 0) {
       round_leaf(prev, v);
-      push_f<NL, J - 1>(v, st);
+      push_f<T, NL, J - 1>(v, st);
     }
     // past the piece's last leaf the stage store writes a stage nobody reads
     // and the fetch requests nothing, so the leaf sequence needs no branch
@@ -236,7 +220,7 @@ struct MmWg {
       leaves<NL, J + 1, P0>(j + 1, r0, r1, acc, prev, v, st);
     } else {
       round_leaf(prev, v);
-      push_f<NL, NL - 1>(v, st);  // the subtree's last leaf: v becomes its root
+      push_f<T, NL, NL - 1>(v, st);  // the subtree's last leaf: v becomes its root
     }
   }
 
@@ -258,7 +242,7 @@ struct MmWg {
         const int64_t m = m0 + 32 * wm + 16 * tm + r16, n = n0 + 64 * wn + 16 * tn + 4 * g4;
         if (m >= p.M || n >= p.N) continue;
         const int i = (tn * kMmTM + tm) * 4;
-        const uint32_t lo2 = pack_hi(v[i], v[i + 1]), hi2 = pack_hi(v[i + 2], v[i + 3]);
+        const uint32_t lo2 = T::pack_x(v[i], v[i + 1]), hi2 = T::pack_x(v[i + 2], v[i + 3]);
         uint16_t *dst = out + m * ldo + n;
         if (n + 3 < p.N) {
           *reinterpret_cast<uint2 *>(dst) = make_uint2(lo2, hi2);
@@ -273,24 +257,26 @@ struct MmWg {
 };
 
 // Pending left subtrees of the top levels, in this wave's own LDS region as
-// packed BF16 pairs: level t, pair q of lane l at base[(t kMmNP + q) 64 + l]
+// packed pairs of stored values: level t, pair q of lane l at base[(t kMmNP + q) 64 + l]
 // (each lane reads back only what it wrote; consecutive lanes, consecutive
 // dwords).
+template <class T>
 __device__ __forceinline__ void park(uint32_t *base, int t, const float (&v)[kMmNV]) {
 #pragma unroll
-  for (int q = 0; q < kMmNP; ++q) base[(t * kMmNP + q) * 64] = pack_hi(v[2 * q], v[2 * q + 1]);
+  for (int q = 0; q < kMmNP; ++q) base[(t * kMmNP + q) * 64] = T::pack_x(v[2 * q], v[2 * q + 1]);
 }
+template <class T>
 __device__ __forceinline__ void merge(const uint32_t *base, int t, float (&v)[kMmNV]) {
 #pragma unroll
   for (int q = 0; q < kMmNP; ++q) {
     const uint32_t l = base[(t * kMmNP + q) * 64];
-    v[2 * q] = rbf(bf_lo(l) + v[2 * q]);
-    v[2 * q + 1] = rbf(bf_hi(l) + v[2 * q + 1]);
+    v[2 * q] = T::rf(T::lo(l) + v[2 * q]);
+    v[2 * q + 1] = T::rf(T::hi(l) + v[2 * q + 1]);
   }
 }
 
 // NLH: the larger of the two lower-subtree sizes (the smaller is NLH - 1).
-template <int NLH, bool TAIL>
+template <class T, int NLH, bool TAIL>
 __global__ __launch_bounds__(kMmWaves * 64) void k_mm(GemmParams p) {
   extern __shared__ __attribute__((aligned(16))) uint16_t mm_lds[];
   const int kd = p.ksplit_depth, up = p.stack_slots;  // K-piece depth; upper levels cut inside the piece
@@ -309,7 +295,7 @@ __global__ __launch_bounds__(kMmWaves * 64) void k_mm(GemmParams p) {
       (void *)(p.A[b] + m0 * p.lda[b]), (short)0, (int)(ra < 0x7fffffff ? ra : 0x7fffffff), 0x00020000);
   const __amdgpu_buffer_rsrc_t sb_tile = __builtin_amdgcn_make_buffer_rsrc(
       (void *)(p.B[b] + n0 * p.ldb[b]), (short)0, (int)(rb < 0x7fffffff ? rb : 0x7fffffff), 0x00020000);
-  MmWg<TAIL> w{p,
+  MmWg<T, TAIL> w{p,
          mm_lds,
          p.A[b],
          p.B[b],
@@ -363,8 +349,8 @@ __global__ __launch_bounds__(kMmWaves * 64) void k_mm(GemmParams p) {
     // left subtrees its position closes (trailing ones of sidx), then park it
     // at its level unless it is the last
     int t = 0;
-    for (; (sidx >> t) & 1; ++t) merge(upl, t, v);
-    if (sidx + 1 < nsub) park(upl, t, v);
+    for (; (sidx >> t) & 1; ++t) merge<T>(upl, t, v);
+    if (sidx + 1 < nsub) park<T>(upl, t, v);
   }
   if (p.to_part)
     w.store_root(v, p.part + ((int64_t)b * (1 << kd) + piece) * p.part_stride, p.ldp);
@@ -385,24 +371,30 @@ int mm_upper_levels(int Lp) {
 }
 
 // nlh: the largest lower-subtree size of the plan (1..kMmMaxNL); the others are nlh - 1.
-hipError_t launch_mm(GemmParams p, int nb, int nlh, hipStream_t stream) {
+template <class T>
+hipError_t launch_mm_t(GemmParams p, int nb, int nlh, hipStream_t stream) {
   const int64_t tiles = ((p.M + kMmBM - 1) / kMmBM) * ((p.N + kMmBN - 1) / kMmBN);
   const dim3 grid((unsigned)tiles, 1u, (unsigned)(nb << p.ksplit_depth));
   const dim3 block(kMmWaves * 64);
   const size_t shm = mm_lds_bytes();
   const bool tail = p.K % kLeaf != 0;
   switch (nlh * 2 + (tail ? 1 : 0)) {
-    case 2: dgf_launch(k_mm<1, false>, grid, block, shm, stream, p); break;
-    case 3: dgf_launch(k_mm<1, true>, grid, block, shm, stream, p); break;
-    case 4: dgf_launch(k_mm<2, false>, grid, block, shm, stream, p); break;
-    case 5: dgf_launch(k_mm<2, true>, grid, block, shm, stream, p); break;
-    case 6: dgf_launch(k_mm<3, false>, grid, block, shm, stream, p); break;
-    case 7: dgf_launch(k_mm<3, true>, grid, block, shm, stream, p); break;
-    case 8: dgf_launch(k_mm<4, false>, grid, block, shm, stream, p); break;
-    case 9: dgf_launch(k_mm<4, true>, grid, block, shm, stream, p); break;
+    case 2: dgf_launch(k_mm<T, 1, false>, grid, block, shm, stream, p); break;
+    case 3: dgf_launch(k_mm<T, 1, true>, grid, block, shm, stream, p); break;
+    case 4: dgf_launch(k_mm<T, 2, false>, grid, block, shm, stream, p); break;
+    case 5: dgf_launch(k_mm<T, 2, true>, grid, block, shm, stream, p); break;
+    case 6: dgf_launch(k_mm<T, 3, false>, grid, block, shm, stream, p); break;
+    case 7: dgf_launch(k_mm<T, 3, true>, grid, block, shm, stream, p); break;
+    case 8: dgf_launch(k_mm<T, 4, false>, grid, block, shm, stream, p); break;
+    case 9: dgf_launch(k_mm<T, 4, true>, grid, block, shm, stream, p); break;
     default: return hipErrorInvalidValue;  // lower subtrees hold at most kMmMaxNL leaves
   }
   return hipGetLastError();
+}
+
+hipError_t launch_mm(GemmParams p, int nb, int nlh, hipStream_t stream) {
+  if (p.fmt == FMT_F16) return launch_mm_t<F16>(p, nb, nlh, stream);
+  return launch_mm_t<Bf16>(p, nb, nlh, stream);
 }
 
 }  // namespace dgf

@@ -61,15 +61,15 @@ struct WFrag<DGF_LAYOUT_NN, RT> {
   u32x4 v[RT];  // slab rows 32 S + lrow + (32 / RT) i, columns 8 lcol .. 8 lcol + 7
 };
 
-template <int MT>
+template <class T, int MT>
 struct XFrag {
-  bf16x8 v[kMaxNL][MT][2];
+  typename T::frag v[kMaxNL][MT][2];
 };
 
 // Static-shape post-order reduction of a wave's NL <= 4 leaves (midpoint
 // tree: 3 leaves split 1 | 2, 4 leaves split 2 | 2).  v holds leaf J of the
 // tile on entry and, after the last leaf, the subtree root.
-template <int NP, int NL, int J>
+template <class T, int NP, int NL, int J>
 __device__ __forceinline__ void leaf_reduce(uint32_t (&v)[NP], uint32_t (&s0)[NP], uint32_t (&s1)[NP]) {
   if constexpr (NL == 2) {
     if constexpr (J == 0) {
@@ -77,7 +77,7 @@ __device__ __forceinline__ void leaf_reduce(uint32_t (&v)[NP], uint32_t (&s0)[NP
       for (int q = 0; q < NP; ++q) s0[q] = v[q];
     } else {
 #pragma unroll
-      for (int q = 0; q < NP; ++q) v[q] = node2(s0[q], v[q]);
+      for (int q = 0; q < NP; ++q) v[q] = node2t<T>(s0[q], v[q]);
     }
   } else if constexpr (NL == 3) {
     if constexpr (J == 0) {
@@ -88,7 +88,7 @@ __device__ __forceinline__ void leaf_reduce(uint32_t (&v)[NP], uint32_t (&s0)[NP
       for (int q = 0; q < NP; ++q) s1[q] = v[q];
     } else {
 #pragma unroll
-      for (int q = 0; q < NP; ++q) v[q] = node2(s0[q], node2(s1[q], v[q]));
+      for (int q = 0; q < NP; ++q) v[q] = node2t<T>(s0[q], node2t<T>(s1[q], v[q]));
     }
   } else if constexpr (NL == 4) {
     if constexpr (J == 0) {
@@ -96,22 +96,22 @@ __device__ __forceinline__ void leaf_reduce(uint32_t (&v)[NP], uint32_t (&s0)[NP
       for (int q = 0; q < NP; ++q) s0[q] = v[q];
     } else if constexpr (J == 1) {
 #pragma unroll
-      for (int q = 0; q < NP; ++q) s0[q] = node2(s0[q], v[q]);
+      for (int q = 0; q < NP; ++q) s0[q] = node2t<T>(s0[q], v[q]);
     } else if constexpr (J == 2) {
 #pragma unroll
       for (int q = 0; q < NP; ++q) s1[q] = v[q];
     } else {
 #pragma unroll
-      for (int q = 0; q < NP; ++q) v[q] = node2(s0[q], node2(s1[q], v[q]));
+      for (int q = 0; q < NP; ++q) v[q] = node2t<T>(s0[q], node2t<T>(s1[q], v[q]));
     }
   }
 }
 
-template <int LAYOUT, int MT>
+template <class T, int LAYOUT, int MT>
 struct XsWave {
   static constexpr bool NN = LAYOUT == DGF_LAYOUT_NN;
   static constexpr int RT = rt_of<LAYOUT, MT>();
-  static constexpr int NP = RT * MT * 2;  // packed BF16 pairs per lane: index (rt MT + t) 2 + h
+  static constexpr int NP = RT * MT * 2;  // packed pairs of stored values per lane: index (rt MT + t) 2 + h
   static constexpr int NI = 2 * RT;       // NN: lanes per slab row (16 bytes each)
   static constexpr int ROWS = 32 / RT;    // NN: slab rows per load instruction
   static constexpr int COLS = 16 * RT;    // output columns per tile
@@ -127,14 +127,14 @@ struct XsWave {
   int b, lo, nl;
   bool tail;
   int64_t m0;
-  int tiles_n, t0, T;  // this workgroup's tiles: t0 .. t0 + T - 1
+  int tiles_n, t0, ntl;  // this workgroup's tiles: t0 .. t0 + ntl - 1
   const uint16_t *W;
   int64_t ldw;
   uint16_t *out;
   int64_t ldo;
   int64_t wbytes;  // bytes of W the loads may touch: N rows (NT) or K rows (NN) of ldw elements
 
-  __device__ __forceinline__ int tile_at(int i) const { return t0 + (i < T ? i : T - 1); }
+  __device__ __forceinline__ int tile_at(int i) const { return t0 + (i < ntl ? i : ntl - 1); }
 
   // Weights of unit (tile i clamped, leaf lo + j, half s): NT the whole leaf
   // (s ignored), NN rows 32 s .. 32 s + 31 of the leaf's slab.  Buffer loads:
@@ -148,7 +148,7 @@ struct XsWave {
     const int64_t n0 = (int64_t)tile_at(i) * COLS;
     const int64_t kb = (int64_t)(lo + j) * kLeaf;
     const int64_t base = NN ? ((kb + 32 * s) * ldw + n0) * 2 : (n0 * ldw + kb) * 2;
-    const int64_t left = i < T ? wbytes - base : 0;
+    const int64_t left = i < ntl ? wbytes - base : 0;
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         (void *)((const char *)W + base), (short)0, (int)(left > 0 ? (left < 0x7fffffff ? left : 0x7fffffff) : 0),
         0x00020000);
@@ -178,7 +178,7 @@ struct XsWave {
 #pragma unroll
       for (int i2 = 0; i2 < 2 * RT; ++i2) {
         const int64_t n = n0 + 8 * i2 + (lane >> 3) < p.N ? n0 + 8 * i2 + (lane >> 3) : p.N - 1;
-        w.v[i2] = __builtin_bit_cast(u32x4, load_frag_tail(W + n * ldw, kb + 8 * (lane & 7), p.K));
+        w.v[i2] = __builtin_bit_cast(u32x4, load_frag_tail<T>(W + n * ldw, kb + 8 * (lane & 7), p.K));
       }
     } else {
       // rows past K read row K-1 and are zeroed
@@ -200,17 +200,17 @@ struct XsWave {
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
       for (int t = 0; t < MT; ++t) {
-        v[(rt * MT + t) * 2 + 0] = pack_rne(acc[rt][t][0], acc[rt][t][1]);
-        v[(rt * MT + t) * 2 + 1] = pack_rne(acc[rt][t][2], acc[rt][t][3]);
+        v[(rt * MT + t) * 2 + 0] = T::pack(acc[rt][t][0], acc[rt][t][1]);
+        v[(rt * MT + t) * 2 + 1] = T::pack(acc[rt][t][2], acc[rt][t][3]);
       }
   }
 
   // NT: both K halves of a leaf (the second unless `half1` is false: an
-  // all-zero block leaves the sum unchanged), packed to BF16.  The rows pass
+  // all-zero block leaves the sum unchanged), rounded and packed.  The rows pass
   // through this wave's LDS slab: row r's 16-byte chunk c at r*64 + 8 (c ^ (r&7)),
   // which keeps both the row-wise writes and the MFMA-layout reads (lane:
   // row 16 rt + r16, chunk 4 h + g4) on distinct banks.
-  __device__ __forceinline__ void leaf_nt(const WF &w, const bf16x8 (&x)[MT][2], bool half1, uint32_t (&v)[NP]) const {
+  __device__ __forceinline__ void leaf_nt(const WF &w, const typename T::frag (&x)[MT][2], bool half1, uint32_t (&v)[NP]) const {
     const int wr = lane >> 3, wc = lane & 7;
 #pragma unroll
     for (int i2 = 0; i2 < 2 * RT; ++i2)
@@ -220,12 +220,12 @@ struct XsWave {
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       const int r = 16 * rt + r16;
-      const bf16x8 w0 = *reinterpret_cast<const bf16x8 *>(&slab[r * 64 + 8 * ((0 + g4) ^ (r & 7))]);
-      const bf16x8 w1 = *reinterpret_cast<const bf16x8 *>(&slab[r * 64 + 8 * ((4 + g4) ^ (r & 7))]);
+      const typename T::frag w0 = *reinterpret_cast<const typename T::frag *>(&slab[r * 64 + 8 * ((0 + g4) ^ (r & 7))]);
+      const typename T::frag w1 = *reinterpret_cast<const typename T::frag *>(&slab[r * 64 + 8 * ((4 + g4) ^ (r & 7))]);
 #pragma unroll
       for (int t = 0; t < MT; ++t) {
-        acc[rt][t] = mfma16(w0, x[t][0], f32x4{0.f, 0.f, 0.f, 0.f});
-        if (half1) acc[rt][t] = mfma16(w1, x[t][1], acc[rt][t]);
+        acc[rt][t] = T::mfma(w0, x[t][0], f32x4{0.f, 0.f, 0.f, 0.f});
+        if (half1) acc[rt][t] = T::mfma(w1, x[t][1], acc[rt][t]);
       }
     }
     wave_lds_sync();  // slab reads done before the next leaf overwrites it
@@ -238,7 +238,7 @@ struct XsWave {
   // (k>>3) ^ swz(n) is c ^ lx with c = ((32 S + ROWS i2) / 8) ^ e and
   // lx = (lrow>>3) ^ lcol: eight base addresses plus the immediate 64 e.
   template <int S>
-  __device__ __forceinline__ void half_nn(const WF &w, const bf16x8 (&x)[MT][2], f32x4 (&acc)[RT][MT]) const {
+  __device__ __forceinline__ void half_nn(const WF &w, const typename T::frag (&x)[MT][2], f32x4 (&acc)[RT][MT]) const {
     const int lrow = lane / NI, lcol = lane % NI;
     const int lx = (lrow >> 3) ^ lcol;
     uint16_t *wp[8];
@@ -255,9 +255,9 @@ struct XsWave {
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       const int n = 16 * rt + r16;
-      const bf16x8 wf = *reinterpret_cast<const bf16x8 *>(&slab[n * 64 + 8 * ((4 * S + g4) ^ xs_swz(n))]);
+      const typename T::frag wf = *reinterpret_cast<const typename T::frag *>(&slab[n * 64 + 8 * ((4 * S + g4) ^ xs_swz(n))]);
 #pragma unroll
-      for (int t = 0; t < MT; ++t) acc[rt][t] = mfma16(wf, x[t][S], S == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[rt][t]);
+      for (int t = 0; t < MT; ++t) acc[rt][t] = T::mfma(wf, x[t][S], S == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[rt][t]);
     }
     wave_lds_sync();  // slab reads done before the next unit overwrites it
   }
@@ -285,10 +285,10 @@ struct XsWave {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
 #pragma unroll
-        for (int k2 = 0; k2 < 4; ++k2) l1[k2][h] = node2(r[2 * k2][h], r[2 * k2 + 1][h]);
+        for (int k2 = 0; k2 < 4; ++k2) l1[k2][h] = node2t<T>(r[2 * k2][h], r[2 * k2 + 1][h]);
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) l2[k2][h] = node2(l1[2 * k2][h], l1[2 * k2 + 1][h]);
-        l3[h] = node2(l2[0][h], l2[1][h]);
+        for (int k2 = 0; k2 < 2; ++k2) l2[k2][h] = node2t<T>(l1[2 * k2][h], l1[2 * k2 + 1][h]);
+        l3[h] = node2t<T>(l2[0][h], l2[1][h]);
       }
       uint32_t o[2];
 #pragma unroll
@@ -314,7 +314,7 @@ struct XsWave {
   // index g = Q UN + U and lives in ring slot g % PR, and each unit first
   // issues the loads of unit g + PR - 1 (possibly of a later tile) into its slot.
   template <int NL, int NF, int Q, int U>
-  __device__ __forceinline__ void units(int i, WF (&ring)[PR], const XFrag<MT> &xs, f32x4 (&acc)[RT][MT],
+  __device__ __forceinline__ void units(int i, WF (&ring)[PR], const XFrag<T, MT> &xs, f32x4 (&acc)[RT][MT],
                                         uint32_t (&v)[NP], uint32_t (&s0)[NP], uint32_t (&s1)[NP],
                                         const uint32_t (&voff)[2 * RT]) const {
     constexpr int UN = NN ? 2 * NF : NF;
@@ -329,12 +329,12 @@ struct XsWave {
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (!NN) {
         leaf_nt(ring[slot], xs.v[J], true, v);
-        leaf_reduce<NP, NL, J>(v, s0, s1);
+        leaf_reduce<T, NP, NL, J>(v, s0, s1);
       } else {
         half_nn<S>(ring[slot], xs.v[J], acc);
         if constexpr (S == 1) {
           pack(acc, v);
-          leaf_reduce<NP, NL, J>(v, s0, s1);
+          leaf_reduce<T, NP, NL, J>(v, s0, s1);
         }
       }
       units<NL, NF, Q, U + 1>(i, ring, xs, acc, v, s0, s1, voff);
@@ -344,7 +344,7 @@ struct XsWave {
   // One tile (index i) of a wave with NL leaves, the last partial when TAIL
   // (loaded without prefetch); NF = NL - TAIL go through the ring.
   template <int NL, bool TAIL, int Q>
-  __device__ __forceinline__ void tile(int i, WF (&ring)[PR], const XFrag<MT> &xs, const uint32_t (&voff)[2 * RT]) const {
+  __device__ __forceinline__ void tile(int i, WF (&ring)[PR], const XFrag<T, MT> &xs, const uint32_t (&voff)[2 * RT]) const {
     constexpr int NF = NL - (TAIL ? 1 : 0);
     uint32_t s0[NP], s1[NP], v[NP];
     f32x4 acc[RT][MT];
@@ -365,7 +365,7 @@ struct XsWave {
         }
         pack(acc, v);
       }
-      leaf_reduce<NP, NL, NF>(v, s0, s1);
+      leaf_reduce<T, NP, NL, NF>(v, s0, s1);
     }
     finish_tile(i, v);
   }
@@ -373,7 +373,7 @@ struct XsWave {
   template <int NL, bool TAIL>
   __device__ __forceinline__ void run() const {
     constexpr int NF = NL - (TAIL ? 1 : 0);
-    if (T <= 0) return;  // no tile for this workgroup (the same for all its waves)
+    if (ntl <= 0) return;  // no tile for this workgroup (the same for all its waves)
     // the first weight units are issued before the activation loads, so that
     // their HBM latency overlaps the activation's (registers only: the slab
     // is free for the rearrangement below)
@@ -393,7 +393,7 @@ struct XsWave {
     // 16-byte chunk lane % 8 of the leaf; rows past M clamped, never stored;
     // zeros past K) and rearranged into the MFMA layout through this wave's
     // slab: fragment-layout loads would split every line over two instructions
-    XFrag<MT> xs;
+    XFrag<T, MT> xs;
     {
       u32x4 raw[NL][MT][2];
 #pragma unroll
@@ -405,7 +405,7 @@ struct XsWave {
 #pragma unroll
           for (int j = 0; j < NL; ++j) {
             const int64_t k = (int64_t)(lo + j) * kLeaf + 8 * (lane & 7);
-            raw[j][t][s] = __builtin_bit_cast(u32x4, (TAIL && j == NF) ? load_frag_tail(row, k, p.K) : load_frag(row, k));
+            raw[j][t][s] = __builtin_bit_cast(u32x4, (TAIL && j == NF) ? load_frag_tail<T>(row, k, p.K) : load_frag<T>(row, k));
           }
         }
       const int wr = lane >> 3, wc = lane & 7;
@@ -419,23 +419,23 @@ struct XsWave {
           wave_lds_sync();
 #pragma unroll
           for (int s = 0; s < 2; ++s)
-            xs.v[j][t][s] = *reinterpret_cast<const bf16x8 *>(&slab[r16 * 64 + 8 * ((4 * s + g4) ^ (r16 & 7))]);
+            xs.v[j][t][s] = *reinterpret_cast<const typename T::frag *>(&slab[r16 * 64 + 8 * ((4 * s + g4) ^ (r16 & 7))]);
           wave_lds_sync();  // the slab's reads are done before it is rewritten
         }
     }
-    for (int i = 0; i < T; i += PR) {
+    for (int i = 0; i < ntl; i += PR) {
       tile<NL, TAIL, 0>(i, ring, xs, voff);
-      if (i + 1 < T) tile<NL, TAIL, 1>(i + 1, ring, xs, voff);
+      if (i + 1 < ntl) tile<NL, TAIL, 1>(i + 1, ring, xs, voff);
       if constexpr (PR > 2)
-        if (i + 2 < T) tile<NL, TAIL, 2>(i + 2, ring, xs, voff);
+        if (i + 2 < ntl) tile<NL, TAIL, 2>(i + 2, ring, xs, voff);
     }
   }
 };
 
-template <int LAYOUT, int MT>
+template <class T, int LAYOUT, int MT>
 __global__ __launch_bounds__(kXsWaves * 64) void k_xs(GemmParams p) {
   extern __shared__ __attribute__((aligned(16))) uint32_t xs_lds[];
-  using Wv = XsWave<LAYOUT, MT>;
+  using Wv = XsWave<T, LAYOUT, MT>;
   const int waves = blockDim.x >> 6;
   const int dw = __builtin_ctz(waves);
   const int lane = threadIdx.x & 63;
@@ -461,7 +461,7 @@ __global__ __launch_bounds__(kXsWaves * 64) void k_xs(GemmParams p) {
   // contiguous tile ranges: workgroup g takes tiles g*per .. g*per + per - 1
   const int per = (tiles_n + (int)gridDim.x - 1) / (int)gridDim.x;
   const int t0 = vx * per;
-  const int T = t0 < tiles_n ? min(per, tiles_n - t0) : 0;
+  const int ntl = t0 < tiles_n ? min(per, tiles_n - t0) : 0;
   Wv w{p,
        xs_lds,
        reinterpret_cast<uint16_t *>(xs_lds + (size_t)2 * waves * Wv::NP * 64) + (size_t)wave * Wv::COLS * 64,
@@ -477,7 +477,7 @@ __global__ __launch_bounds__(kXsWaves * 64) void k_xs(GemmParams p) {
        (int64_t)vy * 16 * MT,
        tiles_n,
        t0,
-       T,
+       ntl,
        p.B[b],
        p.ldb[b],
        p.to_part ? p.part + ((int64_t)b * (1 << kd) + piece) * p.part_stride : p.C[b],
@@ -510,7 +510,8 @@ size_t xs_lds_bytes(int layout, int mt, int waves) {
   return 2 * (size_t)waves * np * 64 * 4 + (size_t)waves * cols * 64 * 2;
 }
 
-hipError_t launch_xs(int layout, GemmParams p, int nb, int waves, int groups, hipStream_t stream) {
+template <class T>
+hipError_t launch_xs_t(int layout, GemmParams p, int nb, int waves, int groups, hipStream_t stream) {
   const int mt = p.M <= 16 ? 1 : 2;
   const int64_t tiles_m = (p.M + 16 * mt - 1) / (16 * mt);
   const dim3 grid((unsigned)groups, (unsigned)tiles_m, (unsigned)(nb << p.ksplit_depth));
@@ -518,16 +519,21 @@ hipError_t launch_xs(int layout, GemmParams p, int nb, int waves, int groups, hi
   const size_t shm = xs_lds_bytes(layout, mt, waves);
   if (layout == DGF_LAYOUT_NT) {
     if (mt == 1)
-      dgf_launch((k_xs<DGF_LAYOUT_NT, 1>), grid, block, shm, stream, p);
+      dgf_launch((k_xs<T, DGF_LAYOUT_NT, 1>), grid, block, shm, stream, p);
     else
-      dgf_launch((k_xs<DGF_LAYOUT_NT, 2>), grid, block, shm, stream, p);
+      dgf_launch((k_xs<T, DGF_LAYOUT_NT, 2>), grid, block, shm, stream, p);
   } else {
     if (mt == 1)
-      dgf_launch((k_xs<DGF_LAYOUT_NN, 1>), grid, block, shm, stream, p);
+      dgf_launch((k_xs<T, DGF_LAYOUT_NN, 1>), grid, block, shm, stream, p);
     else
-      dgf_launch((k_xs<DGF_LAYOUT_NN, 2>), grid, block, shm, stream, p);
+      dgf_launch((k_xs<T, DGF_LAYOUT_NN, 2>), grid, block, shm, stream, p);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_xs(int layout, GemmParams p, int nb, int waves, int groups, hipStream_t stream) {
+  if (p.fmt == FMT_F16) return launch_xs_t<F16>(layout, p, nb, waves, groups, stream);
+  return launch_xs_t<Bf16>(layout, p, nb, waves, groups, stream);
 }
 
 }  // namespace dgf

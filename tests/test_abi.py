@@ -28,7 +28,8 @@ def lib():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for required in ("dgf_ffn_fwd", "dgf_ffn_bwd", "dgf_tree_combine", "dgf_tree_combine_typed", "dgf_gemm_tree",
-                     "dgf_act_fwd", "dgf_act_bwd", "dgf_last_error"):
+                     "dgf_act_fwd", "dgf_act_bwd", "dgf_last_error", "dgf_ffn_fwd_typed", "dgf_ffn_bwd_typed",
+                     "dgf_gemm_tree_typed", "dgf_act_fwd_typed", "dgf_act_bwd_typed"):
         assert required in names
 
 
@@ -39,7 +40,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_constants(lib):
-    assert lib.dgf_abi_version() == 1
+    assert lib.dgf_abi_version() == 2
     assert lib.dgf_leaf_size() == 64
 
 
@@ -132,6 +133,31 @@ def test_gemm_validation(lib):
                              4, 4, (1 << 23) + 8, None, 0, None) == 2
     assert lib.dgf_act_fwd(None, FAKE, FAKE, 10, None) == 1
     assert lib.dgf_act_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == 0
+
+
+def test_typed_entry_points_validate_the_dtype(lib):
+    # FP32 has no declared leaf: unsupported; an unknown code: invalid; both before any HIP call
+    fwd = lambda dt, M=4: lib.dgf_ffn_fwd_typed(FAKE, 256, FAKE, 256, FAKE, 256, FAKE, 768, FAKE, 256, None, None, 0,
+                                                M, 256, 768, FAKE, 1 << 30, dt, None)
+    assert fwd(binding.DGF_FP32) == 2
+    assert b"FP32" in lib.dgf_last_error()
+    assert fwd(9) == 1
+    assert b"dtype" in lib.dgf_last_error()
+    assert fwd(binding.DGF_FP16, M=0) == 0  # empty input: no launch
+    assert lib.dgf_ffn_fwd_typed(None, 256, FAKE, 256, FAKE, 256, FAKE, 768, FAKE, 256, None, None, 0,
+                                 4, 256, 768, FAKE, 1 << 30, binding.DGF_FP16, None) == 1
+    assert b"x" in lib.dgf_last_error()
+    bwd = lambda dt: lib.dgf_ffn_bwd_typed(FAKE, 256, FAKE, 256, FAKE, FAKE, 768, FAKE, 256, FAKE, 256, FAKE, 768,
+                                           FAKE, None, None, 256, FAKE, 256, FAKE, 256, FAKE, 768, 4, 256, 768,
+                                           FAKE, 0, dt, None)
+    assert bwd(binding.DGF_FP32) == 2
+    assert bwd(binding.DGF_FP16) == 3  # reaches the workspace check: no workspace given
+    gemm = lambda dt: lib.dgf_gemm_tree_typed(binding.DGF_TN, FAKE, 8, FAKE, 8, FAKE, 8, 4, 4, 100, None, 0, dt, None)
+    assert gemm(binding.DGF_FP32) == 2 and gemm(-1) == 1 and gemm(binding.DGF_FP16) == 3
+    assert lib.dgf_act_fwd_typed(FAKE, FAKE, FAKE, 10, binding.DGF_FP32, None) == 2
+    assert lib.dgf_act_fwd_typed(None, FAKE, FAKE, 10, binding.DGF_FP16, None) == 1
+    assert lib.dgf_act_bwd_typed(FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, binding.DGF_FP16, None) == 0
+    assert lib.dgf_act_bwd_typed(FAKE, FAKE, FAKE, FAKE, FAKE, None, 10, 5, None) == 1
 
 
 def test_profile_hook_validation(lib):
