@@ -153,6 +153,10 @@ def main():
     ap.add_argument("--copies", type=int, default=3, help="resident weight copies rotated per step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quick", action="store_true", help="skip the forward-only and CPU legs (profiling runs)")
+    ap.add_argument("--workload", choices=("train32", "long4096"), default="train32",
+                    help="long4096: only the M=4096 training step (--warmup, then --samples regions of --steps "
+                         "steps), for profiling; prints that leg's JSON instead of the benchmark line")
+    ap.add_argument("--dtype", choices=("bf16", "fp16"), default="bf16", help="stored type of the long4096 workload")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -171,6 +175,19 @@ def main():
     torch.cuda.set_device(0)
     dgf.load()
     print(f"[bench] device {torch.cuda.get_device_name(0)}; building inputs", file=sys.stderr, flush=True)
+
+    if args.workload == "long4096":
+        dt = torch.float16 if args.dtype == "fp16" else torch.bfloat16
+        weights = tuple(t.cuda() for t in inputs.ffn_weights(dtype=dt))
+        # one runtime device copy of known size (W_gate, 100,663,296 bytes read and written): the
+        # calibration of a profiler's memory counters
+        calibration = weights[0].clone()
+        torch.cuda.synchronize()
+        del calibration
+        out = long_sequence(weights, steps=args.steps, warmup=args.warmup, samples=args.samples)
+        out["dtype"] = args.dtype
+        print(json.dumps({"long_sequence": out}), flush=True)
+        return
 
     M = 32
     wg_c, wu_c, wd_c = inputs.ffn_weights()
@@ -299,6 +316,7 @@ def main():
 
     if not args.quick:
         result["long_sequence"] = long_sequence(W[0], samples=args.samples)
+        result["fp16"] = fp16_leg(args)
 
     if not args.no_cpu_baseline and not args.quick:
         # the outputs of one step, kept as BF16 bits for the comparison with the oracle's sample
@@ -312,15 +330,60 @@ def main():
     print(json.dumps(result), flush=True)
 
 
+def fp16_leg(args) -> dict:
+    """The same workloads in FP16 storage (the *_typed entry points, one tree for
+    both types): the M=32 training step, the forward at 1/8/32 tokens and the
+    M=4096 step.  Bytes and flops per step are those of the BF16 workloads."""
+    import torch
+    from deterministic_gated_ffn_amd import binding as dgf
+    from deterministic_gated_ffn_amd import inputs
+
+    F16 = torch.float16
+    wg_c, wu_c, wd_c = inputs.ffn_weights(dtype=F16)
+    W = [(wg_c.cuda(), wu_c.cuda(), wd_c.cuda())]
+    for _ in range(args.copies - 1):
+        W.append(tuple(t.clone() for t in W[0]))
+    M = 32
+    x_c, dy_c = inputs.activations(M, dtype=F16)
+    x, dy = x_c.cuda(), dy_c.cuda()
+
+    def step(k):
+        wg, wu, wd = W[k % len(W)]
+        y, g, u = dgf.ffn_fwd(x, wg, wu, wd, training=True)
+        return dgf.ffn_bwd(dy, x, g, u, wg, wu, wd)
+
+    for k in range(args.warmup):
+        step(k)
+    out = {"dtype": "f16", "fwd_bwd": {"32": stats_entry(sample_us(step, args.steps, args.samples), step_bytes(M))}}
+    fwd = {}
+    for Mf in (1, 8, 32):
+        xf = x[:Mf]
+
+        def fwd_m(k, xf=xf):
+            wg, wu, wd = W[k % len(W)]
+            dgf.ffn_fwd(xf, wg, wu, wd)
+
+        for k in range(args.warmup):
+            fwd_m(k)
+        fwd[str(Mf)] = stats_entry(sample_us(fwd_m, args.steps, args.samples), fwd_bytes(Mf))
+    out["forward"] = fwd
+    print(f"[bench] FP16: fwd+bwd M=32 {out['fwd_bwd']['32']['us']:.1f} us; forward M=1/8/32 "
+          f"{fwd['1']['us']:.1f}/{fwd['8']['us']:.1f}/{fwd['32']['us']:.1f} us", file=sys.stderr, flush=True)
+    out["long_sequence"] = long_sequence(W[0], samples=args.samples)
+    del W
+    return out
+
+
 def long_sequence(weights, M: int = 4096, steps: int = 5, warmup: int = 2, samples: int = 5) -> dict:
     """The compute-bound shape: fwd+bwd at M=4096 tokens (8 sequences x 512),
-    `samples` regions of `steps` steps; 18 M H I flops per step (nine products)."""
+    `samples` regions of `steps` steps; 18 M H I flops per step (nine products).
+    The stored type is the weights' (FP16 takes the same 2.5 PFLOP/s MFMA peak)."""
     import torch
     from deterministic_gated_ffn_amd import binding as dgf
     from deterministic_gated_ffn_amd import inputs
 
     wg, wu, wd = weights
-    x_c, dy_c = inputs.activations(M)
+    x_c, dy_c = inputs.activations(M, dtype=wg.dtype)
     x, dy = x_c.cuda(), dy_c.cuda()
 
     def step(k):
