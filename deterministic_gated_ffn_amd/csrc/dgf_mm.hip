@@ -177,15 +177,26 @@ struct MmWg {
   // j + 1's tiles (fetched two leaves earlier into register set `nx`) into
   // the other stage and the fetch of leaf j + 3 into that set; the barrier
   // publishes the stage just written and frees the one just read.
-  template <int NL, int J>
+  // FIN: at J = 0 the tree work beside the MFMAs is the last step of the
+  // previous lower subtree (of the same size, its last leaf in prev): its
+  // root in v afterwards.
+  template <int NL, int J, bool FIN>
   __device__ __forceinline__ void one_leaf(int j, int s, u32x4 (&nx)[4], const f32x4 (&prev)[kMmTN][kMmTM],
                                            f32x4 (&acc)[kMmTN][kMmTM], float (&v)[kMmNV],
                                            float (&st)[2][kMmNV]) const {
+    // merges of the tree step beside the MFMAs (-1: none), and the VALU
+    // instructions to put beside each MFMA (a rounding, then an add and a
+    // rounding per merge, per value)
+    constexpr int m = J > 0 ? leaf_pos(NL, J - 1).m : FIN ? leaf_pos(NL, NL - 1).m : -1;
+    constexpr int vpm = m < 0 ? 1 : (kMmNV * (1 + 2 * m) + 15) / 16;
     __builtin_amdgcn_sched_barrier(0);
     leaf_mfma(s, acc);
     if constexpr (J > 0) {
       round_leaf(prev, v);
       push_f<T, NL, J - 1>(v, st);
+    } else if constexpr (FIN) {
+      round_leaf(prev, v);
+      push_f<T, NL, NL - 1>(v, st);
     }
     // past the piece's last leaf the stage store writes a stage nobody reads
     // and the fetch requests nothing, so the leaf sequence needs no branch
@@ -195,8 +206,8 @@ struct MmWg {
       __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);  // fragment reads
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);  // a share of the tree step
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, vpm, 0);  // a share of the tree step
       }
       __builtin_amdgcn_sched_group_barrier(0x200, 4, 0);  // stage store
       __builtin_amdgcn_sched_group_barrier(0x020, 4, 0);  // next fetch
@@ -214,9 +225,9 @@ struct MmWg {
     if constexpr (J < NL) {
       constexpr int S = (P0 ^ J) & 1;
       if constexpr (S == 0)
-        one_leaf<NL, J>(j, 0, r1, prev, acc, v, st);
+        one_leaf<NL, J, false>(j, 0, r1, prev, acc, v, st);
       else
-        one_leaf<NL, J>(j, 1, r0, prev, acc, v, st);
+        one_leaf<NL, J, false>(j, 1, r0, prev, acc, v, st);
       leaves<NL, J + 1, P0>(j + 1, r0, r1, acc, prev, v, st);
     } else {
       round_leaf(prev, v);
@@ -232,6 +243,26 @@ struct MmWg {
       leaves<NL, 0, 0>(j, r0, r1, a0, a1, v, st);
     else
       leaves<NL, 0, 1>(j, r0, r1, a0, a1, v, st);
+  }
+
+  // The same when every lower subtree of the piece has NL leaves: the last
+  // step of a subtree (about 5 VALU instructions per value) is deferred into
+  // the first leaf of the next, beside its MFMAs.  Leaf jj of the piece (jj =
+  // j - plo) accumulates into set jj & 1 (a0 or a1) and reads stage jj & 1;
+  // after leaf 0 of a subtree, `upper` takes the previous subtree's root.
+  template <int NL, int J, int P0, class UP>
+  __device__ __forceinline__ void leaves_d(int j, u32x4 (&r0)[4], u32x4 (&r1)[4], f32x4 (&a0)[kMmTN][kMmTM],
+                                           f32x4 (&a1)[kMmTN][kMmTM], float (&v)[kMmNV], float (&st)[2][kMmNV],
+                                           const UP &upper) const {
+    if constexpr (J < NL) {
+      constexpr int S = (P0 ^ J) & 1;
+      if constexpr (S == 0)
+        one_leaf<NL, J, true>(j, 0, r1, a1, a0, v, st);
+      else
+        one_leaf<NL, J, true>(j, 1, r0, a0, a1, v, st);
+      if constexpr (J == 0) upper(v);
+      leaves_d<NL, J + 1, P0>(j + 1, r0, r1, a0, a1, v, st, upper);
+    }
   }
 
   __device__ __forceinline__ void store_root(const float (&v)[kMmNV], uint16_t *out, int64_t ldo) const {
@@ -337,6 +368,63 @@ __global__ __launch_bounds__(kMmWaves * 64) void k_mm(GemmParams p) {
   uint32_t *upl = reinterpret_cast<uint32_t *>(reinterpret_cast<char *>(mm_lds) + 2 * kMmStage) +
                   (size_t)wave * 3 * kMmNP * 64 + lane;
   const int nsub = 1 << up;
+  // (the deferred form keeps both accumulator sets and the subtree's pending
+  // values live across subtrees: with a partial last leaf that no longer fits
+  // the 256 registers of two waves per SIMD, and with 3-leaf subtrees it fits
+  // at 242 but measured 2% slower than the immediate form)
+  constexpr bool kDefer = NLH != 3 && !TAIL;
+  bool uniform = false;
+  if constexpr (kDefer) uniform = w.phi - w.plo == (NLH << up);
+  if constexpr (kDefer) {
+  if (uniform) {
+    // every lower subtree has NLH leaves: each one's last step runs beside the
+    // next one's first MFMAs (the first subtree's leaf 0 finalises zeros,
+    // which are dropped)
+    f32x4 a0[kMmTN][kMmTM], a1[kMmTN][kMmTM];
+    float st[2][kMmNV];
+#pragma unroll
+    for (int tn = 0; tn < kMmTN; ++tn)
+#pragma unroll
+      for (int tm = 0; tm < kMmTM; ++tm) a0[tn][tm] = a1[tn][tm] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < kMmNV; ++q) st[0][q] = st[1][q] = 0.f;
+    for (int sidx = 0; sidx < nsub; ++sidx) {
+      // root of subtree sidx - 1 into the top levels: merge with the pending
+      // left subtrees its position closes, then park it (it is not the last)
+      auto upper = [&](float (&rv)[kMmNV]) {
+        if (sidx == 0) return;
+        int t = 0;
+        for (; ((sidx - 1) >> t) & 1; ++t) merge<T>(upl, t, rv);
+        park<T>(upl, t, rv);
+      };
+      const int j = w.plo + sidx * NLH;
+      if constexpr ((NLH & 1) == 0) {
+        w.template leaves_d<NLH, 0, 0>(j, r0, r1, a0, a1, v, st, upper);
+      } else {
+        // odd subtree sizes alternate the parity of their first leaf: two
+        // subtrees per iteration, each of compile-time parity
+        w.template leaves_d<NLH, 0, 0>(j, r0, r1, a0, a1, v, st, upper);
+        if (sidx + 1 < nsub) {
+          ++sidx;
+          auto upper1 = [&](float (&rv)[kMmNV]) {
+            int t = 0;
+            for (; ((sidx - 1) >> t) & 1; ++t) merge<T>(upl, t, rv);
+            park<T>(upl, t, rv);
+          };
+          w.template leaves_d<NLH, 0, 1>(j + NLH, r0, r1, a0, a1, v, st, upper1);
+        }
+      }
+    }
+    // the last subtree's last step, then the top levels over its root
+    if ((((NLH << up) - 1) & 1) == 0)
+      w.round_leaf(a0, v);
+    else
+      w.round_leaf(a1, v);
+    push_f<T, NLH, NLH - 1>(v, st);
+    for (int t = 0; ((nsub - 1) >> t) & 1; ++t) merge<T>(upl, t, v);
+  }
+  }
+  if (!uniform) {
   for (int sidx = 0; sidx < nsub; ++sidx) {
     int lo, hi;
     subtree_range(w.phi - w.plo, up, sidx, lo, hi);
@@ -351,6 +439,7 @@ __global__ __launch_bounds__(kMmWaves * 64) void k_mm(GemmParams p) {
     int t = 0;
     for (; (sidx >> t) & 1; ++t) merge<T>(upl, t, v);
     if (sidx + 1 < nsub) park<T>(upl, t, v);
+  }
   }
   if (p.to_part)
     w.store_root(v, p.part + ((int64_t)b * (1 << kd) + piece) * p.part_stride, p.ldp);
