@@ -67,6 +67,7 @@ struct Bf16 {
   static __device__ __forceinline__ float hi(uint32_t p) { return bf_hi(p); }
   static __device__ __forceinline__ uint16_t r(float x) { return f2bf(x); }
   static __device__ __forceinline__ uint32_t pack(float l, float h) { return pack_rne(l, h); }
+  static __device__ __forceinline__ uint32_t pack_prod(float l, float h) { return pack_rne(l, h); }
   static __device__ __forceinline__ f32x4 mfma(const frag &a, const frag &b, const f32x4 &c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
@@ -88,18 +89,25 @@ struct F16 {
   static __device__ __forceinline__ float f(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
   static __device__ __forceinline__ float lo(uint32_t p) { return f((uint16_t)p); }
   static __device__ __forceinline__ float hi(uint32_t p) { return f((uint16_t)(p >> 16)); }
-  // The FP32 value is rounded to FP16 on its own.  Without the empty asm the
-  // compiler folds a producing multiply into v_fma_mixlo_f16, which rounds
-  // the exact product to FP16 once (no FP32 rounding first) and adds +0, so
-  // that a -0 product comes out as +0.
+  // r and pack_prod round an FP32 value that an FP32 multiply produced: the
+  // empty asm keeps the rounding on its own.  Without it the compiler folds
+  // the multiply into v_fma_mixlo_f16, which rounds the exact product to FP16
+  // once (no FP32 rounding first) and adds +0, so that a -0 product comes out
+  // as +0.  pack takes MFMA accumulators and node sums, where such a fold
+  // cannot change the value (nothing to fold into an accumulator; a folded
+  // add of two FP16 values rounds like the FP32 add then FP16: 24 >= 2*11+2
+  // bits), and keeps the registers free.
   static __device__ __forceinline__ uint16_t r(float x) {
     asm volatile("" : "+v"(x));
     return __builtin_bit_cast(uint16_t, (_Float16)x);
   }
   static __device__ __forceinline__ uint32_t pack(float l, float h) {
-    asm volatile("" : "+v"(l), "+v"(h));
     const f32x2 v = {l, h};
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+  }
+  static __device__ __forceinline__ uint32_t pack_prod(float l, float h) {
+    asm volatile("" : "+v"(l), "+v"(h));
+    return pack(l, h);
   }
   static __device__ __forceinline__ f32x4 mfma(const frag &a, const frag &b, const f32x4 &c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);

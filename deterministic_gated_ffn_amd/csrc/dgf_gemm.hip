@@ -273,7 +273,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemm_nt(GemmParams p) {
             const float s = g * sigma_f(g);
             a2[e] = s * u;
           }
-          ap[h] = T::pack(a2[0], a2[1]);
+          ap[h] = T::pack_prod(a2[0], a2[1]);
         }
         store4(p.act_out, p.ld_act, m, n, p.M, p.N, ap[0], ap[1]);
         if (p.C[0]) store4(p.C[0], p.ldc[0], m, n, p.M, p.N, root[qg], root[qg + 1]);

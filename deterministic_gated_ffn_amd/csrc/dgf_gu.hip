@@ -169,7 +169,7 @@ struct GuWave {
       const float ga = T::lo(o[0][h]), gb = T::hi(o[0][h]);
       const float ua = T::lo(o[1][h]), ub = T::hi(o[1][h]);
       const float sa = ga * sigma_f(ga), sb = gb * sigma_f(gb);
-      av[h] = T::pack(sa * ua, sb * ub);
+      av[h] = T::pack_prod(sa * ua, sb * ub);
     }
     const int64_t m = m0 + 16 * t + r16, n = col0(i) + 4 * g4;
     if (m >= p.M || n >= p.N) return;

@@ -67,7 +67,7 @@ __device__ __forceinline__ void join_epi_chunk(const GemmParams &p, int b, int64
       const float g0 = T::lo(r0[q]), g1 = T::hi(r0[q]);
       const float u0 = T::lo(r1[q]), u1 = T::hi(r1[q]);
       const float s0 = g0 * sigma_f(g0), s1 = g1 * sigma_f(g1);
-      a[q] = T::pack(s0 * u0, s1 * u1);
+      a[q] = T::pack_prod(s0 * u0, s1 * u1);
     }
     store8(p.act_out + m * p.ld_act + c, c, p.N, a);
     if (p.C[0]) store8(p.C[0] + m * p.ldc[0] + c, c, p.N, r0);
