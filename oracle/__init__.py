@@ -77,6 +77,8 @@ def lib():
         Ci = ctypes.c_int
         L.oracle_block_step_t.restype = ctypes.c_float
         L.oracle_block_step_t.argtypes = [Ci, ctypes.c_float, P, I64, P, I64, Ci]
+        L.oracle_block_chains_t.restype = None
+        L.oracle_block_chains_t.argtypes = [Ci, P, P, P, P, I64, Ci]
         L.oracle_leaf_f32_t.restype = ctypes.c_float
         L.oracle_leaf_f32_t.argtypes = [Ci, P, I64, P, I64, I64]
         L.oracle_dot_tree_t.restype = ctypes.c_uint16
@@ -142,6 +144,18 @@ def block_step(acc: float, a, b, dtype: str = "bf16") -> np.float32:
     a, b = _u16(a), _u16(b)
     assert a.shape == b.shape and a.ndim == 1 and a.size <= 8
     return np.float32(lib().oracle_block_step_t(_dt(dtype), ctypes.c_float(acc), _p(a), 1, _p(b), 1, a.size))
+
+
+def block_chains(acc0, a, b, dtype: str = "bf16") -> np.ndarray:
+    """Rows r of a, b [n, k] as block steps of 8 in ascending k from acc0[r]
+    (float32): what a chain of matrix-core instructions computes per output."""
+    a, b = _u16(a), _u16(b)
+    acc0 = np.ascontiguousarray(np.asarray(acc0, np.float32)).ravel()
+    n, k = a.shape
+    assert b.shape == (n, k) and acc0.size == n
+    out = np.zeros(n, np.float32)
+    lib().oracle_block_chains_t(_dt(dtype), _p(acc0), _p(a), _p(b), _p(out), n, k)
+    return out
 
 
 def leaf_f32(a, b, dtype: str = "bf16") -> np.float32:

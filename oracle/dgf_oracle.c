@@ -323,6 +323,23 @@ static float leaf_f32(int dt, const uint16_t *a, ptrdiff_t sa, const uint16_t *b
     return acc;
 }
 
+/* Block steps of 8 in ascending k from an accumulator acc0 (the chain a
+ * matrix-core instruction sequence applies to one output): row r of the
+ * [n][k] arrays a and b against acc0[r], into out[r]. */
+void oracle_block_chains_t(int dt, const float *acc0, const uint16_t *a, const uint16_t *b, float *out,
+                           int64_t n, int k)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n; ++r) {
+        float acc = acc0[r];
+        for (int kb = 0; kb < k; kb += 8) {
+            int w = k - kb < 8 ? k - kb : 8;
+            acc = block_step_t(dt, acc, a + r * k + kb, 1, b + r * k + kb, 1, w);
+        }
+        out[r] = acc;
+    }
+}
+
 float oracle_leaf_f32_t(int dt, const uint16_t *a, ptrdiff_t sa, const uint16_t *b, ptrdiff_t sb, int64_t n)
 {
     return leaf_f32(dt, a, sa, b, sb, n);

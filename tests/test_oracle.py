@@ -636,3 +636,21 @@ def test_f16_ffn_stages_compose_and_dx_is_gate_then_up():
     # FP16 and BF16 storage give different bits from the same FP32 draws
     bb = {k: inputs.bits(v) for k, v in inputs.tiny_case().items()}
     assert not np.array_equal(oracle.ffn_fwd(bb["x"], bb["w_gate"], bb["w_up"], bb["w_down"])["y"], o["y"])
+
+
+def test_block_chains_are_chained_block_steps():
+    # the batched chain (used against the matrix-core instructions) is the
+    # block step applied in ascending blocks of 8 from the given accumulator
+    rng = np.random.default_rng(23)
+    for dtype in ("bf16", "fp16"):
+        a = rng.integers(0, 0x3C00, (20, 32)).astype(np.uint16)
+        b = rng.integers(0, 0x3C00, (20, 32)).astype(np.uint16)
+        acc0 = (rng.standard_normal(20) * 10.0 ** rng.integers(-3, 4, 20)).astype(np.float32)
+        got = oracle.block_chains(acc0, a, b, dtype)
+        for r in range(20):
+            acc = np.float32(acc0[r])
+            for k in range(0, 32, 8):
+                acc = oracle.block_step(float(acc), a[r, k:k + 8], b[r, k:k + 8], dtype)
+            assert f32_bits(acc) == f32_bits(got[r])
+        assert np.array_equal(oracle.block_chains(np.zeros(20), a, b, dtype),
+                              np.array([oracle.leaf_f32(a[r], b[r], dtype) for r in range(20)], np.float32))
