@@ -47,7 +47,17 @@ constexpr int rt_of() {
   return LAYOUT == DGF_LAYOUT_NN ? 4 : (MT == 1 ? 4 : 2);
 }
 
-__device__ __forceinline__ int xs_swz(int n) { return (n ^ (n >> 3)) & 7; }
+// NN slab: the leaf's 64 K rows of 64 columns, row-major in 16-byte chunks,
+// chunk c of row k at c ^ nn_swz(k).  The transposing reads of one operand
+// touch 16 rows k = 8 q + 4 h + r (q = lane / 16, r = lane / 4 % 4) at 32
+// bytes each; this map puts the rows of any 32 lanes on distinct 4-byte banks
+// of a 64-bank LDS and the rows of all 64 lanes on distinct banks of a
+// 128-bank one (bank offset 32 (k mod 2) or 32 (k mod 4) plus 4 c): chunk bit
+// 1 takes q's low bit, chunk bit 2 the parity of k's bit 1 and q's high bit.
+__device__ __forceinline__ int nn_swz(int k) { return ((k >> 2) & 2) | ((((k >> 1) ^ (k >> 4)) & 1) << 2); }
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
 
 // One streaming unit of weights: NT a whole leaf, NN half a leaf.
 template <int LAYOUT, int RT>
@@ -107,7 +117,8 @@ __device__ __forceinline__ void leaf_reduce(uint32_t (&v)[NP], uint32_t (&s0)[NP
   }
 }
 
-template <class T, int LAYOUT, int MT>
+// PR: ring slots of weight units (prefetch distance PR - 1 units).
+template <class T, int LAYOUT, int MT, int PR>
 struct XsWave {
   static constexpr bool NN = LAYOUT == DGF_LAYOUT_NN;
   static constexpr int RT = rt_of<LAYOUT, MT>();
@@ -115,9 +126,6 @@ struct XsWave {
   static constexpr int NI = 2 * RT;       // NN: lanes per slab row (16 bytes each)
   static constexpr int ROWS = 32 / RT;    // NN: slab rows per load instruction
   static constexpr int COLS = 16 * RT;    // output columns per tile
-  // ring slots of weight units (prefetch distance PR - 1 units); a third slot
-  // measured no faster
-  static constexpr int PR = 2;
   using WF = WFrag<LAYOUT, RT>;
 
   const GemmParams &p;
@@ -232,30 +240,33 @@ struct XsWave {
     pack(acc, v);
   }
 
-  // NN: half S of a leaf.  The 32 slab rows go to LDS transposed (element
-  // (k, n) at n*64 + 8 ((k>>3) ^ swz(n)) + (k&7)); this lane's rows are
-  // k = 32 S + lrow + ROWS i2 of columns n = 8 lcol + e, whose chunk
-  // (k>>3) ^ swz(n) is c ^ lx with c = ((32 S + ROWS i2) / 8) ^ e and
-  // lx = (lrow>>3) ^ lcol: eight base addresses plus the immediate 64 e.
+  // NN: half S of a leaf.  The 32 slab rows go to LDS as loaded (row-major,
+  // 16-byte writes), and each weight operand comes back in MFMA layout with
+  // two transposing reads (ds_read_b64_tr_b16: within each 16 lanes, the
+  // 4-element reads of lanes 4 r .. 4 r + 3 form row r of a 4 x 16 block and
+  // lane j receives its column j).  Lane (q = lane / 16, r, c = lane % 4)
+  // reads row k = 32 S + 8 q + 4 h + r, columns 16 rt + 4 c .. + 3, so that
+  // lane l obtains column 16 rt + l % 16 at K rows 32 S + 8 q + 4 h .. + 3.
   template <int S>
   __device__ __forceinline__ void half_nn(const WF &w, const typename T::frag (&x)[MT][2], f32x4 (&acc)[RT][MT]) const {
     const int lrow = lane / NI, lcol = lane % NI;
-    const int lx = (lrow >> 3) ^ lcol;
-    uint16_t *wp[8];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) wp[c] = slab + 8 * lcol * 64 + (lrow & 7) + 8 * (c ^ lx);
-#pragma unroll
-    for (int i2 = 0; i2 < RT; ++i2)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t word = w.v[i2][e >> 1];
-        wp[((32 * S + ROWS * i2) >> 3) ^ e][64 * e] = (uint16_t)((e & 1) ? (word >> 16) : word);
-      }
+    for (int i2 = 0; i2 < RT; ++i2) {
+      const int k = 32 * S + lrow + ROWS * i2;
+      *reinterpret_cast<u32x4 *>(&slab[k * 64 + 8 * (lcol ^ nn_swz(k))]) = w.v[i2];
+    }
     wave_lds_sync();  // this wave's slab writes land before its lanes read them
+    const int q = lane >> 4, r = (lane >> 2) & 3, c = lane & 3;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-      const int n = 16 * rt + r16;
-      const typename T::frag wf = *reinterpret_cast<const typename T::frag *>(&slab[n * 64 + 8 * ((4 * S + g4) ^ xs_swz(n))]);
+      s16x4 hv[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int k = 32 * S + 8 * q + 4 * h + r, n = 16 * rt + 4 * c;
+        hv[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4 *)&slab[k * 64 + 8 * ((n >> 3) ^ nn_swz(k)) + (n & 7)]);
+      }
+      const typename T::frag wf = __builtin_bit_cast(typename T::frag, __builtin_shufflevector(hv[0], hv[1], 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
       for (int t = 0; t < MT; ++t) acc[rt][t] = T::mfma(wf, x[t][S], S == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[rt][t]);
     }
@@ -432,10 +443,18 @@ struct XsWave {
   }
 };
 
-template <class T, int LAYOUT, int MT>
+// NLMAX: the largest leaf count of a wave in this launch.  The midpoint cuts
+// leave every wave ceil or floor of L / 2^(kd + log2 waves) leaves, so one
+// launch holds the shapes NLMAX and NLMAX - 1 only, and each instantiation
+// is register-allocated for those two alone.
+template <class T, int LAYOUT, int MT, int NLMAX>
 __global__ __launch_bounds__(kXsWaves * 64) void k_xs(GemmParams p) {
   extern __shared__ __attribute__((aligned(16))) uint32_t xs_lds[];
-  using Wv = XsWave<T, LAYOUT, MT>;
+  // NN units are half leaves: two of them in flight measured faster than one
+  // (except with 4 leaves and two token tiles, where the third slot spills);
+  // the NT kernel measured fastest with one whole leaf in flight
+  constexpr int PR = LAYOUT == DGF_LAYOUT_NN && !(MT == 2 && NLMAX == 4) ? 3 : 2;
+  using Wv = XsWave<T, LAYOUT, MT, PR>;
   const int waves = blockDim.x >> 6;
   const int dw = __builtin_ctz(waves);
   const int lane = threadIdx.x & 63;
@@ -483,17 +502,18 @@ __global__ __launch_bounds__(kXsWaves * 64) void k_xs(GemmParams p) {
        p.to_part ? p.part + ((int64_t)b * (1 << kd) + piece) * p.part_stride : p.C[b],
        p.to_part ? p.ldp : p.ldc[b],
        (LAYOUT == DGF_LAYOUT_NN ? p.K : p.N) * p.ldb[b] * 2};
-  // the wave's leaf count and whether it owns the partial last leaf, as
-  // compile-time shapes (nl is 1..4 by the launch plan)
-  switch (w.nl * 2 + (w.tail ? 1 : 0)) {
-    case 2: w.template run<1, false>(); break;
-    case 3: w.template run<1, true>(); break;
-    case 4: w.template run<2, false>(); break;
-    case 5: w.template run<2, true>(); break;
-    case 6: w.template run<3, false>(); break;
-    case 7: w.template run<3, true>(); break;
-    case 8: w.template run<4, false>(); break;
-    default: w.template run<4, true>(); break;
+  // the wave's leaf count (NLMAX or NLMAX - 1) and whether it owns the
+  // partial last leaf, as compile-time shapes
+  if (w.nl == NLMAX || NLMAX == 1) {
+    if (w.tail)
+      w.template run<NLMAX, true>();
+    else
+      w.template run<NLMAX, false>();
+  } else if constexpr (NLMAX > 1) {
+    if (w.tail)
+      w.template run<NLMAX - 1, true>();
+    else
+      w.template run<NLMAX - 1, false>();
   }
 }
 
@@ -510,6 +530,16 @@ size_t xs_lds_bytes(int layout, int mt, int waves) {
   return 2 * (size_t)waves * np * 64 * 4 + (size_t)waves * cols * 64 * 2;
 }
 
+template <class T, int LAYOUT, int MT>
+void launch_xs_nl(int nlmax, dim3 grid, dim3 block, size_t shm, hipStream_t stream, const GemmParams &p) {
+  switch (nlmax) {
+    case 1: dgf_launch((k_xs<T, LAYOUT, MT, 1>), grid, block, shm, stream, p); break;
+    case 2: dgf_launch((k_xs<T, LAYOUT, MT, 2>), grid, block, shm, stream, p); break;
+    case 3: dgf_launch((k_xs<T, LAYOUT, MT, 3>), grid, block, shm, stream, p); break;
+    default: dgf_launch((k_xs<T, LAYOUT, MT, 4>), grid, block, shm, stream, p); break;
+  }
+}
+
 template <class T>
 hipError_t launch_xs_t(int layout, GemmParams p, int nb, int waves, int groups, hipStream_t stream) {
   const int mt = p.M <= 16 ? 1 : 2;
@@ -517,16 +547,19 @@ hipError_t launch_xs_t(int layout, GemmParams p, int nb, int waves, int groups, 
   const dim3 grid((unsigned)groups, (unsigned)tiles_m, (unsigned)(nb << p.ksplit_depth));
   const dim3 block((unsigned)(64 * waves));
   const size_t shm = xs_lds_bytes(layout, mt, waves);
+  const int depth = p.ksplit_depth + __builtin_ctz((unsigned)waves);
+  const int nlmax = (p.L + (1 << depth) - 1) >> depth;
+  if (nlmax < 1 || nlmax > kMaxNL || (p.L >> depth) < 1) return hipErrorInvalidValue;
   if (layout == DGF_LAYOUT_NT) {
     if (mt == 1)
-      dgf_launch((k_xs<T, DGF_LAYOUT_NT, 1>), grid, block, shm, stream, p);
+      launch_xs_nl<T, DGF_LAYOUT_NT, 1>(nlmax, grid, block, shm, stream, p);
     else
-      dgf_launch((k_xs<T, DGF_LAYOUT_NT, 2>), grid, block, shm, stream, p);
+      launch_xs_nl<T, DGF_LAYOUT_NT, 2>(nlmax, grid, block, shm, stream, p);
   } else {
     if (mt == 1)
-      dgf_launch((k_xs<T, DGF_LAYOUT_NN, 1>), grid, block, shm, stream, p);
+      launch_xs_nl<T, DGF_LAYOUT_NN, 1>(nlmax, grid, block, shm, stream, p);
     else
-      dgf_launch((k_xs<T, DGF_LAYOUT_NN, 2>), grid, block, shm, stream, p);
+      launch_xs_nl<T, DGF_LAYOUT_NN, 2>(nlmax, grid, block, shm, stream, p);
   }
   return hipGetLastError();
 }
