@@ -1,6 +1,6 @@
 // All-K tree GEMM for few tokens (gfx950): the down projection.
 //
-// C[m][n] = T_K( A[m,:] . B[n,:] ) for M <= 24 tokens, A [M, K] and B [N, K]
+// C[m][n] = T_K( A[m,:] . B[n,:] ) for M <= 18 tokens, A [M, K] and B [N, K]
 // both K-contiguous, with the canonical tree of RL-Kernel PR #325, section
 // "Design".  The activation operand of the down projection (a, M x I) is a
 // few hundred KB, small enough to be read from L2 by every workgroup, so
@@ -17,9 +17,9 @@
 // Every workgroup reads all of A: 16 M_pad x 128 bytes of activation per
 // 2 KB weight leaf.  A compute unit keeps only so many cache-line misses in
 // flight, so activation lines compete with weight lines for them; measured on
-// the Qwen3-8B down projection, the all-K kernel beats the split-K kernel
-// with its join up to 24 tokens (two token tiles from 17), and loses past
-// that, when the activation lines outgrow what the join costs.
+// the Qwen3-8B down projection (forward at 12..24 tokens against the
+// split-K kernel with its join), the all-K kernel is faster up to 17 tokens
+// and slower from 20 (2.6 us at 24), so it takes at most 18.
 #include "dgf_device.hpp"
 #include "dgf_kernels.hpp"
 
@@ -30,6 +30,7 @@ constexpr int kAkWaves = 8;
 constexpr int kAkCols = 16;  // output columns per workgroup
 constexpr int kAkRing = 4;   // ring slots: three leaves in flight per wave
 constexpr int kAkMaxD = 6;   // depth of a wave subtree of at most 32 leaves
+constexpr int kAkMaxM = 18;  // tokens (two token tiles from 17)
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -223,7 +224,7 @@ hipError_t launch_allk_mt(const AllkParams &p, int nw, hipStream_t s) {
 }  // namespace
 
 bool allk_applies(int64_t M, int64_t N, int64_t K) {
-  if (M < 1 || M > 24 || N < 1 || K % kLeaf != 0) return false;
+  if (M < 1 || M > kAkMaxM || N < 1 || K % kLeaf != 0) return false;
   const int64_t L = K / kLeaf;
   if (L % kAkWaves != 0) return false;
   const int64_t nw = L / kAkWaves;
@@ -232,7 +233,7 @@ bool allk_applies(int64_t M, int64_t N, int64_t K) {
 }
 
 hipError_t launch_allk(const AllkParams &p, hipStream_t stream) {
-  if (p.M > 24) return hipErrorInvalidValue;
+  if (p.M > kAkMaxM) return hipErrorInvalidValue;
   if (p.fmt == FMT_F16) {
     if (p.M > 16) return launch_allk_mt<F16, 2>(p, p.L / kAkWaves, stream);
     return launch_allk_mt<F16, 1>(p, p.L / kAkWaves, stream);

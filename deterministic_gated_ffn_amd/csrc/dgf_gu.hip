@@ -14,7 +14,9 @@
 //
 // The activation operand stays on chip for the whole kernel: the first NR
 // leaves of a wave's subtree in registers, the rest in the wave's own LDS
-// region (a wave reads only what it wrote, so no barrier guards it).  Weights
+// region (a wave reads only what it wrote, so no barrier guards it).  It is
+// brought in during the first tile, a few leaves ahead of its first use, so
+// that its loads run beside the weight stream rather than before it.  Weights
 // stream through the wave as whole 128-byte row segments (8 rows per load
 // instruction, buffer loads on a rebased descriptor) staged through a
 // swizzled LDS slab into the MFMA layout; each weight byte is read from HBM
@@ -117,18 +119,67 @@ struct GuWave {
     }
   }
 
+  // Activation leaf j (all token blocks): whole 128-byte row segments (lane:
+  // row 8 s + lane / 8 of token block t, 16-byte chunk lane % 8 of the leaf;
+  // rows past M clamped to a valid row, never stored), every row segment by
+  // one instruction.  Fragment-layout loads would split every line over two.
+  __device__ __forceinline__ void load_x(int j, u32x4 (&raw)[MT][2]) const {
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int64_t r = m0 + 16 * t + 8 * s + (lane >> 3);
+        const uint16_t *row = p.x + (r < p.M ? r : p.M - 1) * p.ldx + 8 * (lane & 7);
+        raw[t][s] = __builtin_bit_cast(u32x4, load_frag<T>(row, (int64_t)(lo + j) * kLeaf));
+      }
+  }
+
+  // ... rearranged into the MFMA layout through the wave's slab, as the weight
+  // units are: the first NR leaves to registers, the rest to the wave's LDS.
+  template <int J>
+  __device__ __forceinline__ void place_x(const u32x4 (&raw)[MT][2], typename T::frag (&xr)[NR][MT][2]) const {
+    const int wr = lane >> 3, wc = lane & 7;
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s) *reinterpret_cast<u32x4 *>(&slab[(8 * s + wr) * 64 + 8 * (wc ^ wr)]) = raw[t][s];
+      wave_lds_sync();
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const typename T::frag f = *reinterpret_cast<const typename T::frag *>(&slab[r16 * 64 + 8 * ((4 * s + g4) ^ (r16 & 7))]);
+        if constexpr (J < NR)
+          xr[J][t][s] = f;
+        else
+          xl[((J - NR) * MT + t) * 2 * 64 + s * 64 + lane] = __builtin_bit_cast(u32x4, f);
+      }
+      wave_lds_sync();  // the slab's reads are done before it is rewritten
+    }
+  }
+
   // Units U.. of one tile: unit U is leaf U % NL of product U / NL, in ring
   // slot U % PR (PR divides the 2 NL units of a tile, so every tile starts in
   // slot 0); each unit first issues the loads of the unit PR - 1 ahead
-  // (possibly of the next tile) into the slot the previous unit freed.
-  template <int NL, int PR, int U>
-  __device__ __forceinline__ void units(int i, WF (&ring)[PR], const typename T::frag (&xr)[NR][MT][2], uint32_t (&v)[NP],
-                                        uint32_t (&st)[3][NP], uint32_t (&rg)[NP], const uint32_t (&voff)[2][2]) const {
+  // (possibly of the next tile) into the slot the previous unit freed.  In
+  // the first tile (FIRST) the gate units also bring in the activation: unit
+  // J issues the loads of activation leaf J + XD and places leaf J, whose
+  // loads went out XD units earlier, so that the activation arrives beside
+  // the weight stream instead of before it.
+  static constexpr int XD = 3;       // activation leaves in flight ahead of their first use
+  static constexpr int XS = XD + 1;  // their register slots
+  template <int NL, int PR, int U, bool FIRST>
+  __device__ __forceinline__ void units(int i, WF (&ring)[PR], typename T::frag (&xr)[NR][MT][2], u32x4 (&raw)[XS][MT][2],
+                                        uint32_t (&v)[NP], uint32_t (&st)[3][NP], uint32_t (&rg)[NP],
+                                        const uint32_t (&voff)[2][2]) const {
     constexpr int UN = 2 * NL;
     if constexpr (U < UN) {
       constexpr int b = U / NL, J = U % NL;
       constexpr int nx = U + PR - 1, nu = nx % UN;
       load_unit(i + nx / UN, nu / NL, nu % NL, ring[nx % PR], voff);
+      if constexpr (FIRST && U < NL) {
+        if constexpr (U + XD < NL) load_x(U + XD, raw[(U + XD) % XS]);
+        __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the placement
+        place_x<U>(raw[U % XS], xr);
+      }
       __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of this unit's MFMAs
       leaf<J>(ring[U % PR], xr, v);
       push_leaf<T, NP, NL, J>(v, st);
@@ -136,7 +187,7 @@ struct GuWave {
 #pragma unroll
         for (int q = 0; q < NP; ++q) rg[q] = v[q];
       }
-      units<NL, PR, U + 1>(i, ring, xr, v, st, rg, voff);
+      units<NL, PR, U + 1, FIRST>(i, ring, xr, raw, v, st, rg, voff);
     }
   }
 
@@ -192,8 +243,8 @@ struct GuWave {
   template <int NL>
   __device__ __forceinline__ void run() const {
     if (ntl <= 0) return;
-    // the first weight units go out before the activation loads: the stream
-    // starts while the activations arrive
+    // the first weight units go out before the first activation loads: the
+    // stream starts while the activations arrive
     uint32_t voff[2][2];
 #pragma unroll
     for (int b = 0; b < 2; ++b)
@@ -204,47 +255,18 @@ struct GuWave {
     WF ring[PR];
 #pragma unroll
     for (int g = 0; g < PR - 1; ++g) load_unit(g / (2 * NL), (g % (2 * NL)) / NL, g % NL, ring[g], voff);
-    // activation fragments of this wave's leaves: the first NR in registers,
-    // the rest in LDS.  They are loaded as whole 128-byte row segments (lane:
-    // row 8 s + lane / 8 of token block t, 16-byte chunk lane % 8 of the leaf;
-    // rows past M clamped to a valid row, never stored), every row segment
-    // by one instruction, and rearranged into the MFMA layout through the
-    // wave's slab, as the weight units are.  Fragment-layout loads would
-    // split every line over two instructions.
     typename T::frag xr[NR][MT][2];
-    u32x4 raw[NL][MT][2];
+    u32x4 raw[XS][MT][2];
 #pragma unroll
-    for (int t = 0; t < MT; ++t)
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const int64_t r = m0 + 16 * t + 8 * s + (lane >> 3);
-        const uint16_t *row = p.x + (r < p.M ? r : p.M - 1) * p.ldx + 8 * (lane & 7);
-#pragma unroll
-        for (int j = 0; j < NL; ++j)
-          raw[j][t][s] = __builtin_bit_cast(u32x4, load_frag<T>(row, (int64_t)(lo + j) * kLeaf));
-      }
-    const int wr = lane >> 3, wc = lane & 7;
-#pragma unroll
-    for (int j = 0; j < NL; ++j)
-#pragma unroll
-      for (int t = 0; t < MT; ++t) {
-#pragma unroll
-        for (int s = 0; s < 2; ++s) *reinterpret_cast<u32x4 *>(&slab[(8 * s + wr) * 64 + 8 * (wc ^ wr)]) = raw[j][t][s];
-        wave_lds_sync();
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const typename T::frag f = *reinterpret_cast<const typename T::frag *>(&slab[r16 * 64 + 8 * ((4 * s + g4) ^ (r16 & 7))]);
-          if (j < NR)
-            xr[j < NR ? j : 0][t][s] = f;
-          else
-            xl[((j - NR) * MT + t) * 2 * 64 + s * 64 + lane] = __builtin_bit_cast(u32x4, f);
-        }
-        wave_lds_sync();  // the slab's reads are done before it is rewritten
-      }
-    wave_lds_sync();
-    for (int i = 0; i < ntl; ++i) {
+    for (int j = 0; j < XD && j < NL; ++j) load_x(j, raw[j]);
+    {
       uint32_t v[NP], st[3][NP], rg[NP];
-      units<NL, PR, 0>(i, ring, xr, v, st, rg, voff);
+      units<NL, PR, 0, true>(0, ring, xr, raw, v, st, rg, voff);
+      finish_tile(0, rg, v);
+    }
+    for (int i = 1; i < ntl; ++i) {
+      uint32_t v[NP], st[3][NP], rg[NP];
+      units<NL, PR, 0, false>(i, ring, xr, raw, v, st, rg, voff);
       finish_tile(i, rg, v);
     }
   }

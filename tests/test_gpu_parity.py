@@ -283,13 +283,14 @@ def test_tiny_ffn_forward_backward_bitwise():
 @pytest.mark.parametrize("M,H,I", [(1, 64, 64), (3, 128, 320), (20, 256, 768), (37, 200, 136), (64, 128, 256),
                                    (5, 512, 200), (17, 960, 1000), (32, 2112, 136), (9, 4096, 40), (32, 576, 24),
                                    (65, 128, 72), (100, 256, 200), (130, 256, 200), (256, 192, 520),
-                                   # down projection over all K per workgroup (M <= 24): 1..32 leaves per wave,
+                                   # down projection over all K per workgroup (M <= 18): 1..32 leaves per wave,
                                    # ragged H
                                    (3, 198, 512), (11, 64, 1024), (16, 136, 1536), (16, 96, 2048), (5, 40, 3072),
                                    (8, 72, 4096), (15, 48, 6144), (12, 16, 12288), (2, 32, 8192), (16, 24, 16384),
                                    (4, 8, 512), (2, 1, 1024),
-                                   # ... and with two token tiles (17 to 24 tokens)
-                                   (17, 64, 1024), (20, 200, 1536), (24, 136, 3072), (23, 16, 12288),
+                                   # ... and with two token tiles (17, 18 tokens); from 19 the streaming kernel
+                                   (17, 64, 1024), (18, 200, 1536), (18, 16, 12288),
+                                   (19, 64, 1024), (20, 200, 1536), (24, 136, 3072), (23, 16, 12288),
                                    # fused gate/up with more 16-column tiles than workgroups, unevenly
                                    # spread (301 and 514 tiles, the last one ragged)
                                    (8, 512, 4810), (32, 576, 8220)])
