@@ -243,8 +243,13 @@ struct GuWave {
   template <int NL>
   __device__ __forceinline__ void run() const {
     if (ntl <= 0) return;
-    // the first weight units go out before the first activation loads: the
-    // stream starts while the activations arrive
+    // the first activation leaves go out before the first weight units: all
+    // workgroups start together, and a load issued behind the weight units
+    // would wait for the whole chip's first units to drain
+    typename T::frag xr[NR][MT][2];
+    u32x4 raw[XS][MT][2];
+#pragma unroll
+    for (int j = 0; j < XD && j < NL; ++j) load_x(j, raw[j]);
     uint32_t voff[2][2];
 #pragma unroll
     for (int b = 0; b < 2; ++b)
@@ -255,10 +260,6 @@ struct GuWave {
     WF ring[PR];
 #pragma unroll
     for (int g = 0; g < PR - 1; ++g) load_unit(g / (2 * NL), (g % (2 * NL)) / NL, g % NL, ring[g], voff);
-    typename T::frag xr[NR][MT][2];
-    u32x4 raw[XS][MT][2];
-#pragma unroll
-    for (int j = 0; j < XD && j < NL; ++j) load_x(j, raw[j]);
     {
       uint32_t v[NP], st[3][NP], rg[NP];
       units<NL, PR, 0, true>(0, ring, xr, raw, v, st, rg, voff);

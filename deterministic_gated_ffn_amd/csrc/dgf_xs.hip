@@ -385,9 +385,29 @@ struct XsWave {
   __device__ __forceinline__ void run() const {
     constexpr int NF = NL - (TAIL ? 1 : 0);
     if (ntl <= 0) return;  // no tile for this workgroup (the same for all its waves)
-    // the first weight units are issued before the activation loads, so that
-    // their HBM latency overlaps the activation's (registers only: the slab
-    // is free for the rearrangement below)
+    // The activation loads go out first, then the first weight units: all
+    // workgroups start together, and an activation load issued behind the
+    // weight units would wait for the whole chip's first units (megabytes)
+    // to drain; this way the activation is rearranged while the weights are
+    // on their way.  Stationary activation fragments of this wave's leaves
+    // are loaded as whole 128-byte row segments (lane: row 8 s + lane / 8 of
+    // token block t, 16-byte chunk lane % 8 of the leaf; rows past M clamped,
+    // never stored; zeros past K) and rearranged into the MFMA layout through
+    // this wave's slab: fragment-layout loads would split every line over two
+    // instructions.
+    u32x4 raw[NL][MT][2];
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int64_t r = m0 + 16 * t + 8 * s + (lane >> 3);
+        const uint16_t *row = p.A[b] + (r < p.M ? r : p.M - 1) * p.lda[b];
+#pragma unroll
+        for (int j = 0; j < NL; ++j) {
+          const int64_t k = (int64_t)(lo + j) * kLeaf + 8 * (lane & 7);
+          raw[j][t][s] = __builtin_bit_cast(u32x4, (TAIL && j == NF) ? load_frag_tail<T>(row, k, p.K) : load_frag<T>(row, k));
+        }
+      }
     WF ring[PR];
     uint32_t voff[2 * RT];
     unit_offsets(voff);
@@ -399,26 +419,8 @@ struct XsWave {
         load_unit(g / UN, NN ? u / 2 : u, NN ? u % 2 : 0, ring[g], voff);
       }
     }
-    // stationary activation fragments of this wave's leaves, loaded as whole
-    // 128-byte row segments (lane: row 8 s + lane / 8 of token block t,
-    // 16-byte chunk lane % 8 of the leaf; rows past M clamped, never stored;
-    // zeros past K) and rearranged into the MFMA layout through this wave's
-    // slab: fragment-layout loads would split every line over two instructions
     XFrag<T, MT> xs;
     {
-      u32x4 raw[NL][MT][2];
-#pragma unroll
-      for (int t = 0; t < MT; ++t)
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const int64_t r = m0 + 16 * t + 8 * s + (lane >> 3);
-          const uint16_t *row = p.A[b] + (r < p.M ? r : p.M - 1) * p.lda[b];
-#pragma unroll
-          for (int j = 0; j < NL; ++j) {
-            const int64_t k = (int64_t)(lo + j) * kLeaf + 8 * (lane & 7);
-            raw[j][t][s] = __builtin_bit_cast(u32x4, (TAIL && j == NF) ? load_frag_tail<T>(row, k, p.K) : load_frag<T>(row, k));
-          }
-        }
       const int wr = lane >> 3, wc = lane & 7;
 #pragma unroll
       for (int j = 0; j < NL; ++j)
