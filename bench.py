@@ -313,6 +313,7 @@ def main():
         fb["32"] = stats_entry(st, step_bytes(M))
         result["fwd_bwd"] = fb
         result["two_stream_lanes"] = two_stream_lanes(W, x, dy, args, kernels)
+        result["shards"] = shard_legs(W, x, dy, args, fwd["32"]["us"], result["fwd_bwd"]["32"]["us"])
 
     if not args.quick:
         result["long_sequence"] = long_sequence(W[0], samples=args.samples)
@@ -441,6 +442,79 @@ def two_stream_lanes(W, x, dy, args, kernels) -> dict:
     print(f"[bench] dX lanes: two streams {out['two_streams']['us']:.1f} us, one stream "
           f"{out['one_stream']['us']:.1f} us, fused launch {out['fused_lanes_kernel_us']} us",
           file=sys.stderr, flush=True)
+    return out
+
+
+def shard_legs(W, x, dy, args, fwd_us: float, step_us: float) -> dict:
+    """The I-sharded forward and training step at M=32 on one GPU, S = 2, 4, 8:
+    every shard's forward (and backward, its dX lanes kept) on the weight
+    shard views (W_gate, W_up rows and W_down columns of the I range), then
+    the rank-tree combines: y over the shards; the gate lane and the up lane
+    over the shards, then dX = combine(G, U), the gate lane first.  Checked
+    bitwise against the unsharded call before timing; the overhead is against
+    the unsharded figures of the same run."""
+    import torch
+    from deterministic_gated_ffn_amd import binding as dgf
+    from deterministic_gated_ffn_amd import inputs
+
+    H, I = x.shape[1], W[0][0].shape[0]
+    out = {}
+    for S in (2, 4, 8):
+        Is = I // S
+
+        def views(k, S=S, Is=Is):
+            wg, wu, wd = W[k % len(W)]
+            return [(wg[r * Is:(r + 1) * Is], wu[r * Is:(r + 1) * Is], wd[:, r * Is:(r + 1) * Is]) for r in range(S)]
+
+        def fwd_s(k):
+            return dgf.tree_combine([dgf.ffn_fwd(x, *v) for v in views(k)])
+
+        def step_s(k):
+            ys, Gs, Us = [], [], []
+            for v in views(k):
+                y, g, u = dgf.ffn_fwd(x, *v, training=True)
+                r = dgf.ffn_bwd(dy, x, g, u, *v, lanes=True)
+                ys.append(y); Gs.append(r["G"]); Us.append(r["U"])
+            G, U = dgf.tree_combine(Gs), dgf.tree_combine(Us)
+            return dgf.tree_combine(ys), dgf.tree_combine([G, U])
+
+        wg, wu, wd = W[0]
+        y_full, g, u = dgf.ffn_fwd(x, wg, wu, wd, training=True)
+        dx_full = dgf.ffn_bwd(dy, x, g, u, wg, wu, wd)["dX"]
+        y_s, dx_s = step_s(0)
+        same = bool((inputs.bits(fwd_s(0)) == inputs.bits(y_full)).all()
+                    and (inputs.bits(y_s) == inputs.bits(y_full)).all()
+                    and (inputs.bits(dx_s) == inputs.bits(dx_full)).all())
+        for k in range(args.warmup):
+            fwd_s(k)
+            step_s(k)
+        f = stats_entry(sample_us(fwd_s, args.steps, args.samples), fwd_bytes(x.shape[0]))
+        t = stats_entry(sample_us(step_s, args.steps, args.samples), step_bytes(x.shape[0]))
+
+        # one rank's share: shard 0's forward and step alone (what each of S GPUs would compute)
+        def fwd_0(k):
+            return dgf.ffn_fwd(x, *views(k)[0])
+
+        def step_0(k):
+            v = views(k)[0]
+            y, g, u = dgf.ffn_fwd(x, *v, training=True)
+            return dgf.ffn_bwd(dy, x, g, u, *v, lanes=True)
+
+        for k in range(args.warmup):
+            fwd_0(k)
+            step_0(k)
+        f0 = stats_entry(sample_us(fwd_0, args.steps, args.samples))
+        t0 = stats_entry(sample_us(step_0, args.steps, args.samples))
+        out[str(S)] = {"forward": f, "fwd_bwd": t, "bitwise_equal_to_unsharded": same,
+                       "forward_overhead_us": round(f["us"] - fwd_us, 2),
+                       "fwd_bwd_overhead_us": round(t["us"] - step_us, 2),
+                       "one_shard_forward": f0, "one_shard_fwd_bwd": t0}
+        print(f"[bench] I-shards S={S}: all shards forward {f['us']:.1f} us (+{f['us'] - fwd_us:.1f}), fwd+bwd "
+              f"{t['us']:.1f} us (+{t['us'] - step_us:.1f}); one shard {f0['us']:.1f} / {t0['us']:.1f} us; "
+              f"bitwise {'equal' if same else 'DIFFERENT'}", file=sys.stderr, flush=True)
+    out["note"] = ("all shards of one GPU run one after the other on one stream, then the combines: the overhead "
+                   "is their extra launches and smaller grids, not a multi-GPU figure; one_shard_* is one "
+                   "rank's own compute at I/S (no exchange)")
     return out
 
 
