@@ -97,6 +97,26 @@ def test_gemm_tree_matches_oracle(layout, M, N, K):
 
 # many tokens: the tiled kernel (128 x 128 output tiles, K pieces of lower
 # subtrees of at most 4 leaves under an LDS-parked top of up to 3 levels)
+# The streaming kernel is compiled per launch for the largest leaf count of
+# its waves (1..4, the waves holding that many or one fewer), with or without
+# a partial last leaf, at one or two token tiles: K over 8 waves gives 1..4
+# leaves per wave (512 .. 2048), the same with a partial last leaf (500 ..
+# 2000), 10 and 33 leaves (waves of unequal counts); N = 96 leaves a ragged
+# column tile in every layout.
+@pytest.mark.parametrize("M", [16, 32])
+@pytest.mark.parametrize("K", [512, 1024, 1536, 2048, 500, 1000, 1500, 2000, 640, 2112])
+@pytest.mark.parametrize("layout", ["NT", "NN"])
+def test_streaming_kernel_leaf_counts(layout, K, M):
+    N = 96
+    rng = np.random.default_rng(7 * K + M)
+    A = rnd(rng, (M, K)); Bnk = rnd(rng, (N, K), 0.02)
+    b = Bnk if layout == "NT" else np.ascontiguousarray(Bnk.T)
+    expect = oracle.gemm_tree(A, b, layout)
+    got = dgf.gemm_tree(layout, padded(A), padded(b))
+    torch.cuda.synchronize()
+    assert_bitwise(got, expect, f"{layout} {M}x{N}x{K}")
+
+
 MM_SHAPES = [(128, 128, 64), (130, 200, 100), (256, 64, 4096), (300, 257, 1000), (256, 256, 12288), (129, 17, 520),
              (512, 384, 3000), (200, 1000, 8)]
 
