@@ -461,10 +461,13 @@ def shard_legs(W, x, dy, args, fwd_us: float, step_us: float) -> dict:
     out = {}
     for S in (2, 4, 8):
         Is = I // S
+        # the shard views of every weight copy, made once: slicing tensors in the timed calls
+        # would make the host, not the GPU, the bottleneck at 8 shards
+        shard_views = [[(wg[r * Is:(r + 1) * Is], wu[r * Is:(r + 1) * Is], wd[:, r * Is:(r + 1) * Is]) for r in range(S)]
+                       for (wg, wu, wd) in W]
 
-        def views(k, S=S, Is=Is):
-            wg, wu, wd = W[k % len(W)]
-            return [(wg[r * Is:(r + 1) * Is], wu[r * Is:(r + 1) * Is], wd[:, r * Is:(r + 1) * Is]) for r in range(S)]
+        def views(k, shard_views=shard_views):
+            return shard_views[k % len(shard_views)]
 
         def fwd_s(k):
             return dgf.tree_combine([dgf.ffn_fwd(x, *v) for v in views(k)])
