@@ -48,24 +48,66 @@ constexpr int kMmMaxNL = 4;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// Tree values stay in FP32 form: the stored type's rounding kept as an FP32
-// value (T::rf; for BF16 one v_cvt_pk_bf16_f32 with a zero partner), so a node
-// is one FP32 add and one rounding; T::pack_x packs two such values.
+// A lane's 32 tree values (tile i = tn TM + tm, element e) in the form that
+// makes a node cheapest for the stored type.
+//  - BF16: 32 FP32 registers, each value in FP32 form (the BF16 rounding kept
+//    as an FP32 value, low half zero: one v_cvt_pk_bf16_f32 with a zero
+//    partner), so a node is one FP32 add and one rounding.
+//  - FP16: 16 registers of packed FP16 pairs (elements 2k and 2k + 1 of a
+//    tile), so that one v_pk_add_f16 makes two nodes.  An FP16 add rounds the
+//    exact sum once; rounding it to FP32 first and then to FP16 gives the same
+//    value, because FP32 carries at least 2 * 11 + 2 significant bits (the
+//    double rounding of a sum is innocuous then), and the exact sum of two
+//    FP16 numbers below the FP16 normal range is exact in FP32.
+template <class T>
+struct Tv;
+template <>
+struct Tv<Bf16> {
+  typedef float V;
+  static constexpr int N = kMmNV;
+  static constexpr int kLeafValu = kMmNV, kNodeValu = 2 * kMmNV;  // VALU per leaf rounding, per merge
+  static __device__ __forceinline__ void leaf(const f32x4 &a, V (&v)[N], int i) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[4 * i + e] = Bf16::rf(a[e]);
+  }
+  static __device__ __forceinline__ V node(V l, V r) { return Bf16::rf(l + r); }
+  // packed pair k (elements 2k, 2k + 1 of the lane's values) of stored values
+  static __device__ __forceinline__ uint32_t pair(const V (&v)[N], int k) { return Bf16::pack_x(v[2 * k], v[2 * k + 1]); }
+  static __device__ __forceinline__ void merge_pair(uint32_t l, V (&v)[N], int k) {
+    v[2 * k] = Bf16::rf(Bf16::lo(l) + v[2 * k]);
+    v[2 * k + 1] = Bf16::rf(Bf16::hi(l) + v[2 * k + 1]);
+  }
+};
+template <>
+struct Tv<F16> {
+  typedef uint32_t V;
+  static constexpr int N = kMmNV / 2;
+  static constexpr int kLeafValu = kMmNV / 2, kNodeValu = kMmNV / 2;
+  static __device__ __forceinline__ void leaf(const f32x4 &a, V (&v)[N], int i) {
+    v[2 * i] = F16::pack(a[0], a[1]);
+    v[2 * i + 1] = F16::pack(a[2], a[3]);
+  }
+  static __device__ __forceinline__ V node(V l, V r) {
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, l) + __builtin_bit_cast(f16x2, r));
+  }
+  static __device__ __forceinline__ uint32_t pair(const V (&v)[N], int k) { return v[k]; }
+  static __device__ __forceinline__ void merge_pair(uint32_t l, V (&v)[N], int k) { v[k] = node(l, v[k]); }
+};
 
-// Feed leaf J (values v, FP32 form) of an N-leaf lower subtree (N <= 4):
-// merge it with the pending left siblings its position closes, then park it
-// at its depth; after the last leaf v is the subtree root.
+// Feed leaf J (values v) of an N-leaf lower subtree (N <= 4): merge it with
+// the pending left siblings its position closes, then park it at its depth;
+// after the last leaf v is the subtree root.
 template <class T, int N, int J>
-__device__ __forceinline__ void push_f(float (&v)[kMmNV], float (&st)[2][kMmNV]) {
+__device__ __forceinline__ void push_f(typename Tv<T>::V (&v)[Tv<T>::N], typename Tv<T>::V (&st)[2][Tv<T>::N]) {
   constexpr LeafPos lp = leaf_pos(N, J);
 #pragma unroll
   for (int t = 0; t < lp.m; ++t)
 #pragma unroll
-    for (int q = 0; q < kMmNV; ++q) v[q] = T::rf(st[lp.D - 1 - t][q] + v[q]);
+    for (int q = 0; q < Tv<T>::N; ++q) v[q] = Tv<T>::node(st[lp.D - 1 - t][q], v[q]);
   constexpr int d = lp.D - lp.m;
   if constexpr (d > 0) {
 #pragma unroll
-    for (int q = 0; q < kMmNV; ++q) st[d - 1][q] = v[q];
+    for (int q = 0; q < Tv<T>::N; ++q) st[d - 1][q] = v[q];
   }
 }
 
@@ -160,14 +202,15 @@ struct MmWg {
       for (int tm = 0; tm < kMmTM; ++tm) acc[tn][tm] = T::mfma(bf1[tn], af1[tm], acc[tn][tm]);
   }
 
-  // A leaf's accumulators rounded to the stored type, FP32 form.
-  __device__ __forceinline__ void round_leaf(const f32x4 (&acc)[kMmTN][kMmTM], float (&v)[kMmNV]) const {
+  typedef typename Tv<T>::V V;
+  static constexpr int NV = Tv<T>::N;
+
+  // A leaf's accumulators rounded to the stored type, as tree values.
+  __device__ __forceinline__ void round_leaf(const f32x4 (&acc)[kMmTN][kMmTM], V (&v)[NV]) const {
 #pragma unroll
     for (int tn = 0; tn < kMmTN; ++tn)
 #pragma unroll
-      for (int tm = 0; tm < kMmTM; ++tm)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[(tn * kMmTM + tm) * 4 + e] = T::rf(acc[tn][tm][e]);
+      for (int tm = 0; tm < kMmTM; ++tm) Tv<T>::leaf(acc[tn][tm], v, tn * kMmTM + tm);
   }
 
   // Leaf j (leaf J of a lower subtree of NL leaves) from stage s into acc, in
@@ -182,13 +225,12 @@ struct MmWg {
   // root in v afterwards.
   template <int NL, int J, bool FIN>
   __device__ __forceinline__ void one_leaf(int j, int s, u32x4 (&nx)[4], const f32x4 (&prev)[kMmTN][kMmTM],
-                                           f32x4 (&acc)[kMmTN][kMmTM], float (&v)[kMmNV],
-                                           float (&st)[2][kMmNV]) const {
+                                           f32x4 (&acc)[kMmTN][kMmTM], V (&v)[NV], V (&st)[2][NV]) const {
     // merges of the tree step beside the MFMAs (-1: none), and the VALU
     // instructions to put beside each MFMA (a rounding, then an add and a
     // rounding per merge, per value)
     constexpr int m = J > 0 ? leaf_pos(NL, J - 1).m : FIN ? leaf_pos(NL, NL - 1).m : -1;
-    constexpr int vpm = m < 0 ? 1 : (kMmNV * (1 + 2 * m) + 15) / 16;
+    constexpr int vpm = m < 0 ? 1 : (Tv<T>::kLeafValu + m * Tv<T>::kNodeValu + 15) / 16;
     __builtin_amdgcn_sched_barrier(0);
     leaf_mfma(s, acc);
     if constexpr (J > 0) {
@@ -221,7 +263,7 @@ struct MmWg {
   // every leaf are compile-time, and the two accumulator sets alternate with J.
   template <int NL, int J, int P0>
   __device__ __forceinline__ void leaves(int j, u32x4 (&r0)[4], u32x4 (&r1)[4], f32x4 (&prev)[kMmTN][kMmTM],
-                                         f32x4 (&acc)[kMmTN][kMmTM], float (&v)[kMmNV], float (&st)[2][kMmNV]) const {
+                                         f32x4 (&acc)[kMmTN][kMmTM], V (&v)[NV], V (&st)[2][NV]) const {
     if constexpr (J < NL) {
       constexpr int S = (P0 ^ J) & 1;
       if constexpr (S == 0)
@@ -236,8 +278,8 @@ struct MmWg {
   }
 
   template <int NL>
-  __device__ __forceinline__ void lower_tree(int j, u32x4 (&r0)[4], u32x4 (&r1)[4], float (&v)[kMmNV]) const {
-    float st[2][kMmNV];
+  __device__ __forceinline__ void lower_tree(int j, u32x4 (&r0)[4], u32x4 (&r1)[4], V (&v)[NV]) const {
+    V st[2][NV];
     f32x4 a0[kMmTN][kMmTM], a1[kMmTN][kMmTM];
     if (((j - plo) & 1) == 0)
       leaves<NL, 0, 0>(j, r0, r1, a0, a1, v, st);
@@ -252,7 +294,7 @@ struct MmWg {
   // after leaf 0 of a subtree, `upper` takes the previous subtree's root.
   template <int NL, int J, int P0, class UP>
   __device__ __forceinline__ void leaves_d(int j, u32x4 (&r0)[4], u32x4 (&r1)[4], f32x4 (&a0)[kMmTN][kMmTM],
-                                           f32x4 (&a1)[kMmTN][kMmTM], float (&v)[kMmNV], float (&st)[2][kMmNV],
+                                           f32x4 (&a1)[kMmTN][kMmTM], V (&v)[NV], V (&st)[2][NV],
                                            const UP &upper) const {
     if constexpr (J < NL) {
       constexpr int S = (P0 ^ J) & 1;
@@ -265,15 +307,15 @@ struct MmWg {
     }
   }
 
-  __device__ __forceinline__ void store_root(const float (&v)[kMmNV], uint16_t *out, int64_t ldo) const {
+  __device__ __forceinline__ void store_root(const V (&v)[NV], uint16_t *out, int64_t ldo) const {
 #pragma unroll
     for (int tn = 0; tn < kMmTN; ++tn)
 #pragma unroll
       for (int tm = 0; tm < kMmTM; ++tm) {
         const int64_t m = m0 + 32 * wm + 16 * tm + r16, n = n0 + 64 * wn + 16 * tn + 4 * g4;
         if (m >= p.M || n >= p.N) continue;
-        const int i = (tn * kMmTM + tm) * 4;
-        const uint32_t lo2 = T::pack_x(v[i], v[i + 1]), hi2 = T::pack_x(v[i + 2], v[i + 3]);
+        const int i = (tn * kMmTM + tm) * 2;  // the tile's two packed pairs
+        const uint32_t lo2 = Tv<T>::pair(v, i), hi2 = Tv<T>::pair(v, i + 1);
         uint16_t *dst = out + m * ldo + n;
         if (n + 3 < p.N) {
           *reinterpret_cast<uint2 *>(dst) = make_uint2(lo2, hi2);
@@ -292,18 +334,14 @@ struct MmWg {
 // (each lane reads back only what it wrote; consecutive lanes, consecutive
 // dwords).
 template <class T>
-__device__ __forceinline__ void park(uint32_t *base, int t, const float (&v)[kMmNV]) {
+__device__ __forceinline__ void park(uint32_t *base, int t, const typename Tv<T>::V (&v)[Tv<T>::N]) {
 #pragma unroll
-  for (int q = 0; q < kMmNP; ++q) base[(t * kMmNP + q) * 64] = T::pack_x(v[2 * q], v[2 * q + 1]);
+  for (int q = 0; q < kMmNP; ++q) base[(t * kMmNP + q) * 64] = Tv<T>::pair(v, q);
 }
 template <class T>
-__device__ __forceinline__ void merge(const uint32_t *base, int t, float (&v)[kMmNV]) {
+__device__ __forceinline__ void merge(const uint32_t *base, int t, typename Tv<T>::V (&v)[Tv<T>::N]) {
 #pragma unroll
-  for (int q = 0; q < kMmNP; ++q) {
-    const uint32_t l = base[(t * kMmNP + q) * 64];
-    v[2 * q] = T::rf(T::lo(l) + v[2 * q]);
-    v[2 * q + 1] = T::rf(T::hi(l) + v[2 * q + 1]);
-  }
+  for (int q = 0; q < kMmNP; ++q) Tv<T>::merge_pair(base[(t * kMmNP + q) * 64], v, q);
 }
 
 // NLH: the larger of the two lower-subtree sizes (the smaller is NLH - 1).
@@ -364,7 +402,9 @@ __global__ __launch_bounds__(kMmWaves * 64) void k_mm(GemmParams p) {
   __syncthreads();
 
   // lower subtrees in order; the top `up` levels over their roots
-  float v[kMmNV];
+  typedef typename Tv<T>::V V;
+  constexpr int NV = Tv<T>::N;
+  V v[NV];
   uint32_t *upl = reinterpret_cast<uint32_t *>(reinterpret_cast<char *>(mm_lds) + 2 * kMmStage) +
                   (size_t)wave * 3 * kMmNP * 64 + lane;
   const int nsub = 1 << up;
@@ -381,17 +421,17 @@ __global__ __launch_bounds__(kMmWaves * 64) void k_mm(GemmParams p) {
     // next one's first MFMAs (the first subtree's leaf 0 finalises zeros,
     // which are dropped)
     f32x4 a0[kMmTN][kMmTM], a1[kMmTN][kMmTM];
-    float st[2][kMmNV];
+    V st[2][NV];
 #pragma unroll
     for (int tn = 0; tn < kMmTN; ++tn)
 #pragma unroll
       for (int tm = 0; tm < kMmTM; ++tm) a0[tn][tm] = a1[tn][tm] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int q = 0; q < kMmNV; ++q) st[0][q] = st[1][q] = 0.f;
+    for (int q = 0; q < NV; ++q) st[0][q] = st[1][q] = V(0);
     for (int sidx = 0; sidx < nsub; ++sidx) {
       // root of subtree sidx - 1 into the top levels: merge with the pending
       // left subtrees its position closes, then park it (it is not the last)
-      auto upper = [&](float (&rv)[kMmNV]) {
+      auto upper = [&](V (&rv)[NV]) {
         if (sidx == 0) return;
         int t = 0;
         for (; ((sidx - 1) >> t) & 1; ++t) merge<T>(upl, t, rv);
@@ -406,7 +446,7 @@ __global__ __launch_bounds__(kMmWaves * 64) void k_mm(GemmParams p) {
         w.template leaves_d<NLH, 0, 0>(j, r0, r1, a0, a1, v, st, upper);
         if (sidx + 1 < nsub) {
           ++sidx;
-          auto upper1 = [&](float (&rv)[kMmNV]) {
+          auto upper1 = [&](V (&rv)[NV]) {
             int t = 0;
             for (; ((sidx - 1) >> t) & 1; ++t) merge<T>(upl, t, rv);
             park<T>(upl, t, rv);

@@ -116,6 +116,54 @@ def test_f16_leaf_block_rule_adversarial(dist, K):
     assert_bitwise(got, expect, f"fp16 leaf {dist} K={K}")
 
 
+@pytest.mark.parametrize("dist", ["wide", "cancel", "subnormal", "ties", "tiny", "negzero", "large"])
+@pytest.mark.parametrize("K", [200, 640, 2048])
+def test_f16_tiled_tree_adversarial(dist, K):
+    # The tiled kernel (128 tokens and more) keeps FP16 tree values as packed
+    # pairs and adds two nodes with one packed FP16 add; these inputs make the
+    # nodes round at ties, sum in the FP16 subnormal range, cancel to zero,
+    # meet negative zeros (leaves of tiny negative products round to -0) and
+    # overflow to infinity.  K = 200 ends in a partial leaf, K = 640 splits
+    # into lower subtrees of 2 and 3 leaves, K = 2048 into eight of 4.
+    rng = np.random.default_rng(zlib.crc32(f"f16/tiled/{dist}/{K}".encode()))
+    M, N = 160, 144
+    if dist == "wide":
+        A, B = wide(rng, (M, K), -14, 3), wide(rng, (N, K), -14, 3)
+    elif dist == "cancel":
+        A = wide(rng, (M, K), -4, 4)
+        A[:, K // 2:] = A[:, :K - K // 2][:, :K // 2] ^ np.uint16(0x8000)
+        B = np.where(rng.random((N, K)) < 0.1, wide(rng, (N, K), -2, 2), np.uint16(0x3C00)).astype(np.uint16)
+    elif dist == "subnormal":
+        A = wide(rng, (M, K), -14, -10, sub=0.5)
+        B = np.where(rng.random((N, K)) < 0.5, wide(rng, (N, K), 0, 4), wide(rng, (N, K), -14, 0, sub=0.3))
+        B = B.astype(np.uint16)
+    elif dist == "ties":
+        A = h(np.where(rng.random((M, K)) < 0.3, 2.0 ** -rng.integers(9, 13, (M, K)), 0)
+              * np.where(rng.random((M, K)) < 0.7, 1, -1))
+        A[:, ::64] = 0x3C00
+        B = np.full((N, K), 0x3C00, np.uint16)
+    elif dist == "tiny":
+        A, B = wide(rng, (M, K), -14, -9, sub=0.3), wide(rng, (N, K), -14, -9, sub=0.3)
+    elif dist == "negzero":
+        # subnormal operands of at most 2^-20: every leaf is below 2^-25 and
+        # rounds to a zero of its sign; whole leaves of B share a sign, mostly
+        # negative, so that some rows have only negative leaves
+        A = rng.integers(1, 17, size=(M, K)).astype(np.uint16)
+        sgn = (rng.random((N, (K + 63) // 64)) < 0.92).repeat(64, axis=1)[:, :K].astype(np.uint16)
+        B = (rng.integers(1, 17, size=(N, K)).astype(np.uint16) | (sgn << 15)).astype(np.uint16)
+        B[rng.random((N, K)) < 0.02] = 0
+    else:  # positive products up to 2^10: leaves and nodes overflow FP16 to +infinity
+        A, B = wide(rng, (M, K), 0, 5) & np.uint16(0x7FFF), wide(rng, (N, K), 0, 5) & np.uint16(0x7FFF)
+    expect = oracle.gemm_tree(A, B, "NT", "fp16")
+    got = dgf.gemm_tree("NT", padded(A), padded(B))
+    torch.cuda.synchronize()
+    assert_bitwise(got, expect, f"fp16 tiled {dist} K={K}")
+    if dist == "negzero":
+        assert (expect == 0x8000).any() and (expect == 0).any(), "the case should make zeros of both signs"
+    if dist == "large":
+        assert (expect == 0x7C00).any(), "the case should overflow"
+
+
 SHAPES = [(1, 16, 64), (4, 48, 256), (5, 33, 100), (16, 20, 24), (17, 100, 1000), (32, 64, 4096),
           (33, 40, 768), (3, 7, 8), (40, 130, 520), (2, 1, 12288), (3, 24, 65600)]
 

@@ -176,6 +176,54 @@ def test_leaf_block_rule_adversarial(dist, K):
     assert_bitwise(got, expect, f"leaf {dist} K={K}")
 
 
+def signed_per_leaf(rng, bits, K, p_neg=0.92):
+    """bits with one sign for each 64-element leaf of a row, negative with
+    probability p_neg, so that whole leaves of products share a sign (and some
+    rows have only negative leaves)."""
+    rows = bits.shape[0]
+    s = (rng.random((rows, (K + 63) // 64)) < p_neg).repeat(64, axis=1)[:, :K].astype(np.uint16)
+    return ((bits & np.uint16(0x7FFF)) | (s << 15)).astype(np.uint16)
+
+
+@pytest.mark.parametrize("dist", ["wide", "cancel", "ties", "tiny", "subnormal_tiny", "negzero"])
+@pytest.mark.parametrize("K", [200, 640, 2048])
+def test_tiled_tree_adversarial(dist, K):
+    # The tiled kernel (128 tokens and more) on inputs whose leaves and tree
+    # nodes round at ties, sum in the FP32 subnormal range, cancel to zero or
+    # are negative zeros (leaves of tiny negative products round to -0; the
+    # node of two -0 children is -0, of -0 and +0 is +0).  K = 200 ends in a
+    # partial leaf, K = 640 splits into lower subtrees of 2 and 3 leaves, K =
+    # 2048 into eight of 4 (the deferred form).
+    rng = np.random.default_rng(zlib.crc32(f"tiled/{dist}/{K}".encode()))
+    M, N = 160, 144
+    if dist == "wide":
+        A, B = wide(rng, (M, K), -30, 30), wide(rng, (N, K), -30, 30)
+    elif dist == "cancel":
+        A = wide(rng, (M, K), -6, 6)
+        A[:, K // 2:] = A[:, :K - K // 2][:, :K // 2] ^ np.uint16(0x8000)
+        B = np.where(rng.random((N, K)) < 0.1, wide(rng, (N, K), -2, 2), F2B(np.ones((N, K), np.float32)))
+        B = B.astype(np.uint16)
+    elif dist == "ties":
+        A = F2B((np.where(rng.random((M, K)) < 0.3, 2.0 ** -rng.integers(6, 10, (M, K)), 0)
+                 * np.where(rng.random((M, K)) < 0.7, 1, -1)).astype(np.float32))
+        A[:, ::64] = F2B(np.ones((M, len(range(0, K, 64))), np.float32))
+        B = F2B(np.ones((N, K), np.float32))
+    elif dist == "tiny":
+        A, B = wide(rng, (M, K), -70, -55), wide(rng, (N, K), -70, -55)
+    elif dist == "subnormal_tiny":
+        A, B = subnormal_mix(rng, (M, K)), wide(rng, (N, K), -30, 10)
+    else:  # products of about 2^-146: every leaf rounds to a zero of its sign
+        A = wide(rng, (M, K), -74, -72) & np.uint16(0x7FFF)
+        B = signed_per_leaf(rng, wide(rng, (N, K), -74, -72), K)
+        B[rng.random((N, K)) < 0.02] = 0
+    expect = oracle.gemm_tree(A, B, "NT")
+    got = dgf.gemm_tree("NT", padded(A), padded(B))
+    torch.cuda.synchronize()
+    assert_bitwise(got, expect, f"tiled {dist} K={K}")
+    if dist == "negzero":
+        assert (expect == 0x8000).any() and (expect == 0).any(), "the case should make zeros of both signs"
+
+
 def test_gemm_k_zero_and_m_zero():
     A = torch.zeros((4, 0), dtype=torch.bfloat16, device="cuda")
     B = torch.zeros((8, 0), dtype=torch.bfloat16, device="cuda")
