@@ -26,11 +26,13 @@
 // goes to C or, with K split or an epilogue, to the partial buffer that the
 // join kernel finishes.
 //
-// Bound.  Per leaf every wave runs 16 MFMAs but about 150 VALU instructions
-// (rounding, the tree nodes, staging), and the barrier keeps the waves in
-// step, so the LDS reads, the MFMAs and the VALU work of a leaf follow each
-// other instead of overlapping: the kernel reaches about 15% of the MFMA
-// peak at the FFN's 4096-token shapes.
+// Bound.  Per leaf every wave runs 16 MFMAs but, for BF16, about 130 other
+// VALU instructions (the rounding of 32 leaf values, about 32 nodes of an add
+// and a rounding each, staging), and the barrier keeps the waves in step, so
+// the LDS reads, the MFMAs and the VALU work of a leaf follow each other
+// instead of overlapping: about 20% of the MFMA peak at the FFN's 4096-token
+// shapes.  FP16 tree values are packed pairs (two roundings per conversion,
+// two nodes per packed add), which halves that VALU work.
 #include "dgf_device.hpp"
 #include "dgf_kernels.hpp"
 
