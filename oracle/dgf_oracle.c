@@ -239,6 +239,8 @@ static int f32_split(float f, int64_t *sig, int *ex)
  *   4. the exact sum T of the cut terms is cut toward minus infinity to 8 bits
  *      below its own FP32 ulp (never finer than 2^-157);
  *   5. that value is rounded to FP32, nearest even.
+ * A zero result is always +0: a block of zero products turns a -0 accumulator
+ * into +0, and a negative sum that rounds to zero gives +0, not -0.
  * The rule is the same for BF16 and FP16 operands; only the split differs.
  */
 static float block_step_t(int dt, float acc, const uint16_t *a, ptrdiff_t sa,
@@ -258,7 +260,7 @@ static float block_step_t(int dt, float acc, const uint16_t *a, ptrdiff_t sa,
         if (pexp[k] > emax) emax = pexp[k];
         any = 1;
     }
-    if (!any) return acc;
+    if (!any) return acc == 0.0f ? 0.0f : acc;  /* a -0 accumulator comes out +0 */
     const int grid = emax - 24;                 /* grid exponent */
 
     int64_t sp = 0;                             /* products, in grid units */
@@ -296,7 +298,8 @@ static float block_step_t(int dt, float acc, const uint16_t *a, ptrdiff_t sa,
         t = floor_shift(t, cut - e);
         e = cut;
     }
-    return round_to_f32(t, e);
+    const float r = round_to_f32(t, e);
+    return r == 0.0f ? 0.0f : r;                /* a sum that rounds to zero is +0 */
 }
 
 float oracle_block_step_t(int dt, float acc, const uint16_t *a, ptrdiff_t sa,

@@ -107,6 +107,18 @@ def case(fmt, dist, n, rng, K=32):
         lo = 10 if fmt == "fp16" else 30
         return (elems(rng, fmt, A_shape, lo, lo + 5), elems(rng, fmt, B_shape, lo, lo + 5),
                 f32s(rng, C_shape, 20, 120))
+    if dist == "signed_zero":
+        # zero results: -0 and +0 accumulators over blocks of zero products, and
+        # (BF16) block sums of a few products near 2^-152, which FP32 rounds to
+        # zero or to its smallest subnormals
+        lo = -14 if fmt == "fp16" else -77
+        A = elems(rng, fmt, A_shape, lo, lo + 1, zero=0.7)
+        B = elems(rng, fmt, B_shape, lo, lo + 1, zero=0.3)
+        A[:, ::2, 8:16] = np.where(rng.random((n, 8, 8)) < 0.5, 0x8000, 0)  # a zero block in half the rows
+        A[:, ::4, :] = np.where(rng.random((n, 4, K)) < 0.5, 0x8000, 0)  # only zero blocks in a quarter
+        C = np.where(rng.random(C_shape) < 0.5, np.float32(-0.0), np.float32(0.0))
+        C = np.where(rng.random(C_shape) < 0.2, f32s(rng, C_shape, -149, -149, subnormal=1.0), C)
+        return A, B, C.astype(np.float32)
     assert dist == "mixed"
     A = elems(rng, fmt, A_shape, -14, hi // 2, sub=0.1, zero=0.25)
     B = elems(rng, fmt, B_shape, -14, hi // 2, sub=0.1)
@@ -121,7 +133,8 @@ def expected(fmt, A, B, C):
     return oracle.block_chains(C.reshape(-1), a, b, fmt).reshape(n, 16, 16)
 
 
-DISTS = ["int", "wide", "wide_acc", "cancel", "subnormal", "subnormal_acc", "ties", "tiny_acc", "big_acc", "mixed"]
+DISTS = ["int", "wide", "wide_acc", "cancel", "subnormal", "subnormal_acc", "ties", "tiny_acc", "big_acc", "mixed",
+         "signed_zero"]
 
 
 @pytest.mark.parametrize("fmt", ["bf16", "fp16"])
