@@ -33,6 +33,8 @@
 // instead of overlapping: about 20% of the MFMA peak at the FFN's 4096-token
 // shapes.  FP16 tree values are packed pairs (two roundings per conversion,
 // two nodes per packed add), which halves that VALU work.
+#include <type_traits>
+
 #include "dgf_device.hpp"
 #include "dgf_kernels.hpp"
 
@@ -412,9 +414,10 @@ __global__ __launch_bounds__(kMmWaves * 64) void k_mm(GemmParams p) {
   const int nsub = 1 << up;
   // (the deferred form keeps both accumulator sets and the subtree's pending
   // values live across subtrees: with a partial last leaf that no longer fits
-  // the 256 registers of two waves per SIMD, and with 3-leaf subtrees it fits
-  // at 242 but measured 2% slower than the immediate form)
-  constexpr bool kDefer = NLH != 3 && !TAIL;
+  // the 256 registers of two waves per SIMD; with BF16 3-leaf subtrees it fits
+  // at 242 but measured 2% slower than the immediate form, while FP16's packed
+  // values fit at 219 and made those launches 7% faster)
+  constexpr bool kDefer = (NLH != 3 || std::is_same<T, F16>::value) && !TAIL;
   bool uniform = false;
   if constexpr (kDefer) uniform = w.phi - w.plo == (NLH << up);
   if constexpr (kDefer) {
