@@ -153,10 +153,12 @@ def main():
     ap.add_argument("--copies", type=int, default=3, help="resident weight copies rotated per step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quick", action="store_true", help="skip the forward-only and CPU legs (profiling runs)")
-    ap.add_argument("--workload", choices=("train32", "long4096"), default="train32",
+    ap.add_argument("--workload", choices=("train32", "long4096", "rank32"), default="train32",
                     help="long4096: only the M=4096 training step (--warmup, then --samples regions of --steps "
-                         "steps), for profiling; prints that leg's JSON instead of the benchmark line")
+                         "steps); rank32: only one rank's share of the I-sharded M=32 forward and step (shard 0 "
+                         "of --shards); both for profiling, printing that leg's JSON instead of the benchmark line")
     ap.add_argument("--dtype", choices=("bf16", "fp16"), default="bf16", help="stored type of the long4096 workload")
+    ap.add_argument("--shards", type=int, choices=(2, 4, 8), default=8, help="I shards of the rank32 workload")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -187,6 +189,10 @@ def main():
         out = long_sequence(weights, steps=args.steps, warmup=args.warmup, samples=args.samples)
         out["dtype"] = args.dtype
         print(json.dumps({"long_sequence": out}), flush=True)
+        return
+
+    if args.workload == "rank32":
+        print(json.dumps({"one_rank": one_rank(args)}), flush=True)
         return
 
     M = 32
@@ -519,6 +525,44 @@ def shard_legs(W, x, dy, args, fwd_us: float, step_us: float) -> dict:
                    "is their extra launches and smaller grids, not a multi-GPU figure; one_shard_* is one "
                    "rank's own compute at I/S (no exchange)")
     return out
+
+
+def one_rank(args) -> dict:
+    """Shard 0 of the I-sharded M=32 forward and training step at --shards
+    shards (W_gate and W_up rows, W_down columns of the first I / S): the
+    forward alone (--warmup calls, then --samples regions of --steps), then
+    the forward with g and u saved followed by the backward with its dX lanes
+    kept, timed the same way, over --copies resident weight copies."""
+    import torch
+    from deterministic_gated_ffn_amd import binding as dgf
+    from deterministic_gated_ffn_amd import inputs
+
+    M, S = 32, args.shards
+    w0 = tuple(t.cuda() for t in inputs.ffn_weights())
+    W = [w0] + [tuple(t.clone() for t in w0) for _ in range(args.copies - 1)]
+    Is = w0[0].shape[0] // S
+    views = [(wg[:Is], wu[:Is], wd[:, :Is]) for (wg, wu, wd) in W]
+    x_c, dy_c = inputs.activations(M)
+    x, dy = x_c.cuda(), dy_c.cuda()
+    torch.cuda.synchronize()
+
+    def fwd(k):
+        return dgf.ffn_fwd(x, *views[k % len(views)])
+
+    def step(k):
+        v = views[k % len(views)]
+        y, g, u = dgf.ffn_fwd(x, *v, training=True)
+        return dgf.ffn_bwd(dy, x, g, u, *v, lanes=True)
+
+    for k in range(args.warmup):
+        fwd(k)
+    f = stats_entry(sample_us(fwd, args.steps, args.samples))
+    for k in range(args.warmup):
+        step(k)
+    t = stats_entry(sample_us(step, args.steps, args.samples))
+    print(f"[bench] one rank of {S} I-shards (I = {Is}): forward {f['us']:.1f} us, fwd+bwd {t['us']:.1f} us",
+          file=sys.stderr, flush=True)
+    return {"shards": S, "I_shard": Is, "M": M, "forward": f, "fwd_bwd": t}
 
 
 def ordinal(b):
