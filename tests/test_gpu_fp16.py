@@ -117,14 +117,15 @@ def test_f16_leaf_block_rule_adversarial(dist, K):
 
 
 @pytest.mark.parametrize("dist", ["wide", "cancel", "subnormal", "ties", "tiny", "negzero", "large"])
-@pytest.mark.parametrize("K", [200, 640, 2048])
+@pytest.mark.parametrize("K", [200, 640, 1536, 2048])
 def test_f16_tiled_tree_adversarial(dist, K):
     # The tiled kernel (128 tokens and more) keeps FP16 tree values as packed
     # pairs and adds two nodes with one packed FP16 add; these inputs make the
     # nodes round at ties, sum in the FP16 subnormal range, cancel to zero,
     # meet negative zeros (leaves of tiny negative products round to -0) and
     # overflow to infinity.  K = 200 ends in a partial leaf, K = 640 splits
-    # into lower subtrees of 2 and 3 leaves, K = 2048 into eight of 4.
+    # into lower subtrees of 2 and 3 leaves, K = 1536 into eight of 3 and K =
+    # 2048 into eight of 4 (both in the deferred form).
     rng = np.random.default_rng(zlib.crc32(f"f16/tiled/{dist}/{K}".encode()))
     M, N = 160, 144
     if dist == "wide":

@@ -186,14 +186,15 @@ def signed_per_leaf(rng, bits, K, p_neg=0.92):
 
 
 @pytest.mark.parametrize("dist", ["wide", "cancel", "ties", "tiny", "subnormal_tiny", "negzero"])
-@pytest.mark.parametrize("K", [200, 640, 2048])
+@pytest.mark.parametrize("K", [200, 640, 1536, 2048])
 def test_tiled_tree_adversarial(dist, K):
     # The tiled kernel (128 tokens and more) on inputs whose leaves and tree
     # nodes round at ties, sum in the FP32 subnormal range, cancel to zero or
     # are negative zeros (leaves of tiny negative products round to -0; the
     # node of two -0 children is -0, of -0 and +0 is +0).  K = 200 ends in a
     # partial leaf, K = 640 splits into lower subtrees of 2 and 3 leaves, K =
-    # 2048 into eight of 4 (the deferred form).
+    # 1536 into eight of 3 and K = 2048 into eight of 4 (both whole: the
+    # deferred form where the stored type uses it).
     rng = np.random.default_rng(zlib.crc32(f"tiled/{dist}/{K}".encode()))
     M, N = 160, 144
     if dist == "wide":
