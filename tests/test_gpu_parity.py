@@ -140,7 +140,16 @@ def subnormal_mix(rng, shape):
     return np.where(rng.random(shape) < 0.5, s | sub, nrm).astype(np.uint16)
 
 
-@pytest.mark.parametrize("dist", ["wide", "wide60", "cancel", "tiny", "ties", "subnormal", "subnormal_tiny"])
+def sparse_tiny(rng, shape, p=0.8):
+    """+-2^-76 at a fraction p of the positions, zeros elsewhere: against 2^-76
+    its products are +-2^-152, so a block's sum of a few of them is too small
+    for FP32 and rounds to zero (the block rule makes that zero +0)."""
+    v = np.where(rng.random(shape) < 0.5, np.uint16(0x1980 | 0x8000), np.uint16(0x1980))  # -+2^-76
+    return np.where(rng.random(shape) < p, v, np.uint16(0)).astype(np.uint16)
+
+
+@pytest.mark.parametrize("dist", ["wide", "wide60", "cancel", "tiny", "ties", "subnormal", "subnormal_tiny",
+                                  "zero_sums"])
 @pytest.mark.parametrize("K", [8, 32, 64, 128, 200])
 def test_leaf_block_rule_adversarial(dist, K):
     # The FP32 leaf's accumulation rule on inputs that separate it from other
@@ -165,6 +174,8 @@ def test_leaf_block_rule_adversarial(dist, K):
     elif dist == "subnormal_tiny":
         # ... and against small ones: products and sums in the FP32 subnormal range
         A, B = subnormal_mix(rng, (M, K)), wide(rng, (N, K), -30, 10)
+    elif dist == "zero_sums":
+        A, B = sparse_tiny(rng, (M, K)), np.full((N, K), np.uint16(0x1980), np.uint16)
     else:
         A = F2B((np.where(rng.random((M, K)) < 0.3, 2.0 ** -rng.integers(22, 27, (M, K)), 0)
                  * np.where(rng.random((M, K)) < 0.7, 1, -1)).astype(np.float32))
@@ -185,7 +196,7 @@ def signed_per_leaf(rng, bits, K, p_neg=0.92):
     return ((bits & np.uint16(0x7FFF)) | (s << 15)).astype(np.uint16)
 
 
-@pytest.mark.parametrize("dist", ["wide", "cancel", "ties", "tiny", "subnormal_tiny", "negzero"])
+@pytest.mark.parametrize("dist", ["wide", "cancel", "ties", "tiny", "subnormal_tiny", "negzero", "zero_sums"])
 @pytest.mark.parametrize("K", [200, 640, 1536, 2048])
 def test_tiled_tree_adversarial(dist, K):
     # The tiled kernel (128 tokens and more) on inputs whose leaves and tree
@@ -213,6 +224,8 @@ def test_tiled_tree_adversarial(dist, K):
         A, B = wide(rng, (M, K), -70, -55), wide(rng, (N, K), -70, -55)
     elif dist == "subnormal_tiny":
         A, B = subnormal_mix(rng, (M, K)), wide(rng, (N, K), -30, 10)
+    elif dist == "zero_sums":
+        A, B = sparse_tiny(rng, (M, K)), np.full((N, K), np.uint16(0x1980), np.uint16)
     else:  # products of about 2^-146: every leaf rounds to a zero of its sign
         A = wide(rng, (M, K), -74, -72) & np.uint16(0x7FFF)
         B = signed_per_leaf(rng, wide(rng, (N, K), -74, -72), K)
