@@ -41,8 +41,12 @@
  *  - Errors are status codes; nothing aborts or throws across the ABI.
  *    dgf_last_error() describes the last non-OK status of the calling thread.
  *    Arguments are validated before any HIP call is made.
- *  - Inputs are finite.  NaN/Inf propagate through the FP32 operations but the
- *    leaf's block rule is specified for finite values only.
+ *  - Inputs are finite.  Products and sums may still overflow: the leaf's block
+ *    rule makes a product of magnitude 2^128 or more an infinity of its sign,
+ *    keeps an infinite accumulator over finite products, and gives the NaN
+ *    0xFFC00000 for infinities of both signs; past the leaf, infinities and
+ *    NaN propagate through the FP32 operations (a NaN's sign and payload are
+ *    not specified).
  */
 #ifndef DGF_H
 #define DGF_H

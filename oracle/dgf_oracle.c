@@ -241,8 +241,20 @@ static int f32_split(float f, int64_t *sig, int *ex)
  *   5. that value is rounded to FP32, nearest even.
  * A zero result is always +0: a block of zero products turns a -0 accumulator
  * into +0, and a negative sum that rounds to zero gives +0, not -0.
+ * Past FP32's range: a product of magnitude 2^128 or more is an infinity of its
+ * sign before any sum; an infinite accumulator passes a block of finite
+ * products unchanged; infinities of both signs, or a NaN accumulator, give the
+ * NaN 0xFFC00000.
  * The rule is the same for BF16 and FP16 operands; only the split differs.
  */
+static float nan_f32(void)
+{
+    const uint32_t u = 0xFFC00000u;
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
 static float block_step_t(int dt, float acc, const uint16_t *a, ptrdiff_t sa,
                           const uint16_t *b, ptrdiff_t sb, int n)
 {
@@ -260,6 +272,25 @@ static float block_step_t(int dt, float acc, const uint16_t *a, ptrdiff_t sa,
         if (pexp[k] > emax) emax = pexp[k];
         any = 1;
     }
+    if (isnan(acc)) return nan_f32();
+    /* products of magnitude >= 2^128 are infinite */
+    int pinf = 0, ninf = 0;
+    for (int k = 0; k < n; ++k) {
+        if (!nz[k]) continue;
+        const uint32_t mag = (uint32_t)(psig[k] < 0 ? -psig[k] : psig[k]);
+        int lead = 31 - __builtin_clz(mag) + pexp[k] - 2 * fb;
+        if (lead >= 128) {
+            if (psig[k] > 0) pinf = 1;
+            else ninf = 1;
+        }
+    }
+    if (pinf && ninf) return nan_f32();
+    if (isinf(acc)) {
+        if ((acc > 0 && ninf) || (acc < 0 && pinf)) return nan_f32();
+        return acc;
+    }
+    if (pinf) return INFINITY;
+    if (ninf) return -INFINITY;
     if (!any) return acc == 0.0f ? 0.0f : acc;  /* a -0 accumulator comes out +0 */
     const int grid = emax - 24;                 /* grid exponent */
 

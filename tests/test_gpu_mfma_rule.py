@@ -119,6 +119,17 @@ def case(fmt, dist, n, rng, K=32):
         C = np.where(rng.random(C_shape) < 0.5, np.float32(-0.0), np.float32(0.0))
         C = np.where(rng.random(C_shape) < 0.2, f32s(rng, C_shape, -149, -149, subnormal=1.0), C)
         return A, B, C.astype(np.float32)
+    if dist == "overflow":
+        # past FP32's range: BF16 products up to 2^130 (those of 2^128 and more are
+        # infinities of their sign) against infinite, NaN, large and zero
+        # accumulators; FP16 products stay finite, so there only the accumulators
+        lo, hi = (56, 64) if fmt == "bf16" else (8, 15)
+        A = elems(rng, fmt, A_shape, lo, hi, zero=0.85)
+        B = elems(rng, fmt, B_shape, lo, hi)
+        pick = rng.random(C_shape)
+        C = np.where(pick < 0.2, np.float32(np.inf), np.where(pick < 0.4, np.float32(-np.inf),
+                     np.where(pick < 0.5, np.float32(np.nan), np.where(pick < 0.75, f32s(rng, C_shape, 120, 127), 0))))
+        return A, B, C.astype(np.float32)
     assert dist == "mixed"
     A = elems(rng, fmt, A_shape, -14, hi // 2, sub=0.1, zero=0.25)
     B = elems(rng, fmt, B_shape, -14, hi // 2, sub=0.1)
@@ -134,7 +145,7 @@ def expected(fmt, A, B, C):
 
 
 DISTS = ["int", "wide", "wide_acc", "cancel", "subnormal", "subnormal_acc", "ties", "tiny_acc", "big_acc", "mixed",
-         "signed_zero"]
+         "signed_zero", "overflow"]
 
 
 @pytest.mark.parametrize("fmt", ["bf16", "fp16"])
