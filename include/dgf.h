@@ -41,12 +41,14 @@
  *  - Errors are status codes; nothing aborts or throws across the ABI.
  *    dgf_last_error() describes the last non-OK status of the calling thread.
  *    Arguments are validated before any HIP call is made.
- *  - Inputs are finite.  Products and sums may still overflow: the leaf's block
- *    rule makes a product of magnitude 2^128 or more an infinity of its sign,
- *    keeps an infinite accumulator over finite products, and gives the NaN
- *    0xFFC00000 for infinities of both signs; past the leaf, infinities and
- *    NaN propagate through the FP32 operations (a NaN's sign and payload are
- *    not specified).
+ *  - Inputs are finite.  Products, sums and FP16 stage boundaries may still
+ *    overflow, and later GEMMs then see infinite operands: the leaf's block
+ *    rule makes a product of magnitude 2^128 or more, or an infinity times a
+ *    nonzero value, an infinity of its sign, keeps an infinite accumulator over
+ *    finite products, and gives the NaN 0xFFC00000 for infinities of both
+ *    signs, NaN operands and an infinity times zero; past the leaf, infinities
+ *    and NaN propagate through the FP32 operations (a NaN's sign and payload
+ *    are not specified).
  */
 #ifndef DGF_H
 #define DGF_H

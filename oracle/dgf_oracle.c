@@ -214,6 +214,14 @@ static int elem_split(int dt, uint16_t h, int32_t *sig, int *ex)
     return 1;
 }
 
+/* Class of a stored value: 0 finite, 1 infinity, 2 NaN. */
+static int elem_special(int dt, uint16_t h)
+{
+    const uint16_t emask = dt == DT_FP16 ? 0x7C00 : 0x7F80;
+    if ((h & emask) != emask) return 0;
+    return (h & (uint16_t)~(emask | 0x8000)) ? 2 : 1;
+}
+
 /* Split a finite FP32 so that value = sig * 2^(ex - 23); zero returns 0. */
 static int f32_split(float f, int64_t *sig, int *ex)
 {
@@ -242,9 +250,10 @@ static int f32_split(float f, int64_t *sig, int *ex)
  * A zero result is always +0: a block of zero products turns a -0 accumulator
  * into +0, and a negative sum that rounds to zero gives +0, not -0.
  * Past FP32's range: a product of magnitude 2^128 or more is an infinity of its
- * sign before any sum; an infinite accumulator passes a block of finite
- * products unchanged; infinities of both signs, or a NaN accumulator, give the
- * NaN 0xFFC00000.
+ * sign before any sum, and so is the product of an infinite operand and a
+ * nonzero one; an infinite accumulator passes a block of finite products
+ * unchanged; infinities of both signs, a NaN operand or accumulator, and an
+ * infinity times zero give the NaN 0xFFC00000.
  * The rule is the same for BF16 and FP16 operands; only the split differs.
  */
 static float nan_f32(void)
@@ -262,19 +271,28 @@ static float block_step_t(int dt, float acc, const uint16_t *a, ptrdiff_t sa,
     int32_t psig[8];
     int pexp[8], nz[8];
     int emax = -100000, any = 0;
+    int pinf = 0, ninf = 0, anynan = isnan(acc);
     for (int k = 0; k < n; ++k) {
         int32_t sa_, sb_;
         int ea, eb;
-        nz[k] = elem_split(dt, a[k * sa], &sa_, &ea) & elem_split(dt, b[k * sb], &sb_, &eb);
+        const uint16_t ak = a[k * sa], bk = b[k * sb];
+        const int ca = elem_special(dt, ak), cb = elem_special(dt, bk);
+        if (ca || cb) {                         /* an infinite or NaN operand */
+            nz[k] = 0;
+            if (ca == 2 || cb == 2 || (ak & 0x7FFF) == 0 || (bk & 0x7FFF) == 0) anynan = 1;
+            else if ((ak ^ bk) & 0x8000) ninf = 1;
+            else pinf = 1;
+            continue;
+        }
+        nz[k] = elem_split(dt, ak, &sa_, &ea) & elem_split(dt, bk, &sb_, &eb);
         if (!nz[k]) continue;
         psig[k] = sa_ * sb_;                    /* |psig| < 2^(2fb+2) */
         pexp[k] = ea + eb;                      /* product = psig * 2^(pexp-2fb) */
         if (pexp[k] > emax) emax = pexp[k];
         any = 1;
     }
-    if (isnan(acc)) return nan_f32();
+    if (anynan) return nan_f32();
     /* products of magnitude >= 2^128 are infinite */
-    int pinf = 0, ninf = 0;
     for (int k = 0; k < n; ++k) {
         if (!nz[k]) continue;
         const uint32_t mag = (uint32_t)(psig[k] < 0 ? -psig[k] : psig[k]);

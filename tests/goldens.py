@@ -103,13 +103,21 @@ def tree_cases(fmt: str = "bf16"):
     return out
 
 
+def _stored(tok: str, enc) -> int:
+    """An operand token: 'inf', '-inf', 'nan' (the stored type's infinities and
+    a quiet NaN), or an exact value as parse_value reads it."""
+    special = {"inf": 0x7F80, "-inf": 0xFF80, "nan": 0x7FC0} if enc is bf16_bits_exact else \
+              {"inf": 0x7C00, "-inf": 0xFC00, "nan": 0x7E00}
+    return special[tok] if tok in special else enc(parse_value(tok))
+
+
 def block_cases(fmt: str = "bf16"):
     enc = _ENC[fmt][0]
     name_ = {"bf16": "block_rule_cases.txt", "fp16": "block_rule_f16_cases.txt"}[fmt]
     out = []
     for name, acc, av, bv, exp, why in load_table(name_):
-        a = np.array([enc(parse_value(t)) for t in av.split()], np.uint16)
-        b = np.array([enc(parse_value(t)) for t in bv.split()], np.uint16)
+        a = np.array([_stored(t, enc) for t in av.split()], np.uint16)
+        b = np.array([_stored(t, enc) for t in bv.split()], np.uint16)
         accf = np.array([int(acc, 16)], np.uint32).view(np.float32)[0]
         out.append((name, accf, a, b, int(exp, 16), why))
     return out

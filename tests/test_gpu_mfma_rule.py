@@ -130,6 +130,20 @@ def case(fmt, dist, n, rng, K=32):
         C = np.where(pick < 0.2, np.float32(np.inf), np.where(pick < 0.4, np.float32(-np.inf),
                      np.where(pick < 0.5, np.float32(np.nan), np.where(pick < 0.75, f32s(rng, C_shape, 120, 127), 0))))
         return A, B, C.astype(np.float32)
+    if dist == "special":
+        # infinite and NaN operands beside zeros and ordinary values: an infinity
+        # times a nonzero value is an infinity of the product's sign, times zero a
+        # NaN; a NaN operand, or infinities of both signs, give NaN
+        A = elems(rng, fmt, A_shape, -4, 4, zero=0.3)
+        B = elems(rng, fmt, B_shape, -4, 4, zero=0.3)
+        inf, nan = (0x7F80, 0x7FC0) if fmt == "bf16" else (0x7C00, 0x7E00)
+        pa = rng.random(A_shape)
+        A = np.where(pa < 0.015, np.uint16(inf), np.where(pa < 0.03, np.uint16(inf | 0x8000),
+                     np.where(pa < 0.035, np.uint16(nan), A))).astype(np.uint16)
+        pb = rng.random(B_shape)
+        B = np.where(pb < 0.01, np.uint16(inf), B).astype(np.uint16)
+        C = np.where(rng.random(C_shape) < 0.1, np.float32(-np.inf), f32s(rng, C_shape, -4, 4)).astype(np.float32)
+        return A, B, C
     assert dist == "mixed"
     A = elems(rng, fmt, A_shape, -14, hi // 2, sub=0.1, zero=0.25)
     B = elems(rng, fmt, B_shape, -14, hi // 2, sub=0.1)
@@ -145,7 +159,7 @@ def expected(fmt, A, B, C):
 
 
 DISTS = ["int", "wide", "wide_acc", "cancel", "subnormal", "subnormal_acc", "ties", "tiny_acc", "big_acc", "mixed",
-         "signed_zero", "overflow"]
+         "signed_zero", "overflow", "special"]
 
 
 @pytest.mark.parametrize("fmt", ["bf16", "fp16"])
