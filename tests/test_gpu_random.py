@@ -101,3 +101,45 @@ def test_random_gemms_and_ffns_match_the_oracle():
             failures.append(f"case {case}: {tag}: {bad} mismatches")
     torch.cuda.synchronize()
     assert not failures, "\n".join(failures[:10])
+
+
+def test_random_bit_patterns_through_combine_and_activation():
+    # every 16-bit pattern is fair game here (NaN, infinities, subnormals, -0):
+    # the rank-tree combine in BF16, FP16 and FP32, and the activation forward
+    # and backward, against the oracle; a NaN matches any NaN
+    rng = np.random.default_rng(77)
+    failures = []
+    for case in range(48):
+        S = int(rng.choice([1, 2, 4, 8]))
+        n = int(rng.integers(1, 100) if rng.random() < 0.3 else rng.integers(100, 60000))
+        cd = str(rng.choice(["bf16", "fp16", "fp32"]))
+        if cd == "fp32":
+            with np.errstate(over="ignore"):  # values past FP32's range become infinities on purpose
+                parts = [(rng.standard_normal(n) * 2.0 ** rng.integers(-140, 128, n)).astype(np.float32)
+                         for _ in range(S)]
+            for p in parts:
+                p[rng.random(n) < 0.01] = np.float32(np.inf)
+                p[rng.random(n) < 0.01] = np.float32(-0.0)
+            want = oracle.tree_combine_typed(parts, "fp32")
+            got = dgf.tree_combine([torch.from_numpy(p).cuda() for p in parts]).cpu().numpy()
+            bad = int(((got.view(np.uint32) != want.view(np.uint32)) & ~(np.isnan(got) & np.isnan(want))).sum())
+        else:
+            parts = [rng.integers(0, 65536, n, dtype=np.uint64).astype(np.uint16) for _ in range(S)]
+            want = oracle.tree_combine_typed(parts, cd)
+            tdt = torch.float16 if cd == "fp16" else torch.bfloat16
+            got = host(dgf.tree_combine([torch.from_numpy(p.view(np.int16)).cuda().view(tdt) for p in parts]))
+            bad = mismatches(got, want, cd)
+        if bad:
+            failures.append(f"combine {cd} S={S} n={n}: {bad} mismatches")
+        ad = str(rng.choice(["bf16", "fp16"]))
+        m = int(rng.integers(1, 40000))
+        G, U, DA = (rng.integers(0, 65536, m, dtype=np.uint64).astype(np.uint16) for _ in range(3))
+        tdt = torch.float16 if ad == "fp16" else torch.bfloat16
+        dv = lambda b: torch.from_numpy(b.view(np.int16)).cuda().view(tdt)
+        bad = mismatches(host(dgf.act_fwd(dv(G), dv(U))), oracle.act_fwd(G, U, ad), ad)
+        for got, want in zip(dgf.act_bwd(dv(DA), dv(G), dv(U)), oracle.act_bwd(DA, G, U, ad)):
+            bad += mismatches(host(got), want, ad)
+        if bad:
+            failures.append(f"act {ad} n={m}: {bad} mismatches")
+    torch.cuda.synchronize()
+    assert not failures, "\n".join(failures[:10])
