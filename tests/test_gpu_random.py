@@ -1,6 +1,7 @@
 """Seeded random sweep against the oracle: tree GEMMs in the three layouts and
 the FFN forward and backward, in BF16 and FP16 storage, over random shapes
-(ragged K, token counts across every kernel's range) and value mixes (scaled
+(ragged K, any H and I, token counts across every kernel's range; the dX
+lanes and the forward without allocation on some cases) and value mixes (scaled
 normals, exponents spread over 24 binades, sparse values, small integers),
 with padded leading dimensions.  Large scales push FP16 stage boundaries past
 65504, so infinities and NaN flow into later GEMMs: results must still equal
@@ -17,7 +18,7 @@ from deterministic_gated_ffn_amd import binding as dgf
 
 pytestmark = pytest.mark.gpu
 
-CASES = 240
+CASES = 480
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -84,7 +85,7 @@ def test_random_gemms_and_ffns_match_the_oracle():
             tag = f"gemm {fmt} {layout} {kind} M={M} N={N} K={K}"
         else:
             M = int(rng.integers(1, 40) if rng.random() < 0.5 else rng.integers(40, 260))
-            H, I = int(rng.integers(1, 40)) * 8, int(rng.integers(1, 60)) * 8
+            H, I = int(rng.integers(1, 320)), int(rng.integers(1, 480))
             x, dy = gen(rng, fmt, (M, H), "normal"), gen(rng, fmt, (M, H), "normal")
             wg, wu, wd = gen(rng, fmt, (I, H), kind), gen(rng, fmt, (I, H), kind), gen(rng, fmt, (H, I), kind)
             o = oracle.ffn_fwd(x, wg, wu, wd, *dt)
@@ -92,11 +93,18 @@ def test_random_gemms_and_ffns_match_the_oracle():
             W = [dev(rng, w, fmt) for w in (wg, wu, wd)]
             xd = dev(rng, x, fmt)
             y, g, u = dgf.ffn_fwd(xd, *W, training=True)
-            r = dgf.ffn_bwd(dev(rng, dy, fmt), xd, g, u, *W)
-            bad = sum(mismatches(host(t), ref, fmt) for t, ref in
-                      ((y, o["y"]), (g, o["g"]), (u, o["u"]), (r["dX"], ob["dX"]), (r["dW_gate"], ob["dW_gate"]),
-                       (r["dW_up"], ob["dW_up"]), (r["dW_down"], ob["dW_down"])))
-            tag = f"ffn {fmt} {kind} M={M} H={H} I={I}"
+            lanes = bool(rng.random() < 0.3)
+            r = dgf.ffn_bwd(dev(rng, dy, fmt), xd, g, u, *W, lanes=lanes)
+            outs = [(y, o["y"]), (g, o["g"]), (u, o["u"]), (r["dX"], ob["dX"]), (r["dW_gate"], ob["dW_gate"]),
+                    (r["dW_up"], ob["dW_up"]), (r["dW_down"], ob["dW_down"])]
+            if lanes:
+                outs += [(r["G"], ob["G"]), (r["U"], ob["U"])]
+            if fmt == "bf16" and rng.random() < 0.3:
+                # the entry point without allocation, into a padded y of its own
+                ys = torch.empty(M, (H + 7) // 8 * 8, dtype=torch.bfloat16, device="cuda")[:, :H]
+                outs.append((dgf.ffn_fwd_static(xd, *W, ys), o["y"]))
+            bad = sum(mismatches(host(t), ref, fmt) for t, ref in outs)
+            tag = f"ffn {fmt} {kind} M={M} H={H} I={I} lanes={lanes}"
         if bad:
             failures.append(f"case {case}: {tag}: {bad} mismatches")
     torch.cuda.synchronize()
