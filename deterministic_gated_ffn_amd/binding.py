@@ -186,13 +186,17 @@ def ffn_fwd_static(x, w_gate, w_up, w_down, y, g=None, u=None, stream=None):
     """dgf_ffn_fwd_static: the forward into caller-given y (and g, u when
     training) with the library's own scratch; allocates nothing."""
     L = load()
+    if (g is None) != (u is None):
+        raise ValueError("give both g and u (training) or neither (inference)")
+    if _stored(x, w_gate, w_up, w_down, y, *([g, u] if g is not None else [])) != DGF_BF16:
+        raise TypeError("dgf_ffn_fwd_static takes bfloat16 tensors only")
     M, H = x.shape
     I = w_gate.shape[0]
     xp, ldx = _mat(x, "x"); wg, ldwg = _mat(w_gate, "w_gate"); wu, ldwu = _mat(w_up, "w_up")
     wd, ldwd = _mat(w_down, "w_down"); yp, ldy = _mat(y, "y")
     gp = up = None
     ld_gu = 0
-    if g is not None or u is not None:
+    if g is not None:
         (gp, ld_gu), (up, ldu) = _mat(g, "g"), _mat(u, "u")
         if ldu != ld_gu:
             raise ValueError("g and u must share a leading dimension")

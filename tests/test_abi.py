@@ -173,3 +173,15 @@ def test_profile_hook_validation(lib):
     assert lib.dgf_profile_end() == 0
     assert lib.dgf_profile_name(0) == b""
     assert lib.dgf_profile_name(-1) == b""
+
+
+def test_static_forward_binding_checks_its_arguments(lib):
+    # the entry point without allocation takes BF16 only and both saves or neither;
+    # the binding refuses other calls before anything reaches the library
+    import torch
+    t16 = torch.zeros(4, 8, dtype=torch.float16)
+    tb = torch.zeros(4, 8, dtype=torch.bfloat16)
+    with pytest.raises(TypeError, match="bfloat16"):
+        binding.ffn_fwd_static(t16, t16, t16, t16, t16)
+    with pytest.raises(ValueError, match="both g and u"):
+        binding.ffn_fwd_static(tb, tb, tb, tb, tb, g=tb)
