@@ -99,3 +99,55 @@ def test_two_stream_lanes_equal_the_fused_backward_and_the_oracle(M, H, I):
     odx = oracle.tree_combine([OG, OU]).reshape(OG.shape)
     assert (inputs.bits(runs[0][0]) == odx).all(), int((inputs.bits(runs[0][0]) != odx).sum())
     assert (inputs.bits(runs[0][1]) == OG).all()
+
+
+def test_concurrent_calls_from_two_host_threads():
+    # The library keeps no shared state between calls (the error message and
+    # the timing hook are per thread), so two host threads may drive it at once,
+    # each on a stream of its own (ctypes releases the GIL during each call).
+    # Every result must equal the same call made alone; the second thread's
+    # errors must not leak into the first thread's message.
+    import threading
+
+    M, H, I = 40, 512, 1536
+    rng = np.random.default_rng(11)
+    f = lambda shape, s=1.0: torch.from_numpy(rng.standard_normal(shape).astype(np.float32) * s).to(torch.bfloat16).cuda()
+    w = [f((I, H), 0.02), f((I, H), 0.02), f((H, I), 0.02)]
+    work = [(f((M, H)), f((M, H))) for _ in range(2)]
+
+    def run(x, dy):
+        y, g, u = dgf.ffn_fwd(x, *w, training=True)
+        r = dgf.ffn_bwd(dy, x, g, u, *w)
+        return [y, r["dX"], r["dW_gate"], r["dW_up"], r["dW_down"]]
+
+    alone = [[inputs.bits(t) for t in run(x, dy)] for x, dy in work]
+    torch.cuda.synchronize()
+    got = [None, None]
+    errors = []
+
+    def worker(i):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                for _ in range(5):
+                    outs = run(*work[i])
+                    if i == 1:  # a rejected call on this thread only: x's leading dimension is not a multiple of 8
+                        bad_x = torch.zeros((M, H + 1), dtype=torch.bfloat16, device="cuda")[:, :H]
+                        with pytest.raises(dgf.DgfError, match="leading dimension"):
+                            dgf.ffn_fwd(bad_x, *w)
+                s.synchronize()
+            got[i] = [inputs.bits(t) for t in outs]
+        except Exception as e:  # reported by the main thread
+            errors.append(f"thread {i}: {e!r}")
+
+    before = dgf.load().dgf_last_error()
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    for i in range(2):
+        for k, (a, b) in enumerate(zip(got[i], alone[i])):
+            assert (a == b).all(), f"thread {i} output {k}: {(a != b).sum()} differ from the call made alone"
+    assert dgf.load().dgf_last_error() == before  # the other thread's error stayed on that thread
