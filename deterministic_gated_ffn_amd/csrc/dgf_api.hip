@@ -93,14 +93,14 @@ dgf_status check_mat(const char *name, const void *p, int64_t ld, int64_t rows, 
   if (ld < cols) return fail(DGF_EINVAL, "%s: leading dimension %lld < row width %lld", name, (long long)ld, (long long)cols);
   if (ld % 8 != 0) return fail(DGF_EINVAL, "%s: leading dimension %lld is not a multiple of 8", name, (long long)ld);
   // a 128-row tile's byte offsets from its first row stay below 2^31
-  if (ld >= kMaxLd) return fail(DGF_EUNSUPPORTED, "%s: leading dimension %lld beyond this build's limit (< 2^23)", name, (long long)ld);
+  if (ld >= kMaxLd) return fail(DGF_EUNSUPPORTED, "%s: leading dimension %lld beyond the library's limit (< 2^23)", name, (long long)ld);
   return DGF_OK;
 }
 
 dgf_status check_dims(int64_t M, int64_t N, int64_t K) {
   if (M < 0 || N < 0 || K < 0) return fail(DGF_EINVAL, "negative dimension (M=%lld N=%lld K=%lld)", (long long)M, (long long)N, (long long)K);
   if (M > ((int64_t)1 << 21) || N > ((int64_t)1 << 30) || K > ((int64_t)1 << 23))
-    return fail(DGF_EUNSUPPORTED, "dimensions beyond this build's limits (M<=2^21, N<=2^30, K<=2^23)");
+    return fail(DGF_EUNSUPPORTED, "dimensions beyond the library's limits (M<=2^21, N<=2^30, K<=2^23)");
   return DGF_OK;
 }
 
@@ -473,7 +473,7 @@ void *g_scratch_ptr[kMaxDevices] = {};
 dgf_status static_scratch(void **out) {
   int dev = -1;
   DGF_TRY(hip_check(hipGetDevice(&dev), "hipGetDevice"));
-  if (dev < 0 || dev >= kMaxDevices) return fail(DGF_EUNSUPPORTED, "device %d beyond this build's %d devices", dev, kMaxDevices);
+  if (dev < 0 || dev >= kMaxDevices) return fail(DGF_EUNSUPPORTED, "device %d beyond the library's %d devices", dev, kMaxDevices);
   std::lock_guard<std::mutex> lock(g_scratch_mu);
   if (!g_scratch_ptr[dev]) {
     void *ptr = nullptr;

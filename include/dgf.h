@@ -63,7 +63,7 @@ extern "C" {
 typedef enum {
     DGF_OK = 0,
     DGF_EINVAL = 1,       /* null required pointer, bad size, leading dim or alignment */
-    DGF_EUNSUPPORTED = 2, /* a valid request this build does not implement (e.g. S=3) */
+    DGF_EUNSUPPORTED = 2, /* a valid request the library does not implement (e.g. S=3) */
     DGF_EWORKSPACE = 3,   /* workspace missing or smaller than the size query */
     DGF_EHIP = 4          /* a HIP runtime call or kernel launch failed */
 } dgf_status;
