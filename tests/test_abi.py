@@ -185,3 +185,37 @@ def test_static_forward_binding_checks_its_arguments(lib):
         binding.ffn_fwd_static(t16, t16, t16, t16, t16)
     with pytest.raises(ValueError, match="both g and u"):
         binding.ffn_fwd_static(tb, tb, tb, tb, tb, g=tb)
+
+
+C_CALLER = r"""
+#include <stdio.h>
+#include <string.h>
+#include "dgf.h"
+
+int main(void) {
+    if (dgf_abi_version() != 2 || dgf_leaf_size() != 64) return 1;
+    size_t ws = dgf_ffn_fwd_workspace(32, 4096, 12288);
+    /* a NULL input is refused before any HIP call */
+    dgf_status st = dgf_ffn_fwd(NULL, 4096, NULL, 4096, NULL, 4096, NULL, 12288, NULL, 4096,
+                                NULL, NULL, 0, 32, 4096, 12288, NULL, ws, NULL);
+    if (st != DGF_EINVAL || strlen(dgf_last_error()) == 0) return 2;
+    printf("%zu %d %s\n", ws, (int)st, dgf_last_error());
+    return 0;
+}
+"""
+
+
+def test_header_compiles_and_links_as_plain_c(lib, tmp_path):
+    # the boundary is a C ABI: the header compiles as C11 with warnings as
+    # errors, and a C program links the library and gets its validation
+    import subprocess
+    src = tmp_path / "caller.c"
+    src.write_text(C_CALLER)
+    exe = tmp_path / "caller"
+    libdir = os.path.dirname(binding.lib_path())
+    subprocess.run(["gcc", "-std=c11", "-Wall", "-Wextra", "-Werror", "-I", os.path.join(ROOT, "include"),
+                    str(src), "-L", libdir, "-ldgf", f"-Wl,-rpath,{libdir}", "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert out.returncode == 0, (out.returncode, out.stdout, out.stderr)
+    ws, st, msg = out.stdout.split(" ", 2)
+    assert int(ws) == lib.dgf_ffn_fwd_workspace(32, 4096, 12288) and int(st) == 1 and msg.strip()
