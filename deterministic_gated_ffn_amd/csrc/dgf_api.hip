@@ -662,7 +662,18 @@ dgf_status ffn_bwd_impl(int fmt, const void *dy, int64_t lddy, const void *x, in
   DGF_TRY(check_dims(M, I, H));
   DGF_TRY(check_dims(M, H, I));
   if (H == 0 || I == 0) return fail(DGF_EINVAL, "H and I must be positive (H=%lld I=%lld)", (long long)H, (long long)I);
-  if (M == 0) return ok();
+  if (M == 0) {
+    // no tokens: dX is empty, and each weight gradient is the tree over K = M = 0
+    // leaves, whose value is +0 (the same as a tree GEMM with K = 0)
+    DGF_TRY(check_mat("dw_gate", dw_gate, ld_dwg, I, H));
+    DGF_TRY(check_mat("dw_up", dw_up, ld_dwu, I, H));
+    DGF_TRY(check_mat("dw_down", dw_down, ld_dwd, H, I));
+    hipStream_t s0 = (hipStream_t)stream;
+    DGF_TRY(zero_mat((uint16_t *)dw_gate, ld_dwg, I, H, s0));
+    DGF_TRY(zero_mat((uint16_t *)dw_up, ld_dwu, I, H, s0));
+    DGF_TRY(zero_mat((uint16_t *)dw_down, ld_dwd, H, I, s0));
+    return ok();
+  }
   DGF_TRY(check_mat("dy", dy, lddy, M, H));
   DGF_TRY(check_mat("x", x, ldx, M, H));
   DGF_TRY(check_mat("g", g, ld_gu, M, I));

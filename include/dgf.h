@@ -144,7 +144,9 @@ dgf_status dgf_ffn_fwd_static(const void *x, int64_t ldx,
  * dw_gate [I,H] (ld_dwg), dw_up [I,H] (ld_dwu), dw_down [H,I] (ld_dwd), each
  * non-NULL.  At least one of dx and the two lanes must be given.  dW are fresh
  * tensors (no accumulation into existing gradients).
- * Workspace: dgf_ffn_bwd_workspace(M,H,I) bytes.  M = 0: DGF_OK, nothing launched.
+ * Workspace: dgf_ffn_bwd_workspace(M,H,I) bytes.  M = 0: dX is empty and the
+ * three dW are written as +0 (each is the tree over K = M = 0 leaves, as a
+ * tree GEMM with K = 0); no workspace is needed and nothing else is launched.
  */
 size_t dgf_ffn_bwd_workspace(int64_t M, int64_t H, int64_t I);
 dgf_status dgf_ffn_bwd(const void *dy, int64_t lddy,

@@ -265,8 +265,40 @@ def test_gemm_k_zero_and_m_zero():
     C = dgf.gemm_tree("NT", A, B)
     torch.cuda.synchronize()
     assert (C.float() == 0).all()
+    assert (inputs.bits(C) == 0).all()  # the empty tree is +0
     A0 = torch.zeros((0, 64), dtype=torch.bfloat16, device="cuda")
     assert dgf.gemm_tree("NT", A0, torch.zeros((8, 64), dtype=torch.bfloat16, device="cuda")).shape == (0, 8)
+
+
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float16])
+def test_ffn_with_no_tokens(dt):
+    # M = 0: the forward and dX are empty; each weight gradient is the tree over
+    # K = M = 0 leaves, +0 as in the oracle, written over whatever dW held
+    H, I = 40, 72
+    rng = np.random.default_rng(3)
+    w = [torch.from_numpy(rng.standard_normal(s).astype(np.float32) * 0.02).to(dt).cuda()
+         for s in ((I, H), (I, H), (H, I))]
+    x = torch.zeros((0, H), dtype=dt, device="cuda")
+    y, g, u = dgf.ffn_fwd(x, *w, training=True)
+    assert y.shape == (0, H) and g.shape == (0, I) and u.shape == (0, I)
+    dw = [torch.full(s, float("nan"), dtype=dt, device="cuda") for s in ((I, H), (I, H), (H, I))]
+    dx = torch.empty((0, H), dtype=dt, device="cuda")
+    L = dgf.load()
+    st = L.dgf_ffn_bwd_typed(None, H, None, H, None, None, I, w[0].data_ptr(), H, w[1].data_ptr(), H,
+                             w[2].data_ptr(), I, dx.data_ptr(), None, None, H, dw[0].data_ptr(), H,
+                             dw[1].data_ptr(), H, dw[2].data_ptr(), I, 0, H, I, None, 0,
+                             dgf.DGF_FP16 if dt == torch.float16 else dgf.DGF_BF16,
+                             torch.cuda.current_stream().cuda_stream)
+    assert st == 0, L.dgf_last_error()
+    r = dgf.ffn_bwd(torch.zeros((0, H), dtype=dt, device="cuda"), x, g, u, *w)
+    torch.cuda.synchronize()
+    hb = lambda shape: np.zeros(shape, np.uint16)
+    zx, zu = hb((0, H)), hb((0, I))
+    o = oracle.ffn_bwd(zx, zx, zu, zu, hb((I, H)), hb((I, H)), hb((H, I)),
+                       *([] if dt == torch.bfloat16 else ["fp16"]))
+    for got, name in zip(dw + [r["dW_gate"], r["dW_up"], r["dW_down"]], ["dW_gate", "dW_up", "dW_down"] * 2):
+        assert (inputs.bits(got) == np.asarray(o[name], np.uint16)).all(), name
+    assert r["dX"].shape == (0, H)
 
 
 # ---------------------------------------------------------------- activation
