@@ -93,6 +93,10 @@ def test_bwd_validation(lib):
     args[17] = FAKE
     args[-2] = 100
     assert lib.dgf_ffn_bwd(*args) == 3
+    # no tokens: the weight gradients are still written (+0), so their buffers are checked
+    empty = [None, 256, None, 256, None, None, 768, FAKE, 256, FAKE, 256, FAKE, 768,
+             None, None, None, 256, None, 256, FAKE, 256, FAKE, 768, 0, 256, 768, None, 0, None]
+    assert lib.dgf_ffn_bwd(*empty) == 1 and b"dw_gate" in lib.dgf_last_error()
 
 
 def test_combine_validation(lib):
