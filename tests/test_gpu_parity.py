@@ -764,3 +764,51 @@ def test_concurrent_calls_on_two_streams():
         assert (inputs.bits(y) == inputs.bits(y0)).all()
         for k in r0:
             assert (inputs.bits(r[k]) == inputs.bits(r0[k])).all(), k
+
+
+@pytest.mark.parametrize("M", [5, 32, 48, 200])
+@pytest.mark.parametrize("outs", ["lanes", "gate_lane_and_dx", "up_lane_only", "dx_only"])
+def test_bwd_dx_outputs_in_any_combination(M, outs):
+    # dx and the two lanes are each optional (at least one given): every
+    # combination writes exactly the outputs given, each equal to the oracle's
+    # (the lanes G and U, and dX = bf16(G + U) with the gate lane first)
+    H, I, ld_h, ld_i = 196, 516, 200, 520
+    rng = np.random.default_rng(M)
+    f = lambda r, c, s=1.0: F2B((rng.standard_normal((r, c)) * s).astype(np.float32))
+    x, dy = f(M, H), f(M, H)
+    wg, wu, wd = f(I, H, 0.02), f(I, H, 0.02), f(H, I, 0.02)
+    o = oracle.ffn_fwd(x, wg, wu, wd)
+    ob = oracle.ffn_bwd(dy, x, o["g"], o["u"], wg, wu, wd)
+
+    def padded(b, ld):
+        full = np.zeros((b.shape[0], ld), np.uint16)
+        full[:, :b.shape[1]] = b
+        return torch.from_numpy(full.view(np.int16)).cuda()
+
+    X, DY = padded(x, ld_h), padded(dy, ld_h)
+    G_, U_ = padded(o["g"], ld_i), padded(o["u"], ld_i)
+    WG, WU, WD = padded(wg, ld_h), padded(wu, ld_h), padded(wd, ld_i)
+    nan = lambda r, c: torch.full((r, c), 0x7FC0, dtype=torch.int16, device="cuda")
+    dx, gl, ul = nan(M, ld_h), nan(M, ld_h), nan(M, ld_h)
+    dwg, dwu, dwd = nan(I, ld_h), nan(I, ld_h), nan(H, ld_i)
+    want = {"lanes": ("G", "U"), "gate_lane_and_dx": ("G", "dX"), "up_lane_only": ("U",), "dx_only": ("dX",)}[outs]
+    bufs = {"dX": dx, "G": gl, "U": ul}
+    ptr = lambda k: bufs[k].data_ptr() if k in want else None
+    L = dgf.load()
+    ws = torch.empty(max(L.dgf_ffn_bwd_workspace(M, H, I), 16), dtype=torch.uint8, device="cuda")
+    st = L.dgf_ffn_bwd(DY.data_ptr(), ld_h, X.data_ptr(), ld_h, G_.data_ptr(), U_.data_ptr(), ld_i,
+                       WG.data_ptr(), ld_h, WU.data_ptr(), ld_h, WD.data_ptr(), ld_i,
+                       ptr("dX"), ptr("G"), ptr("U"), ld_h, dwg.data_ptr(), ld_h, dwu.data_ptr(), ld_h,
+                       dwd.data_ptr(), ld_i, M, H, I, ws.data_ptr(), ws.numel(),
+                       torch.cuda.current_stream().cuda_stream)
+    assert st == 0, L.dgf_last_error()
+    torch.cuda.synchronize()
+    host = lambda t, c: t.cpu().numpy().view(np.uint16)[:, :c]
+    for k, buf in bufs.items():
+        got = host(buf, H)
+        if k in want:
+            assert (got == ob[k]).all(), f"M={M} {outs} {k}: {(got != ob[k]).sum()} differ from the oracle"
+        else:
+            assert (got == 0x7FC0).all(), f"M={M} {outs}: {k} was not asked for but was written"
+    for k, buf, c in (("dW_gate", dwg, H), ("dW_up", dwu, H), ("dW_down", dwd, I)):
+        assert (host(buf, c) == ob[k]).all(), f"M={M} {outs} {k}"
